@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the masked, tiled fp32 matrix multiply.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark.  It holds no matrix-multiply arithmetic: it only draws operands and
+places them in (possibly padded) row-major buffers.
+
+Workload shapes follow the tiled matmul the pages build ("My Triton From
+Scratch, Part 14: Shared-Memory Tiles", section "The canonical source pattern":
+A is M x K, B is K x N, both row-major, C = A @ B).  Five shapes are used:
+
+  name        M      N      K      entries
+  small128    128    128    128    uniform[-1, 1)      one tile, several K tiles
+  ragged      1000   999    513    uniform[-1, 1)      every tile edge masked
+  square4096  4096   4096   4096   standard normal     compute-bound square
+  deepk       2048   256    16384  uniform[-1, 1)      long K loop
+  square8192  8192   8192   8192   standard normal     large square
+
+Generator: NumPy PCG64 (``numpy.random.default_rng(seed)``); A is drawn before
+B from one generator.  Uniform entries are ``uniform(-1, 1)`` cast to float32;
+normal entries are ``standard_normal(dtype=float32)``.  "Integer" operands
+(entries uniform in {-4, ..., 4}) make every partial sum of a product exactly
+representable in fp32, so any summation order gives the same bits.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class GemmConfig:
+    name: str
+    M: int
+    N: int
+    K: int
+    dist: str  # "uniform" or "normal"
+    seed: int
+    sampled: bool  # large shapes: the oracle checks sampled rows and columns
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def min_bytes(self) -> int:
+        return 4 * (self.M * self.K + self.K * self.N + self.M * self.N)
+
+
+CONFIGS: tuple[GemmConfig, ...] = (
+    GemmConfig("small128", 128, 128, 128, "uniform", 1, False),
+    GemmConfig("ragged", 1000, 999, 513, "uniform", 2, False),
+    GemmConfig("square4096", 4096, 4096, 4096, "normal", 3, True),
+    GemmConfig("deepk", 2048, 256, 16384, "uniform", 4, False),
+    GemmConfig("square8192", 8192, 8192, 8192, "normal", 5, True),
+)
+
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+
+# Seed offsets: sampled rows/columns use seed + 100, integer operands seed + 200.
+SAMPLE_SEED_OFFSET = 100
+INTEGER_SEED_OFFSET = 200
+
+
+def draw(rng: np.random.Generator, shape: tuple[int, int], dist: str) -> np.ndarray:
+    """One float32 matrix of the given distribution."""
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    if dist == "normal":
+        return rng.standard_normal(size=shape, dtype=np.float32)
+    if dist == "integer":
+        return rng.integers(-4, 5, size=shape).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def make_operands(M: int, N: int, K: int, dist: str, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Packed row-major A (M x K) and B (K x N), A drawn first."""
+    rng = np.random.default_rng(seed)
+    a = draw(rng, (M, K), dist)
+    b = draw(rng, (K, N), dist)
+    return a, b
+
+
+def config_operands(cfg: GemmConfig, integer: bool = False) -> tuple[np.ndarray, np.ndarray]:
+    if integer:
+        return make_operands(cfg.M, cfg.N, cfg.K, "integer", cfg.seed + INTEGER_SEED_OFFSET)
+    return make_operands(cfg.M, cfg.N, cfg.K, cfg.dist, cfg.seed)
+
+
+def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
+    """Sorted distinct indices in [0, n): always 0 and n-1, the rest drawn
+    without replacement from a seeded generator."""
+    if n <= count:
+        return np.arange(n, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    inner = rng.choice(np.arange(1, n - 1), size=count - 2, replace=False)
+    idx = np.concatenate([[0, n - 1], inner]).astype(np.int64)
+    return np.sort(idx)
+
+
+def sample_rows_cols(cfg: GemmConfig, count: int = 64) -> tuple[np.ndarray, np.ndarray]:
+    seed = cfg.seed + SAMPLE_SEED_OFFSET
+    return sample_indices(cfg.M, count, seed), sample_indices(cfg.N, count, seed + 1)
+
+
+def embed(mat: np.ndarray, ld: int, fill: float = float("nan"), extra_rows: int = 0) -> np.ndarray:
+    """Place a rows x cols matrix in a row-major buffer of leading dimension
+    ``ld`` (>= cols).  Gap columns and ``extra_rows`` trailing rows hold
+    ``fill``.  Returns the flat buffer; element (r, c) is at r * ld + c."""
+    rows, cols = mat.shape
+    assert ld >= cols
+    buf = np.full((rows + extra_rows) * ld, fill, dtype=np.float32)
+    view = buf[: rows * ld].reshape(rows, ld)
+    view[:, :cols] = mat
+    return buf
