@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked, LDS-tiled fp32 GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--variant auto] [--workload square4096]
+
+One step is one C = A @ B call through the C ABI on operands already resident
+in device memory (4096 x 4096 x 4096, entries normal(0,1), seed 3, by default).
+Prints ONE JSON line with the whole-job TFLOP/s (wall clock over K steps
+bracketed by device synchronisation), the dominant kernel's roofline position
+(its average duration from HIP events on the launch stream) and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and packed vector): 256 CUs x 256 flop/clk x 2.4 GHz
+METRIC = "fp32 GEMM TFLOP/s at 4096³ on 1 MI355X; % of fp32 peak"
+KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "lds_layout.hpp", "pad_choice.hpp"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "dense_fp32_tiled_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(variant_name: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = ROOT / "profiles" / f"{variant_name}_{workload}_traffic.txt"
+    if not path.exists():
+        return None
+    fields = {}
+    for line in path.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--variant", default="auto", help="auto, mfma, valu, mfma_stages1, mfma_nopad, mfma_scalar")
+    ap.add_argument("--workload", default="square4096")
+    ap.add_argument("--cpu-sample-rows", type=int, default=512,
+                    help="rows of C the CPU oracle computes for its baseline (0 = skip)")
+    ap.add_argument("--ablations", default="",
+                    help="also time every variant and write one JSON line per variant to this file")
+    return ap.parse_args(argv)
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the GEMM kernel is measured on "
+              "one GPU's share; multi-GPU sharding is not built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_fp32_tiled_amd as dft
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    names = {v: k for k, v in dft.VARIANT_NAMES.items()}
+    variant = names[args.variant]
+    cfg = workloads.CONFIG_BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    a_np, b_np = workloads.config_operands(cfg)
+    a = torch.from_numpy(a_np).to(dev)
+    b = torch.from_numpy(b_np).to(dev)
+    c = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    M, N, K = cfg.M, cfg.N, cfg.K
+    pa, pb, pc = a.data_ptr(), b.data_ptr(), c.data_ptr()
+
+    def step(v=variant):
+        st = dft.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, handle, v)
+        if st != dft.GEMM_OK:
+            raise dft.GemmError(st, "gemm_f32_ex")
+
+    def time_variant(v, steps, warmup):
+        for _ in range(warmup):
+            step(v)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(v)
+        torch.cuda.synchronize()
+        wall_s = (time.perf_counter() - t0) / steps
+        # per-launch durations from HIP events recorded on the launch stream
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            step(v)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        durs = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in ev)
+        return wall_s, sum(durs) / len(durs), durs[len(durs) // 2], durs[0]
+
+    wall_s, kern_avg_s, kern_med_s, kern_min_s = time_variant(variant, args.steps, args.warmup)
+    tflops = cfg.flops / wall_s / 1e12
+    achieved = cfg.flops / kern_avg_s / 1e12
+    tile = dft.gemm_f32_tile_config(variant)
+    run_name = dft.VARIANT_NAMES[tile["variant"] if variant != dft.VARIANT_AUTO else dft.VARIANT_MFMA]
+
+    # correctness spot check and CPU baseline: the oracle on a bounded row sample
+    cpu_baseline = None
+    parity = None
+    if args.cpu_sample_rows > 0:
+        import oracle
+
+        rows = workloads.sample_indices(cfg.M, min(args.cpu_sample_rows, cfg.M),
+                                        cfg.seed + workloads.SAMPLE_SEED_OFFSET)
+        threads = oracle.host_threads()
+        t0 = time.perf_counter()
+        cref, den = oracle.reference(a_np, b_np, rows=rows, threads=threads)
+        cpu_s = time.perf_counter() - t0
+        cpu_flops = 2.0 * len(rows) * cfg.N * cfg.K
+        cpu_baseline = {
+            "value": cpu_flops / cpu_s / 1e12,
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {cfg.M} rows of C (all {cfg.N} columns, K={cfg.K}), seeded sample; "
+                      f"{cpu_s:.2f} s wall on {threads} threads",
+        }
+        c_rows = c[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        parity = {"rows_checked": int(len(rows)), "max_normalised_error": oracle.normalised_error(c_rows, cref, den)}
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: C[{M},{N}] = A[{M},{K}] @ B[{K},{N}], row-major fp32, "
+                        f"entries {'normal(0,1)' if cfg.dist == 'normal' else 'uniform[-1,1)'}, seed {cfg.seed}",
+            "M": M, "N": N, "K": K,
+            "variant": run_name,
+            "tile": f"{tile['bm']}x{tile['bn']}x{tile['bk']}, {tile['threads']} threads, "
+                    f"{tile['stages']} LDS stages, pads A/B {tile['a_pad']}/{tile['b_pad']}",
+            "fraction_of_fp32_peak": tflops / PEAK_FP32_TFLOPS,
+        },
+        "roofline": {
+            "bound": "mfma" if run_name.startswith("mfma") else "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS,
+            "traffic": measured_traffic(run_name, cfg.name),
+            "kernel_ms": {"avg": kern_avg_s * 1e3, "median": kern_med_s * 1e3, "min": kern_min_s * 1e3},
+            "flops_per_launch": cfg.flops,
+        },
+        "cpu_baseline": cpu_baseline,
+        "parity_sample": parity,
+    }
+
+    if args.ablations:
+        with open(args.ablations, "w") as f:
+            for v in range(1, dft.VARIANT_COUNT):
+                w, kavg, kmed, kmin = time_variant(v, args.steps, args.warmup)
+                f.write(json.dumps({"variant": dft.VARIANT_NAMES[v], "workload": cfg.name,
+                                    "tflops_wall": cfg.flops / w / 1e12, "tflops_kernel_avg": cfg.flops / kavg / 1e12,
+                                    "kernel_ms_avg": kavg * 1e3, "kernel_ms_median": kmed * 1e3,
+                                    "kernel_ms_min": kmin * 1e3}) + "\n")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+"""Python binding for the gfx950 masked, LDS-tiled fp32 GEMM.
+
+Argument marshalling only: every function below forwards to the entry point of
+the same name in libdense_fp32_tiled.so (declared in include/dense_fp32_tiled.h)
+through ctypes.  ``matmul`` is a convenience wrapper that takes torch tensors,
+passes their device pointers, row pitches and the current HIP stream, and
+raises GemmError on a non-zero status.  There is no fallback: if the HIP
+library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PKG_DIR = Path(__file__).resolve().parent
+LIB_PATH = PKG_DIR / "libdense_fp32_tiled.so"
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_DIM = -1
+GEMM_ERR_INVALID_LD = -2
+GEMM_ERR_NULL = -3
+GEMM_ERR_ALIAS = -4
+GEMM_ERR_UNSUPPORTED = -5
+GEMM_ERR_CONFIG = -6
+GEMM_ERR_HIP = -7
+GEMM_ERR_TOO_LARGE = -8
+
+VARIANT_AUTO = 0
+VARIANT_MFMA = 1
+VARIANT_VALU = 2
+VARIANT_MFMA_STAGES1 = 3
+VARIANT_MFMA_NOPAD = 4
+VARIANT_MFMA_SCALAR = 5
+VARIANT_COUNT = 6
+VARIANT_NAMES = {
+    VARIANT_AUTO: "auto",
+    VARIANT_MFMA: "mfma",
+    VARIANT_VALU: "valu",
+    VARIANT_MFMA_STAGES1: "mfma_stages1",
+    VARIANT_MFMA_NOPAD: "mfma_nopad",
+    VARIANT_MFMA_SCALAR: "mfma_scalar",
+}
+
+# Every symbol the public header declares.
+EXPORTS = (
+    "gemm_f32",
+    "gemm_f32_ex",
+    "gemm_f32_tile_config",
+    "gemm_f32_status_string",
+    "gemm_lds_layout",
+    "gemm_lds_offset",
+    "gemm_lds_bank",
+    "gemm_lds_conflict_degree",
+    "gemm_lds_page_pad",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = gemm_f32_status_string(status)
+        super().__init__(f"{what}: {msg} (status {status})" if what else f"{msg} (status {status})")
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "variant", "bm", "bn", "bk", "threads", "wave_size", "tm", "tn", "stages", "barriers_per_tile",
+        "a_rows", "a_cols", "a_pad", "a_row_stride", "a_stage_elems",
+        "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
+        "lds_bytes", "vec_width", "lds_banks", "a_transposed")]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library(path: Path | None = None):
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"{p} is not built; run `python -m dense_fp32_tiled_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.gemm_f32.argtypes = gemm_args
+    lib.gemm_f32.restype = ctypes.c_int
+    lib.gemm_f32_ex.argtypes = gemm_args + [ctypes.c_int]
+    lib.gemm_f32_ex.restype = ctypes.c_int
+    lib.gemm_f32_tile_config.argtypes = [ctypes.c_int, ctypes.POINTER(TileConfig)]
+    lib.gemm_f32_tile_config.restype = ctypes.c_int
+    lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
+    lib.gemm_f32_status_string.restype = ctypes.c_char_p
+    p32 = ctypes.POINTER(i32)
+    lib.gemm_lds_layout.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
+    lib.gemm_lds_layout.restype = ctypes.c_int
+    lib.gemm_lds_offset.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.gemm_lds_offset.restype = i64
+    lib.gemm_lds_bank.argtypes = [i64, i32]
+    lib.gemm_lds_bank.restype = i32
+    lib.gemm_lds_conflict_degree.argtypes = [ctypes.POINTER(i64), i32, i32, i32, i32]
+    lib.gemm_lds_conflict_degree.restype = i32
+    lib.gemm_lds_page_pad.argtypes = [i32, i32, i32]
+    lib.gemm_lds_page_pad.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+# ---- entry points, same names as the C ABI --------------------------------------
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return library().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream=None, variant=VARIANT_AUTO) -> int:
+    return library().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, variant)
+
+
+def gemm_f32_tile_config(variant: int) -> dict:
+    cfg = TileConfig()
+    st = library().gemm_f32_tile_config(variant, ctypes.byref(cfg))
+    if st != GEMM_OK:
+        raise GemmError(st, f"gemm_f32_tile_config({variant})")
+    return cfg.as_dict()
+
+
+def gemm_f32_status_string(status: int) -> str:
+    return library().gemm_f32_status_string(status).decode()
+
+
+def gemm_lds_layout(rows: int, cols: int, pad: int, stages: int):
+    """(status, row_stride, stage_elems, total_elems, bytes)."""
+    out = [ctypes.c_int32(-1) for _ in range(4)]
+    st = library().gemm_lds_layout(rows, cols, pad, stages, *[ctypes.byref(x) for x in out])
+    return (st, *[x.value for x in out])
+
+
+def gemm_lds_offset(rows, cols, pad, stages, stage, row, col) -> int:
+    return library().gemm_lds_offset(rows, cols, pad, stages, stage, row, col)
+
+
+def gemm_lds_bank(word_offset: int, banks: int) -> int:
+    return library().gemm_lds_bank(word_offset, banks)
+
+
+def gemm_lds_conflict_degree(lane_words, width: int, banks: int, group: int) -> int:
+    arr = (ctypes.c_int64 * len(lane_words))(*lane_words)
+    return library().gemm_lds_conflict_degree(arr, len(lane_words), width, banks, group)
+
+
+def gemm_lds_page_pad(columns: int, simultaneous_rows: int, banks: int = 32) -> int:
+    return library().gemm_lds_page_pad(columns, simultaneous_rows, banks)
+
+
+# ---- torch convenience -------------------------------------------------------------
+def _operand(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return t.data_ptr(), max(ld, cols, 1)
+
+
+def matmul(a, b, out=None, variant: int = VARIANT_AUTO, stream=None):
+    """C = a @ b on the GPU with the HIP kernels.  a: M x K, b: K x N, float32,
+    unit column stride (row pitch may exceed the width).  Enqueued on `stream`
+    (a torch.cuda.Stream or raw handle) or torch's current stream."""
+    import torch
+
+    pa, lda = _operand(a, "a")
+    pb, ldb = _operand(b, "b")
+    M, K = a.shape
+    if b.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.shape != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    pc, ldc = _operand(out, "out")
+    if stream is None:
+        handle = torch.cuda.current_stream(a.device).cuda_stream
+    elif isinstance(stream, int):
+        handle = stream
+    else:
+        handle = stream.cuda_stream
+    with torch.cuda.device(a.device):
+        st = gemm_f32_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, handle, variant)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_f32_ex")
+    return out

@@ -1,0 +1,420 @@
+// gemm_kernels.hpp -- gfx950 kernels for C[M,N] = A[M,K] @ B[K,N], fp32.
+//
+// Structure common to every kernel (one workgroup per BM x BN output tile):
+//   accumulators = 0
+//   prologue: masked cooperative load of K tile 0 -> registers -> LDS stage 0, barrier
+//   for t in [0, T):                                 T = ceil(K / BK)
+//       issue the global loads of K tile t+1 into registers (if any)
+//       inner product over LDS stage t & 1
+//       write the registers into LDS stage (t+1) & 1, barrier
+//   masked store of the accumulators
+//
+// The tiling, masks and zero fill are those of "My Triton From Scratch, Part
+// 14: Shared-Memory Tiles" (sections "The canonical source pattern",
+// "Cooperative copy mapping", "Zero-filled boundary tiles", "Synchronizing
+// the block"); the padded, two-stage LDS layout and the single barrier per K
+// tile are those of "Part 18: Shared Memory Optimization" (sections "A shared
+// buffer needs a physical row stride", "One stage versus two stages", "What
+// ping-pong changes about synchronization").  Unlike Part 18, the global loads
+// of tile t+1 are in flight while tile t is multiplied.
+//
+// Why one barrier per tile is enough with two stages: the LDS writes of
+// iteration t go to stage (t+1)&1, last read during iteration t-1, and every
+// wave finished those reads before the barrier that ended iteration t-1.  The
+// reads of iteration t hit stage t&1, whose writes (iteration t-1 or the
+// prologue) all precede that same barrier.  The loop bounds are uniform across
+// the workgroup, so every wave reaches every barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_layout.hpp"
+
+namespace dft {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = kWaveLanes;
+
+// --------------------------------------------------------------------------
+// A tile of a row-major global matrix: rows [row0, row0 + ROWS) and columns
+// [col0, col0 + COLS), read under the mask (row < row_bound) & (col < col_bound)
+// with zero fill.  Threads map to VEC-wide column groups in row-major order
+// (consecutive threads take consecutive column groups of a row), so each
+// wavefront reads whole row segments.
+template <int ROWS, int COLS, int THREADS, int VEC>
+struct TileLoader {
+    static_assert(VEC == 1 || VEC == 4, "VEC must be 1 or 4");
+    static_assert(COLS % VEC == 0, "tile width must be a multiple of VEC");
+    static constexpr int VCOLS = COLS / VEC;
+    static constexpr int SLOTS = ROWS * VCOLS;
+    static_assert(SLOTS % THREADS == 0, "tile must split evenly over the threads");
+    static constexpr int PER_THREAD = SLOTS / THREADS;
+
+    float v[PER_THREAD][VEC];
+
+    __device__ static int slot_row(int tid, int i) { return (tid + i * THREADS) / VCOLS; }
+    __device__ static int slot_col(int tid, int i) { return ((tid + i * THREADS) % VCOLS) * VEC; }
+
+    // `tile` points at element (row0, col0); rows_left = row_bound - row0 and
+    // cols_left = col_bound - col0 (either may be <= 0: then all zero).  Both
+    // are uniform over the workgroup, so the branch between the unmasked path
+    // (the whole tile is in range) and the per-element masked path is a scalar
+    // branch; only edge tiles take the masked path.
+    __device__ void load(const float* __restrict__ tile, int64_t ld, int64_t rows_left,
+                         int64_t cols_left, int tid) {
+        if (rows_left >= ROWS && cols_left >= COLS) {
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                const float* p = tile + (int64_t)slot_row(tid, i) * ld + slot_col(tid, i);
+                if constexpr (VEC == 4) {
+                    const floatx4 x = *reinterpret_cast<const floatx4*>(p);
+                    v[i][0] = x[0]; v[i][1] = x[1]; v[i][2] = x[2]; v[i][3] = x[3];
+                } else {
+                    v[i][0] = *p;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                const int r = slot_row(tid, i);
+                const int c = slot_col(tid, i);
+                const float* p = tile + (int64_t)r * ld + c;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    v[i][e] = (r < rows_left && c + e < cols_left) ? p[e] : 0.0f;
+            }
+        }
+    }
+
+    // Row-major LDS destination: element (r, c) of the tile -> Tile::offset(stage, r, c).
+    template <class Tile>
+    __device__ void store(float* lds, int stage, int tid) const {
+        static_assert(Tile::rows == ROWS && Tile::cols == COLS, "LDS tile shape mismatch");
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            float* q = lds + Tile::offset(stage, slot_row(tid, i), slot_col(tid, i));
+            if constexpr (VEC == 4) {
+                *reinterpret_cast<floatx4*>(q) = floatx4{v[i][0], v[i][1], v[i][2], v[i][3]};
+            } else {
+                *q = v[i][0];
+            }
+        }
+    }
+
+    // Transposed LDS destination: element (r, c) -> Tile::offset(stage, c, r).
+    template <class Tile>
+    __device__ void store_transposed(float* lds, int stage, int tid) const {
+        static_assert(Tile::rows == COLS && Tile::cols == ROWS, "LDS tile shape mismatch");
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int r = slot_row(tid, i), c = slot_col(tid, i);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) lds[Tile::offset(stage, c + e, r)] = v[i][e];
+        }
+    }
+};
+
+// Workgroup -> output tile.  Plain row-major order over the tile grid.
+struct TileCoord {
+    int64_t m0, n0;
+};
+__device__ inline TileCoord tile_of_block(int64_t tiles_n, int bm, int bn) {
+    const int64_t b = blockIdx.x;
+    return TileCoord{(b / tiles_n) * bm, (b % tiles_n) * bn};
+}
+
+// --------------------------------------------------------------------------
+// Matrix-core variant.  4 wavefronts as WAVES_M x WAVES_N; each wavefront owns
+// a WM x WN sub-tile made of 32x32 blocks computed by v_mfma_f32_32x32x2_f32.
+//
+// Operand layout of v_mfma_f32_32x32x2_f32 (lane l, h = l / 32, r = l % 32):
+//   A operand: A[row r][k h],   B operand: B[k h][col r],
+//   result register v (0..15): D[row 8*(v/4) + 4*h + v%4][col r].
+// Within a BK tile, lane half h reduces the k range [h*BK/2, (h+1)*BK/2): MFMA
+// step j consumes k = h*BK/2 + j for half h.  Every k of the tile is used
+// exactly once per output element (a permutation of the summation order),
+// and each lane's A values for one tile are BK/2 consecutive floats of one
+// LDS row, read with 16-byte loads.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int PADA_, int PADB_, int VEC_>
+struct MfmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int STAGES = STAGES_, PADA = PADA_, PADB = PADB_, VEC = VEC_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
+    static constexpr int MI = WM / 32, NI = WN / 32;
+    static constexpr int KH = BK / 2;  // k values per lane half per tile
+    // Register budget: 4 waves per SIMD (<= 128 VGPRs) for the 16-byte load
+    // path, so that four 256-thread workgroups fit on a CU; the 4-byte load
+    // path holds 4x more load registers and is limited to 2 waves per SIMD.
+    static constexpr int MIN_WAVES = VEC == 4 ? 4 : 2;
+    using TileA = LdsTile<BM, BK, PADA, STAGES>;
+    using TileB = LdsTile<BK, BN, PADB, STAGES>;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
+    static_assert(KH % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
+    static_assert(TileB::row_stride % VEC == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
+    static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel(
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
+    using TileA = typename Cfg::TileA;
+    using TileB = typename Cfg::TileB;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, KH = Cfg::KH;
+    constexpr int MI = Cfg::MI, NI = Cfg::NI, THREADS = Cfg::THREADS;
+
+    __shared__ __attribute__((aligned(16))) float lds_a[TileA::total_elems];
+    __shared__ __attribute__((aligned(16))) float lds_b[TileB::total_elems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int h = lane / 32, r = lane % 32;
+
+    const TileCoord tc = tile_of_block(tiles_n, BM, BN);
+    const int64_t m0 = tc.m0, n0 = tc.n0;
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    TileLoader<BM, BK, THREADS, Cfg::VEC> ldr_a;
+    TileLoader<BK, BN, THREADS, Cfg::VEC> ldr_b;
+    const float* a_tile = A + m0 * lda;  // advances by BK columns per K tile
+    const float* b_tile = B + n0;        // advances by BK rows per K tile
+    const int64_t T = (K + BK - 1) / BK;
+
+    auto load_tile = [&](int64_t t) {
+        const int64_t k0 = t * BK;
+        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, tid);
+        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, tid);
+    };
+    auto multiply = [&](int stage) {
+        floatx4 af[MI][KH / 4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int q = 0; q < KH / 4; ++q)
+                af[i][q] = *reinterpret_cast<const floatx4*>(
+                    lds_a + TileA::offset(stage, wm0 + i * 32 + r, h * KH + 4 * q));
+#pragma unroll
+        for (int j = 0; j < KH; ++j) {
+            float bf[NI];
+#pragma unroll
+            for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, h * KH + j, wn0 + n * 32 + r)];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n)
+                    acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][j / 4][j % 4], bf[n], acc[i][n], 0, 0, 0);
+        }
+    };
+
+    if constexpr (Cfg::STAGES == 2) {
+        if (T > 0) {
+            load_tile(0);
+            ldr_a.template store<TileA>(lds_a, 0, tid);
+            ldr_b.template store<TileB>(lds_b, 0, tid);
+        }
+        __syncthreads();
+        for (int64_t t = 0; t < T; ++t) {
+            const int s = (int)(t & 1);
+            const bool more = t + 1 < T;
+            if (more) load_tile(t + 1);
+            multiply(s);
+            if (more) {
+                ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
+                ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
+            }
+            __syncthreads();
+        }
+    } else {
+        // One stage: write, barrier, read, barrier (the two-barrier protocol).
+        for (int64_t t = 0; t < T; ++t) {
+            load_tile(t);
+            ldr_a.template store<TileA>(lds_a, 0, tid);
+            ldr_b.template store<TileB>(lds_b, 0, tid);
+            __syncthreads();
+            multiply(0);
+            __syncthreads();
+        }
+    }
+
+    // Store: unmasked when the whole BM x BN tile is in range (a uniform
+    // branch), else under the mask rows < M and columns < N.  For a fixed
+    // result register, lanes 0-31 write 32 consecutive floats of one row.
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            const int64_t gn = n0 + wn0 + n * 32 + r;
+            const int64_t gm0 = m0 + wm0 + i * 32 + 4 * h;
+            float* cp = C + gm0 * ldc + gn;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dr = 8 * (v / 4) + (v % 4);
+                if (full || (gm0 + dr < M && gn < N)) cp[dr * ldc] = acc[i][n][v];
+            }
+        }
+}
+
+// --------------------------------------------------------------------------
+// Vector-ALU variant.  THREADS = (BM/TM) x (BN/TN) threads; thread (ty, tx)
+// owns a TM x TN register tile made of two TM/2-row halves (rows ty*TM/2 and
+// BM/2 + ty*TM/2) and two TN/2-column halves, so that neighbouring threads
+// read neighbouring 16-byte LDS words.  A is stored k-major in LDS (At[k][m]),
+// B row-major (B[k][n]); per k each thread reads TM + TN values with 16-byte
+// loads and issues TM * TN FMAs.
+template <int BM_, int BN_, int BK_, int TM_, int TN_, int STAGES_, int PADA_, int PADB_, int VEC_>
+struct ValuCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_;
+    static constexpr int STAGES = STAGES_, PADA = PADA_, PADB = PADB_, VEC = VEC_;
+    static constexpr int THREADS_M = BM / TM, THREADS_N = BN / TN;
+    static constexpr int THREADS = THREADS_M * THREADS_N;
+    static constexpr int MIN_WAVES = 2;
+    using TileA = LdsTile<BK, BM, PADA, STAGES>;  // k-major
+    using TileB = LdsTile<BK, BN, PADB, STAGES>;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    static_assert(TM == 8 && TN == 8, "register tile is two 4-wide halves per axis");
+    static_assert(TileA::row_stride % 4 == 0 && TileB::row_stride % 4 == 0, "16-byte LDS reads");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel(
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
+    using TileA = typename Cfg::TileA;
+    using TileB = typename Cfg::TileB;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, THREADS = Cfg::THREADS;
+
+    __shared__ __attribute__((aligned(16))) float lds_a[TileA::total_elems];
+    __shared__ __attribute__((aligned(16))) float lds_b[TileB::total_elems];
+
+    const int tid = threadIdx.x;
+    const int ty = tid / Cfg::THREADS_N, tx = tid % Cfg::THREADS_N;
+    const TileCoord tc = tile_of_block(tiles_n, BM, BN);
+    const int64_t m0 = tc.m0, n0 = tc.n0;
+
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    TileLoader<BM, BK, THREADS, Cfg::VEC> ldr_a;
+    TileLoader<BK, BN, THREADS, Cfg::VEC> ldr_b;
+    const float* a_tile = A + m0 * lda;
+    const float* b_tile = B + n0;
+    const int64_t T = (K + BK - 1) / BK;
+    const int am = ty * 4, bn = tx * 4;
+
+    auto load_tile = [&](int64_t t) {
+        const int64_t k0 = t * BK;
+        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, tid);
+        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, tid);
+    };
+    // Per k: four 16-byte LDS reads (TM values of A, TN values of B) and
+    // TM * TN FMAs.  The reads for k+1 are issued before the FMAs of k.  After
+    // each k an empty asm statement that takes every accumulator as an operand
+    // and clobbers memory pins the FMAs of k before the reads of k+2: without
+    // it the compiler hoists all BK steps' reads (BK * 16 registers) and spills.
+    auto multiply = [&](int stage) {
+        floatx4 cur[4], nxt[4];
+        auto read_k = [&](int k, floatx4* x) {
+            x[0] = *reinterpret_cast<const floatx4*>(lds_a + TileA::offset(stage, k, am));
+            x[1] = *reinterpret_cast<const floatx4*>(lds_a + TileA::offset(stage, k, BM / 2 + am));
+            x[2] = *reinterpret_cast<const floatx4*>(lds_b + TileB::offset(stage, k, bn));
+            x[3] = *reinterpret_cast<const floatx4*>(lds_b + TileB::offset(stage, k, BN / 2 + bn));
+        };
+        read_k(0, cur);
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            if (k + 1 < BK) read_k(k + 1, nxt);
+            const float a[8] = {cur[0][0], cur[0][1], cur[0][2], cur[0][3], cur[1][0], cur[1][1], cur[1][2], cur[1][3]};
+            const float b[8] = {cur[2][0], cur[2][1], cur[2][2], cur[2][3], cur[3][0], cur[3][1], cur[3][2], cur[3][3]};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]), "+v"(acc[i][3]),
+                             "+v"(acc[i][4]), "+v"(acc[i][5]), "+v"(acc[i][6]), "+v"(acc[i][7])::"memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+        }
+    };
+
+    if constexpr (Cfg::STAGES == 2) {
+        if (T > 0) {
+            load_tile(0);
+            ldr_a.template store_transposed<TileA>(lds_a, 0, tid);
+            ldr_b.template store<TileB>(lds_b, 0, tid);
+        }
+        __syncthreads();
+        for (int64_t t = 0; t < T; ++t) {
+            const int s = (int)(t & 1);
+            const bool more = t + 1 < T;
+            if (more) load_tile(t + 1);
+            multiply(s);
+            if (more) {
+                ldr_a.template store_transposed<TileA>(lds_a, s ^ 1, tid);
+                ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int64_t t = 0; t < T; ++t) {
+            load_tile(t);
+            ldr_a.template store_transposed<TileA>(lds_a, 0, tid);
+            ldr_b.template store<TileB>(lds_b, 0, tid);
+            __syncthreads();
+            multiply(0);
+            __syncthreads();
+        }
+    }
+
+    // Masked store; 16-byte stores where the four columns are in range and aligned.
+    const bool vec_ok = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t gm = m0 + (i < 4 ? am + i : BM / 2 + am + i - 4);
+        if (gm >= M) continue;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t gn = n0 + (half == 0 ? bn : BN / 2 + bn);
+            float* p = C + gm * ldc + gn;
+            if (vec_ok && gn + 4 <= N) {
+                *reinterpret_cast<floatx4*>(p) =
+                    floatx4{acc[i][4 * half], acc[i][4 * half + 1], acc[i][4 * half + 2], acc[i][4 * half + 3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gn + e < N) p[e] = acc[i][4 * half + e];
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// K == 0: C's M x N region is an empty sum.
+__global__ void zero_fill_kernel(int64_t M, int64_t N, float* __restrict__ C, int64_t ldc) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x)
+        C[(i / N) * ldc + (i % N)] = 0.0f;
+}
+
+}  // namespace dft

@@ -1,0 +1,112 @@
+// lds_layout.hpp -- LDS tile layout and bank model (host and device, constexpr).
+//
+// A tile staged in LDS has a logical shape (rows x cols), a physical row
+// stride (cols + pad) and a number of stages.  Producers (the cooperative
+// global->LDS copy) and consumers (the inner product) both address it through
+// LdsTile::offset, so a change of padding or staging cannot desynchronise them
+// ("My Triton From Scratch, Part 18: Shared Memory Optimization", sections "A
+// shared buffer needs a physical row stride" and "Every producer and consumer
+// must use the new stride").
+//
+// The bank model generalises the pages' one-warp rule (32 banks,
+// bank = word % 32, section "Why shared-memory banks matter"): the bank count
+// and the number of lanes the LDS services together per access width are
+// parameters, and the conflict degree of an instruction is computed from the
+// actual lane -> address pattern, for reads and writes alike.
+#pragma once
+
+#include <stdint.h>
+
+namespace dft {
+
+constexpr int kWaveLanes = 64;  // lanes per wavefront on gfx950
+
+// --------------------------------------------------------------------------
+// Physical layout of one staged tile.
+struct LdsLayout {
+    int rows, cols, pad, stages;
+
+    constexpr bool valid() const { return rows > 0 && cols > 0 && pad >= 0 && stages > 0; }
+    constexpr int row_stride() const { return cols + pad; }
+    constexpr int stage_elems() const { return rows * row_stride(); }
+    constexpr int total_elems() const { return stages * stage_elems(); }
+    constexpr int bytes() const { return total_elems() * 4; }
+    constexpr int offset(int stage, int row, int col) const {
+        return stage * stage_elems() + row * row_stride() + col;
+    }
+};
+
+template <int Rows, int Cols, int Pad, int Stages>
+struct LdsTile {
+    static_assert(Rows > 0 && Cols > 0 && Pad >= 0 && Stages > 0, "invalid LDS tile");
+    static constexpr int rows = Rows, cols = Cols, pad = Pad, stages = Stages;
+    static constexpr int row_stride = Cols + Pad;
+    static constexpr int stage_elems = Rows * row_stride;
+    static constexpr int total_elems = Stages * stage_elems;
+    static constexpr int bytes = total_elems * 4;
+    static constexpr LdsLayout layout() { return LdsLayout{Rows, Cols, Pad, Stages}; }
+
+    __host__ __device__ static constexpr int offset(int stage, int row, int col) {
+        return stage * stage_elems + row * row_stride + col;
+    }
+};
+
+// --------------------------------------------------------------------------
+// Bank model.
+struct LdsGeometry {
+    int banks;          // 4-byte banks
+    int lanes_b32;      // lanes serviced together by a 4-byte access
+    int lanes_b64;      // ... by an 8-byte access
+    int lanes_b128;     // ... by a 16-byte access
+
+    constexpr int group_for_width(int width_words) const {
+        return width_words == 1 ? lanes_b32 : width_words == 2 ? lanes_b64 : lanes_b128;
+    }
+};
+
+// gfx950 LDS geometry the kernels' padding is derived for: 64 banks of 4
+// bytes, a 4/8/16-byte access serviced 64/32/16 lanes at a time (256 bytes
+// per pass).  This is an assumption about CDNA4, not a figure from the pages
+// (their 32 banks are NVIDIA's); the LDS probe kernel measures it.
+constexpr LdsGeometry kGfx950Lds{64, 64, 32, 16};
+
+constexpr int bank_of(int64_t word, int banks) { return (int)(((word % banks) + banks) % banks); }
+
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// The pages' rule: a stride of `columns` words reaches banks/gcd(columns,banks)
+// distinct banks before repeating; pad one word when more rows are read at once.
+constexpr int page_pad(int columns, int simultaneous_rows, int banks) {
+    return simultaneous_rows > banks / gcd_int(columns, banks) ? 1 : 0;
+}
+
+// Conflict degree of one access pattern (see gemm_lds_conflict_degree in the
+// public header for the definition).  `addr(l)` gives lane l's first dword.
+// Limits: group * width <= 256 dwords, banks <= 128; returns -1 beyond them.
+template <class Addr>
+constexpr int conflict_degree(Addr addr, int lanes, int width, int banks, int group) {
+    if (lanes < 1 || width < 1 || banks < 1 || banks > 128 || group < 1 || group * width > 256) return -1;
+    int worst = 1;
+    for (int g0 = 0; g0 < lanes; g0 += group) {
+        const int g1 = g0 + group < lanes ? g0 + group : lanes;
+        int64_t words[256] = {};
+        int n = 0;
+        for (int l = g0; l < g1; ++l) {
+            for (int w = 0; w < width; ++w) {
+                const int64_t word = addr(l) + w;
+                bool seen = false;
+                for (int i = 0; i < n; ++i)
+                    if (words[i] == word) { seen = true; break; }
+                if (!seen) words[n++] = word;
+            }
+        }
+        int count[128] = {};
+        for (int i = 0; i < n; ++i) {
+            const int b = bank_of(words[i], banks);
+            if (++count[b] > worst) worst = count[b];
+        }
+    }
+    return worst;
+}
+
+}  // namespace dft

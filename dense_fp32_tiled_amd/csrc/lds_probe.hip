@@ -1,0 +1,101 @@
+// lds_probe.hip -- timing of one LDS read pattern (see include/lds_probe.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_probe.h"
+
+namespace {
+
+struct Pattern {
+    int32_t byte_addr[64];
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16 reads per asm block, then a wait for all of them, so the outputs are
+// defined when the block ends (early-clobber keeps them off the address
+// register).  Reusing four destinations is a write-after-write on loads that
+// complete in order.
+template <int WIDTH>
+__device__ inline void read16(uint32_t addr, float& sink) {
+    if constexpr (WIDTH == 1) {
+        float r0, r1, r2, r3;
+        asm volatile(
+            "ds_read_b32 %0, %4\n ds_read_b32 %1, %4\n ds_read_b32 %2, %4\n ds_read_b32 %3, %4\n"
+            "ds_read_b32 %0, %4\n ds_read_b32 %1, %4\n ds_read_b32 %2, %4\n ds_read_b32 %3, %4\n"
+            "ds_read_b32 %0, %4\n ds_read_b32 %1, %4\n ds_read_b32 %2, %4\n ds_read_b32 %3, %4\n"
+            "ds_read_b32 %0, %4\n ds_read_b32 %1, %4\n ds_read_b32 %2, %4\n ds_read_b32 %3, %4\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+            : "v"(addr)
+            : "memory");
+        sink += r0 + r1 + r2 + r3;
+    } else if constexpr (WIDTH == 2) {
+        f32x2 r0, r1, r2, r3;
+        asm volatile(
+            "ds_read_b64 %0, %4\n ds_read_b64 %1, %4\n ds_read_b64 %2, %4\n ds_read_b64 %3, %4\n"
+            "ds_read_b64 %0, %4\n ds_read_b64 %1, %4\n ds_read_b64 %2, %4\n ds_read_b64 %3, %4\n"
+            "ds_read_b64 %0, %4\n ds_read_b64 %1, %4\n ds_read_b64 %2, %4\n ds_read_b64 %3, %4\n"
+            "ds_read_b64 %0, %4\n ds_read_b64 %1, %4\n ds_read_b64 %2, %4\n ds_read_b64 %3, %4\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+            : "v"(addr)
+            : "memory");
+        sink += r0[0] + r1[0] + r2[1] + r3[1];
+    } else {
+        f32x4 r0, r1, r2, r3;
+        asm volatile(
+            "ds_read_b128 %0, %4\n ds_read_b128 %1, %4\n ds_read_b128 %2, %4\n ds_read_b128 %3, %4\n"
+            "ds_read_b128 %0, %4\n ds_read_b128 %1, %4\n ds_read_b128 %2, %4\n ds_read_b128 %3, %4\n"
+            "ds_read_b128 %0, %4\n ds_read_b128 %1, %4\n ds_read_b128 %2, %4\n ds_read_b128 %3, %4\n"
+            "ds_read_b128 %0, %4\n ds_read_b128 %1, %4\n ds_read_b128 %2, %4\n ds_read_b128 %3, %4\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+            : "v"(addr)
+            : "memory");
+        sink += r0[0] + r1[1] + r2[2] + r3[3];
+    }
+}
+
+template <int WIDTH>
+__global__ __launch_bounds__(1024) void lds_probe_kernel(Pattern p, int reps, uint64_t* cycles_out,
+                                                          float* never_written) {
+    __shared__ __attribute__((aligned(16))) float buf[LDS_PROBE_WORDS];
+    for (int i = threadIdx.x; i < LDS_PROBE_WORDS; i += blockDim.x) buf[i] = (float)(i & 7);
+    __syncthreads();
+    const int lane = threadIdx.x % 64;
+    // ds_read takes an LDS byte offset: cast buf to the LDS address space.
+    typedef __attribute__((address_space(3))) float lds_float;
+    const uint32_t addr = (uint32_t)(uintptr_t)((lds_float*)buf) + (uint32_t)p.byte_addr[lane];
+    float sink = 0.0f;
+    const uint64_t t0 = clock64();
+    for (int r = 0; r < reps; ++r) read16<WIDTH>(addr, sink);
+    const uint64_t t1 = clock64();
+    if (lane == 0) cycles_out[threadIdx.x / 64] = t1 - t0;
+    // keep the reads observable; sink is finite, so this store never happens
+    if (sink < -1.0f && never_written) never_written[threadIdx.x] = sink;
+}
+
+}  // namespace
+
+extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int32_t waves, int32_t reps,
+                             uint64_t* cycles_out, void* stream) {
+    if (lane_words == nullptr || cycles_out == nullptr) return -1;
+    if (width_words != 1 && width_words != 2 && width_words != 4) return -1;
+    if (waves < 1 || waves > 16 || reps < 1 || reps > 100000) return -1;
+    Pattern p;
+    for (int l = 0; l < 64; ++l) {
+        const int32_t w = lane_words[l];
+        if (w < 0 || w % width_words != 0 || w + width_words > LDS_PROBE_WORDS) return -1;
+        p.byte_addr[l] = w * 4;
+    }
+    const dim3 grid(1), block(64 * waves);
+    hipStream_t s = (hipStream_t)stream;
+    switch (width_words) {
+        case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
+        case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
+        default: hipLaunchKernelGGL(lds_probe_kernel<4>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}

@@ -1,0 +1,113 @@
+"""Measure the gfx950 LDS bank geometry with liblds_probe.so.
+
+    python -m dense_fp32_tiled_amd.lds_probe [--out FILE]
+
+Times a fixed set of one-instruction LDS read patterns (strided 4/8/16-byte
+reads, and the exact fragment-read patterns of the GEMM kernels at their
+candidate paddings) and prints cycles per instruction next to the conflict
+degree the bank model predicts for each candidate geometry.  The geometry
+whose predictions track the measurements is the one the kernels' padding is
+derived for.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+PROBE_LIB = PKG / "liblds_probe.so"
+
+# candidate geometries: (banks, lanes per pass for b32, b64, b128)
+GEOMETRIES = {
+    "32 banks, 128 B/pass": (32, 32, 16, 8),
+    "64 banks, 256 B/pass": (64, 64, 32, 16),
+}
+
+
+def load():
+    if not PROBE_LIB.exists():
+        raise ImportError(f"{PROBE_LIB} is not built; run `python -m dense_fp32_tiled_amd.build`")
+    lib = ctypes.CDLL(str(PROBE_LIB))
+    lib.lds_probe_run.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.lds_probe_run.restype = ctypes.c_int
+    return lib
+
+
+def patterns():
+    """(name, width_words, lane -> dword address list)."""
+    pats = []
+    for s in (0, 1, 2, 3, 4, 8, 16, 32, 33, 64, 65, 128):
+        pats.append((f"b32 stride {s}", 1, [l * s for l in range(64)]))
+    for s in (2, 4, 8, 16, 32, 64, 128):
+        pats.append((f"b64 stride {s}", 2, [l * s for l in range(64)]))
+    for s in (4, 8, 12, 16, 20, 24, 28, 32, 36, 64, 128):
+        pats.append((f"b128 stride {s}", 4, [l * s for l in range(64)]))
+    # which lanes share a pass: lanes >= G repeat lanes < G's banks at another address
+    for g in (8, 16, 32):
+        pats.append((f"b32 halves at lane {g}", 1, [(l % g) + (l // g) * 1024 for l in range(64)]))
+        pats.append((f"b128 groups of {g}", 4, [4 * (l % g) + (l // g) * 1024 for l in range(64)]))
+    # the GEMM kernels' own fragment reads
+    for pad in (0, 4, 8, 12):
+        stride = 16 + pad
+        pats.append((f"mfma A read, row stride {stride}", 4, [(l % 32) * stride + (l // 32) * 8 for l in range(64)]))
+    for pad in (0, 4, 8, 16, 32):
+        stride = 128 + pad
+        pats.append((f"mfma B read, row stride {stride}", 1, [(l // 32) * 8 * stride + (l % 32) for l in range(64)]))
+    pats.append(("valu A read (broadcast groups of 16)", 4, [(l // 16) * 4 for l in range(64)]))
+    pats.append(("valu B read", 4, [(l % 16) * 4 for l in range(64)]))
+    return pats
+
+
+def predicted(words, width, geom):
+    import dense_fp32_tiled_amd as dft
+
+    banks, g32, g64, g128 = geom
+    group = {1: g32, 2: g64, 4: g128}[width]
+    return dft.gemm_lds_conflict_degree(words, width, banks, group)
+
+
+def run(reps: int = 2000, waves: int = 4):
+    import torch
+
+    lib = load()
+    out = torch.zeros(16, dtype=torch.int64, device="cuda")
+    rows = []
+    for name, width, words in patterns():
+        arr = (ctypes.c_int32 * 64)(*words)
+        st = lib.lds_probe_run(arr, width, waves, reps, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"lds_probe_run failed ({st}) for {name}")
+        torch.cuda.synchronize()
+        cyc = out[:waves].cpu().tolist()
+        per_instr = max(cyc) / (reps * 16)
+        rows.append({"pattern": name, "width_bytes": 4 * width, "cycles_per_instr_per_wave": per_instr,
+                     "predicted_degree": {g: predicted(words, width, v) for g, v in GEOMETRIES.items()}})
+    return rows
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default="")
+    ap.add_argument("--reps", type=int, default=2000)
+    ap.add_argument("--waves", type=int, default=4)
+    args = ap.parse_args(argv)
+    rows = run(args.reps, args.waves)
+    lines = [f"# LDS probe: {args.waves} waves x {args.reps} x 16 reads per pattern; cycles per instruction per wave",
+             "pattern | bytes/lane | cycles/instr | " + " | ".join(f"degree[{g}]" for g in GEOMETRIES)]
+    for r in rows:
+        lines.append(f"{r['pattern']} | {r['width_bytes']} | {r['cycles_per_instr_per_wave']:.2f} | " +
+                     " | ".join(str(r["predicted_degree"][g]) for g in GEOMETRIES))
+    text = "\n".join(lines)
+    print(text)
+    if args.out:
+        Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

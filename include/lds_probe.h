@@ -1,0 +1,45 @@
+/*
+ * lds_probe.h -- microbenchmark of the gfx950 LDS bank geometry.
+ *
+ * The pages model shared memory as 32 four-byte banks serviced one warp at a
+ * time ("My Triton From Scratch, Part 18: Shared Memory Optimization",
+ * section "Why shared-memory banks matter"), which is NVIDIA's geometry.  The
+ * LDS padding of the GEMM kernels is derived from a bank count and from how
+ * many lanes the LDS services together per access width; this probe measures
+ * those on the device by timing one access pattern: every lane of `waves`
+ * wavefronts (one workgroup) issues `reps` x 16 LDS reads of `width_words`
+ * dwords at its own dword address, with no other work, and the time per
+ * instruction is returned.  Conflicting patterns take proportionally longer.
+ */
+#ifndef LDS_PROBE_H
+#define LDS_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest dword address + width a pattern may touch (a 64 KiB LDS buffer). */
+#define LDS_PROBE_WORDS 16384
+
+/*
+ * lane_words: HOST array of 64 dword addresses, one per lane (the same
+ *             pattern is used by every wavefront).
+ * width_words: 1, 2 or 4 (ds_read_b32 / b64 / b128); every address must be a
+ *             multiple of width_words and address + width_words <= LDS_PROBE_WORDS.
+ * waves: 1..16 wavefronts in the workgroup.  reps: 1..100000.
+ * cycles_out: DEVICE buffer of `waves` uint64 values, owned by the caller;
+ *             wave w writes the shader-clock cycles its read loop took.
+ * stream: hipStream_t (NULL = null stream).
+ * Returns 0, -1 for invalid arguments (nothing is launched), -2 if the
+ * launch failed.  Asynchronous: read cycles_out after synchronising.
+ */
+int lds_probe_run(const int32_t *lane_words, int32_t width_words, int32_t waves, int32_t reps,
+                  uint64_t *cycles_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LDS_PROBE_H */

@@ -18,3 +18,13 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+@pytest.fixture(scope="session")
+def gemm_lib():
+    """The HIP library (built in-tree if it is not there yet)."""
+    import dense_fp32_tiled_amd as dft
+    if not dft.LIB_PATH.exists():
+        from dense_fp32_tiled_amd import build
+        build.build()
+    return dft.library()

@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host before touching a device (CPU only)."""
+
+from __future__ import annotations
+
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import dense_fp32_tiled_amd as dft
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "dense_fp32_tiled.h"
+
+
+def declared_functions() -> set[str]:
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == set(dft.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(gemm_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(dft.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = declared_functions() - exported
+    assert not missing, f"declared but not exported: {missing}"
+    for name in dft.EXPORTS:
+        assert hasattr(gemm_lib, name)
+
+
+def test_status_strings(gemm_lib):
+    for st in range(-8, 1):
+        s = dft.gemm_f32_status_string(st)
+        assert s and s != "unknown status"
+    assert dft.gemm_f32_status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("variant", range(dft.VARIANT_COUNT))
+def test_tile_config_is_consistent(variant, gemm_lib):
+    c = dft.gemm_f32_tile_config(variant)
+    assert c["variant"] == variant
+    assert c["wave_size"] == 64
+    assert c["a_row_stride"] == c["a_cols"] + c["a_pad"]
+    assert c["b_row_stride"] == c["b_cols"] + c["b_pad"]
+    assert c["a_stage_elems"] == c["a_rows"] * c["a_row_stride"]
+    assert c["b_stage_elems"] == c["b_rows"] * c["b_row_stride"]
+    # the pages' budget formula, on the physical (padded, staged) sizes
+    assert c["lds_bytes"] == c["stages"] * (c["a_stage_elems"] + c["b_stage_elems"]) * 4
+    assert c["lds_bytes"] <= 160 * 1024
+    assert c["barriers_per_tile"] == (1 if c["stages"] == 2 else 2)
+    if c["a_transposed"]:
+        assert (c["a_rows"], c["a_cols"]) == (c["bk"], c["bm"])
+    else:
+        assert (c["a_rows"], c["a_cols"]) == (c["bm"], c["bk"])
+    assert (c["b_rows"], c["b_cols"]) == (c["bk"], c["bn"])
+    assert c["vec_width"] in (1, 4)
+    assert (c["a_row_stride"] % 4 == 0) and (c["b_row_stride"] % 4 == 0)
+
+
+def test_tile_config_rejects(gemm_lib):
+    with pytest.raises(dft.GemmError):
+        dft.gemm_f32_tile_config(dft.VARIANT_COUNT)
+    with pytest.raises(dft.GemmError):
+        dft.gemm_f32_tile_config(-1)
+    assert gemm_lib.gemm_f32_tile_config(0, None) == dft.GEMM_ERR_NULL
+
+
+def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
+    base = dft.gemm_f32_tile_config(dft.VARIANT_MFMA)
+    assert dft.gemm_f32_tile_config(dft.VARIANT_AUTO) | {"variant": 1} == base
+    s1 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_STAGES1)
+    assert s1["stages"] == 1 and s1["barriers_per_tile"] == 2
+    assert s1 | {"variant": 1, "stages": 2, "barriers_per_tile": 1, "lds_bytes": base["lds_bytes"]} == base
+    nopad = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_NOPAD)
+    assert nopad["a_pad"] == 0 and nopad["b_pad"] == 0
+    sc = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_SCALAR)
+    assert sc["vec_width"] == 1
+    assert sc | {"variant": 1, "vec_width": 4} == base
+
+
+# ---- host-side argument validation: every case returns before any device call ----
+FAKE_A, FAKE_B, FAKE_C = 0x10000, 0x200000, 0x4000000  # never dereferenced
+
+
+def call(M, N, K, A=FAKE_A, lda=None, B=FAKE_B, ldb=None, C=FAKE_C, ldc=None, variant=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return dft.gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, None, variant)
+
+
+@pytest.mark.parametrize("dims", [(-1, 4, 4), (4, -1, 4), (4, 4, -1)])
+def test_negative_dims(dims, gemm_lib):
+    assert call(*dims) == dft.GEMM_ERR_INVALID_DIM
+
+
+@pytest.mark.parametrize("kw", [dict(lda=3), dict(ldb=7), dict(ldc=7), dict(lda=0), dict(ldc=-1)])
+def test_small_leading_dimension(kw, gemm_lib):
+    assert call(5, 8, 4, **kw) == dft.GEMM_ERR_INVALID_LD
+
+
+def test_leading_dimension_with_zero_extent(gemm_lib):
+    # ld must still be >= 1 when the width is 0
+    assert call(3, 0, 0, lda=0) == dft.GEMM_ERR_INVALID_LD
+    assert call(3, 0, 0) == dft.GEMM_OK  # N == 0: nothing to do
+
+
+@pytest.mark.parametrize("kw", [dict(A=0), dict(B=0), dict(C=0)])
+def test_null_operands(kw, gemm_lib):
+    assert call(5, 8, 4, **kw) == dft.GEMM_ERR_NULL
+
+
+def test_null_allowed_for_empty_extent(gemm_lib):
+    assert call(0, 8, 4, A=0, B=0, C=0) == dft.GEMM_OK
+    assert call(5, 0, 4, A=0, B=0, C=0) == dft.GEMM_OK
+
+
+def test_alias(gemm_lib):
+    # C overlapping A's last element
+    M, N, K = 4, 4, 4
+    a_end = FAKE_A + ((M - 1) * K + K) * 4
+    assert call(M, N, K, C=a_end - 4) == dft.GEMM_ERR_ALIAS
+    assert call(M, N, K, C=FAKE_B) == dft.GEMM_ERR_ALIAS
+    assert call(M, N, K, C=FAKE_B - 4) == dft.GEMM_ERR_ALIAS  # C's span reaches into B
+
+
+def test_too_large(gemm_lib):
+    assert call(1 << 40, 4, 1 << 30, lda=1 << 30) == dft.GEMM_ERR_TOO_LARGE
+
+
+def test_unknown_variant(gemm_lib):
+    assert call(4, 4, 4, variant=99) == dft.GEMM_ERR_UNSUPPORTED
+    assert call(4, 4, 4, variant=-1) == dft.GEMM_ERR_UNSUPPORTED
+
+
+def test_binding_requires_the_library(tmp_path):
+    with pytest.raises(ImportError):
+        dft.library(tmp_path / "missing.so")

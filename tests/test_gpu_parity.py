@@ -1,0 +1,222 @@
+"""Parity of the HIP kernels with the fp64 CPU oracle, through the C ABI.
+
+Bar (from the method's own pass criterion): max |C - Cref| / (|A||B|)_ij
+<= 1e-5 per element, full comparison for the small and deep-K shapes and
+sampled rows and columns (64 of each, always including the first and last)
+for the 4096^3 and 8192^3 squares.  Integer-valued operands (entries in
+{-4..4}) make every partial sum exact in fp32, so there the GPU result must
+equal the oracle bit for bit in any summation order.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_fp32_tiled_amd as dft
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+SENTINEL_BITS = np.uint32(0x7FC0DEAD)  # a quiet NaN with a recognisable payload
+SENTINEL = SENTINEL_BITS.view(np.float32)
+
+ALL_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA_NOPAD,
+                dft.VARIANT_MFMA_SCALAR]
+VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
+
+
+@pytest.fixture(scope="module")
+def torch_gpu(gemm_lib):
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), f"expected a gfx950 device, found {name}"
+    return torch
+
+
+def run_gemm(torch, a: np.ndarray, b: np.ndarray, variant: int, lda=None, ldb=None, ldc=None,
+             offset: int = 0, stream=None, c_rows_extra: int = 1):
+    """Copy a, b into (possibly padded) device buffers, run the GEMM, return
+    (C, full C buffer as a rows x ldc array).  The C buffer is pre-filled with
+    a NaN sentinel; `offset` shifts every operand by that many floats."""
+    M, K = a.shape
+    N = b.shape[1]
+    lda = lda or max(K, 1)
+    ldb = ldb or max(N, 1)
+    ldc = ldc or max(N, 1)
+    abuf = np.concatenate([np.full(offset, SENTINEL, np.float32), workloads.embed(a, lda, SENTINEL)])
+    bbuf = np.concatenate([np.full(offset, SENTINEL, np.float32), workloads.embed(b, ldb, SENTINEL)])
+    cbuf = np.full(offset + (M + c_rows_extra) * ldc, SENTINEL, np.float32)
+    da, db, dc = (torch.from_numpy(x).cuda() for x in (abuf, bbuf, cbuf))
+    handle = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    st = dft.gemm_f32_ex(M, N, K, da.data_ptr() + 4 * offset, lda, db.data_ptr() + 4 * offset, ldb,
+                         dc.data_ptr() + 4 * offset, ldc, handle, variant)
+    assert st == dft.GEMM_OK, dft.gemm_f32_status_string(st)
+    torch.cuda.synchronize()
+    full = dc.cpu().numpy()[offset:].reshape(M + c_rows_extra, ldc)
+    return full[:M, :N].copy(), full
+
+
+def check_sentinels(full: np.ndarray, M: int, N: int):
+    bits = full.view(np.uint32)
+    outside = np.ones(full.shape, bool)
+    outside[:M, :N] = False
+    assert np.all(bits[outside] == SENTINEL_BITS), "a write landed outside the M x N region"
+
+
+_oracle_cache: dict = {}
+
+
+def reference_for(cfg: workloads.GemmConfig, integer: bool):
+    key = (cfg.name, integer)
+    if key not in _oracle_cache:
+        a, b = workloads.config_operands(cfg, integer=integer)
+        if cfg.sampled:
+            rows, cols = workloads.sample_rows_cols(cfg)
+            ref = (oracle.reference(a, b, rows=rows), oracle.reference(a, b, cols=cols), rows, cols)
+        else:
+            ref = (oracle.reference(a, b),)
+        _oracle_cache[key] = (a, b, ref)
+    return _oracle_cache[key]
+
+
+def compare(cfg, c: np.ndarray, ref, exact: bool) -> float:
+    if cfg.sampled:
+        (cr, dr), (cc, dc), rows, cols = ref
+        pairs = [(c[rows, :], cr, dr), (c[:, cols], cc, dc)]
+    else:
+        (cf, df), = ref
+        pairs = [(c, cf, df)]
+    if exact:
+        for got, want, _ in pairs:
+            assert np.array_equal(got.astype(np.float64), want), "integer-valued product differs"
+        return 0.0
+    return max(oracle.normalised_error(got, want, den) for got, want, den in pairs)
+
+
+CONFIG_ORDER = ["small128", "ragged", "deepk", "square4096", "square8192"]
+
+
+@pytest.mark.parametrize("cfg_name", CONFIG_ORDER)
+@pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
+def test_config_parity(cfg_name, variant, torch_gpu):
+    cfg = workloads.CONFIG_BY_NAME[cfg_name]
+    a, b, ref = reference_for(cfg, integer=False)
+    c, full = run_gemm(torch_gpu, a, b, variant)
+    check_sentinels(full, cfg.M, cfg.N)
+    err = compare(cfg, c, ref, exact=False)
+    print(f"{cfg_name} {dft.VARIANT_NAMES[variant]}: normalised error {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("cfg_name", CONFIG_ORDER)
+@pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
+def test_config_integer_exact(cfg_name, variant, torch_gpu):
+    cfg = workloads.CONFIG_BY_NAME[cfg_name]
+    a, b, ref = reference_for(cfg, integer=True)
+    c, _ = run_gemm(torch_gpu, a, b, variant)
+    compare(cfg, c, ref, exact=True)
+
+
+EDGE_SHAPES = [
+    (1, 1, 1), (1, 1, 17), (2, 3, 5), (3, 2, 4), (31, 33, 15), (127, 129, 15), (128, 128, 16),
+    (129, 127, 17), (255, 1, 300), (1, 257, 33), (64, 64, 1), (300, 200, 48), (257, 131, 129),
+    (16, 520, 64), (520, 16, 64),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1],
+                         ids=["mfma", "valu", "mfma_stages1"])
+def test_edge_shapes(shape, variant, torch_gpu):
+    M, N, K = shape
+    a, b = workloads.make_operands(M, N, K, "uniform", M * 7 + N * 13 + K)
+    cref, den = oracle.reference(a, b)
+    for offset in (0, 1):  # offset 1 float: unaligned operands take the 4-byte load path
+        c, full = run_gemm(torch_gpu, a, b, variant, offset=offset)
+        check_sentinels(full, M, N)
+        assert oracle.normalised_error(c, cref, den) <= TOL, (shape, offset)
+    ai, bi = workloads.make_operands(M, N, K, "integer", M + N + K)
+    ci, _ = run_gemm(torch_gpu, ai, bi, variant)
+    assert np.array_equal(ci.astype(np.float64), oracle.reference(ai, bi)[0])
+
+
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU], ids=["mfma", "valu"])
+@pytest.mark.parametrize("pitch", [(3, 5, 2), (2, 4, 4), (1, 0, 9), (0, 8, 0)], ids=str)
+def test_pitched_operands(pitch, variant, torch_gpu):
+    """Leading dimensions beyond the width: NaN in every gap must never be
+    read (the result stays finite and exact) and no gap of C is written."""
+    M, N, K = 150, 140, 70
+    a, b = workloads.make_operands(M, N, K, "integer", 77)
+    cref, _ = oracle.reference(a, b)
+    pa, pb, pc = pitch
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=K + pa, ldb=N + pb, ldc=N + pc, c_rows_extra=3)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref)
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
+def test_k_zero_writes_zeros(variant, torch_gpu):
+    a = np.zeros((37, 0), np.float32)
+    b = np.zeros((0, 45), np.float32)
+    c, full = run_gemm(torch_gpu, a, b, variant, ldc=50)
+    check_sentinels(full, 37, 45)
+    assert np.array_equal(c, np.zeros((37, 45), np.float32))
+
+
+def test_empty_m_or_n_touches_nothing(torch_gpu):
+    torch = torch_gpu
+    cbuf = torch.from_numpy(np.full(64, SENTINEL, np.float32)).cuda()
+    a = torch.ones(16, device="cuda")
+    b = torch.ones(16, device="cuda")
+    for (M, N, K) in [(0, 4, 4), (4, 0, 4), (0, 0, 0)]:
+        st = dft.gemm_f32(M, N, K, a.data_ptr(), max(K, 1), b.data_ptr(), max(N, 1), cbuf.data_ptr(),
+                          max(N, 1), None)
+        assert st == dft.GEMM_OK
+    torch.cuda.synchronize()
+    assert np.all(cbuf.cpu().numpy().view(np.uint32) == SENTINEL_BITS)
+
+
+def test_tall_and_wide(torch_gpu):
+    for (M, N, K) in [(70000, 3, 7), (2, 100003, 9), (1, 1, 70001)]:
+        a, b = workloads.make_operands(M, N, K, "integer", 5)
+        c, _ = run_gemm(torch_gpu, a, b, dft.VARIANT_AUTO)
+        assert np.array_equal(c.astype(np.float64), oracle.reference(a, b)[0]), (M, N, K)
+
+
+def test_deterministic_and_stream_ordered(torch_gpu):
+    torch = torch_gpu
+    cfg = workloads.CONFIG_BY_NAME["ragged"]
+    a, b = workloads.config_operands(cfg)
+    c0, _ = run_gemm(torch, a, b, dft.VARIANT_MFMA)
+    s = torch.cuda.Stream()
+    c1, _ = run_gemm(torch, a, b, dft.VARIANT_MFMA, stream=s)
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+
+
+def test_matmul_wrapper(torch_gpu):
+    torch = torch_gpu
+    a, b = workloads.make_operands(200, 300, 100, "uniform", 9)
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    c = dft.matmul(ta, tb).cpu().numpy()
+    cref, den = oracle.reference(a, b)
+    assert oracle.normalised_error(c, cref, den) <= TOL
+    # a strided view (row pitch > width) goes through as lda
+    big = torch.from_numpy(workloads.embed(a, 128).reshape(200, 128)).cuda()
+    c2 = dft.matmul(big[:, :100], tb).cpu().numpy()
+    assert np.array_equal(c, c2)
+    with pytest.raises(TypeError):
+        dft.matmul(ta.double(), tb)
+    with pytest.raises(ValueError):
+        dft.matmul(ta, tb[:50])
+
+
+def test_rejects_overlap_on_device(torch_gpu):
+    torch = torch_gpu
+    buf = torch.zeros(64 * 64, device="cuda")
+    p = buf.data_ptr()
+    st = dft.gemm_f32(8, 8, 8, p, 8, p + 4 * 64, 8, p + 4 * 32, 8, None)
+    assert st == dft.GEMM_ERR_ALIAS
