@@ -66,6 +66,9 @@ def parse_args(argv=None):
                     help="rows of C the CPU oracle computes for its baseline (0 = skip)")
     ap.add_argument("--ablations", default="",
                     help="also time every variant and write one JSON line per variant to this file")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one device-to-device copy of this many MiB (a "
+                         "reference kernel of known traffic for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args(argv)
 
 
@@ -198,6 +201,21 @@ def main(argv=None) -> int:
                                     "tflops_wall": cfg.flops / w / 1e12, "tflops_kernel_avg": cfg.flops / kavg / 1e12,
                                     "kernel_ms_avg": kavg * 1e3, "kernel_ms_median": kmed * 1e3,
                                     "kernel_ms_min": kmin * 1e3}) + "\n")
+
+    if args.copy_calibration_mib > 0:
+        import ctypes
+
+        probe = ctypes.CDLL(str(ROOT / "dense_fp32_tiled_amd" / "liblds_probe.so"))
+        probe.probe_copy_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        probe.probe_copy_f32.restype = ctypes.c_int
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        if probe.probe_copy_f32(src.data_ptr(), dst.data_ptr(), n, handle) != 0:
+            raise RuntimeError("probe_copy_f32 failed")
+        torch.cuda.synchronize()
+        del src, dst
 
     print(json.dumps(result), flush=True)
     return 0

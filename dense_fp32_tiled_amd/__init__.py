@@ -68,7 +68,8 @@ class TileConfig(ctypes.Structure):
         "variant", "bm", "bn", "bk", "threads", "wave_size", "tm", "tn", "stages", "barriers_per_tile",
         "a_rows", "a_cols", "a_pad", "a_row_stride", "a_stage_elems",
         "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
-        "lds_bytes", "vec_width", "lds_banks", "a_transposed")]
+        "lds_bytes", "vec_width", "lds_banks_b32", "lds_lanes_b32", "lds_banks_b128", "lds_lanes_b128",
+        "a_transposed")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -41,22 +41,30 @@ struct Args {
 
 using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
 
+// Launches go through hipLaunchKernel so that the returned status is this
+// launch's own (hipGetLastError would also report errors left by earlier,
+// unrelated runtime calls on the thread).
+template <class Kernel>
+hipError_t launch_tiles(Kernel kernel, int bm, int bn, int threads, const Args& a, hipStream_t stream) {
+    int64_t M = a.M, N = a.N, K = a.K, lda = a.lda, ldb = a.ldb, ldc = a.ldc;
+    const float* A = a.A;
+    const float* B = a.B;
+    float* C = a.C;
+    const int64_t tiles_m = (M + bm - 1) / bm;
+    int64_t tiles_n = (N + bn - 1) / bn;
+    void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(threads), args, 0, stream);
+}
+
 template <class Cfg>
 hipError_t launch_mfma(const Args& a, hipStream_t stream) {
-    const int64_t tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
-    const int64_t tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-    hipLaunchKernelGGL(gemm_mfma_kernel<Cfg>, dim3((unsigned)(tiles_m * tiles_n)), dim3(Cfg::THREADS), 0,
-                       stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, tiles_n);
-    return hipGetLastError();
+    return launch_tiles(gemm_mfma_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, stream);
 }
 
 template <class Cfg>
 hipError_t launch_valu(const Args& a, hipStream_t stream) {
-    const int64_t tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
-    const int64_t tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-    hipLaunchKernelGGL(gemm_valu_kernel<Cfg>, dim3((unsigned)(tiles_m * tiles_n)), dim3(Cfg::THREADS), 0,
-                       stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, tiles_n);
-    return hipGetLastError();
+    return launch_tiles(gemm_valu_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, stream);
 }
 
 template <class Cfg>
@@ -74,7 +82,8 @@ gemm_tile_config mfma_config(int variant, int vec) {
     c.b_row_stride = Cfg::TileB::row_stride; c.b_stage_elems = Cfg::TileB::stage_elems;
     c.lds_bytes = Cfg::LDS_BYTES;
     c.vec_width = vec;
-    c.lds_banks = kGfx950Lds.banks;
+    c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
+    c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.a_transposed = 0;
     return c;
 }
@@ -94,7 +103,8 @@ gemm_tile_config valu_config(int variant, int vec) {
     c.b_row_stride = Cfg::TileB::row_stride; c.b_stage_elems = Cfg::TileB::stage_elems;
     c.lds_bytes = Cfg::LDS_BYTES;
     c.vec_width = vec;
-    c.lds_banks = kGfx950Lds.banks;
+    c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
+    c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.a_transposed = 1;
     return c;
 }
@@ -191,8 +201,13 @@ int run(const Args& a, hipStream_t stream, int variant) {
         const int64_t total = a.M * a.N;
         int64_t blocks = (total + 255) / 256;
         if (blocks > 65536) blocks = 65536;
-        hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.M, a.N, a.C, a.ldc);
-        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+        int64_t M = a.M, N = a.N, ldc = a.ldc;
+        float* C = a.C;
+        void* args[] = {&M, &N, &C, &ldc};
+        return hipLaunchKernel(reinterpret_cast<const void*>(zero_fill_kernel), dim3((unsigned)blocks), dim3(256),
+                               args, 0, stream) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
     }
 
     const Variant& v = kVariants[variant];

@@ -52,23 +52,31 @@ struct LdsTile {
 };
 
 // --------------------------------------------------------------------------
-// Bank model.
+// Bank model.  For each access width the LDS services a group of lanes per
+// pass over a number of 4-byte banks; the cost of an instruction is the pass
+// count times the worst number of distinct dwords that one bank must deliver
+// within one pass (its conflict degree).
 struct LdsGeometry {
-    int banks;          // 4-byte banks
-    int lanes_b32;      // lanes serviced together by a 4-byte access
-    int lanes_b64;      // ... by an 8-byte access
-    int lanes_b128;     // ... by a 16-byte access
+    int banks_b32, lanes_b32;    // 4-byte accesses
+    int banks_b64, lanes_b64;    // 8-byte accesses
+    int banks_b128, lanes_b128;  // 16-byte accesses
 
+    constexpr int banks_for_width(int width_words) const {
+        return width_words == 1 ? banks_b32 : width_words == 2 ? banks_b64 : banks_b128;
+    }
     constexpr int group_for_width(int width_words) const {
         return width_words == 1 ? lanes_b32 : width_words == 2 ? lanes_b64 : lanes_b128;
     }
 };
 
-// gfx950 LDS geometry the kernels' padding is derived for: 64 banks of 4
-// bytes, a 4/8/16-byte access serviced 64/32/16 lanes at a time (256 bytes
-// per pass).  This is an assumption about CDNA4, not a figure from the pages
-// (their 32 banks are NVIDIA's); the LDS probe kernel measures it.
-constexpr LdsGeometry kGfx950Lds{64, 64, 32, 16};
+// gfx950 (MI355X), measured with the LDS probe (timed single-instruction
+// patterns, 4 wavefronts): 4-byte reads behave as 32 banks serviced 32 lanes
+// per pass (a stride of 64 dwords costs no more than a stride of 32); 8-byte
+// reads as 64 banks, 32 lanes per pass; 16-byte reads as 64 banks, 16 lanes
+// per pass (256 bytes per pass; a stride of 64 dwords is 16-way, 32 is 8-way).
+// The pages' figure (32 banks per 32-lane warp) is NVIDIA's and matches only
+// the 4-byte case.
+constexpr LdsGeometry kGfx950Lds{32, 32, 64, 32, 64, 16};
 
 constexpr int bank_of(int64_t word, int banks) { return (int)(((word % banks) + banks) % banks); }
 

@@ -77,7 +77,32 @@ __global__ __launch_bounds__(1024) void lds_probe_kernel(Pattern p, int reps, ui
     if (sink < -1.0f && never_written) never_written[threadIdx.x] = sink;
 }
 
+__global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
+                                                       int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
 }  // namespace
+
+extern "C" int probe_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
+    if (n < 0 || n % 4 != 0) return -1;
+    if (n == 0) return 0;
+    if (src == nullptr || dst == nullptr) return -1;
+    if ((((uintptr_t)src) & 15) != 0 || (((uintptr_t)dst) & 15) != 0) return -1;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst, bytes = (uintptr_t)n * 4;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return -1;
+    int64_t n4 = n / 4;
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+    f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    void* args[] = {&s4, &d4, &n4};
+    return hipLaunchKernel(reinterpret_cast<const void*>(copy_f32_kernel), dim3((unsigned)blocks), dim3(256), args, 0,
+                           (hipStream_t)stream) == hipSuccess
+               ? 0
+               : -2;
+}
 
 extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int32_t waves, int32_t reps,
                              uint64_t* cycles_out, void* stream) {
@@ -90,12 +115,10 @@ extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int
         if (w < 0 || w % width_words != 0 || w + width_words > LDS_PROBE_WORDS) return -1;
         p.byte_addr[l] = w * 4;
     }
-    const dim3 grid(1), block(64 * waves);
-    hipStream_t s = (hipStream_t)stream;
-    switch (width_words) {
-        case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
-        case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
-        default: hipLaunchKernelGGL(lds_probe_kernel<4>, grid, block, 0, s, p, reps, cycles_out, nullptr); break;
-    }
-    return hipGetLastError() == hipSuccess ? 0 : -2;
+    float* never_written = nullptr;
+    void* args[] = {&p, &reps, &cycles_out, &never_written};
+    const void* kernel = width_words == 1   ? reinterpret_cast<const void*>(lds_probe_kernel<1>)
+                         : width_words == 2 ? reinterpret_cast<const void*>(lds_probe_kernel<2>)
+                                            : reinterpret_cast<const void*>(lds_probe_kernel<4>);
+    return hipLaunchKernel(kernel, dim3(1), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : -2;
 }

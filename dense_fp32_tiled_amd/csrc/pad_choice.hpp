@@ -26,36 +26,43 @@ struct MfmaShape {
 constexpr int mfma_a_read_degree(MfmaShape s, int pad, LdsGeometry g) {
     const int stride = s.bk + pad;
     return conflict_degree([=](int l) { return (int64_t)(l % 32) * stride + (l / 32) * s.kh(); },
-                           kWaveLanes, 4, g.banks, g.group_for_width(4));
+                           kWaveLanes, 4, g.banks_for_width(4), g.group_for_width(4));
 }
 // Cooperative store of A (vec-wide): slot l -> row l/(BK/vec), column vec*(l%(BK/vec)).
 constexpr int mfma_a_write_degree(MfmaShape s, int pad, LdsGeometry g) {
     const int stride = s.bk + pad, vcols = s.bk / s.vec;
     return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks, g.group_for_width(s.vec));
+                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
 }
 // B fragment read (4-byte): lane l reads row (l/32)*BK/2 + j at column l%32.
 constexpr int mfma_b_read_degree(MfmaShape s, int pad, LdsGeometry g) {
     const int stride = s.bn + pad;
     return conflict_degree([=](int l) { return (int64_t)((l / 32) * s.kh()) * stride + (l % 32); },
-                           kWaveLanes, 1, g.banks, g.group_for_width(1));
+                           kWaveLanes, 1, g.banks_for_width(1), g.group_for_width(1));
 }
 constexpr int mfma_b_write_degree(MfmaShape s, int pad, LdsGeometry g) {
     const int stride = s.bn + pad, vcols = s.bn / s.vec;
     return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks, g.group_for_width(s.vec));
+                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
 }
 
-// Instructions per wavefront per K tile, used as weights.
+// LDS passes one access of `width_words` costs at conflict degree `degree`.
+constexpr int access_cost(int degree, int width_words, LdsGeometry g) {
+    return degree * (kWaveLanes / g.group_for_width(width_words));
+}
+
+// Cost per wavefront per K tile: instructions x passes x degree.
 constexpr int mfma_a_cost(MfmaShape s, int pad, LdsGeometry g) {
     const int reads = (s.wm / 32) * (s.kh() / 4);
     const int writes = (s.bm * s.bk) / (s.vec * s.threads);
-    return reads * mfma_a_read_degree(s, pad, g) + writes * mfma_a_write_degree(s, pad, g);
+    return reads * access_cost(mfma_a_read_degree(s, pad, g), 4, g) +
+           writes * access_cost(mfma_a_write_degree(s, pad, g), s.vec, g);
 }
 constexpr int mfma_b_cost(MfmaShape s, int pad, LdsGeometry g) {
     const int reads = (s.wn / 32) * s.kh();
     const int writes = (s.bk * s.bn) / (s.vec * s.threads);
-    return reads * mfma_b_read_degree(s, pad, g) + writes * mfma_b_write_degree(s, pad, g);
+    return reads * access_cost(mfma_b_read_degree(s, pad, g), 1, g) +
+           writes * access_cost(mfma_b_write_degree(s, pad, g), s.vec, g);
 }
 
 template <class Cost>
@@ -83,36 +90,36 @@ struct ValuShape {
 // At read (16-byte): lane l of wave 0 reads At[k][(l/threads_n)*4].
 constexpr int valu_a_read_degree(ValuShape s, int pad, LdsGeometry g) {
     (void)pad;
-    return conflict_degree([=](int l) { return (int64_t)(l / s.threads_n) * 4; }, kWaveLanes, 4, g.banks,
-                           g.group_for_width(4));
+    return conflict_degree([=](int l) { return (int64_t)(l / s.threads_n) * 4; }, kWaveLanes, 4,
+                           g.banks_for_width(4), g.group_for_width(4));
 }
 // Transposed store of A: slot l holds A[l/(BK/vec)][vec*(l%(BK/vec)) + e]; element e goes to
 // At[vec*(l%(BK/vec)) + e][l/(BK/vec)] with a 4-byte store.
 constexpr int valu_a_write_degree(ValuShape s, int pad, LdsGeometry g) {
     const int stride = s.bm + pad, vcols = s.bk / s.vec;
     return conflict_degree([=](int l) { return (int64_t)(s.vec * (l % vcols)) * stride + l / vcols; },
-                           kWaveLanes, 1, g.banks, g.group_for_width(1));
+                           kWaveLanes, 1, g.banks_for_width(1), g.group_for_width(1));
 }
 constexpr int valu_b_read_degree(ValuShape s, int pad, LdsGeometry g) {
     (void)pad;
-    return conflict_degree([=](int l) { return (int64_t)(l % s.threads_n) * 4; }, kWaveLanes, 4, g.banks,
-                           g.group_for_width(4));
+    return conflict_degree([=](int l) { return (int64_t)(l % s.threads_n) * 4; }, kWaveLanes, 4,
+                           g.banks_for_width(4), g.group_for_width(4));
 }
 constexpr int valu_b_write_degree(ValuShape s, int pad, LdsGeometry g) {
     const int stride = s.bn + pad, vcols = s.bn / s.vec;
     return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks, g.group_for_width(s.vec));
+                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
 }
 constexpr int valu_pad_a(ValuShape s, LdsGeometry g) {
     return argmin_pad([=](int pad) {
-        return 2 * s.bk * valu_a_read_degree(s, pad, g) +
-               (s.bm * s.bk / s.threads) * valu_a_write_degree(s, pad, g);
+        return 2 * s.bk * access_cost(valu_a_read_degree(s, pad, g), 4, g) +
+               (s.bm * s.bk / s.threads) * access_cost(valu_a_write_degree(s, pad, g), 1, g);
     });
 }
 constexpr int valu_pad_b(ValuShape s, LdsGeometry g) {
     return argmin_pad([=](int pad) {
-        return 2 * s.bk * valu_b_read_degree(s, pad, g) +
-               (s.bk * s.bn / (s.vec * s.threads)) * valu_b_write_degree(s, pad, g);
+        return 2 * s.bk * access_cost(valu_b_read_degree(s, pad, g), 4, g) +
+               (s.bk * s.bn / (s.vec * s.threads)) * access_cost(valu_b_write_degree(s, pad, g), s.vec, g);
     });
 }
 

@@ -21,10 +21,11 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 PROBE_LIB = PKG / "liblds_probe.so"
 
-# candidate geometries: (banks, lanes per pass for b32, b64, b128)
+# candidate geometries: access width in dwords -> (banks, lanes serviced per pass)
 GEOMETRIES = {
-    "32 banks, 128 B/pass": (32, 32, 16, 8),
-    "64 banks, 256 B/pass": (64, 64, 32, 16),
+    "32 banks x 128 B/pass": {1: (32, 32), 2: (32, 16), 4: (32, 8)},
+    "64 banks x 256 B/pass": {1: (64, 64), 2: (64, 32), 4: (64, 16)},
+    "b32 32x32, b64 64x32, b128 64x16": {1: (32, 32), 2: (64, 32), 4: (64, 16)},
 }
 
 
@@ -66,9 +67,31 @@ def patterns():
 def predicted(words, width, geom):
     import dense_fp32_tiled_amd as dft
 
-    banks, g32, g64, g128 = geom
-    group = {1: g32, 2: g64, 4: g128}[width]
+    banks, group = geom[width]
     return dft.gemm_lds_conflict_degree(words, width, banks, group)
+
+
+def measured_degree(cycles_per_instr: float, width: int, waves: int, geom, issue_floor: float) -> int:
+    """Conflict degree implied by a timing.  An instruction occupies the LDS
+    for (64 / lanes per pass) passes of one cycle per unit of degree, and
+    `waves` wavefronts share it, so cycles = waves * passes * degree unless
+    that is below the issue floor (the time of a broadcast read), where every
+    degree-1 access lands."""
+    if cycles_per_instr < 1.1 * issue_floor:
+        return 1
+    passes = 64 // geom[width][1]
+    return max(1, round(cycles_per_instr / (waves * passes)))
+
+
+def fit(rows, waves):
+    """Patterns whose measured degree equals each geometry's prediction."""
+    floor = next(r["cycles_per_instr_per_wave"] for r in rows if r["pattern"] == "b32 stride 0")
+    score = {}
+    for g, geom in GEOMETRIES.items():
+        score[g] = sum(1 for r in rows
+                       if measured_degree(r["cycles_per_instr_per_wave"], r["width_bytes"] // 4, waves, geom, floor)
+                       == r["predicted_degree"][g])
+    return score
 
 
 def run(reps: int = 2000, waves: int = 4):
@@ -102,6 +125,11 @@ def main(argv=None) -> int:
     for r in rows:
         lines.append(f"{r['pattern']} | {r['width_bytes']} | {r['cycles_per_instr_per_wave']:.2f} | " +
                      " | ".join(str(r["predicted_degree"][g]) for g in GEOMETRIES))
+    score = fit(rows, args.waves)
+    lines.append("")
+    lines.append("patterns whose timing matches the predicted degree (of %d):" % len(rows))
+    for g, ok in score.items():
+        lines.append(f"  {g}: {ok}")
     text = "\n".join(lines)
     print(text)
     if args.out:

@@ -81,7 +81,10 @@ typedef struct {
     int32_t b_rows, b_cols, b_pad, b_row_stride, b_stage_elems; /* LDS tile of B */
     int32_t lds_bytes;           /* stages * (a_stage_elems + b_stage_elems) * 4 */
     int32_t vec_width;           /* fp32 elements per global load when aligned (1 or 4) */
-    int32_t lds_banks;           /* LDS bank count the padding was derived for */
+    int32_t lds_banks_b32;       /* LDS geometry the padding was derived for: banks and */
+    int32_t lds_lanes_b32;       /*   lanes serviced per pass for 4-byte accesses ... */
+    int32_t lds_banks_b128;      /*   ... and for 16-byte accesses */
+    int32_t lds_lanes_b128;
     int32_t a_transposed;        /* 1 if A is stored k-major in LDS (a_rows = BK) */
 } gemm_tile_config;
 

@@ -38,6 +38,15 @@ extern "C" {
 int lds_probe_run(const int32_t *lane_words, int32_t width_words, int32_t waves, int32_t reps,
                   uint64_t *cycles_out, void *stream);
 
+/*
+ * Reference kernel for calibrating the HBM traffic counters: dst[i] = src[i]
+ * for i < n, 16-byte loads and stores, grid-stride.  It reads and writes
+ * exactly 4*n bytes.  src and dst are DEVICE pointers owned by the caller,
+ * 16-byte aligned and not overlapping; n >= 0 and a multiple of 4.  Returns
+ * 0, -1 for invalid arguments (nothing is launched), -2 if the launch failed.
+ */
+int probe_copy_f32(const float *src, float *dst, int64_t n, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def oracle_lib():
 def gemm_lib():
     """The HIP library (built in-tree if it is not there yet)."""
     import dense_fp32_tiled_amd as dft
-    if not dft.LIB_PATH.exists():
-        from dense_fp32_tiled_amd import build
-        build.build()
+    from dense_fp32_tiled_amd import build, lds_probe
+    if not dft.LIB_PATH.exists() or not lds_probe.PROBE_LIB.exists():
+        build.build_all()
     return dft.library()

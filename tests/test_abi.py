@@ -12,11 +12,25 @@ import pytest
 import dense_fp32_tiled_amd as dft
 
 HEADER = Path(__file__).resolve().parent.parent / "include" / "dense_fp32_tiled.h"
+PROBE_HEADER = HEADER.with_name("lds_probe.h")
 
 
-def declared_functions() -> set[str]:
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+def declared_functions(header: Path = HEADER) -> set[str]:
+    text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
     return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def exported(lib: Path) -> set[str]:
+    out = subprocess.run(["nm", "-D", "--defined-only", str(lib)], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+def test_probe_library_exports_its_header(gemm_lib):
+    from dense_fp32_tiled_amd import lds_probe
+
+    assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32"}
+    assert declared_functions(PROBE_HEADER) <= exported(lds_probe.PROBE_LIB)
 
 
 def test_header_declares_the_binding_exports():
@@ -24,10 +38,7 @@ def test_header_declares_the_binding_exports():
 
 
 def test_library_exports_every_declared_symbol(gemm_lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", str(dft.LIB_PATH)], capture_output=True,
-                         text=True, check=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    missing = declared_functions() - exported
+    missing = declared_functions() - exported(dft.LIB_PATH)
     assert not missing, f"declared but not exported: {missing}"
     for name in dft.EXPORTS:
         assert hasattr(gemm_lib, name)
