@@ -78,6 +78,19 @@ class TileConfig(ctypes.Structure):
 _lib = None
 
 
+def _share_torch_hip_runtime():
+    """Load torch (if installed) before the HIP library.  torch ships its own
+    HIP runtime with the same soname (libamdhip64.so.7) as ROCm's; loaded
+    first, it satisfies this library's dependency, so both share one runtime
+    and torch's streams and allocations are valid here.  Loaded the other way
+    round, the process would hold two runtimes and torch's stream handles
+    would be rejected by this library's launches."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def library(path: Path | None = None):
     """The loaded HIP library (raises if it has not been built)."""
     global _lib
@@ -86,6 +99,7 @@ def library(path: Path | None = None):
     p = Path(path) if path else LIB_PATH
     if not p.exists():
         raise ImportError(f"{p} is not built; run `python -m dense_fp32_tiled_amd.build`")
+    _share_torch_hip_runtime()
     lib = ctypes.CDLL(str(p))
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]

@@ -32,6 +32,9 @@ GEOMETRIES = {
 def load():
     if not PROBE_LIB.exists():
         raise ImportError(f"{PROBE_LIB} is not built; run `python -m dense_fp32_tiled_amd.build`")
+    import dense_fp32_tiled_amd as dft
+
+    dft._share_torch_hip_runtime()
     lib = ctypes.CDLL(str(PROBE_LIB))
     lib.lds_probe_run.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p]

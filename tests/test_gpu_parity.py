@@ -37,6 +37,14 @@ def torch_gpu(gemm_lib):
     return torch
 
 
+def test_one_hip_runtime_in_the_process(torch_gpu):
+    """The library must share torch's HIP runtime (one libamdhip64 mapped)."""
+    torch_gpu.zeros(1, device="cuda")
+    maps = open("/proc/self/maps").read().splitlines()
+    runtimes = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
+
+
 def run_gemm(torch, a: np.ndarray, b: np.ndarray, variant: int, lda=None, ldb=None, ldc=None,
              offset: int = 0, stream=None, c_rows_extra: int = 1):
     """Copy a, b into (possibly padded) device buffers, run the GEMM, return
