@@ -66,6 +66,9 @@ def parse_args(argv=None):
                     help="rows of C the CPU oracle computes for its baseline (0 = skip)")
     ap.add_argument("--ablations", default="",
                     help="also time every variant and write one JSON line per variant to this file")
+    ap.add_argument("--splits", type=int, default=-1,
+                    help="run gemm_f32_splitk with this many K slices (0 = the library's choice) "
+                         "instead of gemm_f32_ex; the workspace is allocated before timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB (a "
                          "reference kernel of known traffic for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -103,10 +106,20 @@ def main(argv=None) -> int:
     M, N, K = cfg.M, cfg.N, cfg.K
     pa, pb, pc = a.data_ptr(), b.data_ptr(), c.data_ptr()
 
+    ws, ws_bytes = None, 0
+    if args.splits >= 0:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        ws_bytes = dft.gemm_f32_splitk_workspace_bytes(M, N, K, args.splits, cus)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        splits_used = args.splits or dft.gemm_f32_splitk_auto_splits(M, N, K, cus)
+
     def step(v=variant):
-        st = dft.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, handle, v)
+        if args.splits >= 0 and v == variant:
+            st = dft.gemm_f32_splitk(M, N, K, pa, K, pb, N, pc, N, ws.data_ptr(), ws_bytes, args.splits, handle)
+        else:
+            st = dft.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, handle, v)
         if st != dft.GEMM_OK:
-            raise dft.GemmError(st, "gemm_f32_ex")
+            raise dft.GemmError(st, "gemm")
 
     def time_variant(v, steps, warmup):
         for _ in range(warmup):
@@ -130,8 +143,14 @@ def main(argv=None) -> int:
     wall_s, kern_avg_s, kern_med_s, kern_min_s = time_variant(variant, args.steps, args.warmup)
     tflops = cfg.flops / wall_s / 1e12
     achieved = cfg.flops / kern_avg_s / 1e12
-    tile = dft.gemm_f32_tile_config(variant)
-    run_name = dft.VARIANT_NAMES[tile["variant"] if variant != dft.VARIANT_AUTO else dft.VARIANT_MFMA]
+    if args.splits >= 0:
+        resolved = dft.VARIANT_MFMA_128
+    elif variant == dft.VARIANT_AUTO:
+        resolved = dft.gemm_f32_auto_variant(M, N, K, torch.cuda.get_device_properties(dev).multi_processor_count)
+    else:
+        resolved = variant
+    tile = dft.gemm_f32_tile_config(resolved)
+    run_name = dft.VARIANT_NAMES[resolved] + (f"+splitk{splits_used}" if args.splits >= 0 else "")
 
     # correctness spot check and CPU baseline: the oracle on a bounded row sample
     cpu_baseline = None
@@ -175,12 +194,14 @@ def main(argv=None) -> int:
                         f"entries {'normal(0,1)' if cfg.dist == 'normal' else 'uniform[-1,1)'}, seed {cfg.seed}",
             "M": M, "N": N, "K": K,
             "variant": run_name,
-            "tile": f"{tile['bm']}x{tile['bn']}x{tile['bk']}, {tile['threads']} threads, "
-                    f"{tile['stages']} LDS stages, pads A/B {tile['a_pad']}/{tile['b_pad']}",
+            "tile": f"{tile['bm']}x{tile['bn']}x{tile['bk']}, {tile['threads']} threads, MFMA block "
+                    f"{tile['mfma_block']}, {tile['stages']} LDS stages, LDS layout A pad {tile['a_pad']} "
+                    f"swizzle {tile['a_swz_unit']}/{tile['a_swz_shift']}/{tile['a_swz_mask']}, B pad "
+                    f"{tile['b_pad']} swizzle {tile['b_swz_unit']}/{tile['b_swz_shift']}/{tile['b_swz_mask']}",
             "fraction_of_fp32_peak": tflops / PEAK_FP32_TFLOPS,
         },
         "roofline": {
-            "bound": "mfma" if run_name.startswith("mfma") else "alu",
+            "bound": "mfma" if tile["mfma_block"] else "alu",
             "achieved": achieved,
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",

@@ -25,6 +25,7 @@ GEMM_ERR_UNSUPPORTED = -5
 GEMM_ERR_CONFIG = -6
 GEMM_ERR_HIP = -7
 GEMM_ERR_TOO_LARGE = -8
+GEMM_ERR_WORKSPACE = -9
 
 VARIANT_AUTO = 0
 VARIANT_MFMA = 1
@@ -32,7 +33,10 @@ VARIANT_VALU = 2
 VARIANT_MFMA_STAGES1 = 3
 VARIANT_MFMA_NOPAD = 4
 VARIANT_MFMA_SCALAR = 5
-VARIANT_COUNT = 6
+VARIANT_MFMA16 = 6
+VARIANT_MFMA_128 = 7
+VARIANT_MFMA_128_BK32 = 8
+VARIANT_COUNT = 9
 VARIANT_NAMES = {
     VARIANT_AUTO: "auto",
     VARIANT_MFMA: "mfma",
@@ -40,6 +44,9 @@ VARIANT_NAMES = {
     VARIANT_MFMA_STAGES1: "mfma_stages1",
     VARIANT_MFMA_NOPAD: "mfma_nopad",
     VARIANT_MFMA_SCALAR: "mfma_scalar",
+    VARIANT_MFMA16: "mfma16",
+    VARIANT_MFMA_128: "mfma_128",
+    VARIANT_MFMA_128_BK32: "mfma_128_bk32",
 }
 
 # Every symbol the public header declares.
@@ -48,6 +55,11 @@ EXPORTS = (
     "gemm_f32_ex",
     "gemm_f32_tile_config",
     "gemm_f32_status_string",
+    "gemm_f32_splitk",
+    "gemm_f32_splitk_workspace_bytes",
+    "gemm_f32_splitk_auto_splits",
+    "gemm_f32_auto_variant",
+    "gemm_lds_choose_mfma_layout",
     "gemm_lds_layout",
     "gemm_lds_offset",
     "gemm_lds_bank",
@@ -69,7 +81,8 @@ class TileConfig(ctypes.Structure):
         "a_rows", "a_cols", "a_pad", "a_row_stride", "a_stage_elems",
         "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
         "lds_bytes", "vec_width", "lds_banks_b32", "lds_lanes_b32", "lds_banks_b128", "lds_lanes_b128",
-        "a_transposed")]
+        "a_transposed", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_swz_unit", "b_swz_shift", "b_swz_mask",
+        "mfma_block", "xcd_tile_order")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -111,6 +124,16 @@ def library(path: Path | None = None):
     lib.gemm_f32_tile_config.restype = ctypes.c_int
     lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
     lib.gemm_f32_status_string.restype = ctypes.c_char_p
+    lib.gemm_f32_splitk.argtypes = gemm_args[:9] + [vp, i64, ctypes.c_int, vp]
+    lib.gemm_f32_splitk.restype = ctypes.c_int
+    lib.gemm_f32_splitk_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, i32]
+    lib.gemm_f32_splitk_workspace_bytes.restype = i64
+    lib.gemm_f32_splitk_auto_splits.argtypes = [i64, i64, i64, i32]
+    lib.gemm_f32_splitk_auto_splits.restype = ctypes.c_int
+    lib.gemm_f32_auto_variant.argtypes = [i64, i64, i64, i32]
+    lib.gemm_f32_auto_variant.restype = ctypes.c_int
+    lib.gemm_lds_choose_mfma_layout.argtypes = [i32] * 7 + [ctypes.POINTER(i32)]
+    lib.gemm_lds_choose_mfma_layout.restype = ctypes.c_int
     p32 = ctypes.POINTER(i32)
     lib.gemm_lds_layout.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
     lib.gemm_lds_layout.restype = ctypes.c_int
@@ -146,6 +169,29 @@ def gemm_f32_tile_config(variant: int) -> dict:
 
 def gemm_f32_status_string(status: int) -> str:
     return library().gemm_f32_status_string(status).decode()
+
+
+def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits=0, stream=None) -> int:
+    return library().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits, stream)
+
+
+def gemm_f32_splitk_workspace_bytes(M: int, N: int, K: int, splits: int, num_cus: int) -> int:
+    return library().gemm_f32_splitk_workspace_bytes(M, N, K, splits, num_cus)
+
+
+def gemm_f32_splitk_auto_splits(M: int, N: int, K: int, num_cus: int) -> int:
+    return library().gemm_f32_splitk_auto_splits(M, N, K, num_cus)
+
+
+def gemm_f32_auto_variant(M: int, N: int, K: int, num_cus: int) -> int:
+    return library().gemm_f32_auto_variant(M, N, K, num_cus)
+
+
+def gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec):
+    """(status, (pad, unit, shift, mask) of A, (pad, unit, shift, mask) of B)."""
+    out = (ctypes.c_int32 * 8)()
+    st = library().gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec, out)
+    return st, tuple(out[:4]), tuple(out[4:])
 
 
 def gemm_lds_layout(rows: int, cols: int, pad: int, stages: int):
@@ -187,6 +233,43 @@ def _operand(t, name):
         raise ValueError(f"{name} must have unit column stride")
     ld = t.stride(0) if rows > 1 else max(cols, 1)
     return t.data_ptr(), max(ld, cols, 1)
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None):
+    """C = a @ b with gemm_f32_splitk.  The workspace (a float32 tensor on the
+    same device) is allocated here when not given."""
+    import torch
+
+    pa, lda = _operand(a, "a")
+    pb, ldb = _operand(b, "b")
+    M, K = a.shape
+    if b.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    pc, ldc = _operand(out, "out")
+    cus = torch.cuda.get_device_properties(a.device).multi_processor_count
+    need = gemm_f32_splitk_workspace_bytes(M, N, K, splits, cus)
+    if need < 0:
+        raise GemmError(need, "gemm_f32_splitk_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=a.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(a.device):
+        st = gemm_f32_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, wp, wbytes, splits, _stream_handle(stream, a.device))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_f32_splitk")
+    return out
 
 
 def matmul(a, b, out=None, variant: int = VARIANT_AUTO, stream=None):

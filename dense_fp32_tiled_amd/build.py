@@ -2,8 +2,10 @@
 
     python -m dense_fp32_tiled_amd.build
 
-produces dense_fp32_tiled_amd/libdense_fp32_tiled.so from csrc/gemm_api.hip
-and the LDS bank-geometry probe liblds_probe.so from csrc/lds_probe.hip.
+first runs the host LDS layout search (csrc/layout_gen.cpp -> 
+csrc/generated/mfma_layouts.hpp), then produces
+dense_fp32_tiled_amd/libdense_fp32_tiled.so from csrc/gemm_api.hip and the
+LDS bank-geometry probe liblds_probe.so from csrc/lds_probe.hip.
 Packed fp32 VALU instructions are disabled for all device code
 (-packed-fp32-ops); hipcc's host pass warns that it does not know that
 feature, which is harmless.
@@ -42,6 +44,25 @@ def hipcc() -> str:
     return str(Path(rocm) / "bin" / "hipcc")
 
 
+GENERATED = CSRC / "generated"
+LAYOUT_GEN_SRC = CSRC / "layout_gen.cpp"
+LAYOUT_HEADER = GENERATED / "mfma_layouts.hpp"
+
+
+def generate_layouts() -> Path:
+    """Compile and run the host layout search (layout_gen.cpp, plain C++17
+    with g++), writing csrc/generated/mfma_layouts.hpp for the kernels."""
+    GENERATED.mkdir(exist_ok=True)
+    exe = GENERATED / "layout_gen"
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", f"-I{CSRC}", str(LAYOUT_GEN_SRC), "-o", str(exe)],
+                   check=True)
+    text = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    tmp = LAYOUT_HEADER.with_suffix(".tmp")
+    tmp.write_text(text)
+    os.replace(tmp, LAYOUT_HEADER)
+    return LAYOUT_HEADER
+
+
 def build(out: Path = LIB, extra: list[str] | None = None, sources: list[Path] | None = None) -> Path:
     """Compile the library (always recompiles)."""
     tmp = out.with_name(out.name + ".tmp")
@@ -56,6 +77,7 @@ def build(out: Path = LIB, extra: list[str] | None = None, sources: list[Path] |
 
 
 def build_all() -> list[Path]:
+    generate_layouts()
     return [build(LIB, sources=SOURCES), build(PROBE_LIB, sources=PROBE_SOURCES)]
 
 

@@ -8,19 +8,34 @@
 
 #include "dense_fp32_tiled.h"
 #include "gemm_kernels.hpp"
+#include "generated/mfma_layouts.hpp"
 #include "pad_choice.hpp"
+#include <type_traits>
 
 namespace {
 
 using namespace dft;
 
 // ---- tile configurations ------------------------------------------------------
-constexpr MfmaShape kMfmaShape{128, 128, 16, 64, 64, 256, 4};
-constexpr int kMfmaPadA = mfma_pad_a(kMfmaShape, kGfx950Lds);
-constexpr int kMfmaPadB = mfma_pad_b(kMfmaShape, kGfx950Lds);
+// LDS layouts come from the host layout search (generated/mfma_layouts.hpp,
+// one entry per shape in mfma_shapes.def and global load width).
+template <class L, int STAGES, int VEC, int BM, int BN, int BK, int MB>
+using MfmaAt = MfmaCfg<BM, BN, BK, 64, 64, STAGES, MB, typename L::A, typename L::B, VEC, kXcdGroupedOrder>;
 
-template <int STAGES, int PADA, int PADB, int VEC>
-using MfmaT = MfmaCfg<128, 128, 16, 64, 64, STAGES, PADA, PADB, VEC>;
+template <int STAGES, int VEC>
+using Mfma256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_256x128x16_v4, layouts::m32_256x128x16_v1>,
+                       STAGES, VEC, 256, 128, 16, 32>;
+template <int VEC>
+using Mfma256Plain = MfmaCfg<256, 128, 16, 64, 64, 2, 32, TileLayout<0>, TileLayout<0>, VEC, kXcdGroupedOrder>;
+template <int VEC>
+using Mfma16x256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m16_256x128x16_v4, layouts::m16_256x128x16_v1>,
+                          2, VEC, 256, 128, 16, 16>;
+template <int VEC>
+using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
+                       2, VEC, 128, 128, 16, 32>;
+template <int VEC>
+using Mfma128Bk32 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x32_v4, layouts::m32_128x128x32_v1>,
+                           2, VEC, 128, 128, 32, 32>;
 
 constexpr ValuShape kValuShape{128, 128, 16, 16, 256, 4};
 constexpr int kValuPadA = valu_pad_a(kValuShape, kGfx950Lds);
@@ -39,107 +54,132 @@ struct Args {
     int64_t ldc;
 };
 
-using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
+struct Split;
+using LaunchFn = hipError_t (*)(const Args&, Split, hipStream_t);
 
 // Launches go through hipLaunchKernel so that the returned status is this
 // launch's own (hipGetLastError would also report errors left by earlier,
 // unrelated runtime calls on the thread).
+// K slicing of one launch: `splits` slices of k_chunk (a multiple of BK)
+// along gridDim.y, slice s writing C + s * c_split_stride.  A plain launch is
+// one slice covering all of K.
+struct Split {
+    int64_t splits = 1, k_chunk = 0, c_split_stride = 0;
+};
+
 template <class Kernel>
-hipError_t launch_tiles(Kernel kernel, int bm, int bn, int threads, const Args& a, hipStream_t stream) {
+hipError_t launch_tiles(Kernel kernel, int bm, int bn, int threads, const Args& a, Split sp, hipStream_t stream) {
     int64_t M = a.M, N = a.N, K = a.K, lda = a.lda, ldb = a.ldb, ldc = a.ldc;
     const float* A = a.A;
     const float* B = a.B;
     float* C = a.C;
-    const int64_t tiles_m = (M + bm - 1) / bm;
+    int64_t tiles_m = (M + bm - 1) / bm;
     int64_t tiles_n = (N + bn - 1) / bn;
-    void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)(tiles_m * tiles_n)),
+    int64_t k_chunk = sp.splits > 1 ? sp.k_chunk : (K > 0 ? K : 1);
+    int64_t c_split_stride = sp.c_split_stride;
+    void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_m, &tiles_n, &k_chunk, &c_split_stride};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)(tiles_m * tiles_n), (unsigned)sp.splits),
                            dim3(threads), args, 0, stream);
 }
 
 template <class Cfg>
-hipError_t launch_mfma(const Args& a, hipStream_t stream) {
-    return launch_tiles(gemm_mfma_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, stream);
+hipError_t launch_mfma(const Args& a, Split sp, hipStream_t stream) {
+    return launch_tiles(gemm_mfma_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
 }
 
 template <class Cfg>
-hipError_t launch_valu(const Args& a, hipStream_t stream) {
-    return launch_tiles(gemm_valu_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, stream);
+hipError_t launch_valu(const Args& a, Split sp, hipStream_t stream) {
+    return launch_tiles(gemm_valu_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
+}
+
+template <class Cfg>
+void describe_common(gemm_tile_config& c, int variant, int vec) {
+    c.variant = variant;
+    c.bm = Cfg::BM; c.bn = Cfg::BN; c.bk = Cfg::BK;
+    c.threads = Cfg::THREADS; c.wave_size = kWave;
+    c.stages = Cfg::STAGES;
+    c.barriers_per_tile = Cfg::STAGES == 2 ? 1 : 2;
+    using TA = typename Cfg::TileA;
+    using TB = typename Cfg::TileB;
+    c.a_rows = TA::rows; c.a_cols = TA::cols; c.a_pad = TA::pad;
+    c.a_row_stride = TA::row_stride; c.a_stage_elems = TA::stage_elems;
+    c.b_rows = TB::rows; c.b_cols = TB::cols; c.b_pad = TB::pad;
+    c.b_row_stride = TB::row_stride; c.b_stage_elems = TB::stage_elems;
+    c.a_swz_unit = TA::swizzle.unit; c.a_swz_shift = TA::swizzle.shift; c.a_swz_mask = TA::swizzle.mask;
+    c.b_swz_unit = TB::swizzle.unit; c.b_swz_shift = TB::swizzle.shift; c.b_swz_mask = TB::swizzle.mask;
+    c.lds_bytes = Cfg::LDS_BYTES;
+    c.vec_width = vec;
+    c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
+    c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
+    c.xcd_tile_order = Cfg::ORDER == kXcdGroupedOrder ? 1 : 0;
 }
 
 template <class Cfg>
 gemm_tile_config mfma_config(int variant, int vec) {
     gemm_tile_config c{};
-    c.variant = variant;
-    c.bm = Cfg::BM; c.bn = Cfg::BN; c.bk = Cfg::BK;
-    c.threads = Cfg::THREADS; c.wave_size = kWave;
+    describe_common<Cfg>(c, variant, vec);
     c.tm = Cfg::WM; c.tn = Cfg::WN;
-    c.stages = Cfg::STAGES;
-    c.barriers_per_tile = Cfg::STAGES == 2 ? 1 : 2;
-    c.a_rows = Cfg::TileA::rows; c.a_cols = Cfg::TileA::cols; c.a_pad = Cfg::TileA::pad;
-    c.a_row_stride = Cfg::TileA::row_stride; c.a_stage_elems = Cfg::TileA::stage_elems;
-    c.b_rows = Cfg::TileB::rows; c.b_cols = Cfg::TileB::cols; c.b_pad = Cfg::TileB::pad;
-    c.b_row_stride = Cfg::TileB::row_stride; c.b_stage_elems = Cfg::TileB::stage_elems;
-    c.lds_bytes = Cfg::LDS_BYTES;
-    c.vec_width = vec;
-    c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
-    c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.a_transposed = 0;
+    c.mfma_block = Cfg::Op::MB;
     return c;
 }
 
 template <class Cfg>
 gemm_tile_config valu_config(int variant, int vec) {
     gemm_tile_config c{};
-    c.variant = variant;
-    c.bm = Cfg::BM; c.bn = Cfg::BN; c.bk = Cfg::BK;
-    c.threads = Cfg::THREADS; c.wave_size = kWave;
+    describe_common<Cfg>(c, variant, vec);
     c.tm = Cfg::TM; c.tn = Cfg::TN;
-    c.stages = Cfg::STAGES;
-    c.barriers_per_tile = Cfg::STAGES == 2 ? 1 : 2;
-    c.a_rows = Cfg::TileA::rows; c.a_cols = Cfg::TileA::cols; c.a_pad = Cfg::TileA::pad;
-    c.a_row_stride = Cfg::TileA::row_stride; c.a_stage_elems = Cfg::TileA::stage_elems;
-    c.b_rows = Cfg::TileB::rows; c.b_cols = Cfg::TileB::cols; c.b_pad = Cfg::TileB::pad;
-    c.b_row_stride = Cfg::TileB::row_stride; c.b_stage_elems = Cfg::TileB::stage_elems;
-    c.lds_bytes = Cfg::LDS_BYTES;
-    c.vec_width = vec;
-    c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
-    c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.a_transposed = 1;
+    c.mfma_block = 0;
     return c;
 }
 
 struct Variant {
     LaunchFn vec4;    // 16-byte global loads (needs aligned A/B and ld % 4 == 0)
     LaunchFn scalar;  // 4-byte masked loads, any alignment
-    gemm_tile_config (*config)(int variant, int vec);
+    gemm_tile_config (*config4)(int variant, int vec);
+    gemm_tile_config (*config1)(int variant, int vec);
     int lds_bytes;
 };
 
+template <class C4, class C1>
+Variant mfma_variant() {
+    return Variant{launch_mfma<C4>, launch_mfma<C1>, mfma_config<C4>, mfma_config<C1>,
+                   C4::LDS_BYTES > C1::LDS_BYTES ? C4::LDS_BYTES : C1::LDS_BYTES};
+}
+
+// Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
+// to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO   */ {launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 4>>, launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 1>>,
-                  mfma_config<MfmaT<2, kMfmaPadA, kMfmaPadB, 4>>, MfmaT<2, kMfmaPadA, kMfmaPadB, 4>::LDS_BYTES},
-    /* MFMA   */ {launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 4>>, launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 1>>,
-                  mfma_config<MfmaT<2, kMfmaPadA, kMfmaPadB, 4>>, MfmaT<2, kMfmaPadA, kMfmaPadB, 4>::LDS_BYTES},
-    /* VALU   */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, ValuT<4>::LDS_BYTES},
-    /* STAGES1*/ {launch_mfma<MfmaT<1, kMfmaPadA, kMfmaPadB, 4>>, launch_mfma<MfmaT<1, kMfmaPadA, kMfmaPadB, 1>>,
-                  mfma_config<MfmaT<1, kMfmaPadA, kMfmaPadB, 4>>, MfmaT<1, kMfmaPadA, kMfmaPadB, 4>::LDS_BYTES},
-    /* NOPAD  */ {launch_mfma<MfmaT<2, 0, 0, 4>>, launch_mfma<MfmaT<2, 0, 0, 1>>, mfma_config<MfmaT<2, 0, 0, 4>>,
-                  MfmaT<2, 0, 0, 4>::LDS_BYTES},
-    /* SCALAR */ {launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 1>>, launch_mfma<MfmaT<2, kMfmaPadA, kMfmaPadB, 1>>,
-                  mfma_config<MfmaT<2, kMfmaPadA, kMfmaPadB, 1>>, MfmaT<2, kMfmaPadA, kMfmaPadB, 1>::LDS_BYTES},
+    /* AUTO          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
+    /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
+    /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, valu_config<ValuT<1>>,
+                         ValuT<4>::LDS_BYTES},
+    /* MFMA_STAGES1  */ mfma_variant<Mfma256<1, 4>, Mfma256<1, 1>>(),
+    /* MFMA_NOPAD    */ mfma_variant<Mfma256Plain<4>, Mfma256Plain<1>>(),
+    /* MFMA_SCALAR   */ mfma_variant<Mfma256<2, 1>, Mfma256<2, 1>>(),
+    /* MFMA16        */ mfma_variant<Mfma16x256<4>, Mfma16x256<1>>(),
+    /* MFMA_128      */ mfma_variant<Mfma128<4>, Mfma128<1>>(),
+    /* MFMA_128_BK32 */ mfma_variant<Mfma128Bk32<4>, Mfma128Bk32<1>>(),
 };
+
+int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
+    const int64_t tiles256 = ((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles256 >= num_cus) return GEMM_VARIANT_MFMA;
+    return K >= 4096 ? GEMM_VARIANT_MFMA_128_BK32 : GEMM_VARIANT_MFMA_128;
+}
 
 // ---- per-device properties (cached) ---------------------------------------------
 struct DeviceInfo {
     int state;  // 0 unknown, 1 gfx950, -1 unsupported
     int max_lds;
+    int num_cus;
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_devices_mu;
 
-int device_check(int* max_lds) {
+int device_check(int* max_lds, int* num_cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
@@ -150,9 +190,11 @@ int device_check(int* max_lds) {
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
         d.state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
         d.max_lds = (int)prop.sharedMemPerBlock;
+        d.num_cus = prop.multiProcessorCount;
     }
     if (d.state != 1) return GEMM_ERR_UNSUPPORTED;
     *max_lds = d.max_lds;
+    *num_cus = d.num_cus;
     return GEMM_OK;
 }
 
@@ -188,38 +230,131 @@ int validate(const Args& a) {
     return GEMM_OK;
 }
 
-int run(const Args& a, hipStream_t stream, int variant) {
-    if (variant < 0 || variant >= GEMM_VARIANT_COUNT) return GEMM_ERR_UNSUPPORTED;
+int launch_zero_fill(const Args& a, hipStream_t stream) {
+    const int64_t total = a.M * a.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    int64_t M = a.M, N = a.N, ldc = a.ldc;
+    float* C = a.C;
+    void* args[] = {&M, &N, &C, &ldc};
+    return hipLaunchKernel(reinterpret_cast<const void*>(zero_fill_kernel), dim3((unsigned)blocks), dim3(256), args,
+                           0, stream) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+// Checks shared by every entry point; on GEMM_OK with *done set, nothing is
+// left to do (empty M or N, or K == 0 handled by a zero fill).
+int prologue(const Args& a, hipStream_t stream, int* max_lds, int* num_cus, bool* done) {
+    *done = false;
     int st = validate(a);
     if (st != GEMM_OK) return st;
-    if (a.M == 0 || a.N == 0) return GEMM_OK;
-    int max_lds = 0;
-    st = device_check(&max_lds);
-    if (st != GEMM_OK) return st;
-
-    if (a.K == 0) {
-        const int64_t total = a.M * a.N;
-        int64_t blocks = (total + 255) / 256;
-        if (blocks > 65536) blocks = 65536;
-        int64_t M = a.M, N = a.N, ldc = a.ldc;
-        float* C = a.C;
-        void* args[] = {&M, &N, &C, &ldc};
-        return hipLaunchKernel(reinterpret_cast<const void*>(zero_fill_kernel), dim3((unsigned)blocks), dim3(256),
-                               args, 0, stream) == hipSuccess
-                   ? GEMM_OK
-                   : GEMM_ERR_HIP;
+    if (a.M == 0 || a.N == 0) {
+        *done = true;
+        return GEMM_OK;
     }
+    st = device_check(max_lds, num_cus);
+    if (st != GEMM_OK) return st;
+    if (a.K == 0) {
+        *done = true;
+        return launch_zero_fill(a, stream);
+    }
+    return GEMM_OK;
+}
 
+int launch_variant(const Args& a, int variant, int max_lds, Split sp, hipStream_t stream) {
     const Variant& v = kVariants[variant];
     if (v.lds_bytes > max_lds) return GEMM_ERR_CONFIG;
-    const gemm_tile_config cfg = v.config(variant, 4);
+    const gemm_tile_config cfg = v.config4(variant, 4);
     const int64_t tiles = ((a.M + cfg.bm - 1) / cfg.bm) * ((a.N + cfg.bn - 1) / cfg.bn);
     if (tiles > (int64_t)0x7fffffff / cfg.threads) return GEMM_ERR_TOO_LARGE;
-
     const bool aligned = (a.lda % 4 == 0) && (a.ldb % 4 == 0) && (((uintptr_t)a.A & 15) == 0) &&
                          (((uintptr_t)a.B & 15) == 0);
     const LaunchFn fn = aligned ? v.vec4 : v.scalar;
-    return fn(a, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    return fn(a, sp, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int run(const Args& a, hipStream_t stream, int variant) {
+    if (variant < 0 || variant >= GEMM_VARIANT_COUNT) return GEMM_ERR_UNSUPPORTED;
+    int max_lds = 0, num_cus = 0;
+    bool done = false;
+    const int st = prologue(a, stream, &max_lds, &num_cus, &done);
+    if (st != GEMM_OK || done) return st;
+    if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(a.M, a.N, a.K, num_cus);
+    return launch_variant(a, variant, max_lds, Split{}, stream);
+}
+
+// ---- split-K ------------------------------------------------------------------------
+constexpr int kSplitKVariant = GEMM_VARIANT_MFMA_128;
+constexpr int64_t kSplitKTileBk = 16;  // BK of kSplitKVariant: slices are multiples of it
+constexpr int kMaxSplits = 64;
+
+int64_t splitk_chunk(int64_t K, int64_t splits) {
+    const int64_t tiles = (K + kSplitKTileBk - 1) / kSplitKTileBk;
+    return ((tiles + splits - 1) / splits) * kSplitKTileBk;
+}
+
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) { return splits * M * N * 4; }
+
+int splitk_auto_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
+    // Enough slices to give every CU four workgroups (the occupancy of the
+    // 128x128 kernel), keeping at least eight K tiles per slice.
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t ktiles = (K + kSplitKTileBk - 1) / kSplitKTileBk;
+    int64_t s = (4 * (int64_t)num_cus + tiles - 1) / tiles;
+    if (s > ktiles / 8) s = ktiles / 8;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
+}
+
+int check_workspace(const Args& a, const void* workspace, int64_t workspace_bytes, int splits) {
+    if (splits <= 1) return GEMM_OK;
+    const int64_t need = splitk_workspace_bytes(a.M, a.N, splits);
+    if (workspace == nullptr || workspace_bytes < need) return GEMM_ERR_WORKSPACE;
+    if (overlaps(workspace, need, a.C, span_bytes(a.M, a.N, a.ldc)) ||
+        overlaps(workspace, need, a.A, span_bytes(a.M, a.K, a.lda)) ||
+        overlaps(workspace, need, a.B, span_bytes(a.K, a.N, a.ldb)))
+        return GEMM_ERR_ALIAS;
+    return GEMM_OK;
+}
+
+int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int splits, hipStream_t stream) {
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_DIM;
+    int st = validate(a);
+    if (st != GEMM_OK) return st;
+    // an explicit split count is checked against the workspace before any device call
+    if (a.M > 0 && a.N > 0 && a.K > 0 && splits > 1) {
+        st = check_workspace(a, workspace, workspace_bytes, splits);
+        if (st != GEMM_OK) return st;
+    }
+    int max_lds = 0, num_cus = 0;
+    bool done = false;
+    st = prologue(a, stream, &max_lds, &num_cus, &done);
+    if (st != GEMM_OK || done) return st;
+    if (splits == 0) {
+        splits = splitk_auto_splits(a.M, a.N, a.K, num_cus);
+        st = check_workspace(a, workspace, workspace_bytes, splits);
+        if (st != GEMM_OK) return st;
+    }
+    if (splits == 1) return launch_variant(a, kSplitKVariant, max_lds, Split{}, stream);
+    // 1. every slice writes its partial product, packed M x N, into the workspace
+    Args part = a;
+    part.C = static_cast<float*>(workspace);
+    part.ldc = a.N;
+    const Split sp{splits, splitk_chunk(a.K, splits), a.M * a.N};
+    st = launch_variant(part, kSplitKVariant, max_lds, sp, stream);
+    if (st != GEMM_OK) return st;
+    // 2. C = sum of the slices in ascending slice order
+    int64_t M = a.M, N = a.N, S = splits, ldc = a.ldc;
+    const float* W = static_cast<const float*>(workspace);
+    float* C = a.C;
+    int64_t blocks = (M * N + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    void* args[] = {&M, &N, &S, &W, &C, &ldc};
+    return hipLaunchKernel(reinterpret_cast<const void*>(splitk_reduce_kernel), dim3((unsigned)blocks), dim3(256),
+                           args, 0, stream) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
 }
 
 }  // namespace
@@ -240,9 +375,46 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, co
 int gemm_f32_tile_config(int variant, gemm_tile_config* out) {
     if (out == nullptr) return GEMM_ERR_NULL;
     if (variant < 0 || variant >= GEMM_VARIANT_COUNT) return GEMM_ERR_UNSUPPORTED;
-    const int vec = variant == GEMM_VARIANT_MFMA_SCALAR ? 1 : 4;
-    *out = kVariants[variant].config(variant, vec);
+    *out = variant == GEMM_VARIANT_MFMA_SCALAR ? kVariants[variant].config1(variant, 1)
+                                               : kVariants[variant].config4(variant, 4);
     return GEMM_OK;
+}
+
+int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
+    if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+    return auto_variant(M, N, K, num_cus);
+}
+
+int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
+                                int32_t vec, int32_t* out) {
+    if (out == nullptr || (mb != 32 && mb != 16) || (vec != 1 && vec != 4)) return GEMM_ERR_INVALID_DIM;
+    if (bm < 1 || bn < 1 || bk < 1 || wm < mb || wn < mb || bm % wm || bn % wn || wm % mb || wn % mb)
+        return GEMM_ERR_INVALID_DIM;
+    const int kb = 64 / mb, threads = (bm / wm) * (bn / wn) * kWaveLanes;
+    if (bk % (4 * kb) || bk % vec || bn % vec || threads > 1024 || (bm * bk / vec) % threads ||
+        (bk * bn / vec) % threads)
+        return GEMM_ERR_INVALID_DIM;
+    const MfmaShape shape{bm, bn, bk, wm, wn, threads, vec, mb, mb, kb};
+    const LayoutChoice a = mfma_layout_a(shape, kGfx950Lds), b = mfma_layout_b(shape, kGfx950Lds);
+    const int32_t v[8] = {a.pad, a.swz.unit, a.swz.shift, a.swz.mask, b.pad, b.swz.unit, b.swz.shift, b.swz.mask};
+    for (int i = 0; i < 8; ++i) out[i] = v[i];
+    return GEMM_OK;
+}
+
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                    float* C, int64_t ldc, void* workspace, int64_t workspace_bytes, int splits, void* stream) {
+    return run_splitk(Args{M, N, K, A, lda, B, ldb, C, ldc}, workspace, workspace_bytes, splits, (hipStream_t)stream);
+}
+
+int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits, int32_t num_cus) {
+    if (M < 0 || N < 0 || K < 0 || splits < 0 || splits > kMaxSplits || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+    if (splits == 0) splits = splitk_auto_splits(M, N, K, num_cus);
+    return splits > 1 ? splitk_workspace_bytes(M, N, splits) : 0;
+}
+
+int gemm_f32_splitk_auto_splits(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
+    if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+    return splitk_auto_splits(M, N, K, num_cus);
 }
 
 const char* gemm_f32_status_string(int status) {
@@ -256,6 +428,7 @@ const char* gemm_f32_status_string(int status) {
         case GEMM_ERR_CONFIG: return "tile configuration exceeds the device's LDS per workgroup";
         case GEMM_ERR_HIP: return "HIP runtime error or launch failure";
         case GEMM_ERR_TOO_LARGE: return "problem too large for the kernel's index range";
+        case GEMM_ERR_WORKSPACE: return "split-K workspace missing or smaller than gemm_f32_splitk_workspace_bytes";
         default: return "unknown status";
     }
 }

@@ -117,55 +117,143 @@ struct TileLoader {
     }
 };
 
-// Workgroup -> output tile.  Plain row-major order over the tile grid.
+// Workgroup -> output tile.
 struct TileCoord {
     int64_t m0, n0;
 };
-__device__ inline TileCoord tile_of_block(int64_t tiles_n, int bm, int bn) {
-    const int64_t b = blockIdx.x;
+
+// Plain row-major order over the tile grid.
+__device__ inline TileCoord tile_row_major(int64_t b, int64_t tiles_n, int bm, int bn) {
     return TileCoord{(b / tiles_n) * bm, (b % tiles_n) * bn};
 }
 
+// XCD-aware order.  The dispatcher hands workgroup b to XCD b % 8, and each
+// XCD has its own L2.  Workgroups are first renumbered so that every XCD's
+// share is one contiguous range of tile indices, then tile indices walk the
+// grid GROUP_M tile rows at a time, column-major inside a group, so an XCD's
+// tiles form a compact block that shares A rows and B columns in its L2.
+template <int GROUP_M>
+__device__ inline TileCoord tile_xcd_grouped(int64_t b, int64_t tiles_m, int64_t tiles_n, int bm, int bn) {
+    constexpr int64_t kXcds = 8;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t q = tiles / kXcds, rem = tiles % kXcds;
+    const int64_t x = b % kXcds, j = b / kXcds;
+    const int64_t t = x < rem ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
+    const int64_t per_group = GROUP_M * tiles_n;
+    const int64_t first = (t / per_group) * GROUP_M;
+    const int64_t rows = tiles_m - first < GROUP_M ? tiles_m - first : GROUP_M;
+    const int64_t in = t % per_group;
+    return TileCoord{(first + in % rows) * bm, (in / rows) * bn};
+}
+
 // --------------------------------------------------------------------------
-// Matrix-core variant.  4 wavefronts as WAVES_M x WAVES_N; each wavefront owns
-// a WM x WN sub-tile made of 32x32 blocks computed by v_mfma_f32_32x32x2_f32.
+// Matrix-core variant.  Wavefronts tile the workgroup's BM x BN block as
+// WAVES_M x WAVES_N; each owns a WM x WN sub-tile of MB x NB MFMA blocks.
 //
-// Operand layout of v_mfma_f32_32x32x2_f32 (lane l, h = l / 32, r = l % 32):
-//   A operand: A[row r][k h],   B operand: B[k h][col r],
-//   result register v (0..15): D[row 8*(v/4) + 4*h + v%4][col r].
-// Within a BK tile, lane half h reduces the k range [h*BK/2, (h+1)*BK/2): MFMA
-// step j consumes k = h*BK/2 + j for half h.  Every k of the tile is used
-// exactly once per output element (a permutation of the summation order),
-// and each lane's A values for one tile are BK/2 consecutive floats of one
-// LDS row, read with 16-byte loads.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int PADA_, int PADB_, int VEC_>
+// fp32 MFMA operand layouts (lane l, g = l / MB, r = l % MB):
+//   A operand: A[row r][k g],  B operand: B[k g][col r]  (KB = 64 / MB k-groups)
+//   v_mfma_f32_32x32x2_f32: result register v (0..15) is D[8*(v/4) + 4*g + v%4][r]
+//   v_mfma_f32_16x16x4_f32: result register v (0..3)  is D[4*g + v][r]
+// Within a BK tile, k-group g reduces k in [g*KG, (g+1)*KG), KG = BK / KB:
+// MFMA step j consumes k = g*KG + j for group g.  Every k of the tile is used
+// exactly once per output element (a permutation of the summation order), and
+// each lane's A values for one tile are KG consecutive floats of one LDS row,
+// read with 16-byte loads.
+template <int MB, int KB>
+struct MfmaOp;
+
+template <>
+struct MfmaOp<32, 2> {
+    static constexpr int MB = 32, NB = 32, KB = 2, ACC = 16;
+    using acc_t = floatx16;
+    __device__ static acc_t mma(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static int out_row(int lane, int v) { return 8 * (v / 4) + 4 * (lane / 32) + (v % 4); }
+};
+
+template <>
+struct MfmaOp<16, 4> {
+    static constexpr int MB = 16, NB = 16, KB = 4, ACC = 4;
+    using acc_t = floatx4;
+    __device__ static acc_t mma(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static int out_row(int lane, int v) { return 4 * (lane / 16) + v; }
+};
+
+// LDS layout of one operand tile: row pad, or XOR swizzle (see LdsTile).
+template <int Pad, int Unit = 0, int Shift = 0, int Mask = 0>
+struct TileLayout {
+    static constexpr int pad = Pad, unit = Unit, shift = Shift, mask = Mask;
+};
+
+enum TileOrder { kRowMajorOrder = 0, kXcdGroupedOrder = 1 };
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MB_, class LayA, class LayB, int VEC_,
+          int ORDER_ = kRowMajorOrder>
 struct MfmaCfg {
+    using Op = MfmaOp<MB_, 64 / MB_>;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int STAGES = STAGES_, PADA = PADA_, PADB = PADB_, VEC = VEC_;
+    static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
-    static constexpr int MI = WM / 32, NI = WN / 32;
-    static constexpr int KH = BK / 2;  // k values per lane half per tile
+    static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
+    static constexpr int KG = BK / Op::KB;  // k values per lane group per tile
     // Register budget: 4 waves per SIMD (<= 128 VGPRs) for the 16-byte load
     // path, so that four 256-thread workgroups fit on a CU; the 4-byte load
     // path holds 4x more load registers and is limited to 2 waves per SIMD.
-    static constexpr int MIN_WAVES = VEC == 4 ? 4 : 2;
-    using TileA = LdsTile<BM, BK, PADA, STAGES>;
-    using TileB = LdsTile<BK, BN, PADB, STAGES>;
+    static constexpr int MIN_WAVES = (VEC == 4 && WM * WN <= 64 * 64) ? 4 : 2;
+    using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;
+    using TileB = LdsTile<BK, BN, LayB::pad, STAGES, LayB::unit, LayB::shift, LayB::mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
-    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
-    static_assert(KH % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
+    static_assert(KG % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
     static_assert(TileB::row_stride % VEC == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
     static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
 };
 
 template <class Cfg>
+__device__ inline TileCoord tile_of_block(int64_t tiles_m, int64_t tiles_n) {
+    if constexpr (Cfg::ORDER == kXcdGroupedOrder)
+        return tile_xcd_grouped<8>(blockIdx.x, tiles_m, tiles_n, Cfg::BM, Cfg::BN);
+    else
+        return tile_row_major(blockIdx.x, tiles_n, Cfg::BM, Cfg::BN);
+}
+
+// Slice of the K range a workgroup reduces: blockIdx.y selects k in
+// [y * k_chunk, min(K, (y + 1) * k_chunk)) and output C + y * c_split_stride
+// (split-K); a plain launch has gridDim.y == 1 and k_chunk >= K.  k_chunk is a
+// multiple of BK, so 16-byte alignment of the operand tiles is preserved.
+struct KSlice {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t K;  // length of this slice (may be <= 0: an empty sum)
+};
+__device__ inline KSlice k_slice(const float* A, const float* B, float* C, int64_t K, int64_t ldb, int64_t k_chunk,
+                                 int64_t c_split_stride) {
+    const int64_t y = blockIdx.y;
+    const int64_t kb = y * k_chunk;
+    const int64_t len = K - kb < k_chunk ? K - kb : k_chunk;
+    return KSlice{A + kb, B + kb * ldb, C + y * c_split_stride, len};
+}
+
+template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel(
-    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
+    int64_t M, int64_t N, int64_t K_total, const float* __restrict__ A_in, int64_t lda,
+    const float* __restrict__ B_in, int64_t ldb, float* __restrict__ C_out, int64_t ldc, int64_t tiles_m,
+    int64_t tiles_n, int64_t k_chunk, int64_t c_split_stride) {
+    const KSlice ks = k_slice(A_in, B_in, C_out, K_total, ldb, k_chunk, c_split_stride);
+    const float* __restrict__ A = ks.A;
+    const float* __restrict__ B = ks.B;
+    float* __restrict__ C = ks.C;
+    const int64_t K = ks.K;
+    using Op = typename Cfg::Op;
     using TileA = typename Cfg::TileA;
     using TileB = typename Cfg::TileB;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, KH = Cfg::KH;
+    using acc_t = typename Op::acc_t;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, KG = Cfg::KG;
     constexpr int MI = Cfg::MI, NI = Cfg::NI, THREADS = Cfg::THREADS;
 
     __shared__ __attribute__((aligned(16))) float lds_a[TileA::total_elems];
@@ -176,24 +264,24 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
     const int wave = tid / kWave;
     const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
     const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
-    const int h = lane / 32, r = lane % 32;
+    const int g = lane / Op::MB, r = lane % Op::MB;
 
-    const TileCoord tc = tile_of_block(tiles_n, BM, BN);
+    const TileCoord tc = tile_of_block<Cfg>(tiles_m, tiles_n);
     const int64_t m0 = tc.m0, n0 = tc.n0;
 
-    floatx16 acc[MI][NI];
+    acc_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
 
     TileLoader<BM, BK, THREADS, Cfg::VEC> ldr_a;
     TileLoader<BK, BN, THREADS, Cfg::VEC> ldr_b;
     const float* a_tile = A + m0 * lda;  // advances by BK columns per K tile
     const float* b_tile = B + n0;        // advances by BK rows per K tile
-    const int64_t T = (K + BK - 1) / BK;
+    const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
 
     auto load_tile = [&](int64_t t) {
         const int64_t k0 = t * BK;
@@ -201,23 +289,22 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, tid);
     };
     auto multiply = [&](int stage) {
-        floatx4 af[MI][KH / 4];
+        floatx4 af[MI][KG / 4];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int q = 0; q < KH / 4; ++q)
+            for (int q = 0; q < KG / 4; ++q)
                 af[i][q] = *reinterpret_cast<const floatx4*>(
-                    lds_a + TileA::offset(stage, wm0 + i * 32 + r, h * KH + 4 * q));
+                    lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, g * KG + 4 * q));
 #pragma unroll
-        for (int j = 0; j < KH; ++j) {
+        for (int j = 0; j < KG; ++j) {
             float bf[NI];
 #pragma unroll
-            for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, h * KH + j, wn0 + n * 32 + r)];
+            for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, g * KG + j, wn0 + n * Op::NB + r)];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int n = 0; n < NI; ++n)
-                    acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][j / 4][j % 4], bf[n], acc[i][n], 0, 0, 0);
+                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[n], acc[i][n]);
         }
     };
 
@@ -253,18 +340,19 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
 
     // Store: unmasked when the whole BM x BN tile is in range (a uniform
     // branch), else under the mask rows < M and columns < N.  For a fixed
-    // result register, lanes 0-31 write 32 consecutive floats of one row.
+    // result register, the MB lanes of a k-group write consecutive floats of
+    // one row.
     const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
-            const int64_t gn = n0 + wn0 + n * 32 + r;
-            const int64_t gm0 = m0 + wm0 + i * 32 + 4 * h;
+            const int64_t gn = n0 + wn0 + n * Op::NB + r;
+            const int64_t gm0 = m0 + wm0 + i * Op::MB;
             float* cp = C + gm0 * ldc + gn;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int dr = 8 * (v / 4) + (v % 4);
+            for (int v = 0; v < Op::ACC; ++v) {
+                const int dr = Op::out_row(lane, v);
                 if (full || (gm0 + dr < M && gn < N)) cp[dr * ldc] = acc[i][n][v];
             }
         }
@@ -284,6 +372,7 @@ struct ValuCfg {
     static constexpr int THREADS_M = BM / TM, THREADS_N = BN / TN;
     static constexpr int THREADS = THREADS_M * THREADS_N;
     static constexpr int MIN_WAVES = 2;
+    static constexpr int ORDER = kRowMajorOrder;
     using TileA = LdsTile<BK, BM, PADA, STAGES>;  // k-major
     using TileB = LdsTile<BK, BN, PADB, STAGES>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
@@ -293,8 +382,14 @@ struct ValuCfg {
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel(
-    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
+    int64_t M, int64_t N, int64_t K_total, const float* __restrict__ A_in, int64_t lda,
+    const float* __restrict__ B_in, int64_t ldb, float* __restrict__ C_out, int64_t ldc, int64_t tiles_m,
+    int64_t tiles_n, int64_t k_chunk, int64_t c_split_stride) {
+    const KSlice ks = k_slice(A_in, B_in, C_out, K_total, ldb, k_chunk, c_split_stride);
+    const float* __restrict__ A = ks.A;
+    const float* __restrict__ B = ks.B;
+    float* __restrict__ C = ks.C;
+    const int64_t K = ks.K;
     using TileA = typename Cfg::TileA;
     using TileB = typename Cfg::TileB;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, THREADS = Cfg::THREADS;
@@ -304,7 +399,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel
 
     const int tid = threadIdx.x;
     const int ty = tid / Cfg::THREADS_N, tx = tid % Cfg::THREADS_N;
-    const TileCoord tc = tile_of_block(tiles_n, BM, BN);
+    const TileCoord tc = tile_of_block<Cfg>(tiles_m, tiles_n);
     const int64_t m0 = tc.m0, n0 = tc.n0;
 
     float acc[8][8];
@@ -317,7 +412,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel
     TileLoader<BK, BN, THREADS, Cfg::VEC> ldr_b;
     const float* a_tile = A + m0 * lda;
     const float* b_tile = B + n0;
-    const int64_t T = (K + BK - 1) / BK;
+    const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
     const int am = ty * 4, bn = tx * 4;
 
     auto load_tile = [&](int64_t t) {
@@ -405,6 +500,22 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel
                     if (gn + e < N) p[e] = acc[i][4 * half + e];
             }
         }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Split-K reduction: C[i][j] = sum over s = 0, 1, ..., S-1 (in that order) of
+// W[s][i][j], where W holds S packed M x N partial products.  The fixed order
+// makes the result deterministic.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N, int64_t S,
+                                                            const float* __restrict__ W, float* __restrict__ C,
+                                                            int64_t ldc) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = W[i];
+        for (int64_t s = 1; s < S; ++s) acc += W[s * total + i];
+        C[(i / N) * ldc + (i % N)] = acc;
     }
 }
 

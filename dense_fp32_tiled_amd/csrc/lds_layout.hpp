@@ -36,18 +36,33 @@ struct LdsLayout {
     }
 };
 
-template <int Rows, int Cols, int Pad, int Stages>
+// Optional XOR swizzle of columns by row: physical column =
+// col ^ (unit * ((row >> shift) & mask)).  unit is a multiple of 4 words, so
+// 16-byte groups of four columns stay contiguous and aligned; the XOR only
+// permutes columns within aligned blocks of unit * (mask + 1) words.
+struct Swizzle {
+    int unit, shift, mask;  // unit == 0: no swizzle
+    constexpr int apply(int row, int col) const { return unit ? (col ^ (unit * ((row >> shift) & mask))) : col; }
+};
+constexpr Swizzle kNoSwizzle{0, 0, 0};
+
+template <int Rows, int Cols, int Pad, int Stages, int SwzUnit = 0, int SwzShift = 0, int SwzMask = 0>
 struct LdsTile {
     static_assert(Rows > 0 && Cols > 0 && Pad >= 0 && Stages > 0, "invalid LDS tile");
+    static_assert(SwzUnit == 0 || (SwzUnit % 4 == 0 && (SwzMask & (SwzMask + 1)) == 0 &&
+                                   Cols % (SwzUnit * (SwzMask + 1)) == 0),
+                  "swizzle must permute 16-byte groups within aligned blocks of the row");
     static constexpr int rows = Rows, cols = Cols, pad = Pad, stages = Stages;
     static constexpr int row_stride = Cols + Pad;
     static constexpr int stage_elems = Rows * row_stride;
     static constexpr int total_elems = Stages * stage_elems;
     static constexpr int bytes = total_elems * 4;
+    static constexpr Swizzle swizzle{SwzUnit, SwzShift, SwzMask};
     static constexpr LdsLayout layout() { return LdsLayout{Rows, Cols, Pad, Stages}; }
 
-    __host__ __device__ static constexpr int offset(int stage, int row, int col) {
-        return stage * stage_elems + row * row_stride + col;
+    // constexpr functions are callable from both host and device code in HIP
+    static constexpr int offset(int stage, int row, int col) {
+        return stage * stage_elems + row * row_stride + Swizzle{SwzUnit, SwzShift, SwzMask}.apply(row, col);
     }
 };
 
@@ -89,32 +104,43 @@ constexpr int page_pad(int columns, int simultaneous_rows, int banks) {
 }
 
 // Conflict degree of one access pattern (see gemm_lds_conflict_degree in the
-// public header for the definition).  `addr(l)` gives lane l's first dword.
+// public header for the definition).  `addr(l, e)` gives the dword that lane
+// l touches as its element e (e < width); for a plain access these are
+// consecutive, for a two-address access (ds_read2) they are not.
 // Limits: group * width <= 256 dwords, banks <= 128; returns -1 beyond them.
 template <class Addr>
-constexpr int conflict_degree(Addr addr, int lanes, int width, int banks, int group) {
+constexpr int conflict_degree2(Addr addr, int lanes, int width, int banks, int group) {
     if (lanes < 1 || width < 1 || banks < 1 || banks > 128 || group < 1 || group * width > 256) return -1;
     int worst = 1;
     for (int g0 = 0; g0 < lanes; g0 += group) {
         const int g1 = g0 + group < lanes ? g0 + group : lanes;
-        int64_t words[256] = {};
-        int n = 0;
-        for (int l = g0; l < g1; ++l) {
-            for (int w = 0; w < width; ++w) {
-                const int64_t word = addr(l) + w;
-                bool seen = false;
-                for (int i = 0; i < n; ++i)
-                    if (words[i] == word) { seen = true; break; }
-                if (!seen) words[n++] = word;
-            }
-        }
+        // distinct dwords per bank, as per-bank linked lists
+        int head[128] = {};
         int count[128] = {};
-        for (int i = 0; i < n; ++i) {
-            const int b = bank_of(words[i], banks);
-            if (++count[b] > worst) worst = count[b];
+        int64_t word_of[257] = {};
+        int next_of[257] = {};
+        int n = 1;  // entry 0 is the list terminator
+        for (int l = g0; l < g1; ++l) {
+            for (int e = 0; e < width; ++e) {
+                const int64_t word = addr(l, e);
+                const int b = bank_of(word, banks);
+                bool seen = false;
+                for (int i = head[b]; i != 0; i = next_of[i])
+                    if (word_of[i] == word) { seen = true; break; }
+                if (seen) continue;
+                word_of[n] = word;
+                next_of[n] = head[b];
+                head[b] = n++;
+                if (++count[b] > worst) worst = count[b];
+            }
         }
     }
     return worst;
+}
+
+template <class Addr>
+constexpr int conflict_degree(Addr addr, int lanes, int width, int banks, int group) {
+    return conflict_degree2([=](int l, int e) { return addr(l) + e; }, lanes, width, banks, group);
 }
 
 }  // namespace dft

@@ -58,6 +58,36 @@ __device__ inline void read16(uint32_t addr, float& sink) {
     }
 }
 
+// Two-address reads: dwords at base and base + OFF1 (ds_read2_b32 offset1).
+template <int OFF1>
+__device__ inline void read2_16(uint32_t addr, float& sink) {
+    f32x2 r0, r1, r2, r3;
+    asm volatile(
+        "ds_read2_b32 %0, %4 offset1:%5\n ds_read2_b32 %1, %4 offset1:%5\n"
+        "ds_read2_b32 %2, %4 offset1:%5\n ds_read2_b32 %3, %4 offset1:%5\n"
+        "ds_read2_b32 %0, %4 offset1:%5\n ds_read2_b32 %1, %4 offset1:%5\n"
+        "ds_read2_b32 %2, %4 offset1:%5\n ds_read2_b32 %3, %4 offset1:%5\n"
+        "ds_read2_b32 %0, %4 offset1:%5\n ds_read2_b32 %1, %4 offset1:%5\n"
+        "ds_read2_b32 %2, %4 offset1:%5\n ds_read2_b32 %3, %4 offset1:%5\n"
+        "ds_read2_b32 %0, %4 offset1:%5\n ds_read2_b32 %1, %4 offset1:%5\n"
+        "ds_read2_b32 %2, %4 offset1:%5\n ds_read2_b32 %3, %4 offset1:%5\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(addr), "i"(OFF1)
+        : "memory");
+    sink += r0[0] + r1[1] + r2[0] + r3[1];
+}
+
+// MODE 1, 2, 4: ds_read_b32/b64/b128 of MODE dwords; MODE -16, -32:
+// ds_read2_b32 with offset1 16 or 32 dwords.
+template <int MODE>
+__device__ inline void read_mode(uint32_t addr, float& sink) {
+    if constexpr (MODE > 0)
+        read16<MODE>(addr, sink);
+    else
+        read2_16<-MODE>(addr, sink);
+}
+
 template <int WIDTH>
 __global__ __launch_bounds__(1024) void lds_probe_kernel(Pattern p, int reps, uint64_t* cycles_out,
                                                           float* never_written) {
@@ -70,7 +100,7 @@ __global__ __launch_bounds__(1024) void lds_probe_kernel(Pattern p, int reps, ui
     const uint32_t addr = (uint32_t)(uintptr_t)((lds_float*)buf) + (uint32_t)p.byte_addr[lane];
     float sink = 0.0f;
     const uint64_t t0 = clock64();
-    for (int r = 0; r < reps; ++r) read16<WIDTH>(addr, sink);
+    for (int r = 0; r < reps; ++r) read_mode<WIDTH>(addr, sink);
     const uint64_t t1 = clock64();
     if (lane == 0) cycles_out[threadIdx.x / 64] = t1 - t0;
     // keep the reads observable; sink is finite, so this store never happens
@@ -107,18 +137,24 @@ extern "C" int probe_copy_f32(const float* src, float* dst, int64_t n, void* str
 extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int32_t waves, int32_t reps,
                              uint64_t* cycles_out, void* stream) {
     if (lane_words == nullptr || cycles_out == nullptr) return -1;
-    if (width_words != 1 && width_words != 2 && width_words != 4) return -1;
+    if (width_words != 1 && width_words != 2 && width_words != 4 && width_words != -16 && width_words != -32)
+        return -1;
     if (waves < 1 || waves > 16 || reps < 1 || reps > 100000) return -1;
+    // dwords one lane touches past its base, and the alignment the base needs
+    const int32_t span = width_words > 0 ? width_words : -width_words + 1;
+    const int32_t align = width_words > 0 ? width_words : 1;
     Pattern p;
     for (int l = 0; l < 64; ++l) {
         const int32_t w = lane_words[l];
-        if (w < 0 || w % width_words != 0 || w + width_words > LDS_PROBE_WORDS) return -1;
+        if (w < 0 || w % align != 0 || w + span > LDS_PROBE_WORDS) return -1;
         p.byte_addr[l] = w * 4;
     }
     float* never_written = nullptr;
     void* args[] = {&p, &reps, &cycles_out, &never_written};
-    const void* kernel = width_words == 1   ? reinterpret_cast<const void*>(lds_probe_kernel<1>)
-                         : width_words == 2 ? reinterpret_cast<const void*>(lds_probe_kernel<2>)
-                                            : reinterpret_cast<const void*>(lds_probe_kernel<4>);
+    const void* kernel = width_words == 1     ? reinterpret_cast<const void*>(lds_probe_kernel<1>)
+                         : width_words == 2   ? reinterpret_cast<const void*>(lds_probe_kernel<2>)
+                         : width_words == 4   ? reinterpret_cast<const void*>(lds_probe_kernel<4>)
+                         : width_words == -16 ? reinterpret_cast<const void*>(lds_probe_kernel<-16>)
+                                              : reinterpret_cast<const void*>(lds_probe_kernel<-32>);
     return hipLaunchKernel(kernel, dim3(1), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : -2;
 }

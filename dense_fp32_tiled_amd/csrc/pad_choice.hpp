@@ -1,13 +1,16 @@
-// pad_choice.hpp -- LDS row padding for each kernel, derived at compile time
-// from the bank model and the kernel's own lane -> address patterns.
+// pad_choice.hpp -- LDS layout (row padding or XOR swizzle) for each kernel,
+// derived at compile time from the bank model and the kernel's own lane ->
+// address patterns.
 //
-// For every LDS access a kernel issues on a tile (fragment reads, cooperative
-// stores) the conflict degree is computed from the exact addresses the lanes
-// of one wavefront touch; the pad minimises the sum of degree x instructions
-// per K tile over those accesses, among pads that keep 16-byte alignment.
-// This replaces the pages' one-pattern rule ("My Triton From Scratch, Part
-// 18: Shared Memory Optimization", section "Choosing padding instead of
-// hard-coding it"), which models a single one-warp read of A.
+// For every LDS access a kernel issues on a tile (fragment reads by every
+// wavefront, cooperative stores by every thread) the conflict degree is
+// computed from the exact addresses the lanes touch; a layout's cost is the
+// sum over those accesses of passes x degree, per K tile.  Candidates are row
+// pads that keep 16-byte alignment and XOR swizzles of 16-byte column groups
+// (no pad); the cheapest wins, ties going to no change, then to a pad, then to
+// a swizzle.  This replaces the pages' one-pattern rule ("My Triton From
+// Scratch, Part 18: Shared Memory Optimization", section "Choosing padding
+// instead of hard-coding it"), which models a single one-warp read of A.
 #pragma once
 
 #include "lds_layout.hpp"
@@ -16,34 +19,13 @@ namespace dft {
 
 constexpr int kMaxPad = 32;
 
-// ---- matrix-core kernel: A row-major [BM][BK+pad], B row-major [BK][BN+pad] --
-struct MfmaShape {
-    int bm, bn, bk, wm, wn, threads, vec;
-    constexpr int kh() const { return bk / 2; }
+struct LayoutChoice {
+    int pad;
+    Swizzle swz;
 };
 
-// A fragment read (16-byte): lane l reads row l%32 at column (l/32)*BK/2.
-constexpr int mfma_a_read_degree(MfmaShape s, int pad, LdsGeometry g) {
-    const int stride = s.bk + pad;
-    return conflict_degree([=](int l) { return (int64_t)(l % 32) * stride + (l / 32) * s.kh(); },
-                           kWaveLanes, 4, g.banks_for_width(4), g.group_for_width(4));
-}
-// Cooperative store of A (vec-wide): slot l -> row l/(BK/vec), column vec*(l%(BK/vec)).
-constexpr int mfma_a_write_degree(MfmaShape s, int pad, LdsGeometry g) {
-    const int stride = s.bk + pad, vcols = s.bk / s.vec;
-    return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
-}
-// B fragment read (4-byte): lane l reads row (l/32)*BK/2 + j at column l%32.
-constexpr int mfma_b_read_degree(MfmaShape s, int pad, LdsGeometry g) {
-    const int stride = s.bn + pad;
-    return conflict_degree([=](int l) { return (int64_t)((l / 32) * s.kh()) * stride + (l % 32); },
-                           kWaveLanes, 1, g.banks_for_width(1), g.group_for_width(1));
-}
-constexpr int mfma_b_write_degree(MfmaShape s, int pad, LdsGeometry g) {
-    const int stride = s.bn + pad, vcols = s.bn / s.vec;
-    return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
+constexpr int64_t layout_word(LayoutChoice c, int cols, int row, int col) {
+    return (int64_t)row * (cols + c.pad) + c.swz.apply(row, col);
 }
 
 // LDS passes one access of `width_words` costs at conflict degree `degree`.
@@ -51,35 +33,123 @@ constexpr int access_cost(int degree, int width_words, LdsGeometry g) {
     return degree * (kWaveLanes / g.group_for_width(width_words));
 }
 
-// Cost per wavefront per K tile: instructions x passes x degree.
-constexpr int mfma_a_cost(MfmaShape s, int pad, LdsGeometry g) {
-    const int reads = (s.wm / 32) * (s.kh() / 4);
-    const int writes = (s.bm * s.bk) / (s.vec * s.threads);
-    return reads * access_cost(mfma_a_read_degree(s, pad, g), 4, g) +
-           writes * access_cost(mfma_a_write_degree(s, pad, g), s.vec, g);
-}
-constexpr int mfma_b_cost(MfmaShape s, int pad, LdsGeometry g) {
-    const int reads = (s.wn / 32) * s.kh();
-    const int writes = (s.bk * s.bn) / (s.vec * s.threads);
-    return reads * access_cost(mfma_b_read_degree(s, pad, g), 1, g) +
-           writes * access_cost(mfma_b_write_degree(s, pad, g), s.vec, g);
+// Cost of one wavefront-wide access: lane l touches (row(l), col(l)) .. +width.
+template <class RowCol>
+constexpr int pattern_cost(LayoutChoice c, int cols, int width, LdsGeometry g, RowCol rc) {
+    const int d = conflict_degree(
+        [=](int l) {
+            int row = 0, col = 0;
+            rc(l, row, col);
+            return layout_word(c, cols, row, col);
+        },
+        kWaveLanes, width, g.banks_for_width(width), g.group_for_width(width));
+    return access_cost(d, width, g);
 }
 
+// Cost of a two-address access (ds_read2_b32): lane l touches (row(l, e),
+// col(l, e)) for e = 0, 1.  Measured on gfx950 (LDS probe), the LDS serves it
+// as two 4-byte accesses, one per address, each with the 4-byte geometry.
+template <class RowCol2>
+constexpr int pattern_cost_pair(LayoutChoice c, int cols, LdsGeometry g, RowCol2 rc) {
+    int total = 0;
+    for (int e = 0; e < 2; ++e)
+        total += pattern_cost(c, cols, 1, g, [=](int l, int& row, int& col) { rc(l, e, row, col); });
+    return total;
+}
+
+// Search pads 0, 4, ..., kMaxPad, then swizzles; `cost(choice)` sums a tile's
+// access costs.
 template <class Cost>
-constexpr int argmin_pad(Cost cost) {
-    int best_pad = 0, best = cost(0);
+constexpr LayoutChoice choose_layout(Cost cost, int cols) {
+    LayoutChoice best{0, kNoSwizzle};
+    int best_cost = cost(best);
     for (int pad = 4; pad <= kMaxPad; pad += 4) {
-        const int c = cost(pad);
-        if (c < best) { best = c; best_pad = pad; }
+        const LayoutChoice c{pad, kNoSwizzle};
+        const int v = cost(c);
+        if (v < best_cost) { best = c; best_cost = v; }
     }
-    return best_pad;
+    for (int unit = 4; unit <= 32; unit *= 2)
+        for (int mask = 1; mask <= 7; mask = 2 * mask + 1)
+            for (int shift = 0; shift <= 4; ++shift) {
+                if (cols % (unit * (mask + 1)) != 0) continue;
+                const LayoutChoice c{0, Swizzle{unit, shift, mask}};
+                const int v = cost(c);
+                if (v < best_cost) { best = c; best_cost = v; }
+            }
+    return best;
 }
 
-constexpr int mfma_pad_a(MfmaShape s, LdsGeometry g) {
-    return argmin_pad([=](int pad) { return mfma_a_cost(s, pad, g); });
+// ---- matrix-core kernel ---------------------------------------------------------
+// A row-major [BM][BK], B row-major [BK][BN]; MFMA block MB x NB x KB; lane l
+// belongs to k-group l / MB and reduces k in [group * KG, (group + 1) * KG),
+// KG = BK / KB, one k per MFMA step.
+struct MfmaShape {
+    int bm, bn, bk, wm, wn, threads, vec, mb, nb, kb;
+    constexpr int kg() const { return bk / kb; }
+    constexpr int waves() const { return threads / kWaveLanes; }
+    constexpr int waves_n() const { return bn / wn; }
+};
+
+// Every A access of one K tile: fragment reads (16-byte, KG/4 per block row
+// of every wavefront) and the cooperative stores (vec-wide).
+constexpr int mfma_a_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    for (int w = 0; w < s.waves(); ++w) {
+        const int wm0 = (w / s.waves_n()) * s.wm;
+        for (int mi = 0; mi < s.wm / s.mb; ++mi)
+            for (int q = 0; q < s.kg() / 4; ++q)
+                total += pattern_cost(c, s.bk, 4, g, [=](int l, int& row, int& col) {
+                    row = wm0 + mi * s.mb + l % s.mb;
+                    col = (l / s.mb) * s.kg() + 4 * q;
+                });
+        const int vcols = s.bk / s.vec;
+        for (int i = 0; i < (s.bm * vcols) / s.threads; ++i)
+            total += pattern_cost(c, s.bk, s.vec, g, [=](int l, int& row, int& col) {
+                const int idx = w * kWaveLanes + l + i * s.threads;
+                row = idx / vcols;
+                col = (idx % vcols) * s.vec;
+            });
+    }
+    return total;
 }
-constexpr int mfma_pad_b(MfmaShape s, LdsGeometry g) {
-    return argmin_pad([=](int pad) { return mfma_b_cost(s, pad, g); });
+
+// Every B access of one K tile: the 4-byte fragment reads (KG per block
+// column of every wavefront) and the cooperative stores.  The compiler merges
+// the reads of block columns 2p and 2p+1 (same row, NB words apart) into one
+// two-address ds_read2_b32, costed as such a pair.
+constexpr int mfma_b_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    const int ni_count = s.wn / s.nb;
+    for (int w = 0; w < s.waves(); ++w) {
+        const int wn0 = (w % s.waves_n()) * s.wn;
+        for (int j = 0; j < s.kg(); ++j) {
+            for (int ni = 0; ni + 1 < ni_count; ni += 2)
+                total += pattern_cost_pair(c, s.bn, g, [=](int l, int e, int& row, int& col) {
+                    row = (l / s.nb) * s.kg() + j;
+                    col = wn0 + (ni + e) * s.nb + l % s.nb;
+                });
+            if (ni_count % 2)
+                total += pattern_cost(c, s.bn, 1, g, [=](int l, int& row, int& col) {
+                    row = (l / s.nb) * s.kg() + j;
+                    col = wn0 + (ni_count - 1) * s.nb + l % s.nb;
+                });
+        }
+        const int vcols = s.bn / s.vec;
+        for (int i = 0; i < (s.bk * vcols) / s.threads; ++i)
+            total += pattern_cost(c, s.bn, s.vec, g, [=](int l, int& row, int& col) {
+                const int idx = w * kWaveLanes + l + i * s.threads;
+                row = idx / vcols;
+                col = (idx % vcols) * s.vec;
+            });
+    }
+    return total;
+}
+
+constexpr LayoutChoice mfma_layout_a(MfmaShape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return mfma_a_cost(s, c, g); }, s.bk);
+}
+constexpr LayoutChoice mfma_layout_b(MfmaShape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn);
 }
 
 // ---- vector-ALU kernel: A k-major [BK][BM+pad], B row-major [BK][BN+pad] ----
@@ -110,6 +180,17 @@ constexpr int valu_b_write_degree(ValuShape s, int pad, LdsGeometry g) {
     return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
                            kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
 }
+
+template <class Cost>
+constexpr int argmin_pad(Cost cost) {
+    int best_pad = 0, best = cost(0);
+    for (int pad = 4; pad <= kMaxPad; pad += 4) {
+        const int c = cost(pad);
+        if (c < best) { best = c; best_pad = pad; }
+    }
+    return best_pad;
+}
+
 constexpr int valu_pad_a(ValuShape s, LdsGeometry g) {
     return argmin_pad([=](int pad) {
         return 2 * s.bk * access_cost(valu_a_read_degree(s, pad, g), 4, g) +

@@ -62,6 +62,15 @@ def patterns():
     for pad in (0, 4, 8, 16, 32):
         stride = 128 + pad
         pats.append((f"mfma B read, row stride {stride}", 1, [(l // 32) * 8 * stride + (l % 32) for l in range(64)]))
+    # two-address reads (ds_read2_b32): MFMA B fragments of block columns 2p, 2p+1
+    for stride in (128, 132, 136, 144):
+        pats.append((f"read2 +16, mfma16 B, row stride {stride}", -16,
+                     [(l // 16) * 4 * stride + (l % 16) for l in range(64)]))
+        pats.append((f"read2 +32, mfma32 B, row stride {stride}", -32,
+                     [(l // 32) * 8 * stride + (l % 32) for l in range(64)]))
+    pats.append(("read2 +16, consecutive lanes", -16, list(range(64))))
+    pats.append(("read2 +32, consecutive lanes", -32, list(range(64))))
+    pats.append(("read2 +16, lanes 32 apart", -16, [(l % 32) + (l // 32) * 1024 for l in range(64)]))
     pats.append(("valu A read (broadcast groups of 16)", 4, [(l // 16) * 4 for l in range(64)]))
     pats.append(("valu B read", 4, [(l % 16) * 4 for l in range(64)]))
     return pats
@@ -70,6 +79,10 @@ def patterns():
 def predicted(words, width, geom):
     import dense_fp32_tiled_amd as dft
 
+    if width < 0:  # ds_read2_b32: two 4-byte accesses, one per address; report the worse
+        banks, group = geom[1]
+        return max(dft.gemm_lds_conflict_degree(words, 1, banks, group),
+                   dft.gemm_lds_conflict_degree([w - width for w in words], 1, banks, group))
     banks, group = geom[width]
     return dft.gemm_lds_conflict_degree(words, width, banks, group)
 
@@ -82,7 +95,7 @@ def measured_degree(cycles_per_instr: float, width: int, waves: int, geom, issue
     degree-1 access lands."""
     if cycles_per_instr < 1.1 * issue_floor:
         return 1
-    passes = 64 // geom[width][1]
+    passes = 64 // geom[width][1] if width > 0 else 2 * (64 // geom[1][1])
     return max(1, round(cycles_per_instr / (waves * passes)))
 
 
@@ -92,7 +105,8 @@ def fit(rows, waves):
     score = {}
     for g, geom in GEOMETRIES.items():
         score[g] = sum(1 for r in rows
-                       if measured_degree(r["cycles_per_instr_per_wave"], r["width_bytes"] // 4, waves, geom, floor)
+                       if measured_degree(r["cycles_per_instr_per_wave"], r.get("mode", r["width_bytes"] // 4), waves,
+                                          geom, floor)
                        == r["predicted_degree"][g])
     return score
 
@@ -111,7 +125,8 @@ def run(reps: int = 2000, waves: int = 4):
         torch.cuda.synchronize()
         cyc = out[:waves].cpu().tolist()
         per_instr = max(cyc) / (reps * 16)
-        rows.append({"pattern": name, "width_bytes": 4 * width, "cycles_per_instr_per_wave": per_instr,
+        rows.append({"pattern": name, "width_bytes": 4 * width if width > 0 else 8, "mode": width,
+                     "cycles_per_instr_per_wave": per_instr,
                      "predicted_degree": {g: predicted(words, width, v) for g, v in GEOMETRIES.items()}})
     return rows
 

@@ -50,19 +50,23 @@ typedef enum {
     GEMM_ERR_UNSUPPORTED = -5,  /* no gfx950 device current, or unknown variant */
     GEMM_ERR_CONFIG = -6,       /* variant's LDS footprint exceeds the device limit */
     GEMM_ERR_HIP = -7,          /* a HIP runtime call or the launch failed */
-    GEMM_ERR_TOO_LARGE = -8     /* a size overflows the kernel's index range */
+    GEMM_ERR_TOO_LARGE = -8,    /* a size overflows the kernel's index range */
+    GEMM_ERR_WORKSPACE = -9     /* split-K workspace missing or too small */
 } gemm_status;
 
 /* Kernel variants.  Every variant computes the same operation; they differ in
  * how (see gemm_f32_tile_config for each one's tile geometry). */
 typedef enum {
-    GEMM_VARIANT_AUTO = 0,          /* the default: currently GEMM_VARIANT_MFMA */
-    GEMM_VARIANT_MFMA = 1,          /* fp32 matrix-core (v_mfma_f32_32x32x2_f32) inner product */
-    GEMM_VARIANT_VALU = 2,          /* register-tiled vector-ALU fp32 FMA inner product */
-    GEMM_VARIANT_MFMA_STAGES1 = 3,  /* ablation: one LDS stage, two barriers per K tile, no prefetch */
-    GEMM_VARIANT_MFMA_NOPAD = 4,    /* ablation: LDS rows without padding */
-    GEMM_VARIANT_MFMA_SCALAR = 5,   /* ablation: 4-byte global loads even when 16-byte loads are legal */
-    GEMM_VARIANT_COUNT = 6
+    GEMM_VARIANT_AUTO = 0,          /* picks one of the MFMA variants from M, N, K (gemm_f32_auto_variant) */
+    GEMM_VARIANT_MFMA = 1,          /* v_mfma_f32_32x32x2_f32, 256x128x16 workgroup tile, 8 waves of 64x64 */
+    GEMM_VARIANT_VALU = 2,          /* register-tiled vector-ALU fp32 FMA, 128x128x16, 8x8 per thread */
+    GEMM_VARIANT_MFMA_STAGES1 = 3,  /* ablation of MFMA: one LDS stage, two barriers per K tile, no prefetch */
+    GEMM_VARIANT_MFMA_NOPAD = 4,    /* ablation of MFMA: plain LDS rows (no padding, no swizzle) */
+    GEMM_VARIANT_MFMA_SCALAR = 5,   /* ablation of MFMA: 4-byte global loads even when 16-byte loads are legal */
+    GEMM_VARIANT_MFMA16 = 6,        /* as MFMA with v_mfma_f32_16x16x4_f32 */
+    GEMM_VARIANT_MFMA_128 = 7,      /* as MFMA with a 128x128x16 workgroup tile (4 waves) */
+    GEMM_VARIANT_MFMA_128_BK32 = 8, /* as MFMA_128 with BK = 32 */
+    GEMM_VARIANT_COUNT = 9
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -81,11 +85,15 @@ typedef struct {
     int32_t b_rows, b_cols, b_pad, b_row_stride, b_stage_elems; /* LDS tile of B */
     int32_t lds_bytes;           /* stages * (a_stage_elems + b_stage_elems) * 4 */
     int32_t vec_width;           /* fp32 elements per global load when aligned (1 or 4) */
-    int32_t lds_banks_b32;       /* LDS geometry the padding was derived for: banks and */
+    int32_t lds_banks_b32;       /* LDS geometry the layout was derived for: banks and */
     int32_t lds_lanes_b32;       /*   lanes serviced per pass for 4-byte accesses ... */
     int32_t lds_banks_b128;      /*   ... and for 16-byte accesses */
     int32_t lds_lanes_b128;
     int32_t a_transposed;        /* 1 if A is stored k-major in LDS (a_rows = BK) */
+    int32_t a_swz_unit, a_swz_shift, a_swz_mask; /* XOR swizzle of A's LDS columns (unit 0 = none): */
+    int32_t b_swz_unit, b_swz_shift, b_swz_mask; /*   col ^ (unit * ((row >> shift) & mask)) */
+    int32_t mfma_block;          /* MFMA block size (32 or 16), 0 for the VALU variant */
+    int32_t xcd_tile_order;      /* 1 if workgroups are mapped to tiles in the XCD-grouped order */
 } gemm_tile_config;
 
 /* C = A @ B with the default variant.  M, N, K >= 0; lda >= max(1,K),
@@ -106,12 +114,49 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 void *stream, int variant);
 
+/* Split-K: C = A @ B with the K range cut into `splits` slices of whole
+ * 16-deep K tiles, each reduced by its own workgroups (the MFMA_128 kernel),
+ * so that problems with few 128x128 output tiles still occupy every CU.
+ * Slice s writes its partial product, packed M x N, to workspace + s*M*N
+ * floats; a second kernel then sets C = sum of the slices in ascending slice
+ * order, so the result is deterministic for a given `splits`.
+ *   workspace: DEVICE buffer owned by the caller, at least
+ *              gemm_f32_splitk_workspace_bytes(M, N, K, splits, num_cus) bytes
+ *              (may be NULL when that is 0); its contents on entry are ignored
+ *              and on return unspecified.  It must not overlap A, B or C.
+ *   splits: 1..64, or 0 for gemm_f32_splitk_auto_splits on the current
+ *           device.  splits == 1 is a plain launch and needs no workspace.
+ * Other arguments and conventions as gemm_f32.  Returns a gemm_status;
+ * GEMM_ERR_WORKSPACE if the workspace is missing or too small. */
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    void *workspace, int64_t workspace_bytes, int splits, void *stream);
+
+/* Workspace bytes gemm_f32_splitk needs (splits * M * N * 4, or 0 when the
+ * resolved split count is 1); splits == 0 resolves with num_cus compute
+ * units.  Pure host call.  Returns GEMM_ERR_INVALID_DIM on bad arguments. */
+int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits, int32_t num_cus);
+
+/* The split count gemm_f32_splitk uses for splits == 0: enough slices for
+ * four workgroups per CU over the 128x128 output tiles, at most 64, and at
+ * least eight K tiles per slice.  Pure host call. */
+int gemm_f32_splitk_auto_splits(int64_t M, int64_t N, int64_t K, int32_t num_cus);
+
 /* Fills *out with the tile geometry of `variant`.  Pure host call (touches no
  * device).  Returns GEMM_OK, GEMM_ERR_NULL or GEMM_ERR_UNSUPPORTED. */
 int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *gemm_f32_status_string(int status);
+
+/* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
+ * `num_cus` compute units: MFMA when its 256x128 tiles give at least one
+ * workgroup per CU, else MFMA_128_BK32 for K >= 4096, else MFMA_128.  Pure
+ * host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
+ * sizes or num_cus < 1. */
+int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
 /* ---- Host-side layout model -------------------------------------------------
  * The LDS layout and bank model the kernels are compiled from, exported so
@@ -146,6 +191,14 @@ int32_t gemm_lds_bank(int64_t word_offset, int32_t banks);
  * maximum over groups (1 = conflict-free), or -1 on bad arguments. */
 int32_t gemm_lds_conflict_degree(const int64_t *lane_words, int32_t lanes,
                                  int32_t width, int32_t banks, int32_t group);
+
+/* The LDS layout search the MFMA kernels are built with, for a workgroup tile
+ * bm x bn x bk of (bm/wm) x (bn/wn) wavefronts, MFMA blocks mb x mb (32 or
+ * 16) and global loads of `vec` floats (1 or 4).  Writes
+ * {pad, swz_unit, swz_shift, swz_mask} of A to out[0..3] and of B to
+ * out[4..7].  Returns GEMM_OK or GEMM_ERR_INVALID_DIM. */
+int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
+                                int32_t vec, int32_t *out);
 
 /* The pages' padding rule for the A-tile column read ("My Triton From
  * Scratch, Part 18", section "Choosing padding instead of hard-coding it"):

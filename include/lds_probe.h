@@ -26,8 +26,11 @@ extern "C" {
 /*
  * lane_words: HOST array of 64 dword addresses, one per lane (the same
  *             pattern is used by every wavefront).
- * width_words: 1, 2 or 4 (ds_read_b32 / b64 / b128); every address must be a
- *             multiple of width_words and address + width_words <= LDS_PROBE_WORDS.
+ * width_words: 1, 2 or 4 (ds_read_b32 / b64 / b128; every address must be a
+ *             multiple of width_words and address + width_words <=
+ *             LDS_PROBE_WORDS), or -16 / -32: ds_read2_b32 reading the dwords
+ *             at address and address + 16 (or 32); address + 17 (or 33) <=
+ *             LDS_PROBE_WORDS.
  * waves: 1..16 wavefronts in the workgroup.  reps: 1..100000.
  * cycles_out: DEVICE buffer of `waves` uint64 values, owned by the caller;
  *             wave w writes the shader-clock cycles its read loop took.

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(gemm_lib):
 
 
 def test_status_strings(gemm_lib):
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         s = dft.gemm_f32_status_string(st)
         assert s and s != "unknown status"
     assert dft.gemm_f32_status_string(12345) == "unknown status"
@@ -66,11 +66,19 @@ def test_tile_config_is_consistent(variant, gemm_lib):
     assert c["barriers_per_tile"] == (1 if c["stages"] == 2 else 2)
     if c["a_transposed"]:
         assert (c["a_rows"], c["a_cols"]) == (c["bk"], c["bm"])
+        assert c["mfma_block"] == 0
     else:
         assert (c["a_rows"], c["a_cols"]) == (c["bm"], c["bk"])
+        assert c["mfma_block"] in (16, 32)
+        assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64
     assert (c["b_rows"], c["b_cols"]) == (c["bk"], c["bn"])
     assert c["vec_width"] in (1, 4)
     assert (c["a_row_stride"] % 4 == 0) and (c["b_row_stride"] % 4 == 0)
+    for t in "ab":
+        unit, mask = c[f"{t}_swz_unit"], c[f"{t}_swz_mask"]
+        if unit:  # a swizzle permutes whole 16-byte groups inside aligned blocks of a row
+            assert unit % 4 == 0 and (mask & (mask + 1)) == 0
+            assert c[f"{t}_cols"] % (unit * (mask + 1)) == 0
 
 
 def test_tile_config_rejects(gemm_lib):
@@ -81,17 +89,37 @@ def test_tile_config_rejects(gemm_lib):
     assert gemm_lib.gemm_f32_tile_config(0, None) == dft.GEMM_ERR_NULL
 
 
+LAYOUT_KEYS = ("a_pad", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_pad", "b_swz_unit", "b_swz_shift",
+               "b_swz_mask", "a_row_stride", "b_row_stride", "a_stage_elems", "b_stage_elems", "lds_bytes")
+
+
 def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
     base = dft.gemm_f32_tile_config(dft.VARIANT_MFMA)
     assert dft.gemm_f32_tile_config(dft.VARIANT_AUTO) | {"variant": 1} == base
     s1 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_STAGES1)
     assert s1["stages"] == 1 and s1["barriers_per_tile"] == 2
     assert s1 | {"variant": 1, "stages": 2, "barriers_per_tile": 1, "lds_bytes": base["lds_bytes"]} == base
-    nopad = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_NOPAD)
-    assert nopad["a_pad"] == 0 and nopad["b_pad"] == 0
+    plain = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_NOPAD)
+    assert all(plain[k] == 0 for k in LAYOUT_KEYS[:8])
+    assert plain | {"variant": 1} | {k: base[k] for k in LAYOUT_KEYS} == base
     sc = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_SCALAR)
     assert sc["vec_width"] == 1
-    assert sc | {"variant": 1, "vec_width": 4} == base
+    assert sc | {"variant": 1, "vec_width": 4} | {k: base[k] for k in LAYOUT_KEYS} == base
+    m16 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA16)
+    assert m16["mfma_block"] == 16 and base["mfma_block"] == 32
+
+
+def test_auto_variant_selection(gemm_lib):
+    av = dft.gemm_f32_auto_variant
+    assert av(4096, 4096, 4096, 256) == dft.VARIANT_MFMA          # 512 tiles of 256x128
+    assert av(8192, 8192, 8192, 256) == dft.VARIANT_MFMA
+    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_128_BK32  # 16 tiles, deep K
+    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_128
+    assert av(128, 128, 128, 256) == dft.VARIANT_MFMA_128
+    assert av(4096, 4096, 2048, 1024) == dft.VARIANT_MFMA_128      # fewer tiles than CUs
+    assert av(4096, 4096, 4096, 1024) == dft.VARIANT_MFMA_128_BK32
+    assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
+    assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
 
 
 # ---- host-side argument validation: every case returns before any device call ----
@@ -152,3 +180,35 @@ def test_unknown_variant(gemm_lib):
 def test_binding_requires_the_library(tmp_path):
     with pytest.raises(ImportError):
         dft.library(tmp_path / "missing.so")
+
+
+# ---- split-K: host-side checks and pure queries ----
+def splitk(M, N, K, ws=0x9000000, ws_bytes=1 << 40, splits=2, **kw):
+    lda, ldb, ldc = max(K, 1), max(N, 1), max(N, 1)
+    return dft.gemm_f32_splitk(M, N, K, kw.get("A", FAKE_A), lda, kw.get("B", FAKE_B), ldb, kw.get("C", FAKE_C), ldc,
+                               ws, ws_bytes, splits, None)
+
+
+def test_splitk_argument_checks(gemm_lib):
+    assert splitk(64, 64, 64, splits=-1) == dft.GEMM_ERR_INVALID_DIM
+    assert splitk(64, 64, 64, splits=65) == dft.GEMM_ERR_INVALID_DIM
+    assert splitk(64, 64, 64, ws=0) == dft.GEMM_ERR_WORKSPACE
+    assert splitk(64, 64, 64, ws_bytes=2 * 64 * 64 * 4 - 1) == dft.GEMM_ERR_WORKSPACE
+    assert splitk(64, 64, 64, ws=FAKE_C) == dft.GEMM_ERR_ALIAS          # workspace over C
+    assert splitk(64, 64, 64, ws=FAKE_A) == dft.GEMM_ERR_ALIAS          # workspace over A
+    assert splitk(-1, 64, 64) == dft.GEMM_ERR_INVALID_DIM
+    assert splitk(0, 64, 64, ws=0) == dft.GEMM_OK                       # nothing to do
+    assert splitk(64, 0, 64, ws=0) == dft.GEMM_OK
+
+
+def test_splitk_queries(gemm_lib):
+    # 2048 x 256 x 16384: 32 tiles of 128 x 128 -> 1024/32 = 32 slices (<= 1024 K tiles / 8)
+    assert dft.gemm_f32_splitk_auto_splits(2048, 256, 16384, 256) == 32
+    assert dft.gemm_f32_splitk_workspace_bytes(2048, 256, 16384, 0, 256) == 32 * 2048 * 256 * 4
+    assert dft.gemm_f32_splitk_workspace_bytes(2048, 256, 16384, 5, 256) == 5 * 2048 * 256 * 4
+    assert dft.gemm_f32_splitk_auto_splits(4096, 4096, 4096, 256) == 1    # 1024 tiles: no split
+    assert dft.gemm_f32_splitk_workspace_bytes(4096, 4096, 4096, 0, 256) == 0
+    assert dft.gemm_f32_splitk_auto_splits(64, 64, 100, 256) == 1         # too few K tiles
+    assert dft.gemm_f32_splitk_auto_splits(128, 128, 1 << 20, 256) == 64  # capped at 64
+    assert dft.gemm_f32_splitk_auto_splits(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
+    assert dft.gemm_f32_splitk_workspace_bytes(4, 4, 4, 99, 256) == dft.GEMM_ERR_INVALID_DIM

@@ -23,8 +23,9 @@ TOL = 1e-5
 SENTINEL_BITS = np.uint32(0x7FC0DEAD)  # a quiet NaN with a recognisable payload
 SENTINEL = SENTINEL_BITS.view(np.float32)
 
-ALL_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA_NOPAD,
-                dft.VARIANT_MFMA_SCALAR]
+ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1,
+                dft.VARIANT_MFMA_NOPAD, dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
+                dft.VARIANT_MFMA_128_BK32]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -137,8 +138,9 @@ EDGE_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1],
-                         ids=["mfma", "valu", "mfma_stages1"])
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1,
+                                     dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32],
+                         ids=["mfma", "valu", "mfma_stages1", "mfma16", "mfma_128", "mfma_128_bk32"])
 def test_edge_shapes(shape, variant, torch_gpu):
     M, N, K = shape
     a, b = workloads.make_operands(M, N, K, "uniform", M * 7 + N * 13 + K)
@@ -152,7 +154,8 @@ def test_edge_shapes(shape, variant, torch_gpu):
     assert np.array_equal(ci.astype(np.float64), oracle.reference(ai, bi)[0])
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU], ids=["mfma", "valu"])
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128],
+                         ids=["mfma", "valu", "mfma16", "mfma_128"])
 @pytest.mark.parametrize("pitch", [(3, 5, 2), (2, 4, 4), (1, 0, 9), (0, 8, 0)], ids=str)
 def test_pitched_operands(pitch, variant, torch_gpu):
     """Leading dimensions beyond the width: NaN in every gap must never be
@@ -228,3 +231,73 @@ def test_rejects_overlap_on_device(torch_gpu):
     p = buf.data_ptr()
     st = dft.gemm_f32(8, 8, 8, p, 8, p + 4 * 64, 8, p + 4 * 32, 8, None)
     assert st == dft.GEMM_ERR_ALIAS
+
+
+# ---- split-K ----
+def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None):
+    M, K = a.shape
+    N = b.shape[1]
+    ldc = ldc or max(N, 1)
+    da, db = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    dc = torch.from_numpy(np.full((M + 1) * ldc, SENTINEL, np.float32)).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    need = dft.gemm_f32_splitk_workspace_bytes(M, N, K, splits, cus)
+    ws = torch.full((max(need // 4, 1) if ws_elems is None else ws_elems,), float("nan"), device="cuda")
+    st = dft.gemm_f32_splitk(M, N, K, da.data_ptr(), max(K, 1), db.data_ptr(), max(N, 1), dc.data_ptr(), ldc,
+                             ws.data_ptr(), ws.numel() * 4, splits, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    if st != dft.GEMM_OK:
+        return st, None, None
+    full = dc.cpu().numpy().reshape(M + 1, ldc)
+    return st, full[:M, :N].copy(), full
+
+
+@pytest.mark.parametrize("splits", [0, 2, 7, 32, 64])
+def test_splitk_deepk_parity(splits, torch_gpu):
+    cfg = workloads.CONFIG_BY_NAME["deepk"]
+    a, b, ref = reference_for(cfg, integer=False)
+    st, c, full = run_splitk(torch_gpu, a, b, splits)
+    assert st == dft.GEMM_OK
+    check_sentinels(full, cfg.M, cfg.N)
+    err = compare(cfg, c, ref, exact=False)
+    print(f"deepk split-K {splits}: normalised error {err:.3e}")
+    assert err <= TOL
+    ai, bi, refi = reference_for(cfg, integer=True)
+    st, ci, _ = run_splitk(torch_gpu, ai, bi, splits)
+    compare(cfg, ci, refi, exact=True)
+
+
+@pytest.mark.parametrize("shape", [(1000, 999, 513), (129, 127, 17), (300, 200, 48), (64, 64, 1), (5, 7, 4097)],
+                         ids=str)
+@pytest.mark.parametrize("splits", [1, 3, 8, 64])
+def test_splitk_ragged_and_empty_slices(shape, splits, torch_gpu):
+    """Slices past the end of K (e.g. K = 17 in 8 slices of 16) add zero."""
+    M, N, K = shape
+    a, b = workloads.make_operands(M, N, K, "uniform", M + 3 * N + K)
+    cref, den = oracle.reference(a, b)
+    st, c, full = run_splitk(torch_gpu, a, b, splits, ldc=N + 3)
+    assert st == dft.GEMM_OK
+    check_sentinels(full, M, N)
+    assert oracle.normalised_error(c, cref, den) <= TOL
+
+
+def test_splitk_is_deterministic(torch_gpu):
+    cfg = workloads.CONFIG_BY_NAME["deepk"]
+    a, b, _ = reference_for(cfg, integer=False)
+    _, c0, _ = run_splitk(torch_gpu, a, b, 16)
+    _, c1, _ = run_splitk(torch_gpu, a, b, 16)
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+
+
+def test_splitk_rejects_small_workspace(torch_gpu):
+    a, b = workloads.make_operands(256, 256, 1024, "uniform", 1)
+    st, _, _ = run_splitk(torch_gpu, a, b, 4, ws_elems=4 * 256 * 256 - 1)
+    assert st == dft.GEMM_ERR_WORKSPACE
+
+
+def test_matmul_splitk_wrapper(torch_gpu):
+    torch = torch_gpu
+    a, b = workloads.make_operands(300, 130, 5000, "uniform", 2)
+    c = dft.matmul_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()).cpu().numpy()
+    cref, den = oracle.reference(a, b)
+    assert oracle.normalised_error(c, cref, den) <= TOL

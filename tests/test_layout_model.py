@@ -83,28 +83,84 @@ def test_conflict_degree_rules(gemm_lib):
     assert cd([], 1, 64, 64) == -1
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU])
-def test_chosen_pads_are_conflict_free_for_the_fragment_reads(variant, gemm_lib):
-    """The pads the kernels are compiled with make their hot LDS reads
-    conflict-free under the library's own bank geometry."""
+def lds_word(cfg, tile, row, col):
+    """Word offset (stage 0) of logical (row, col) in a variant's LDS tile."""
+    unit, shift, mask = cfg[f"{tile}_swz_unit"], cfg[f"{tile}_swz_shift"], cfg[f"{tile}_swz_mask"]
+    phys = col ^ (unit * ((row >> shift) & mask)) if unit else col
+    return row * cfg[f"{tile}_row_stride"] + phys
+
+
+def mfma_accesses(c):
+    """Every LDS access of one K tile of an MFMA variant, per wavefront:
+    (width in dwords, 64 lane word addresses)."""
+    mb = c["mfma_block"]
+    kg = c["bk"] // (64 // mb)
+    waves_n = c["bn"] // c["tn"]
+    vec = c["vec_width"]
+    out = []
+    for w in range(c["threads"] // 64):
+        wm0, wn0 = (w // waves_n) * c["tm"], (w % waves_n) * c["tn"]
+        for mi in range(c["tm"] // mb):
+            for q in range(kg // 4):
+                out.append((4, [lds_word(c, "a", wm0 + mi * mb + l % mb, (l // mb) * kg + 4 * q) for l in range(64)]))
+        for j in range(kg):  # B reads of block columns 2p, 2p+1 are one ds_read2_b32
+            for ni in range(0, c["tn"] // mb, 2):
+                pair = [[lds_word(c, "b", (l // mb) * kg + j, wn0 + (ni + e) * mb + l % mb) for e in (0, 1)]
+                        for l in range(64)]
+                out.append((-2, pair))
+        for tile, rows, cols in (("a", c["bm"], c["bk"]), ("b", c["bk"], c["bn"])):
+            vcols = cols // vec
+            for i in range(rows * vcols // c["threads"]):
+                idx = [w * 64 + l + i * c["threads"] for l in range(64)]
+                out.append((vec, [lds_word(c, tile, x // vcols, (x % vcols) * vec) for x in idx]))
+    return out
+
+
+def degree(c, width, words):
+    if width == -2:  # two-address access: served as two 4-byte accesses (measured)
+        return max(degree(c, 1, [pair[e] for pair in words]) for e in (0, 1))
+    banks = c["lds_banks_b32"] if width == 1 else c["lds_banks_b128"]
+    lanes = c["lds_lanes_b32"] if width == 1 else c["lds_lanes_b128"]
+    return dft.gemm_lds_conflict_degree(words, width, banks, lanes)
+
+
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
+                                     dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_SCALAR])
+def test_mfma_layouts_are_conflict_free(variant, gemm_lib):
+    """Under the measured geometry, every fragment read and cooperative store
+    of the chosen layouts is conflict-free, while the plain layout is not."""
     c = dft.gemm_f32_tile_config(variant)
-    g128 = (c["lds_banks_b128"], c["lds_lanes_b128"])
-    g32 = (c["lds_banks_b32"], c["lds_lanes_b32"])
-    if variant == dft.VARIANT_MFMA:
-        kh = c["bk"] // 2
-        a = [(l % 32) * c["a_row_stride"] + (l // 32) * kh for l in range(64)]
-        b = [(l // 32) * kh * c["b_row_stride"] + (l % 32) for l in range(64)]
-        assert dft.gemm_lds_conflict_degree(a, 4, *g128) == 1
-        assert dft.gemm_lds_conflict_degree(b, 1, *g32) == 1
-        nopad = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_NOPAD)
-        a0 = [(l % 32) * nopad["a_row_stride"] + (l // 32) * kh for l in range(64)]
-        assert dft.gemm_lds_conflict_degree(a0, 4, *g128) == 4  # rows 0, 4, 8, 12 share banks
-    else:
-        tn = c["bn"] // c["tn"]
-        a = [(l // tn) * 4 for l in range(64)]
-        b = [(l % tn) * 4 for l in range(64)]
-        assert dft.gemm_lds_conflict_degree(a, 4, *g128) == 1
-        assert dft.gemm_lds_conflict_degree(b, 4, *g128) == 1
+    assert all(degree(c, w, words) == 1 for w, words in mfma_accesses(c))
+    plain = c | {k: 0 for k in ("a_pad", "a_swz_unit", "b_pad", "b_swz_unit")}
+    plain["a_row_stride"], plain["b_row_stride"] = c["a_cols"], c["b_cols"]
+    assert max(degree(plain, w, words) for w, words in mfma_accesses(plain)) > 1
+
+
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
+                                     dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_SCALAR])
+def test_built_layouts_match_the_search(variant, gemm_lib):
+    """The layouts compiled into the kernels (generated at build time) are the
+    ones the exported search returns for the same shape."""
+    c = dft.gemm_f32_tile_config(variant)
+    st, la, lb = dft.gemm_lds_choose_mfma_layout(c["bm"], c["bn"], c["bk"], c["tm"], c["tn"], c["mfma_block"],
+                                                 c["vec_width"])
+    assert st == 0
+    assert la == (c["a_pad"], c["a_swz_unit"], c["a_swz_shift"], c["a_swz_mask"])
+    assert lb == (c["b_pad"], c["b_swz_unit"], c["b_swz_shift"], c["b_swz_mask"])
+
+
+def test_layout_search_rejects_bad_shapes(gemm_lib):
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 8, 4)[0] == dft.GEMM_ERR_INVALID_DIM
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 6, 64, 64, 32, 4)[0] == dft.GEMM_ERR_INVALID_DIM
+    assert dft.gemm_lds_choose_mfma_layout(100, 128, 16, 64, 64, 32, 4)[0] == dft.GEMM_ERR_INVALID_DIM
+
+
+def test_valu_reads_are_conflict_free(gemm_lib):
+    c = dft.gemm_f32_tile_config(dft.VARIANT_VALU)
+    tn = c["bn"] // c["tn"]
+    a = [(l // tn) * 4 for l in range(64)]
+    b = [(l % tn) * 4 for l in range(64)]
+    assert degree(c, 4, a) == 1 and degree(c, 4, b) == 1
 
 
 def test_geometry_is_the_measured_one(gemm_lib):
