@@ -26,7 +26,8 @@ if str(ROOT) not in sys.path:
 
 PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and packed vector): 256 CUs x 256 flop/clk x 2.4 GHz
 METRIC = "fp32 GEMM TFLOP/s at 4096³ on 1 MI355X; % of fp32 peak"
-KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "lds_layout.hpp", "pad_choice.hpp"]
+KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "lds_layout.hpp", "pad_choice.hpp", "layout_gen.cpp",
+                  "mfma_shapes.def"]
 
 
 def kernel_source_digest() -> str:
