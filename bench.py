@@ -225,11 +225,9 @@ def main(argv=None) -> int:
                                     "kernel_ms_min": kmin * 1e3}) + "\n")
 
     if args.copy_calibration_mib > 0:
-        import ctypes
+        from dense_fp32_tiled_amd import lds_probe
 
-        probe = ctypes.CDLL(str(ROOT / "dense_fp32_tiled_amd" / "liblds_probe.so"))
-        probe.probe_copy_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-        probe.probe_copy_f32.restype = ctypes.c_int
+        probe = lds_probe.load()
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

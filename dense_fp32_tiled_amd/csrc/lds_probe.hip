@@ -78,11 +78,45 @@ __device__ inline void read2_16(uint32_t addr, float& sink) {
     sink += r0[0] + r1[1] + r2[0] + r3[1];
 }
 
+// 16 writes of WIDTH dwords at the lane's address, then a wait.  Every
+// wavefront writes the same values to the same addresses; the LDS contents
+// are never read back.
+template <int WIDTH>
+__device__ inline void write16(uint32_t addr, float v) {
+    if constexpr (WIDTH == 1) {
+        asm volatile(
+            "ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n"
+            "ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n"
+            "ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n"
+            "ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n ds_write_b32 %0, %1\n"
+            "s_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+    } else if constexpr (WIDTH == 2) {
+        const f32x2 d{v, v};
+        asm volatile(
+            "ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n"
+            "ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n"
+            "ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n"
+            "ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n ds_write_b64 %0, %1\n"
+            "s_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(d) : "memory");
+    } else {
+        const f32x4 d{v, v, v, v};
+        asm volatile(
+            "ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n"
+            "ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n"
+            "ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n"
+            "ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n ds_write_b128 %0, %1\n"
+            "s_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(d) : "memory");
+    }
+}
+
 // MODE 1, 2, 4: ds_read_b32/b64/b128 of MODE dwords; MODE -16, -32:
-// ds_read2_b32 with offset1 16 or 32 dwords.
+// ds_read2_b32 with offset1 16 or 32 dwords; MODE 101, 102, 104:
+// ds_write_b32/b64/b128.
 template <int MODE>
 __device__ inline void read_mode(uint32_t addr, float& sink) {
-    if constexpr (MODE > 0)
+    if constexpr (MODE > 100)
+        write16<MODE - 100>(addr, sink);
+    else if constexpr (MODE > 0)
         read16<MODE>(addr, sink);
     else
         read2_16<-MODE>(addr, sink);
@@ -113,7 +147,22 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4* __restrict__
         dst[i] = src[i];
 }
 
+__global__ void xcc_id_kernel(int32_t* out) {
+    int32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+    if (threadIdx.x == 0) out[blockIdx.x] = x;
+}
+
 }  // namespace
+
+extern "C" int probe_xcc_ids(int32_t* out, int32_t blocks, int32_t threads, void* stream) {
+    if (out == nullptr || blocks < 1 || threads < 1 || threads > 1024) return -1;
+    void* args[] = {&out};
+    return hipLaunchKernel(reinterpret_cast<const void*>(xcc_id_kernel), dim3((unsigned)blocks),
+                           dim3((unsigned)threads), args, 0, (hipStream_t)stream) == hipSuccess
+               ? 0
+               : -2;
+}
 
 extern "C" int probe_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
     if (n < 0 || n % 4 != 0) return -1;
@@ -137,12 +186,14 @@ extern "C" int probe_copy_f32(const float* src, float* dst, int64_t n, void* str
 extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int32_t waves, int32_t reps,
                              uint64_t* cycles_out, void* stream) {
     if (lane_words == nullptr || cycles_out == nullptr) return -1;
-    if (width_words != 1 && width_words != 2 && width_words != 4 && width_words != -16 && width_words != -32)
-        return -1;
+    const bool write = width_words > 100;
+    const int32_t w0 = write ? width_words - 100 : width_words;
+    if (w0 != 1 && w0 != 2 && w0 != 4 && w0 != -16 && w0 != -32) return -1;
+    if (write && w0 < 0) return -1;
     if (waves < 1 || waves > 16 || reps < 1 || reps > 100000) return -1;
     // dwords one lane touches past its base, and the alignment the base needs
-    const int32_t span = width_words > 0 ? width_words : -width_words + 1;
-    const int32_t align = width_words > 0 ? width_words : 1;
+    const int32_t span = w0 > 0 ? w0 : -w0 + 1;
+    const int32_t align = w0 > 0 ? w0 : 1;
     Pattern p;
     for (int l = 0; l < 64; ++l) {
         const int32_t w = lane_words[l];
@@ -155,6 +206,9 @@ extern "C" int lds_probe_run(const int32_t* lane_words, int32_t width_words, int
                          : width_words == 2   ? reinterpret_cast<const void*>(lds_probe_kernel<2>)
                          : width_words == 4   ? reinterpret_cast<const void*>(lds_probe_kernel<4>)
                          : width_words == -16 ? reinterpret_cast<const void*>(lds_probe_kernel<-16>)
-                                              : reinterpret_cast<const void*>(lds_probe_kernel<-32>);
+                         : width_words == -32 ? reinterpret_cast<const void*>(lds_probe_kernel<-32>)
+                         : width_words == 101 ? reinterpret_cast<const void*>(lds_probe_kernel<101>)
+                         : width_words == 102 ? reinterpret_cast<const void*>(lds_probe_kernel<102>)
+                                              : reinterpret_cast<const void*>(lds_probe_kernel<104>);
     return hipLaunchKernel(kernel, dim3(1), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : -2;
 }

@@ -36,9 +36,15 @@ def load():
 
     dft._share_torch_hip_runtime()
     lib = ctypes.CDLL(str(PROBE_LIB))
+    # Every entry point gets its full signature: an undeclared argument is
+    # passed as a C int, which would truncate a 64-bit device pointer.
     lib.lds_probe_run.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.lds_probe_run.restype = ctypes.c_int
+    lib.probe_xcc_ids.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.probe_xcc_ids.restype = ctypes.c_int
+    lib.probe_copy_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.probe_copy_f32.restype = ctypes.c_int
     return lib
 
 
@@ -71,14 +77,80 @@ def patterns():
     pats.append(("read2 +16, consecutive lanes", -16, list(range(64))))
     pats.append(("read2 +32, consecutive lanes", -32, list(range(64))))
     pats.append(("read2 +16, lanes 32 apart", -16, [(l % 32) + (l // 32) * 1024 for l in range(64)]))
+    # writes, to check that stores follow the read geometry of the same width
+    for s_ in (1, 2, 32, 33, 64):
+        pats.append((f"write b32 stride {s_}", 101, [l * s_ for l in range(64)]))
+    for s_ in (4, 8, 16, 20, 32, 64):
+        pats.append((f"write b128 stride {s_}", 104, [l * s_ for l in range(64)]))
+    for g in (8, 16, 32):
+        pats.append((f"write b128 groups of {g}", 104, [4 * (l % g) + (l // g) * 1024 for l in range(64)]))
+    # which lanes of a 16-byte read share a pass: rows 0..15 of a 16-word-stride
+    # tile, 4-word group g ^ ((row >> 2) & 3); the lanes named carry the pattern,
+    # every other lane reads lane 0's address (a broadcast)
+    def quad(row, g):
+        return row * 16 + 4 * (g ^ ((row >> 2) & 3))
+    sel = {"0-15": range(0, 16), "16-31": range(16, 32), "0-31": range(0, 32), "0-15,32-47": [*range(16), *range(32, 48)],
+           "0-7,16-23": [*range(8), *range(16, 24)], "0-15,48-63": [*range(16), *range(48, 64)]}
+    for label, lanes in sel.items():
+        lanes = set(lanes)
+        pats.append((f"b128 rows x groups, lanes {label} (g = l / 16)", 4,
+                     [quad(l % 16, l // 16) if l in lanes else 0 for l in range(64)]))
+    pats.append(("b128 rows x groups, all lanes (g = l / 32, rows 0..31)", 4, [quad(l % 32, l // 32) for l in range(64)]))
     pats.append(("valu A read (broadcast groups of 16)", 4, [(l // 16) * 4 for l in range(64)]))
     pats.append(("valu B read", 4, [(l % 16) * 4 for l in range(64)]))
     return pats
 
 
+def kernel_patterns(variant: int):
+    """Every distinct LDS access pattern one K tile of an MFMA variant issues
+    (fragment reads, ds_read2 pairs, cooperative stores), A tile at dword 0
+    and B tile at dword 8192 as in the kernel's stage-0 layout."""
+    import dense_fp32_tiled_amd as dft
+
+    c = dft.gemm_f32_tile_config(variant)
+    mb = c["mfma_block"]
+    kg = c["bk"] // (64 // mb)
+    waves_n = c["bn"] // c["tn"]
+    vec = c["vec_width"]
+    base = {"a": 0, "b": 8192}
+
+    def word(tile, row, col):
+        unit, shift, mask = c[f"{tile}_swz_unit"], c[f"{tile}_swz_shift"], c[f"{tile}_swz_mask"]
+        phys = col ^ (unit * ((row >> shift) & mask)) if unit else col
+        return base[tile] + row * c[f"{tile}_row_stride"] + phys
+
+    name = dft.VARIANT_NAMES[variant]
+    seen, out = set(), []
+
+    def add(label, mode, words):
+        key = (mode, tuple(words))
+        if key not in seen:
+            seen.add(key)
+            out.append((f"{name} {label}", mode, list(words)))
+
+    for w in range(c["threads"] // 64):
+        wm0, wn0 = (w // waves_n) * c["tm"], (w % waves_n) * c["tn"]
+        for mi in range(c["tm"] // mb):
+            for q in range(kg // 4):
+                add(f"A read w{w} m{mi} q{q}", 4, [word("a", wm0 + mi * mb + l % mb, (l // mb) * kg + 4 * q)
+                                                  for l in range(64)])
+        for j in range(kg):
+            for ni in range(0, c["tn"] // mb, 2):
+                add(f"B read2 w{w} j{j} n{ni}", -mb,
+                    [word("b", (l // mb) * kg + j, wn0 + ni * mb + l % mb) for l in range(64)])
+        for tile, rows, cols in (("a", c["bm"], c["bk"]), ("b", c["bk"], c["bn"])):
+            vcols = cols // vec
+            for i in range(rows * vcols // c["threads"]):
+                idx = [w * 64 + l + i * c["threads"] for l in range(64)]
+                add(f"{tile.upper()} store w{w} s{i}", 100 + vec, [word(tile, x // vcols, (x % vcols) * vec) for x in idx])
+    return out
+
+
 def predicted(words, width, geom):
     import dense_fp32_tiled_amd as dft
 
+    if width > 100:  # a store: modelled with the read geometry of its width
+        width -= 100
     if width < 0:  # ds_read2_b32: two 4-byte accesses, one per address; report the worse
         banks, group = geom[1]
         return max(dft.gemm_lds_conflict_degree(words, 1, banks, group),
@@ -95,6 +167,7 @@ def measured_degree(cycles_per_instr: float, width: int, waves: int, geom, issue
     degree-1 access lands."""
     if cycles_per_instr < 1.1 * issue_floor:
         return 1
+    width = width - 100 if width > 100 else width
     passes = 64 // geom[width][1] if width > 0 else 2 * (64 // geom[1][1])
     return max(1, round(cycles_per_instr / (waves * passes)))
 
@@ -111,13 +184,28 @@ def fit(rows, waves):
     return score
 
 
-def run(reps: int = 2000, waves: int = 4):
+def xcc_map(blocks: int = 512, threads: int = 512):
+    """XCD of each workgroup of a 1-D launch (probe_xcc_ids)."""
+    import torch
+
+    lib = load()
+    out = torch.full((blocks,), -1, dtype=torch.int32, device="cuda")
+    if lib.probe_xcc_ids(out.data_ptr(), blocks, threads, torch.cuda.current_stream().cuda_stream) != 0:
+        raise RuntimeError("probe_xcc_ids failed")
+    torch.cuda.synchronize()
+    return out.cpu().tolist()
+
+
+def run(reps: int = 2000, waves: int = 4, variants=()):
     import torch
 
     lib = load()
     out = torch.zeros(16, dtype=torch.int64, device="cuda")
     rows = []
-    for name, width, words in patterns():
+    pats = list(patterns())
+    for v in variants:
+        pats += kernel_patterns(v)
+    for name, width, words in pats:
         arr = (ctypes.c_int32 * 64)(*words)
         st = lib.lds_probe_run(arr, width, waves, reps, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
         if st != 0:
@@ -125,7 +213,7 @@ def run(reps: int = 2000, waves: int = 4):
         torch.cuda.synchronize()
         cyc = out[:waves].cpu().tolist()
         per_instr = max(cyc) / (reps * 16)
-        rows.append({"pattern": name, "width_bytes": 4 * width if width > 0 else 8, "mode": width,
+        rows.append({"pattern": name, "width_bytes": 4 * (width % 100) if width > 0 else 8, "mode": width,
                      "cycles_per_instr_per_wave": per_instr,
                      "predicted_degree": {g: predicted(words, width, v) for g, v in GEOMETRIES.items()}})
     return rows
@@ -136,13 +224,25 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default="")
     ap.add_argument("--reps", type=int, default=2000)
     ap.add_argument("--waves", type=int, default=4)
+    ap.add_argument("--kernels", action="store_true",
+                    help="also replay every LDS access pattern of the MFMA variants")
+    ap.add_argument("--xcc", action="store_true", help="also report the XCD of each workgroup of a 512-block launch")
     args = ap.parse_args(argv)
-    rows = run(args.reps, args.waves)
+    import dense_fp32_tiled_amd as dft
+
+    variants = (dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128_BK32) if args.kernels else ()
+    rows = run(args.reps, args.waves, variants)
     lines = [f"# LDS probe: {args.waves} waves x {args.reps} x 16 reads per pattern; cycles per instruction per wave",
              "pattern | bytes/lane | cycles/instr | " + " | ".join(f"degree[{g}]" for g in GEOMETRIES)]
     for r in rows:
         lines.append(f"{r['pattern']} | {r['width_bytes']} | {r['cycles_per_instr_per_wave']:.2f} | " +
                      " | ".join(str(r["predicted_degree"][g]) for g in GEOMETRIES))
+    if args.xcc:
+        ids = xcc_map()
+        rr = sum(1 for b, x in enumerate(ids) if x == b % 8)
+        lines.append("")
+        lines.append(f"XCD of workgroups 0..{len(ids) - 1} (512 threads each): {ids[:32]} ...")
+        lines.append(f"workgroups with XCD == index % 8: {rr} of {len(ids)}")
     score = fit(rows, args.waves)
     lines.append("")
     lines.append("patterns whose timing matches the predicted degree (of %d):" % len(rows))

@@ -30,7 +30,9 @@ extern "C" {
  *             multiple of width_words and address + width_words <=
  *             LDS_PROBE_WORDS), or -16 / -32: ds_read2_b32 reading the dwords
  *             at address and address + 16 (or 32); address + 17 (or 33) <=
- *             LDS_PROBE_WORDS.
+ *             LDS_PROBE_WORDS; or 101, 102, 104: ds_write_b32 / b64 / b128 of
+ *             1, 2 or 4 dwords, with the alignment and bound of the read of
+ *             the same width.
  * waves: 1..16 wavefronts in the workgroup.  reps: 1..100000.
  * cycles_out: DEVICE buffer of `waves` uint64 values, owned by the caller;
  *             wave w writes the shader-clock cycles its read loop took.
@@ -40,6 +42,15 @@ extern "C" {
  */
 int lds_probe_run(const int32_t *lane_words, int32_t width_words, int32_t waves, int32_t reps,
                   uint64_t *cycles_out, void *stream);
+
+/*
+ * XCD (accelerator complex die) each workgroup of a 1-D launch runs on:
+ * launches `blocks` workgroups of `threads` threads; workgroup b writes its
+ * XCC_ID hardware register to out[b].  out: DEVICE buffer of `blocks` int32,
+ * owned by the caller.  Returns 0, -1 for invalid arguments, -2 if the launch
+ * failed.
+ */
+int probe_xcc_ids(int32_t *out, int32_t blocks, int32_t threads, void *stream);
 
 /*
  * Reference kernel for calibrating the HBM traffic counters: dst[i] = src[i]

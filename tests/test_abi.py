@@ -3,6 +3,7 @@ rejects bad arguments on the host before touching a device (CPU only)."""
 
 from __future__ import annotations
 
+import ctypes
 import re
 import subprocess
 from pathlib import Path
@@ -29,7 +30,7 @@ def exported(lib: Path) -> set[str]:
 def test_probe_library_exports_its_header(gemm_lib):
     from dense_fp32_tiled_amd import lds_probe
 
-    assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32"}
+    assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32", "probe_xcc_ids"}
     assert declared_functions(PROBE_HEADER) <= exported(lds_probe.PROBE_LIB)
 
 
@@ -212,3 +213,23 @@ def test_splitk_queries(gemm_lib):
     assert dft.gemm_f32_splitk_auto_splits(128, 128, 1 << 20, 256) == 64  # capped at 64
     assert dft.gemm_f32_splitk_auto_splits(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert dft.gemm_f32_splitk_workspace_bytes(4, 4, 4, 99, 256) == dft.GEMM_ERR_INVALID_DIM
+
+
+def test_every_binding_declares_its_full_signature(gemm_lib):
+    """ctypes passes an argument with no declared type as a C int, which
+    truncates a 64-bit device pointer; every exported function of both
+    libraries must have its argument list declared, with pointers as
+    pointer types and as many arguments as the header declares."""
+    from dense_fp32_tiled_amd import lds_probe
+
+    probe = lds_probe.load()
+    for lib, header in ((gemm_lib, HEADER), (probe, PROBE_HEADER)):
+        text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+        for name, params in re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(([^)]*)\)", text, flags=re.M):
+            fn = getattr(lib, name)
+            assert fn.argtypes is not None, f"{name} has no declared argtypes"
+            decl = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+            assert len(fn.argtypes) == len(decl), name
+            for d, t in zip(decl, fn.argtypes):
+                if "*" in d:
+                    assert t is ctypes.c_void_p or t is ctypes.c_char_p or hasattr(t, "contents"), (name, d, t)
