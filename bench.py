@@ -61,7 +61,9 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--variant", default="auto", help="auto, mfma, valu, mfma_stages1, mfma_nopad, mfma_scalar")
+    ap.add_argument("--variant", default="auto",
+                    help="kernel variant by name (auto, mfma, mfma_direct, valu, ...; see VARIANT_NAMES); with "
+                         "--splits, the kernel that computes the slices")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--cpu-sample-rows", type=int, default=512,
                     help="rows of C the CPU oracle computes for its baseline (0 = skip)")
@@ -116,7 +118,8 @@ def main(argv=None) -> int:
 
     def step(v=variant):
         if args.splits >= 0 and v == variant:
-            st = dft.gemm_f32_splitk(M, N, K, pa, K, pb, N, pc, N, ws.data_ptr(), ws_bytes, args.splits, handle)
+            st = dft.gemm_f32_splitk_ex(M, N, K, pa, K, pb, N, pc, N, ws.data_ptr(), ws_bytes, args.splits, handle,
+                                        variant)
         else:
             st = dft.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, handle, v)
         if st != dft.GEMM_OK:
@@ -145,7 +148,7 @@ def main(argv=None) -> int:
     tflops = cfg.flops / wall_s / 1e12
     achieved = cfg.flops / kern_avg_s / 1e12
     if args.splits >= 0:
-        resolved = dft.VARIANT_MFMA_128
+        resolved = dft.gemm_f32_splitk_auto_variant() if variant == dft.VARIANT_AUTO else variant
     elif variant == dft.VARIANT_AUTO:
         resolved = dft.gemm_f32_auto_variant(M, N, K, torch.cuda.get_device_properties(dev).multi_processor_count)
     else:

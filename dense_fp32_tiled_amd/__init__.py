@@ -36,7 +36,10 @@ VARIANT_MFMA_SCALAR = 5
 VARIANT_MFMA16 = 6
 VARIANT_MFMA_128 = 7
 VARIANT_MFMA_128_BK32 = 8
-VARIANT_COUNT = 9
+VARIANT_MFMA_DIRECT = 9
+VARIANT_MFMA_128_DIRECT = 10
+VARIANT_MFMA_128_BK32_DIRECT = 11
+VARIANT_COUNT = 12
 VARIANT_NAMES = {
     VARIANT_AUTO: "auto",
     VARIANT_MFMA: "mfma",
@@ -47,6 +50,9 @@ VARIANT_NAMES = {
     VARIANT_MFMA16: "mfma16",
     VARIANT_MFMA_128: "mfma_128",
     VARIANT_MFMA_128_BK32: "mfma_128_bk32",
+    VARIANT_MFMA_DIRECT: "mfma_direct",
+    VARIANT_MFMA_128_DIRECT: "mfma_128_direct",
+    VARIANT_MFMA_128_BK32_DIRECT: "mfma_128_bk32_direct",
 }
 
 # Every symbol the public header declares.
@@ -56,6 +62,8 @@ EXPORTS = (
     "gemm_f32_tile_config",
     "gemm_f32_status_string",
     "gemm_f32_splitk",
+    "gemm_f32_splitk_ex",
+    "gemm_f32_splitk_auto_variant",
     "gemm_f32_splitk_workspace_bytes",
     "gemm_f32_splitk_auto_splits",
     "gemm_f32_auto_variant",
@@ -82,7 +90,7 @@ class TileConfig(ctypes.Structure):
         "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
         "lds_bytes", "vec_width", "lds_banks_b32", "lds_lanes_b32", "lds_banks_b128", "lds_lanes_b128",
         "a_transposed", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_swz_unit", "b_swz_shift", "b_swz_mask",
-        "mfma_block", "xcd_tile_order")]
+        "mfma_block", "xcd_tile_order", "direct_to_lds")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -126,13 +134,17 @@ def library(path: Path | None = None):
     lib.gemm_f32_status_string.restype = ctypes.c_char_p
     lib.gemm_f32_splitk.argtypes = gemm_args[:9] + [vp, i64, ctypes.c_int, vp]
     lib.gemm_f32_splitk.restype = ctypes.c_int
+    lib.gemm_f32_splitk_ex.argtypes = gemm_args[:9] + [vp, i64, ctypes.c_int, vp, ctypes.c_int]
+    lib.gemm_f32_splitk_ex.restype = ctypes.c_int
+    lib.gemm_f32_splitk_auto_variant.argtypes = []
+    lib.gemm_f32_splitk_auto_variant.restype = ctypes.c_int
     lib.gemm_f32_splitk_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, i32]
     lib.gemm_f32_splitk_workspace_bytes.restype = i64
     lib.gemm_f32_splitk_auto_splits.argtypes = [i64, i64, i64, i32]
     lib.gemm_f32_splitk_auto_splits.restype = ctypes.c_int
     lib.gemm_f32_auto_variant.argtypes = [i64, i64, i64, i32]
     lib.gemm_f32_auto_variant.restype = ctypes.c_int
-    lib.gemm_lds_choose_mfma_layout.argtypes = [i32] * 7 + [ctypes.POINTER(i32)]
+    lib.gemm_lds_choose_mfma_layout.argtypes = [i32] * 8 + [ctypes.POINTER(i32)]
     lib.gemm_lds_choose_mfma_layout.restype = ctypes.c_int
     p32 = ctypes.POINTER(i32)
     lib.gemm_lds_layout.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
@@ -175,6 +187,16 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
     return library().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits, stream)
 
 
+def gemm_f32_splitk_ex(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits=0, stream=None,
+                       variant=VARIANT_AUTO) -> int:
+    return library().gemm_f32_splitk_ex(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits, stream,
+                                        variant)
+
+
+def gemm_f32_splitk_auto_variant() -> int:
+    return library().gemm_f32_splitk_auto_variant()
+
+
 def gemm_f32_splitk_workspace_bytes(M: int, N: int, K: int, splits: int, num_cus: int) -> int:
     return library().gemm_f32_splitk_workspace_bytes(M, N, K, splits, num_cus)
 
@@ -187,10 +209,10 @@ def gemm_f32_auto_variant(M: int, N: int, K: int, num_cus: int) -> int:
     return library().gemm_f32_auto_variant(M, N, K, num_cus)
 
 
-def gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec):
+def gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec, direct=0):
     """(status, (pad, unit, shift, mask) of A, (pad, unit, shift, mask) of B)."""
     out = (ctypes.c_int32 * 8)()
-    st = library().gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec, out)
+    st = library().gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec, direct, out)
     return st, tuple(out[:4]), tuple(out[4:])
 
 
@@ -243,9 +265,10 @@ def _stream_handle(stream, device):
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
-def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None):
-    """C = a @ b with gemm_f32_splitk.  The workspace (a float32 tensor on the
-    same device) is allocated here when not given."""
+def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None, variant: int = VARIANT_AUTO):
+    """C = a @ b with gemm_f32_splitk_ex (slices run by `variant`, AUTO = the
+    library's split-K kernel).  The workspace (a float32 tensor on the same
+    device) is allocated here when not given."""
     import torch
 
     pa, lda = _operand(a, "a")
@@ -266,9 +289,10 @@ def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None):
     wp = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(a.device):
-        st = gemm_f32_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, wp, wbytes, splits, _stream_handle(stream, a.device))
+        st = gemm_f32_splitk_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, wp, wbytes, splits,
+                                _stream_handle(stream, a.device), variant)
     if st != GEMM_OK:
-        raise GemmError(st, "gemm_f32_splitk")
+        raise GemmError(st, "gemm_f32_splitk_ex")
     return out
 
 

@@ -30,6 +30,26 @@ using Mfma256Plain = MfmaCfg<256, 128, 16, 64, 64, 2, 32, TileLayout<0>, TileLay
 template <int VEC>
 using Mfma16x256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m16_256x128x16_v4, layouts::m16_256x128x16_v1>,
                           2, VEC, 256, 128, 16, 16>;
+// Direct global->LDS copies for in-range tiles (16-byte path only; the
+// 4-byte path of this variant loads through registers like MFMA).
+template <int VEC>
+using Mfma256Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 128, 16, 64, 64, 2, 32, layouts::m32_256x128x16_direct::A, layouts::m32_256x128x16_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    Mfma256<2, 1>>;
+template <int VEC>
+using Mfma128Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A, layouts::m32_128x128x16_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
+template <int VEC>
+using Mfma128Bk32Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<128, 128, 32, 64, 64, 2, 32, layouts::m32_128x128x32_direct::A, layouts::m32_128x128x32_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    MfmaAt<layouts::m32_128x128x32_v1, 2, 1, 128, 128, 32, 32>>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -112,6 +132,7 @@ void describe_common(gemm_tile_config& c, int variant, int vec) {
     c.lds_banks_b32 = kGfx950Lds.banks_b32; c.lds_lanes_b32 = kGfx950Lds.lanes_b32;
     c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.xcd_tile_order = Cfg::ORDER == kXcdGroupedOrder ? 1 : 0;
+    c.direct_to_lds = Cfg::LOAD == kLoadDirect ? 1 : 0;
 }
 
 template <class Cfg>
@@ -151,7 +172,7 @@ Variant mfma_variant() {
 // Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
 // to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
+    /* AUTO          */ mfma_variant<Mfma256Direct<4>, Mfma256Direct<1>>(),
     /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
     /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, valu_config<ValuT<1>>,
                          ValuT<4>::LDS_BYTES},
@@ -161,12 +182,15 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA16        */ mfma_variant<Mfma16x256<4>, Mfma16x256<1>>(),
     /* MFMA_128      */ mfma_variant<Mfma128<4>, Mfma128<1>>(),
     /* MFMA_128_BK32 */ mfma_variant<Mfma128Bk32<4>, Mfma128Bk32<1>>(),
+    /* MFMA_DIRECT   */ mfma_variant<Mfma256Direct<4>, Mfma256Direct<1>>(),
+    /* MFMA_128_DIRECT      */ mfma_variant<Mfma128Direct<4>, Mfma128Direct<1>>(),
+    /* MFMA_128_BK32_DIRECT */ mfma_variant<Mfma128Bk32Direct<4>, Mfma128Bk32Direct<1>>(),
 };
 
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     const int64_t tiles256 = ((M + 255) / 256) * ((N + 127) / 128);
-    if (tiles256 >= num_cus) return GEMM_VARIANT_MFMA;
-    return K >= 4096 ? GEMM_VARIANT_MFMA_128_BK32 : GEMM_VARIANT_MFMA_128;
+    if (tiles256 >= num_cus) return GEMM_VARIANT_MFMA_DIRECT;
+    return K >= 4096 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT;
 }
 
 // ---- per-device properties (cached) ---------------------------------------------
@@ -285,23 +309,28 @@ int run(const Args& a, hipStream_t stream, int variant) {
 }
 
 // ---- split-K ------------------------------------------------------------------------
-constexpr int kSplitKVariant = GEMM_VARIANT_MFMA_128;
-constexpr int64_t kSplitKTileBk = 16;  // BK of kSplitKVariant: slices are multiples of it
+constexpr int kSplitKVariant = GEMM_VARIANT_MFMA_DIRECT;  // the slice kernel when none is named
+constexpr int64_t kSplitKTileBm = 256, kSplitKTileBn = 128;  // its output tile
+constexpr int64_t kSplitKTileBk = 16;  // K-tile depth the automatic split count is reckoned in
 constexpr int kMaxSplits = 64;
 
-int64_t splitk_chunk(int64_t K, int64_t splits) {
-    const int64_t tiles = (K + kSplitKTileBk - 1) / kSplitKTileBk;
-    return ((tiles + splits - 1) / splits) * kSplitKTileBk;
+// Slice length: whole K tiles of the slice kernel (depth bk), so slice
+// boundaries fall on tile boundaries and keep 16-byte alignment.
+int64_t splitk_chunk(int64_t K, int64_t splits, int64_t bk) {
+    const int64_t tiles = (K + bk - 1) / bk;
+    return ((tiles + splits - 1) / splits) * bk;
 }
 
 int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) { return splits * M * N * 4; }
 
 int splitk_auto_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
-    // Enough slices to give every CU four workgroups (the occupancy of the
-    // 128x128 kernel), keeping at least eight K tiles per slice.
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    // Enough slices to give every CU one workgroup of the 256x128 slice
+    // kernel (measured best on 2048x256x16384 and 512x4096x4096: more slices
+    // cost more in partial-product traffic than they gain in occupancy),
+    // keeping at least eight 16-deep K tiles per slice.
+    const int64_t tiles = ((M + kSplitKTileBm - 1) / kSplitKTileBm) * ((N + kSplitKTileBn - 1) / kSplitKTileBn);
     const int64_t ktiles = (K + kSplitKTileBk - 1) / kSplitKTileBk;
-    int64_t s = (4 * (int64_t)num_cus + tiles - 1) / tiles;
+    int64_t s = ((int64_t)num_cus + tiles - 1) / tiles;
     if (s > ktiles / 8) s = ktiles / 8;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : (int)s;
@@ -318,7 +347,10 @@ int check_workspace(const Args& a, const void* workspace, int64_t workspace_byte
     return GEMM_OK;
 }
 
-int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int splits, hipStream_t stream) {
+int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int splits, hipStream_t stream,
+               int variant) {
+    if (variant < 0 || variant >= GEMM_VARIANT_COUNT) return GEMM_ERR_UNSUPPORTED;
+    if (variant == GEMM_VARIANT_AUTO) variant = kSplitKVariant;
     if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_DIM;
     int st = validate(a);
     if (st != GEMM_OK) return st;
@@ -336,13 +368,13 @@ int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int spli
         st = check_workspace(a, workspace, workspace_bytes, splits);
         if (st != GEMM_OK) return st;
     }
-    if (splits == 1) return launch_variant(a, kSplitKVariant, max_lds, Split{}, stream);
+    if (splits == 1) return launch_variant(a, variant, max_lds, Split{}, stream);
     // 1. every slice writes its partial product, packed M x N, into the workspace
     Args part = a;
     part.C = static_cast<float*>(workspace);
     part.ldc = a.N;
-    const Split sp{splits, splitk_chunk(a.K, splits), a.M * a.N};
-    st = launch_variant(part, kSplitKVariant, max_lds, sp, stream);
+    const Split sp{splits, splitk_chunk(a.K, splits, kVariants[variant].config4(variant, 4).bk), a.M * a.N};
+    st = launch_variant(part, variant, max_lds, sp, stream);
     if (st != GEMM_OK) return st;
     // 2. C = sum of the slices in ascending slice order
     int64_t M = a.M, N = a.N, S = splits, ldc = a.ldc;
@@ -386,15 +418,17 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
 }
 
 int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
-                                int32_t vec, int32_t* out) {
+                                int32_t vec, int32_t direct, int32_t* out) {
     if (out == nullptr || (mb != 32 && mb != 16) || (vec != 1 && vec != 4)) return GEMM_ERR_INVALID_DIM;
+    if ((direct != 0 && direct != 1) || (direct && vec != 4)) return GEMM_ERR_INVALID_DIM;
     if (bm < 1 || bn < 1 || bk < 1 || wm < mb || wn < mb || bm % wm || bn % wn || wm % mb || wn % mb)
         return GEMM_ERR_INVALID_DIM;
     const int kb = 64 / mb, threads = (bm / wm) * (bn / wn) * kWaveLanes;
     if (bk % (4 * kb) || bk % vec || bn % vec || threads > 1024 || (bm * bk / vec) % threads ||
         (bk * bn / vec) % threads)
         return GEMM_ERR_INVALID_DIM;
-    const MfmaShape shape{bm, bn, bk, wm, wn, threads, vec, mb, mb, kb};
+    if (direct && ((bm * bk) % (threads * 4) || (bk * bn) % (threads * 4))) return GEMM_ERR_INVALID_DIM;
+    const MfmaShape shape{bm, bn, bk, wm, wn, threads, vec, mb, mb, kb, direct == 1};
     const LayoutChoice a = mfma_layout_a(shape, kGfx950Lds), b = mfma_layout_b(shape, kGfx950Lds);
     const int32_t v[8] = {a.pad, a.swz.unit, a.swz.shift, a.swz.mask, b.pad, b.swz.unit, b.swz.shift, b.swz.mask};
     for (int i = 0; i < 8; ++i) out[i] = v[i];
@@ -403,8 +437,18 @@ int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, 
 
 int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
                     float* C, int64_t ldc, void* workspace, int64_t workspace_bytes, int splits, void* stream) {
-    return run_splitk(Args{M, N, K, A, lda, B, ldb, C, ldc}, workspace, workspace_bytes, splits, (hipStream_t)stream);
+    return run_splitk(Args{M, N, K, A, lda, B, ldb, C, ldc}, workspace, workspace_bytes, splits, (hipStream_t)stream,
+                      GEMM_VARIANT_AUTO);
 }
+
+int gemm_f32_splitk_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float* C, int64_t ldc, void* workspace, int64_t workspace_bytes, int splits, void* stream,
+                       int variant) {
+    return run_splitk(Args{M, N, K, A, lda, B, ldb, C, ldc}, workspace, workspace_bytes, splits, (hipStream_t)stream,
+                      variant);
+}
+
+int gemm_f32_splitk_auto_variant(void) { return kSplitKVariant; }
 
 int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits, int32_t num_cus) {
     if (M < 0 || N < 0 || K < 0 || splits < 0 || splits > kMaxSplits || num_cus < 1) return GEMM_ERR_INVALID_DIM;

@@ -190,12 +190,16 @@ struct TileLayout {
 
 enum TileOrder { kRowMajorOrder = 0, kXcdGroupedOrder = 1 };
 
+// How K tiles reach LDS: through registers (global load, then LDS store), or
+// by the direct global->LDS copy for in-range tiles (DirectCopy).
+enum LoadPath { kLoadRegisters = 0, kLoadDirect = 1 };
+
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MB_, class LayA, class LayB, int VEC_,
-          int ORDER_ = kRowMajorOrder>
+          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters>
 struct MfmaCfg {
     using Op = MfmaOp<MB_, 64 / MB_>;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_;
+    static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_, LOAD = LOAD_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
@@ -211,7 +215,94 @@ struct MfmaCfg {
     static_assert(KG % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
     static_assert(TileB::row_stride % VEC == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
     static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
+    static_assert(LOAD == kLoadRegisters || (VEC == 4 && STAGES == 2 && LayA::pad == 0 && LayB::pad == 0),
+                  "direct copies need 16-byte loads, two stages and unpadded rows");
 };
+
+// One direct global->LDS copy instruction (gfx950 global_load_lds_dwordx4):
+// each lane reads 16 bytes at its own global address `src`, and the wavefront
+// writes them to LDS at byte address lds_base + 16 * lane; lds_base must be
+// wave-uniform and is taken from M0, which the statement saves and restores
+// (one wait state is required between writing M0 and the copy).  Written as
+// an asm statement because the compiler's own form of this copy makes it wait
+// for every outstanding copy before any later LDS read, which would serialise
+// the copy of the next K tile with the multiply of the current one; as asm
+// the copy is invisible to the compiler's wait-count tracking, so completion
+// is waited for explicitly (wait_vector_memory) before the barrier that
+// publishes the stage.  The "memory" clobber keeps LDS accesses from being
+// moved across it.
+__device__ inline void copy16_to_lds(const float* src, uint32_t lds_base) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(src), "s"(lds_base)
+        : "memory");
+}
+
+// Direct global->LDS copy of one operand tile.  A stage of an unpadded tile
+// is cut into 1 KiB pieces (64 lanes x 16 bytes), piece i * WAVES + w being
+// written by wavefront w's i-th copy instruction, and the lane that writes
+// LDS word p fetches the element the tile layout keeps there: row p / cols,
+// column swizzle(row, p % cols) (the XOR swizzle is its own inverse).  The
+// fetch offsets do not depend on the K tile, so they are computed once.
+template <class Tile, int THREADS>
+struct DirectCopy {
+    static_assert(Tile::pad == 0, "direct copies write whole rows contiguously");
+    static constexpr int WAVES = THREADS / kWave;
+    static constexpr int PIECE = kWave * 4;  // fp32 words per instruction per wavefront
+    static_assert(Tile::stage_elems % (PIECE * WAVES) == 0, "tile must split evenly over the wavefronts");
+    static constexpr int PER_WAVE = Tile::stage_elems / (PIECE * WAVES);
+
+    // Logical (row, col) of the four elements stored at LDS word `word` of a stage.
+    static constexpr void source(int word, int& row, int& col) {
+        row = word / Tile::cols;
+        col = Swizzle{Tile::swizzle.unit, Tile::swizzle.shift, Tile::swizzle.mask}.apply(row, word % Tile::cols);
+    }
+    // Every 16-byte group of a stage is fetched from the element the tile
+    // layout (which the fragment reads use) places there.
+    static constexpr bool matches_layout() {
+        for (int word = 0; word < Tile::stage_elems; word += 4) {
+            int row = 0, col = 0;
+            source(word, row, col);
+            if (row >= Tile::rows || col % 4 != 0 || col >= Tile::cols || Tile::offset(0, row, col) != word)
+                return false;
+        }
+        return true;
+    }
+    static_assert(matches_layout(), "direct copies must fill the LDS tile in its own layout");
+
+    int64_t off[PER_WAVE];  // element offset of this lane's 16 bytes from the tile origin
+    uint32_t lds_piece;     // byte offset of this wavefront's first piece in a stage (uniform)
+
+    __device__ DirectCopy(int64_t ld, int wave_uniform, int lane) : lds_piece(wave_uniform * PIECE * 4) {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            int row = 0, col = 0;
+            source((i * WAVES + wave_uniform) * PIECE + 4 * lane, row, col);
+            off[i] = (int64_t)row * ld + col;
+        }
+    }
+
+    // Issue the copies of the tile at `origin` into `stage` of the LDS tile
+    // at `lds`; they complete asynchronously (vector memory counter).
+    __device__ void issue(const float* origin, float* lds, int stage) const {
+        typedef __attribute__((address_space(3))) float lds_float;
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_float*)lds + lds_piece + stage * (Tile::stage_elems * 4);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) copy16_to_lds(origin + off[i], base + i * (WAVES * PIECE * 4));
+    }
+};
+
+// Wait until this wavefront's outstanding vector memory operations, direct
+// LDS copies included, have completed (s_waitcnt vmcnt(0); the expcnt and
+// lgkmcnt fields of the immediate are left at their no-wait maxima).
+__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <class Cfg>
 __device__ inline TileCoord tile_of_block(int64_t tiles_m, int64_t tiles_n) {
@@ -308,7 +399,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         }
     };
 
-    if constexpr (Cfg::STAGES == 2) {
+    // Two stages through registers: the global loads of tile t+1 are issued
+    // before the multiply of tile t and written to LDS after it.
+    auto two_stage_registers = [&]() {
         if (T > 0) {
             load_tile(0);
             ldr_a.template store<TileA>(lds_a, 0, tid);
@@ -326,6 +419,52 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
             }
             __syncthreads();
         }
+    };
+
+    if constexpr (Cfg::LOAD == kLoadDirect) {
+        // Two stages filled by direct copies: the copies of tile t+1 are in
+        // flight during the multiply of tile t, and each wave waits for its
+        // own copies before the barrier, after which the whole stage is in
+        // LDS.  A tile not wholly in range (edge workgroups; the last K tile
+        // when BK does not divide K) needs zero fill: it is loaded through
+        // registers with masks after the multiply, so that no staging
+        // registers are live across it.  Both choices are uniform.
+        const DirectCopy<TileA, THREADS> dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
+        const DirectCopy<TileB, THREADS> dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
+        const bool interior = M - m0 >= BM && N - n0 >= BN;
+        auto fill = [&](int64_t t, int stage) {
+            const int64_t k0 = t * BK;
+            if (interior && K - k0 >= BK) {
+                dma_a.issue(a_tile + k0, lds_a, stage);
+                dma_b.issue(b_tile + k0 * ldb, lds_b, stage);
+            } else {
+                load_tile(t);
+                ldr_a.template store<TileA>(lds_a, stage, tid);
+                ldr_b.template store<TileB>(lds_b, stage, tid);
+            }
+        };
+        if (T > 0) fill(0, 0);
+        wait_vector_memory();
+        __syncthreads();
+        for (int64_t t = 0; t < T; ++t) {
+            const int s = (int)(t & 1);
+            const bool more = t + 1 < T;
+            const bool direct = more && interior && K - (t + 1) * BK >= BK;
+            if (direct) {
+                dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
+                dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+            }
+            multiply(s);
+            if (more && !direct) {
+                load_tile(t + 1);
+                ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
+                ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
+            }
+            wait_vector_memory();
+            __syncthreads();
+        }
+    } else if constexpr (Cfg::STAGES == 2) {
+        two_stage_registers();
     } else {
         // One stage: write, barrier, read, barrier (the two-barrier protocol).
         for (int64_t t = 0; t < T; ++t) {
@@ -373,6 +512,7 @@ struct ValuCfg {
     static constexpr int THREADS = THREADS_M * THREADS_N;
     static constexpr int MIN_WAVES = 2;
     static constexpr int ORDER = kRowMajorOrder;
+    static constexpr int LOAD = kLoadRegisters;
     using TileA = LdsTile<BK, BM, PADA, STAGES>;  // k-major
     using TileB = LdsTile<BK, BN, PADB, STAGES>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;

@@ -57,13 +57,13 @@ constexpr int pattern_cost_pair(LayoutChoice c, int cols, LdsGeometry g, RowCol2
     return total;
 }
 
-// Search pads 0, 4, ..., kMaxPad, then swizzles; `cost(choice)` sums a tile's
-// access costs.
+// Search pads 0, 4, ..., kMaxPad (only 0 unless allow_pad), then swizzles;
+// `cost(choice)` sums a tile's access costs.
 template <class Cost>
-constexpr LayoutChoice choose_layout(Cost cost, int cols) {
+constexpr LayoutChoice choose_layout(Cost cost, int cols, bool allow_pad = true) {
     LayoutChoice best{0, kNoSwizzle};
     int best_cost = cost(best);
-    for (int pad = 4; pad <= kMaxPad; pad += 4) {
+    for (int pad = 4; allow_pad && pad <= kMaxPad; pad += 4) {
         const LayoutChoice c{pad, kNoSwizzle};
         const int v = cost(c);
         if (v < best_cost) { best = c; best_cost = v; }
@@ -82,9 +82,14 @@ constexpr LayoutChoice choose_layout(Cost cost, int cols) {
 // ---- matrix-core kernel ---------------------------------------------------------
 // A row-major [BM][BK], B row-major [BK][BN]; MFMA block MB x NB x KB; lane l
 // belongs to k-group l / MB and reduces k in [group * KG, (group + 1) * KG),
-// KG = BK / KB, one k per MFMA step.
+// KG = BK / KB, one k per MFMA step.  `direct`: tiles reach LDS by direct
+// global->LDS copies, whose writes fill 1 KiB of consecutive words per
+// wavefront instruction (no bank conflicts whatever the layout, and no room
+// for row padding), so only the fragment reads are costed and only unpadded
+// layouts are candidates.
 struct MfmaShape {
     int bm, bn, bk, wm, wn, threads, vec, mb, nb, kb;
+    bool direct = false;
     constexpr int kg() const { return bk / kb; }
     constexpr int waves() const { return threads / kWaveLanes; }
     constexpr int waves_n() const { return bn / wn; }
@@ -103,7 +108,7 @@ constexpr int mfma_a_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
                     col = (l / s.mb) * s.kg() + 4 * q;
                 });
         const int vcols = s.bk / s.vec;
-        for (int i = 0; i < (s.bm * vcols) / s.threads; ++i)
+        for (int i = 0; !s.direct && i < (s.bm * vcols) / s.threads; ++i)
             total += pattern_cost(c, s.bk, s.vec, g, [=](int l, int& row, int& col) {
                 const int idx = w * kWaveLanes + l + i * s.threads;
                 row = idx / vcols;
@@ -135,7 +140,7 @@ constexpr int mfma_b_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
                 });
         }
         const int vcols = s.bn / s.vec;
-        for (int i = 0; i < (s.bk * vcols) / s.threads; ++i)
+        for (int i = 0; !s.direct && i < (s.bk * vcols) / s.threads; ++i)
             total += pattern_cost(c, s.bn, s.vec, g, [=](int l, int& row, int& col) {
                 const int idx = w * kWaveLanes + l + i * s.threads;
                 row = idx / vcols;
@@ -146,10 +151,10 @@ constexpr int mfma_b_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
 }
 
 constexpr LayoutChoice mfma_layout_a(MfmaShape s, LdsGeometry g) {
-    return choose_layout([=](LayoutChoice c) { return mfma_a_cost(s, c, g); }, s.bk);
+    return choose_layout([=](LayoutChoice c) { return mfma_a_cost(s, c, g); }, s.bk, !s.direct);
 }
 constexpr LayoutChoice mfma_layout_b(MfmaShape s, LdsGeometry g) {
-    return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn);
+    return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn, !s.direct);
 }
 
 // ---- vector-ALU kernel: A k-major [BK][BM+pad], B row-major [BK][BN+pad] ----

@@ -57,7 +57,7 @@ typedef enum {
 /* Kernel variants.  Every variant computes the same operation; they differ in
  * how (see gemm_f32_tile_config for each one's tile geometry). */
 typedef enum {
-    GEMM_VARIANT_AUTO = 0,          /* picks one of the MFMA variants from M, N, K (gemm_f32_auto_variant) */
+    GEMM_VARIANT_AUTO = 0,          /* picks one of the direct-copy MFMA variants from M, N, K (gemm_f32_auto_variant) */
     GEMM_VARIANT_MFMA = 1,          /* v_mfma_f32_32x32x2_f32, 256x128x16 workgroup tile, 8 waves of 64x64 */
     GEMM_VARIANT_VALU = 2,          /* register-tiled vector-ALU fp32 FMA, 128x128x16, 8x8 per thread */
     GEMM_VARIANT_MFMA_STAGES1 = 3,  /* ablation of MFMA: one LDS stage, two barriers per K tile, no prefetch */
@@ -66,7 +66,10 @@ typedef enum {
     GEMM_VARIANT_MFMA16 = 6,        /* as MFMA with v_mfma_f32_16x16x4_f32 */
     GEMM_VARIANT_MFMA_128 = 7,      /* as MFMA with a 128x128x16 workgroup tile (4 waves) */
     GEMM_VARIANT_MFMA_128_BK32 = 8, /* as MFMA_128 with BK = 32 */
-    GEMM_VARIANT_COUNT = 9
+    GEMM_VARIANT_MFMA_DIRECT = 9,   /* as MFMA with in-range tiles copied global->LDS directly (no registers) */
+    GEMM_VARIANT_MFMA_128_DIRECT = 10,      /* as MFMA_128 with direct global->LDS copies */
+    GEMM_VARIANT_MFMA_128_BK32_DIRECT = 11, /* as MFMA_128_BK32 with direct global->LDS copies */
+    GEMM_VARIANT_COUNT = 12
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -94,6 +97,8 @@ typedef struct {
     int32_t b_swz_unit, b_swz_shift, b_swz_mask; /*   col ^ (unit * ((row >> shift) & mask)) */
     int32_t mfma_block;          /* MFMA block size (32 or 16), 0 for the VALU variant */
     int32_t xcd_tile_order;      /* 1 if workgroups are mapped to tiles in the XCD-grouped order */
+    int32_t direct_to_lds;       /* 1 if in-range tiles are copied global->LDS without registers (16 bytes
+                                    per lane, LDS rows unpadded); edge tiles still go through registers */
 } gemm_tile_config;
 
 /* C = A @ B with the default variant.  M, N, K >= 0; lda >= max(1,K),
@@ -114,9 +119,10 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 void *stream, int variant);
 
-/* Split-K: C = A @ B with the K range cut into `splits` slices of whole
- * 16-deep K tiles, each reduced by its own workgroups (the MFMA_128 kernel),
- * so that problems with few 128x128 output tiles still occupy every CU.
+/* Split-K: C = A @ B with the K range cut into `splits` slices of whole K
+ * tiles, each reduced by its own workgroups (the kernel of
+ * gemm_f32_splitk_auto_variant), so that problems with few 128x128 output
+ * tiles still occupy every CU.
  * Slice s writes its partial product, packed M x N, to workspace + s*M*N
  * floats; a second kernel then sets C = sum of the slices in ascending slice
  * order, so the result is deterministic for a given `splits`.
@@ -134,14 +140,27 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     float *C, int64_t ldc,
                     void *workspace, int64_t workspace_bytes, int splits, void *stream);
 
+/* As gemm_f32_splitk with the slices computed by the kernel of `variant`
+ * (GEMM_VARIANT_AUTO: that of gemm_f32_splitk_auto_variant); slices are
+ * whole K tiles of that kernel.  The workspace and split count rules are
+ * gemm_f32_splitk's.  Returns GEMM_ERR_UNSUPPORTED for an unknown variant. */
+int gemm_f32_splitk_ex(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       float *C, int64_t ldc,
+                       void *workspace, int64_t workspace_bytes, int splits, void *stream, int variant);
+
+/* The variant gemm_f32_splitk runs the slices with.  Pure host call. */
+int gemm_f32_splitk_auto_variant(void);
+
 /* Workspace bytes gemm_f32_splitk needs (splits * M * N * 4, or 0 when the
  * resolved split count is 1); splits == 0 resolves with num_cus compute
  * units.  Pure host call.  Returns GEMM_ERR_INVALID_DIM on bad arguments. */
 int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits, int32_t num_cus);
 
 /* The split count gemm_f32_splitk uses for splits == 0: enough slices for
- * four workgroups per CU over the 128x128 output tiles, at most 64, and at
- * least eight K tiles per slice.  Pure host call. */
+ * one workgroup per CU over the 256x128 output tiles, at most 64, and at
+ * least eight 16-deep K tiles per slice.  Pure host call. */
 int gemm_f32_splitk_auto_splits(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
 /* Fills *out with the tile geometry of `variant`.  Pure host call (touches no
@@ -152,9 +171,9 @@ int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
- * `num_cus` compute units: MFMA when its 256x128 tiles give at least one
- * workgroup per CU, else MFMA_128_BK32 for K >= 4096, else MFMA_128.  Pure
- * host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
+ * `num_cus` compute units: MFMA_DIRECT when its 256x128 tiles give at least
+ * one workgroup per CU, else MFMA_128_BK32_DIRECT for K >= 4096, else
+ * MFMA_128_DIRECT.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
  * sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
@@ -194,11 +213,14 @@ int32_t gemm_lds_conflict_degree(const int64_t *lane_words, int32_t lanes,
 
 /* The LDS layout search the MFMA kernels are built with, for a workgroup tile
  * bm x bn x bk of (bm/wm) x (bn/wn) wavefronts, MFMA blocks mb x mb (32 or
- * 16) and global loads of `vec` floats (1 or 4).  Writes
- * {pad, swz_unit, swz_shift, swz_mask} of A to out[0..3] and of B to
- * out[4..7].  Returns GEMM_OK or GEMM_ERR_INVALID_DIM. */
+ * 16) and global loads of `vec` floats (1 or 4) through registers, or, with
+ * direct = 1 (vec must be 4), direct global->LDS copies: their LDS writes are
+ * contiguous and cannot be padded, so only the fragment reads are costed and
+ * only unpadded layouts are candidates.  Writes {pad, swz_unit, swz_shift,
+ * swz_mask} of A to out[0..3] and of B to out[4..7].  Returns GEMM_OK or
+ * GEMM_ERR_INVALID_DIM. */
 int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
-                                int32_t vec, int32_t *out);
+                                int32_t vec, int32_t direct, int32_t *out);
 
 /* The pages' padding rule for the A-tile column read ("My Triton From
  * Scratch, Part 18", section "Choosing padding instead of hard-coding it"):

@@ -75,6 +75,9 @@ def test_tile_config_is_consistent(variant, gemm_lib):
     assert (c["b_rows"], c["b_cols"]) == (c["bk"], c["bn"])
     assert c["vec_width"] in (1, 4)
     assert (c["a_row_stride"] % 4 == 0) and (c["b_row_stride"] % 4 == 0)
+    if c["direct_to_lds"]:  # 16-byte copies into unpadded rows, two stages, matrix cores
+        assert c["vec_width"] == 4 and c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2
+        assert c["mfma_block"] in (16, 32)
     for t in "ab":
         unit, mask = c[f"{t}_swz_unit"], c[f"{t}_swz_mask"]
         if unit:  # a swizzle permutes whole 16-byte groups inside aligned blocks of a row
@@ -96,7 +99,8 @@ LAYOUT_KEYS = ("a_pad", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_pad", "b_s
 
 def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
     base = dft.gemm_f32_tile_config(dft.VARIANT_MFMA)
-    assert dft.gemm_f32_tile_config(dft.VARIANT_AUTO) | {"variant": 1} == base
+    auto = dft.gemm_f32_tile_config(dft.VARIANT_AUTO)  # AUTO describes its large-problem choice
+    assert auto | {"variant": dft.VARIANT_MFMA_DIRECT} == dft.gemm_f32_tile_config(dft.VARIANT_MFMA_DIRECT)
     s1 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_STAGES1)
     assert s1["stages"] == 1 and s1["barriers_per_tile"] == 2
     assert s1 | {"variant": 1, "stages": 2, "barriers_per_tile": 1, "lds_bytes": base["lds_bytes"]} == base
@@ -108,17 +112,21 @@ def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
     assert sc | {"variant": 1, "vec_width": 4} | {k: base[k] for k in LAYOUT_KEYS} == base
     m16 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA16)
     assert m16["mfma_block"] == 16 and base["mfma_block"] == 32
+    direct = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_DIRECT)
+    assert direct["direct_to_lds"] == 1 and base["direct_to_lds"] == 0
+    assert direct | {"variant": 1, "direct_to_lds": 0} | {k: base[k] for k in LAYOUT_KEYS} == base
 
 
 def test_auto_variant_selection(gemm_lib):
     av = dft.gemm_f32_auto_variant
-    assert av(4096, 4096, 4096, 256) == dft.VARIANT_MFMA          # 512 tiles of 256x128
-    assert av(8192, 8192, 8192, 256) == dft.VARIANT_MFMA
-    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_128_BK32  # 16 tiles, deep K
-    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_128
-    assert av(128, 128, 128, 256) == dft.VARIANT_MFMA_128
-    assert av(4096, 4096, 2048, 1024) == dft.VARIANT_MFMA_128      # fewer tiles than CUs
-    assert av(4096, 4096, 4096, 1024) == dft.VARIANT_MFMA_128_BK32
+    assert av(4096, 4096, 4096, 256) == dft.VARIANT_MFMA_DIRECT          # 512 tiles of 256x128
+    assert av(8192, 8192, 8192, 256) == dft.VARIANT_MFMA_DIRECT
+    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 16 tiles, deep K
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT   # 64 tiles
+    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_128_DIRECT
+    assert av(128, 128, 128, 256) == dft.VARIANT_MFMA_128_DIRECT
+    assert av(4096, 4096, 2048, 1024) == dft.VARIANT_MFMA_128_DIRECT      # fewer tiles than CUs
+    assert av(4096, 4096, 4096, 1024) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
 
@@ -200,14 +208,19 @@ def test_splitk_argument_checks(gemm_lib):
     assert splitk(-1, 64, 64) == dft.GEMM_ERR_INVALID_DIM
     assert splitk(0, 64, 64, ws=0) == dft.GEMM_OK                       # nothing to do
     assert splitk(64, 0, 64, ws=0) == dft.GEMM_OK
+    for bad in (-1, dft.VARIANT_COUNT):  # an unknown slice kernel is refused before anything else
+        assert dft.gemm_f32_splitk_ex(64, 64, 64, FAKE_A, 64, FAKE_B, 64, FAKE_C, 64, 0, 0, 2, None,
+                                      bad) == dft.GEMM_ERR_UNSUPPORTED
 
 
 def test_splitk_queries(gemm_lib):
-    # 2048 x 256 x 16384: 32 tiles of 128 x 128 -> 1024/32 = 32 slices (<= 1024 K tiles / 8)
-    assert dft.gemm_f32_splitk_auto_splits(2048, 256, 16384, 256) == 32
-    assert dft.gemm_f32_splitk_workspace_bytes(2048, 256, 16384, 0, 256) == 32 * 2048 * 256 * 4
+    assert dft.gemm_f32_splitk_auto_variant() == dft.VARIANT_MFMA_DIRECT
+    # 2048 x 256 x 16384: 16 tiles of 256 x 128 -> 256/16 = 16 slices (<= 1024 K tiles / 8)
+    assert dft.gemm_f32_splitk_auto_splits(2048, 256, 16384, 256) == 16
+    assert dft.gemm_f32_splitk_workspace_bytes(2048, 256, 16384, 0, 256) == 16 * 2048 * 256 * 4
     assert dft.gemm_f32_splitk_workspace_bytes(2048, 256, 16384, 5, 256) == 5 * 2048 * 256 * 4
-    assert dft.gemm_f32_splitk_auto_splits(4096, 4096, 4096, 256) == 1    # 1024 tiles: no split
+    assert dft.gemm_f32_splitk_auto_splits(512, 4096, 4096, 256) == 4      # 64 tiles
+    assert dft.gemm_f32_splitk_auto_splits(4096, 4096, 4096, 256) == 1    # 512 tiles: no split
     assert dft.gemm_f32_splitk_workspace_bytes(4096, 4096, 4096, 0, 256) == 0
     assert dft.gemm_f32_splitk_auto_splits(64, 64, 100, 256) == 1         # too few K tiles
     assert dft.gemm_f32_splitk_auto_splits(128, 128, 1 << 20, 256) == 64  # capped at 64

@@ -25,7 +25,8 @@ SENTINEL = SENTINEL_BITS.view(np.float32)
 
 ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1,
                 dft.VARIANT_MFMA_NOPAD, dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
-                dft.VARIANT_MFMA_128_BK32]
+                dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
+                dft.VARIANT_MFMA_128_BK32_DIRECT]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -106,7 +107,7 @@ def compare(cfg, c: np.ndarray, ref, exact: bool) -> float:
     return max(oracle.normalised_error(got, want, den) for got, want, den in pairs)
 
 
-CONFIG_ORDER = ["small128", "ragged", "deepk", "square4096", "square8192"]
+CONFIG_ORDER = ["small128", "ragged", "deepk", "shard8_4096", "square4096", "square8192"]
 
 
 @pytest.mark.parametrize("cfg_name", CONFIG_ORDER)
@@ -137,10 +138,13 @@ EDGE_SHAPES = [
 ]
 
 
+EDGE_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA16,
+                 dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT,
+                 dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT]
+
+
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1,
-                                     dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32],
-                         ids=["mfma", "valu", "mfma_stages1", "mfma16", "mfma_128", "mfma_128_bk32"])
+@pytest.mark.parametrize("variant", EDGE_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in EDGE_VARIANTS])
 def test_edge_shapes(shape, variant, torch_gpu):
     M, N, K = shape
     a, b = workloads.make_operands(M, N, K, "uniform", M * 7 + N * 13 + K)
@@ -154,8 +158,9 @@ def test_edge_shapes(shape, variant, torch_gpu):
     assert np.array_equal(ci.astype(np.float64), oracle.reference(ai, bi)[0])
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128],
-                         ids=["mfma", "valu", "mfma16", "mfma_128"])
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
+                                     dft.VARIANT_MFMA_DIRECT],
+                         ids=["mfma", "valu", "mfma16", "mfma_128", "mfma_direct"])
 @pytest.mark.parametrize("pitch", [(3, 5, 2), (2, 4, 4), (1, 0, 9), (0, 8, 0)], ids=str)
 def test_pitched_operands(pitch, variant, torch_gpu):
     """Leading dimensions beyond the width: NaN in every gap must never be
@@ -167,6 +172,32 @@ def test_pitched_operands(pitch, variant, torch_gpu):
     c, full = run_gemm(torch_gpu, a, b, variant, lda=K + pa, ldb=N + pb, ldc=N + pc, c_rows_extra=3)
     check_sentinels(full, M, N)
     assert np.array_equal(c.astype(np.float64), cref)
+
+
+DIRECT_VARIANTS = [dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT]
+
+
+@pytest.mark.parametrize("variant", DIRECT_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in DIRECT_VARIANTS])
+@pytest.mark.parametrize("K", [1, 15, 16, 17, 31, 32, 33, 100, 256])
+def test_direct_copy_paths(K, variant, torch_gpu):
+    """Direct-copy variants on a grid with interior and edge tiles (600 x 300
+    is 3 x 3 tiles of 256 x 128, 5 x 3 of 128 x 128): interior workgroups copy
+    whole K tiles global->LDS directly and load a ragged last K tile through
+    registers with zero fill; edge workgroups load every tile through
+    registers.  Leading dimensions are
+    multiples of 4 with NaN in every gap, so a copy that strays past column K
+    or into a gap shows up, as does any write outside C."""
+    M, N = 600, 300
+    lda, ldb, ldc = K + (4 - K % 4) % 4 + 4, N + 8, N + 1
+    a, b = workloads.make_operands(M, N, K, "integer", 300 + K)
+    cref, _ = oracle.reference(a, b)
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=ldc, c_rows_extra=2)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref)
+    au, bu = workloads.make_operands(M, N, K, "uniform", 400 + K)
+    cu, _ = run_gemm(torch_gpu, au, bu, variant, lda=lda, ldb=ldb)
+    cref_u, den_u = oracle.reference(au, bu)
+    assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
 @pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
@@ -234,7 +265,7 @@ def test_rejects_overlap_on_device(torch_gpu):
 
 
 # ---- split-K ----
-def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None):
+def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None, variant=dft.VARIANT_AUTO):
     M, K = a.shape
     N = b.shape[1]
     ldc = ldc or max(N, 1)
@@ -243,8 +274,9 @@ def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     need = dft.gemm_f32_splitk_workspace_bytes(M, N, K, splits, cus)
     ws = torch.full((max(need // 4, 1) if ws_elems is None else ws_elems,), float("nan"), device="cuda")
-    st = dft.gemm_f32_splitk(M, N, K, da.data_ptr(), max(K, 1), db.data_ptr(), max(N, 1), dc.data_ptr(), ldc,
-                             ws.data_ptr(), ws.numel() * 4, splits, torch.cuda.current_stream().cuda_stream)
+    st = dft.gemm_f32_splitk_ex(M, N, K, da.data_ptr(), max(K, 1), db.data_ptr(), max(N, 1), dc.data_ptr(), ldc,
+                                ws.data_ptr(), ws.numel() * 4, splits, torch.cuda.current_stream().cuda_stream,
+                                variant)
     torch.cuda.synchronize()
     if st != dft.GEMM_OK:
         return st, None, None
@@ -252,30 +284,36 @@ def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None):
     return st, full[:M, :N].copy(), full
 
 
+SPLITK_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_DIRECT,
+                   dft.VARIANT_VALU]
+
+
+@pytest.mark.parametrize("variant", SPLITK_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in SPLITK_VARIANTS])
 @pytest.mark.parametrize("splits", [0, 2, 7, 32, 64])
-def test_splitk_deepk_parity(splits, torch_gpu):
+def test_splitk_deepk_parity(splits, variant, torch_gpu):
     cfg = workloads.CONFIG_BY_NAME["deepk"]
     a, b, ref = reference_for(cfg, integer=False)
-    st, c, full = run_splitk(torch_gpu, a, b, splits)
+    st, c, full = run_splitk(torch_gpu, a, b, splits, variant=variant)
     assert st == dft.GEMM_OK
     check_sentinels(full, cfg.M, cfg.N)
     err = compare(cfg, c, ref, exact=False)
-    print(f"deepk split-K {splits}: normalised error {err:.3e}")
+    print(f"deepk split-K {splits} {dft.VARIANT_NAMES[variant]}: normalised error {err:.3e}")
     assert err <= TOL
     ai, bi, refi = reference_for(cfg, integer=True)
-    st, ci, _ = run_splitk(torch_gpu, ai, bi, splits)
+    st, ci, _ = run_splitk(torch_gpu, ai, bi, splits, variant=variant)
     compare(cfg, ci, refi, exact=True)
 
 
-@pytest.mark.parametrize("shape", [(1000, 999, 513), (129, 127, 17), (300, 200, 48), (64, 64, 1), (5, 7, 4097)],
-                         ids=str)
+@pytest.mark.parametrize("variant", SPLITK_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in SPLITK_VARIANTS])
+@pytest.mark.parametrize("shape", [(1000, 999, 513), (129, 127, 17), (300, 200, 48), (64, 64, 1), (5, 7, 4097),
+                                   (520, 260, 1000)], ids=str)
 @pytest.mark.parametrize("splits", [1, 3, 8, 64])
-def test_splitk_ragged_and_empty_slices(shape, splits, torch_gpu):
+def test_splitk_ragged_and_empty_slices(shape, splits, variant, torch_gpu):
     """Slices past the end of K (e.g. K = 17 in 8 slices of 16) add zero."""
     M, N, K = shape
     a, b = workloads.make_operands(M, N, K, "uniform", M + 3 * N + K)
     cref, den = oracle.reference(a, b)
-    st, c, full = run_splitk(torch_gpu, a, b, splits, ldc=N + 3)
+    st, c, full = run_splitk(torch_gpu, a, b, splits, ldc=N + 3, variant=variant)
     assert st == dft.GEMM_OK
     check_sentinels(full, M, N)
     assert oracle.normalised_error(c, cref, den) <= TOL

@@ -109,6 +109,8 @@ def mfma_accesses(c):
                         for l in range(64)]
                 out.append((-2, pair))
         for tile, rows, cols in (("a", c["bm"], c["bk"]), ("b", c["bk"], c["bn"])):
+            if c["direct_to_lds"]:  # direct copies write 1 KiB of consecutive words: no LDS store instruction
+                continue
             vcols = cols // vec
             for i in range(rows * vcols // c["threads"]):
                 idx = [w * 64 + l + i * c["threads"] for l in range(64)]
@@ -124,8 +126,11 @@ def degree(c, width, words):
     return dft.gemm_lds_conflict_degree(words, width, banks, lanes)
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
-                                     dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_SCALAR])
+MFMA_LAYOUT_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32,
+                        dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA_DIRECT]
+
+
+@pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
 def test_mfma_layouts_are_conflict_free(variant, gemm_lib):
     """Under the measured geometry, every fragment read and cooperative store
     of the chosen layouts is conflict-free, while the plain layout is not."""
@@ -136,17 +141,29 @@ def test_mfma_layouts_are_conflict_free(variant, gemm_lib):
     assert max(degree(plain, w, words) for w, words in mfma_accesses(plain)) > 1
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
-                                     dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_SCALAR])
+@pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
 def test_built_layouts_match_the_search(variant, gemm_lib):
     """The layouts compiled into the kernels (generated at build time) are the
     ones the exported search returns for the same shape."""
     c = dft.gemm_f32_tile_config(variant)
     st, la, lb = dft.gemm_lds_choose_mfma_layout(c["bm"], c["bn"], c["bk"], c["tm"], c["tn"], c["mfma_block"],
-                                                 c["vec_width"])
+                                                 c["vec_width"], c["direct_to_lds"])
     assert st == 0
     assert la == (c["a_pad"], c["a_swz_unit"], c["a_swz_shift"], c["a_swz_mask"])
     assert lb == (c["b_pad"], c["b_swz_unit"], c["b_swz_shift"], c["b_swz_mask"])
+
+
+def test_direct_copy_layouts_are_unpadded(gemm_lib):
+    """With direct copies the search may only swizzle: a copy instruction
+    fills consecutive LDS words, which leaves no room for row padding."""
+    for shape in ((256, 128, 16, 64, 64, 32), (128, 128, 16, 64, 64, 32), (256, 128, 16, 64, 64, 16),
+                  (128, 128, 32, 64, 64, 32)):
+        st, la, lb = dft.gemm_lds_choose_mfma_layout(*shape, 4, 1)
+        assert st == 0 and la[0] == 0 and lb[0] == 0
+    # 16x16x4 blocks: the search through registers pads B, the direct one cannot
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 16, 4, 0)[2][0] == 4
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 32, 1, 1)[0] == dft.GEMM_ERR_INVALID_DIM
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 32, 4, 2)[0] == dft.GEMM_ERR_INVALID_DIM
 
 
 def test_layout_search_rejects_bad_shapes(gemm_lib):

@@ -15,6 +15,9 @@ A is M x K, B is K x N, both row-major, C = A @ B).  Five shapes are used:
   deepk       2048   256    16384  uniform[-1, 1)      long K loop
   square8192  8192   8192   8192   standard normal     large square
 
+plus one extra shape, shard8_4096 (512 x 4096 x 4096, standard normal): the
+rows of square4096 that one of eight GPUs would own.
+
 Generator: NumPy PCG64 (``numpy.random.default_rng(seed)``); A is drawn before
 B from one generator.  Uniform entries are ``uniform(-1, 1)`` cast to float32;
 normal entries are ``standard_normal(dtype=float32)``.  "Integer" operands
@@ -56,7 +59,14 @@ CONFIGS: tuple[GemmConfig, ...] = (
     GemmConfig("square8192", 8192, 8192, 8192, "normal", 5, True),
 )
 
-CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+# One GPU's share of square4096 when its rows are split over eight GPUs (the
+# row-block sharding of C = A @ B): too few 256 x 128 output tiles to fill
+# the chip, so it exercises the smaller-tile kernels.
+EXTRA_CONFIGS: tuple[GemmConfig, ...] = (
+    GemmConfig("shard8_4096", 512, 4096, 4096, "normal", 6, False),
+)
+
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS + EXTRA_CONFIGS}
 
 # Seed offsets: sampled rows/columns use seed + 100, integer operands seed + 200.
 SAMPLE_SEED_OFFSET = 100
