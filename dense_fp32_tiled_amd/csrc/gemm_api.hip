@@ -49,13 +49,16 @@ using Mfma128Bk32Direct = std::conditional_t<
     VEC == 4,
     MfmaCfg<128, 128, 32, 64, 64, 2, 32, layouts::m32_128x128x32_direct::A, layouts::m32_128x128x32_direct::B, 4,
             kXcdGroupedOrder, kLoadDirect>,
-    MfmaAt<layouts::m32_128x128x32_v1, 2, 1, 128, 128, 32, 32>>;
+    MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
+// BK = 32 with 4-byte loads needs 32 staged values and their addresses per
+// thread, more registers than two waves per SIMD leave (it spilled); the
+// 4-byte fallback of the BK = 32 variants therefore runs BK = 16.
 template <int VEC>
-using Mfma128Bk32 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x32_v4, layouts::m32_128x128x32_v1>,
-                           2, VEC, 128, 128, 32, 32>;
+using Mfma128Bk32 = std::conditional_t<VEC == 4, MfmaAt<layouts::m32_128x128x32_v4, 2, 4, 128, 128, 32, 32>,
+                                       MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
 
 constexpr ValuShape kValuShape{128, 128, 16, 16, 256, 4};
 constexpr int kValuPadA = valu_pad_a(kValuShape, kGfx950Lds);

@@ -65,7 +65,7 @@ typedef enum {
     GEMM_VARIANT_MFMA_SCALAR = 5,   /* ablation of MFMA: 4-byte global loads even when 16-byte loads are legal */
     GEMM_VARIANT_MFMA16 = 6,        /* as MFMA with v_mfma_f32_16x16x4_f32 */
     GEMM_VARIANT_MFMA_128 = 7,      /* as MFMA with a 128x128x16 workgroup tile (4 waves) */
-    GEMM_VARIANT_MFMA_128_BK32 = 8, /* as MFMA_128 with BK = 32 */
+    GEMM_VARIANT_MFMA_128_BK32 = 8, /* as MFMA_128 with BK = 32 (its 4-byte-load fallback uses BK = 16) */
     GEMM_VARIANT_MFMA_DIRECT = 9,   /* as MFMA with in-range tiles copied global->LDS directly (no registers) */
     GEMM_VARIANT_MFMA_128_DIRECT = 10,      /* as MFMA_128 with direct global->LDS copies */
     GEMM_VARIANT_MFMA_128_BK32_DIRECT = 11, /* as MFMA_128_BK32 with direct global->LDS copies */
