@@ -72,6 +72,11 @@ def parse_args(argv=None):
     ap.add_argument("--splits", type=int, default=-1,
                     help="run gemm_f32_splitk with this many K slices (0 = the library's choice) "
                          "instead of gemm_f32_ex; the workspace is allocated before timing")
+    ap.add_argument("--cold-cache-mib", type=int, default=0,
+                    help="after the timed region, time --steps more launches each preceded by a write of this "
+                         "many MiB to a scratch buffer, which evicts A and B from L2 and the 256 MB MALL "
+                         "(reported as cold_cache; 0 = skip, the default, so that a kernel trace of the default "
+                         "command holds only the warm launches the roofline figure averages)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB (a "
                          "reference kernel of known traffic for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -145,6 +150,27 @@ def main(argv=None) -> int:
         return wall_s, sum(durs) / len(durs), durs[len(durs) // 2], durs[0]
 
     wall_s, kern_avg_s, kern_med_s, kern_min_s = time_variant(variant, args.steps, args.warmup)
+
+    # Cold caches: the timed region above re-reads A and B from L2 / MALL on
+    # every launch after the first; here each launch follows a write of a
+    # scratch buffer larger than the MALL (not timed; events bracket the GEMM).
+    cold = None
+    if args.cold_cache_mib > 0:
+        scratch = torch.empty(args.cold_cache_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        durs = []
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(variant)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            durs.append(e0.elapsed_time(e1) / 1e3)
+        del scratch
+        durs.sort()
+        cold = {"flush_mib": args.cold_cache_mib, "kernel_ms_avg": sum(durs) / len(durs) * 1e3,
+                "kernel_ms_median": durs[len(durs) // 2] * 1e3,
+                "tflops_kernel_avg": cfg.flops / (sum(durs) / len(durs)) / 1e12}
     tflops = cfg.flops / wall_s / 1e12
     achieved = cfg.flops / kern_avg_s / 1e12
     if args.splits >= 0:
@@ -175,7 +201,8 @@ def main(argv=None) -> int:
             "cores": threads,
             "kind": "oracle",
             "sample": f"{len(rows)} of {cfg.M} rows of C (all {cfg.N} columns, K={cfg.K}), seeded sample; "
-                      f"{cpu_s:.2f} s wall on {threads} threads",
+                      f"{cpu_s:.2f} s wall on {threads} threads; the whole product would take about "
+                      f"{cpu_s * cfg.M / len(rows):.1f} s at this rate (projection)",
         }
         c_rows = c[torch.from_numpy(rows).to(dev)].cpu().numpy()
         parity = {"rows_checked": int(len(rows)), "max_normalised_error": oracle.normalised_error(c_rows, cref, den)}
@@ -215,6 +242,7 @@ def main(argv=None) -> int:
             "flops_per_launch": cfg.flops,
         },
         "cpu_baseline": cpu_baseline,
+        "cold_cache": cold,
         "parity_sample": parity,
     }
 

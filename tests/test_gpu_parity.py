@@ -122,6 +122,25 @@ def test_config_parity(cfg_name, variant, torch_gpu):
     assert err <= TOL
 
 
+FULL_CHECK_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU]
+
+
+@pytest.mark.parametrize("variant", FULL_CHECK_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in FULL_CHECK_VARIANTS])
+def test_square4096_every_element(variant, torch_gpu):
+    """The headline shape checked on all 16.8 M outputs, not a sample (the
+    oracle's 6.9e10 multiply-adds take a few seconds on the host's cores)."""
+    cfg = workloads.CONFIG_BY_NAME["square4096"]
+    key = ("square4096", "full")
+    if key not in _oracle_cache:
+        a, b = workloads.config_operands(cfg, integer=False)
+        _oracle_cache[key] = (a, b, oracle.reference(a, b))
+    a, b, (cref, den) = _oracle_cache[key]
+    c, _ = run_gemm(torch_gpu, a, b, variant)
+    err = oracle.normalised_error(c, cref, den)
+    print(f"square4096 {dft.VARIANT_NAMES[variant]} all elements: normalised error {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("cfg_name", CONFIG_ORDER)
 @pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
 def test_config_integer_exact(cfg_name, variant, torch_gpu):
