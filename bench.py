@@ -25,9 +25,11 @@ if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 
 PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and packed vector): 256 CUs x 256 flop/clk x 2.4 GHz
+PEAK_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak (no sparsity)
 METRIC = "fp32 GEMM TFLOP/s at 4096³ on 1 MI355X; % of fp32 peak"
+METRIC_16BIT = "{t}-input GEMM (fp32 accumulate) TFLOP/s on 1 MI355X; % of dense {t} peak"
 KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "lds_layout.hpp", "pad_choice.hpp", "layout_gen.cpp",
-                  "mfma_shapes.def"]
+                  "mfma_shapes.def", "mixed_kernels.hpp", "mixed_shapes.def"]
 
 
 def kernel_source_digest() -> str:
@@ -65,6 +67,9 @@ def parse_args(argv=None):
                     help="kernel variant by name (auto, mfma, mfma_direct, valu, ...; see VARIANT_NAMES); with "
                          "--splits, the kernel that computes the slices")
     ap.add_argument("--workload", default="square4096")
+    ap.add_argument("--input", default="f32", choices=["f32", "bf16", "f16"],
+                    help="element type of A and B: f32 (gemm_f32_ex) or 16-bit with fp32 accumulation "
+                         "(gemm_mixed_f32; --variant then names a mixed variant: auto, 256x128, 256x256, ...)")
     ap.add_argument("--cpu-sample-rows", type=int, default=512,
                     help="rows of C the CPU oracle computes for its baseline (0 = skip)")
     ap.add_argument("--ablations", default="",
@@ -99,15 +104,25 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    names = {v: k for k, v in dft.VARIANT_NAMES.items()}
+    mixed = args.input != "f32"
+    names = {v: k for k, v in (dft.MIXED_NAMES if mixed else dft.VARIANT_NAMES).items()}
     variant = names[args.variant]
+    if mixed and args.splits >= 0:
+        print("--splits applies to fp32 inputs only", file=sys.stderr)
+        return 2
     cfg = workloads.CONFIG_BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     a_np, b_np = workloads.config_operands(cfg)
-    a = torch.from_numpy(a_np).to(dev)
-    b = torch.from_numpy(b_np).to(dev)
+    if mixed:
+        # the inputs are the 16-bit values; the oracle multiplies their exact widenings
+        (a_bits, a_np), (b_bits, b_np) = workloads.to_16bit(a_np, args.input), workloads.to_16bit(b_np, args.input)
+        a = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+        b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    else:
+        a = torch.from_numpy(a_np).to(dev)
+        b = torch.from_numpy(b_np).to(dev)
     c = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
@@ -121,8 +136,12 @@ def main(argv=None) -> int:
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
         splits_used = args.splits or dft.gemm_f32_splitk_auto_splits(M, N, K, cus)
 
+    input_type = {"bf16": dft.INPUT_BF16, "f16": dft.INPUT_F16}.get(args.input)
+
     def step(v=variant):
-        if args.splits >= 0 and v == variant:
+        if mixed:
+            st = dft.gemm_mixed_f32(input_type, M, N, K, pa, K, pb, N, pc, N, handle, v)
+        elif args.splits >= 0 and v == variant:
             st = dft.gemm_f32_splitk_ex(M, N, K, pa, K, pb, N, pc, N, ws.data_ptr(), ws_bytes, args.splits, handle,
                                         variant)
         else:
@@ -173,14 +192,21 @@ def main(argv=None) -> int:
                 "tflops_kernel_avg": cfg.flops / (sum(durs) / len(durs)) / 1e12}
     tflops = cfg.flops / wall_s / 1e12
     achieved = cfg.flops / kern_avg_s / 1e12
-    if args.splits >= 0:
-        resolved = dft.gemm_f32_splitk_auto_variant() if variant == dft.VARIANT_AUTO else variant
-    elif variant == dft.VARIANT_AUTO:
-        resolved = dft.gemm_f32_auto_variant(M, N, K, torch.cuda.get_device_properties(dev).multi_processor_count)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if mixed:
+        resolved = dft.gemm_mixed_auto_variant(M, N, K, cus) if variant == dft.MIXED_AUTO else variant
+        tile = dft.gemm_mixed_tile_config(resolved)
+        run_name = f"mixed_{args.input}_{dft.MIXED_NAMES[resolved]}"
     else:
-        resolved = variant
-    tile = dft.gemm_f32_tile_config(resolved)
-    run_name = dft.VARIANT_NAMES[resolved] + (f"+splitk{splits_used}" if args.splits >= 0 else "")
+        if args.splits >= 0:
+            resolved = dft.gemm_f32_splitk_auto_variant() if variant == dft.VARIANT_AUTO else variant
+        elif variant == dft.VARIANT_AUTO:
+            resolved = dft.gemm_f32_auto_variant(M, N, K, cus)
+        else:
+            resolved = variant
+        tile = dft.gemm_f32_tile_config(resolved)
+        run_name = dft.VARIANT_NAMES[resolved] + (f"+splitk{splits_used}" if args.splits >= 0 else "")
+    peak = PEAK_16BIT_TFLOPS if mixed else PEAK_FP32_TFLOPS
 
     # correctness spot check and CPU baseline: the oracle on a bounded row sample
     cpu_baseline = None
@@ -208,7 +234,7 @@ def main(argv=None) -> int:
         parity = {"rows_checked": int(len(rows)), "max_normalised_error": oracle.normalised_error(c_rows, cref, den)}
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_16BIT.format(t=args.input) if mixed else METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -218,25 +244,27 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": args.input,
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: C[{M},{N}] = A[{M},{K}] @ B[{K},{N}], row-major fp32, "
-                        f"entries {'normal(0,1)' if cfg.dist == 'normal' else 'uniform[-1,1)'}, seed {cfg.seed}",
+            "workload": f"{cfg.name}: C[{M},{N}] = A[{M},{K}] @ B[{K},{N}], row-major "
+                        + (f"{args.input} A and B (fp32 draws rounded to nearest even), fp32 accumulation and C, "
+                           if mixed else "fp32, ")
+                        + f"entries {'normal(0,1)' if cfg.dist == 'normal' else 'uniform[-1,1)'}, seed {cfg.seed}",
             "M": M, "N": N, "K": K,
             "variant": run_name,
             "tile": f"{tile['bm']}x{tile['bn']}x{tile['bk']}, {tile['threads']} threads, MFMA block "
                     f"{tile['mfma_block']}, {tile['stages']} LDS stages, LDS layout A pad {tile['a_pad']} "
                     f"swizzle {tile['a_swz_unit']}/{tile['a_swz_shift']}/{tile['a_swz_mask']}, B pad "
                     f"{tile['b_pad']} swizzle {tile['b_swz_unit']}/{tile['b_swz_shift']}/{tile['b_swz_mask']}",
-            "fraction_of_fp32_peak": tflops / PEAK_FP32_TFLOPS,
+            "fraction_of_peak": tflops / peak,
         },
         "roofline": {
             "bound": "mfma" if tile["mfma_block"] else "alu",
             "achieved": achieved,
-            "peak": PEAK_FP32_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_TFLOPS,
+            "frac": achieved / peak,
             "traffic": measured_traffic(run_name, cfg.name),
             "kernel_ms": {"avg": kern_avg_s * 1e3, "median": kern_med_s * 1e3, "min": kern_min_s * 1e3},
             "flops_per_launch": cfg.flops,
@@ -248,9 +276,10 @@ def main(argv=None) -> int:
 
     if args.ablations:
         with open(args.ablations, "w") as f:
-            for v in range(1, dft.VARIANT_COUNT):
+            for v in range(1, dft.MIXED_COUNT if mixed else dft.VARIANT_COUNT):
                 w, kavg, kmed, kmin = time_variant(v, args.steps, args.warmup)
-                f.write(json.dumps({"variant": dft.VARIANT_NAMES[v], "workload": cfg.name,
+                vname = f"mixed_{args.input}_{dft.MIXED_NAMES[v]}" if mixed else dft.VARIANT_NAMES[v]
+                f.write(json.dumps({"variant": vname, "workload": cfg.name,
                                     "tflops_wall": cfg.flops / w / 1e12, "tflops_kernel_avg": cfg.flops / kavg / 1e12,
                                     "kernel_ms_avg": kavg * 1e3, "kernel_ms_median": kmed * 1e3,
                                     "kernel_ms_min": kmin * 1e3}) + "\n")

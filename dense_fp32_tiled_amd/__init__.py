@@ -40,6 +40,18 @@ VARIANT_MFMA_DIRECT = 9
 VARIANT_MFMA_128_DIRECT = 10
 VARIANT_MFMA_128_BK32_DIRECT = 11
 VARIANT_COUNT = 12
+# 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
+INPUT_BF16 = 0
+INPUT_F16 = 1
+INPUT_NAMES = {INPUT_BF16: "bf16", INPUT_F16: "f16"}
+MIXED_AUTO = 0
+MIXED_256x128 = 1
+MIXED_256x256 = 2
+MIXED_256x128_BK64 = 3
+MIXED_128x128_BK64 = 4
+MIXED_COUNT = 5
+MIXED_NAMES = {MIXED_AUTO: "auto", MIXED_256x128: "256x128", MIXED_256x256: "256x256",
+               MIXED_256x128_BK64: "256x128_bk64", MIXED_128x128_BK64: "128x128_bk64"}
 VARIANT_NAMES = {
     VARIANT_AUTO: "auto",
     VARIANT_MFMA: "mfma",
@@ -67,6 +79,9 @@ EXPORTS = (
     "gemm_f32_splitk_workspace_bytes",
     "gemm_f32_splitk_auto_splits",
     "gemm_f32_auto_variant",
+    "gemm_mixed_f32",
+    "gemm_mixed_tile_config",
+    "gemm_mixed_auto_variant",
     "gemm_lds_choose_mfma_layout",
     "gemm_lds_layout",
     "gemm_lds_offset",
@@ -90,7 +105,7 @@ class TileConfig(ctypes.Structure):
         "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
         "lds_bytes", "vec_width", "lds_banks_b32", "lds_lanes_b32", "lds_banks_b128", "lds_lanes_b128",
         "a_transposed", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_swz_unit", "b_swz_shift", "b_swz_mask",
-        "mfma_block", "xcd_tile_order", "direct_to_lds")]
+        "mfma_block", "xcd_tile_order", "direct_to_lds", "elem_bytes")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -144,6 +159,12 @@ def library(path: Path | None = None):
     lib.gemm_f32_splitk_auto_splits.restype = ctypes.c_int
     lib.gemm_f32_auto_variant.argtypes = [i64, i64, i64, i32]
     lib.gemm_f32_auto_variant.restype = ctypes.c_int
+    lib.gemm_mixed_f32.argtypes = [ctypes.c_int] + gemm_args[:9] + [vp, ctypes.c_int]
+    lib.gemm_mixed_f32.restype = ctypes.c_int
+    lib.gemm_mixed_tile_config.argtypes = [ctypes.c_int, ctypes.POINTER(TileConfig)]
+    lib.gemm_mixed_tile_config.restype = ctypes.c_int
+    lib.gemm_mixed_auto_variant.argtypes = [i64, i64, i64, i32]
+    lib.gemm_mixed_auto_variant.restype = ctypes.c_int
     lib.gemm_lds_choose_mfma_layout.argtypes = [i32] * 8 + [ctypes.POINTER(i32)]
     lib.gemm_lds_choose_mfma_layout.restype = ctypes.c_int
     p32 = ctypes.POINTER(i32)
@@ -209,6 +230,22 @@ def gemm_f32_auto_variant(M: int, N: int, K: int, num_cus: int) -> int:
     return library().gemm_f32_auto_variant(M, N, K, num_cus)
 
 
+def gemm_mixed_f32(input_type, M, N, K, A, lda, B, ldb, C, ldc, stream=None, variant=MIXED_AUTO) -> int:
+    return library().gemm_mixed_f32(input_type, M, N, K, A, lda, B, ldb, C, ldc, stream, variant)
+
+
+def gemm_mixed_tile_config(variant: int) -> dict:
+    cfg = TileConfig()
+    st = library().gemm_mixed_tile_config(variant, ctypes.byref(cfg))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_mixed_tile_config")
+    return cfg.as_dict()
+
+
+def gemm_mixed_auto_variant(M: int, N: int, K: int, num_cus: int) -> int:
+    return library().gemm_mixed_auto_variant(M, N, K, num_cus)
+
+
 def gemm_lds_choose_mfma_layout(bm, bn, bk, wm, wn, mb, vec, direct=0):
     """(status, (pad, unit, shift, mask) of A, (pad, unit, shift, mask) of B)."""
     out = (ctypes.c_int32 * 8)()
@@ -241,13 +278,14 @@ def gemm_lds_page_pad(columns: int, simultaneous_rows: int, banks: int = 32) -> 
 
 
 # ---- torch convenience -------------------------------------------------------------
-def _operand(t, name):
+def _operand(t, name, dtype=None):
     import torch
 
+    dtype = dtype or torch.float32
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float32 or t.dim() != 2:
-        raise TypeError(f"{name} must be a 2-D float32 tensor")
+    if t.dtype != dtype or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D {dtype} tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device")
     rows, cols = t.shape
@@ -293,6 +331,31 @@ def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None, 
                                 _stream_handle(stream, a.device), variant)
     if st != GEMM_OK:
         raise GemmError(st, "gemm_f32_splitk_ex")
+    return out
+
+
+def matmul_mixed(a, b, out=None, variant: int = MIXED_AUTO, stream=None):
+    """C (float32) = a @ b for bfloat16 or float16 tensors a (M x K) and b
+    (K x N) of the same dtype, accumulated in fp32 by gemm_mixed_f32."""
+    import torch
+
+    types = {torch.bfloat16: INPUT_BF16, torch.float16: INPUT_F16}
+    if a.dtype not in types or b.dtype != a.dtype:
+        raise TypeError("a and b must both be bfloat16 or both float16")
+    pa, lda = _operand(a, "a", a.dtype)
+    pb, ldb = _operand(b, "b", a.dtype)
+    M, K = a.shape
+    if b.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    pc, ldc = _operand(out, "out")
+    with torch.cuda.device(a.device):
+        st = gemm_mixed_f32(types[a.dtype], M, N, K, pa, lda, pb, ldb, pc, ldc, _stream_handle(stream, a.device),
+                            variant)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_mixed_f32")
     return out
 
 

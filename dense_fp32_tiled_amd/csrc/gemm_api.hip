@@ -8,6 +8,7 @@
 
 #include "dense_fp32_tiled.h"
 #include "gemm_kernels.hpp"
+#include "mixed_kernels.hpp"
 #include "generated/mfma_layouts.hpp"
 #include "pad_choice.hpp"
 #include <type_traits>
@@ -136,6 +137,7 @@ void describe_common(gemm_tile_config& c, int variant, int vec) {
     c.lds_banks_b128 = kGfx950Lds.banks_b128; c.lds_lanes_b128 = kGfx950Lds.lanes_b128;
     c.xcd_tile_order = Cfg::ORDER == kXcdGroupedOrder ? 1 : 0;
     c.direct_to_lds = Cfg::LOAD == kLoadDirect ? 1 : 0;
+    c.elem_bytes = 4;
 }
 
 template <class Cfg>
@@ -232,12 +234,12 @@ bool overlaps(const void* p, int64_t p_bytes, const void* q, int64_t q_bytes) {
 }
 
 // Bytes spanned by a rows x cols row-major matrix with leading dimension ld.
-int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld) {
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t elem_bytes = 4) {
     if (rows == 0 || cols == 0) return 0;
-    return ((rows - 1) * ld + cols) * 4;
+    return ((rows - 1) * ld + cols) * elem_bytes;
 }
 
-int validate(const Args& a) {
+int validate(const Args& a, int64_t ab_elem_bytes = 4) {
     if (a.M < 0 || a.N < 0 || a.K < 0) return GEMM_ERR_INVALID_DIM;
     const int64_t k1 = a.K > 1 ? a.K : 1, n1 = a.N > 1 ? a.N : 1;
     if (a.lda < k1 || a.ldb < n1 || a.ldc < n1) return GEMM_ERR_INVALID_LD;
@@ -250,8 +252,8 @@ int validate(const Args& a) {
     if (ab_used && (a.A == nullptr || a.B == nullptr)) return GEMM_ERR_NULL;
     if (ab_used) {
         const int64_t c_bytes = span_bytes(a.M, a.N, a.ldc);
-        if (overlaps(a.C, c_bytes, a.A, span_bytes(a.M, a.K, a.lda)) ||
-            overlaps(a.C, c_bytes, a.B, span_bytes(a.K, a.N, a.ldb)))
+        if (overlaps(a.C, c_bytes, a.A, span_bytes(a.M, a.K, a.lda, ab_elem_bytes)) ||
+            overlaps(a.C, c_bytes, a.B, span_bytes(a.K, a.N, a.ldb, ab_elem_bytes)))
             return GEMM_ERR_ALIAS;
     }
     return GEMM_OK;
@@ -271,10 +273,11 @@ int launch_zero_fill(const Args& a, hipStream_t stream) {
 }
 
 // Checks shared by every entry point; on GEMM_OK with *done set, nothing is
-// left to do (empty M or N, or K == 0 handled by a zero fill).
-int prologue(const Args& a, hipStream_t stream, int* max_lds, int* num_cus, bool* done) {
+// left to do (empty M or N, or K == 0 handled by a zero fill).  A and B hold
+// ab_elem_bytes-byte elements (4, or 2 for 16-bit inputs).
+int prologue(const Args& a, hipStream_t stream, int* max_lds, int* num_cus, bool* done, int64_t ab_elem_bytes = 4) {
     *done = false;
-    int st = validate(a);
+    int st = validate(a, ab_elem_bytes);
     if (st != GEMM_OK) return st;
     if (a.M == 0 || a.N == 0) {
         *done = true;
@@ -392,6 +395,103 @@ int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int spli
                : GEMM_ERR_HIP;
 }
 
+// ---- 16-bit inputs, fp32 accumulation -----------------------------------------------
+// Tile shapes of the mixed-precision kernels (layouts from the host search,
+// mixed_shapes.def).  VEC 8: 16-byte loads and direct copies; VEC 1: 2-byte
+// loads through registers, for unaligned operands.
+template <int TYPE, int VEC>
+using Mixed256x128 = MixedCfg<TYPE, 256, 128, 32, 64, 64, 32, layouts::x32_256x128x32::A, layouts::x32_256x128x32::B,
+                              VEC, 4>;
+template <int TYPE, int VEC>
+using Mixed256x256 = MixedCfg<TYPE, 256, 256, 32, 128, 64, 32, layouts::x32_256x256x32::A, layouts::x32_256x256x32::B,
+                              VEC, 2>;
+template <int TYPE, int VEC>
+using Mixed256x128Bk64 = MixedCfg<TYPE, 256, 128, 64, 64, 64, 32, layouts::x32_256x128x64::A,
+                                  layouts::x32_256x128x64::B, VEC, 2>;
+template <int TYPE, int VEC>
+using Mixed128x128Bk64 = MixedCfg<TYPE, 128, 128, 64, 64, 64, 32, layouts::x32_128x128x64::A,
+                                  layouts::x32_128x128x64::B, VEC, 4>;
+
+template <class Cfg>
+hipError_t launch_mixed(const Args& a, hipStream_t stream) {
+    int64_t M = a.M, N = a.N, K = a.K, lda = a.lda, ldb = a.ldb, ldc = a.ldc;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A);
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B);
+    float* C = a.C;
+    int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+    int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+    void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_m, &tiles_n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(gemm_mixed_kernel<Cfg>), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(Cfg::THREADS), args, 0, stream);
+}
+
+template <class Cfg>
+gemm_tile_config mixed_config(int variant, int vec) {
+    gemm_tile_config c{};
+    describe_common<Cfg>(c, variant, vec);
+    c.tm = Cfg::WM; c.tn = Cfg::WN;
+    c.a_transposed = 0;
+    c.mfma_block = Cfg::Op::MB;
+    c.elem_bytes = 2;
+    return c;
+}
+
+using MixedLaunchFn = hipError_t (*)(const Args&, hipStream_t);
+struct MixedVariant {
+    MixedLaunchFn vec8[2], scalar[2];  // by input type
+    gemm_tile_config (*config)(int variant, int vec);
+    int lds_bytes;
+};
+
+// Unaligned operands of every variant run the 256x128x32 kernel with 2-byte
+// loads: it is the only shape whose register-path kernel fits its registers
+// without spilling (one staged element per register).
+template <template <int, int> class Shape>
+MixedVariant mixed_variant() {
+    return MixedVariant{{launch_mixed<Shape<kInputBf16, 8>>, launch_mixed<Shape<kInputF16, 8>>},
+                        {launch_mixed<Mixed256x128<kInputBf16, 1>>, launch_mixed<Mixed256x128<kInputF16, 1>>},
+                        mixed_config<Shape<kInputBf16, 8>>,
+                        Shape<kInputBf16, 8>::LDS_BYTES > Mixed256x128<kInputBf16, 1>::LDS_BYTES
+                            ? Shape<kInputBf16, 8>::LDS_BYTES
+                            : Mixed256x128<kInputBf16, 1>::LDS_BYTES};
+}
+
+// Index = gemm_mixed_variant; AUTO's entry describes the large-problem choice.
+const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
+    /* AUTO           */ mixed_variant<Mixed256x256>(),
+    /* 256x128        */ mixed_variant<Mixed256x128>(),
+    /* 256x256        */ mixed_variant<Mixed256x256>(),
+    /* 256x128_BK64   */ mixed_variant<Mixed256x128Bk64>(),
+    /* 128x128_BK64   */ mixed_variant<Mixed128x128Bk64>(),
+};
+
+int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
+    (void)K;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles >= num_cus) return GEMM_MIXED_256x256;
+    const int64_t tiles128 = ((M + 255) / 256) * ((N + 127) / 128);
+    return tiles128 >= num_cus ? GEMM_MIXED_256x128 : GEMM_MIXED_128x128_BK64;
+}
+
+int run_mixed(int input_type, const Args& a, hipStream_t stream, int variant) {
+    if (input_type != GEMM_INPUT_BF16 && input_type != GEMM_INPUT_F16) return GEMM_ERR_UNSUPPORTED;
+    if (variant < 0 || variant >= GEMM_MIXED_COUNT) return GEMM_ERR_UNSUPPORTED;
+    int max_lds = 0, num_cus = 0;
+    bool done = false;
+    const int st = prologue(a, stream, &max_lds, &num_cus, &done, 2);
+    if (st != GEMM_OK || done) return st;
+    if (variant == GEMM_MIXED_AUTO) variant = mixed_auto_variant(a.M, a.N, a.K, num_cus);
+    const MixedVariant& v = kMixedVariants[variant];
+    if (v.lds_bytes > max_lds) return GEMM_ERR_CONFIG;
+    const gemm_tile_config cfg = v.config(variant, 8);
+    const int64_t tiles = ((a.M + cfg.bm - 1) / cfg.bm) * ((a.N + cfg.bn - 1) / cfg.bn);
+    if (tiles > (int64_t)0x7fffffff / cfg.threads) return GEMM_ERR_TOO_LARGE;
+    const bool aligned = (a.lda % 8 == 0) && (a.ldb % 8 == 0) && (((uintptr_t)a.A & 15) == 0) &&
+                         (((uintptr_t)a.B & 15) == 0);
+    const MixedLaunchFn fn = aligned ? v.vec8[input_type] : v.scalar[input_type];
+    return fn(a, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 }  // namespace
 
 // ---- exported C ABI ---------------------------------------------------------------
@@ -452,6 +552,27 @@ int gemm_f32_splitk_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
 }
 
 int gemm_f32_splitk_auto_variant(void) { return kSplitKVariant; }
+
+int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                   int64_t ldb, float* C, int64_t ldc, void* stream, int variant) {
+    // A and B travel in the fp32 argument block as untyped pointers; only
+    // the mixed kernels read them, as 16-bit elements.
+    return run_mixed(input_type,
+                     Args{M, N, K, static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, C, ldc},
+                     (hipStream_t)stream, variant);
+}
+
+int gemm_mixed_tile_config(int variant, gemm_tile_config* out) {
+    if (out == nullptr) return GEMM_ERR_NULL;
+    if (variant < 0 || variant >= GEMM_MIXED_COUNT) return GEMM_ERR_UNSUPPORTED;
+    *out = kMixedVariants[variant].config(variant, 8);
+    return GEMM_OK;
+}
+
+int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
+    if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+    return mixed_auto_variant(M, N, K, num_cus);
+}
 
 int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits, int32_t num_cus) {
     if (M < 0 || N < 0 || K < 0 || splits < 0 || splits > kMaxSplits || num_cus < 1) return GEMM_ERR_INVALID_DIM;

@@ -231,7 +231,7 @@ struct MfmaCfg {
 // is waited for explicitly (wait_vector_memory) before the barrier that
 // publishes the stage.  The "memory" clobber keeps LDS accesses from being
 // moved across it.
-__device__ inline void copy16_to_lds(const float* src, uint32_t lds_base) {
+__device__ inline void copy16_to_lds(const void* src, uint32_t lds_base) {
     uint32_t saved_m0;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -248,11 +248,15 @@ __device__ inline void copy16_to_lds(const float* src, uint32_t lds_base) {
 // Direct global->LDS copy of one operand tile.  A stage of an unpadded tile
 // is cut into 1 KiB pieces (64 lanes x 16 bytes), piece i * WAVES + w being
 // written by wavefront w's i-th copy instruction, and the lane that writes
-// LDS word p fetches the element the tile layout keeps there: row p / cols,
-// column swizzle(row, p % cols) (the XOR swizzle is its own inverse).  The
-// fetch offsets do not depend on the K tile, so they are computed once.
-template <class Tile, int THREADS>
+// LDS word p fetches the elements the tile layout keeps there: row p / cols,
+// word column swizzle(row, p % cols) (the XOR swizzle is its own inverse).
+// The tile is laid out in 4-byte words; an element of type T is
+// 4 / sizeof(T) per word (1 for fp32, 2 for 16-bit inputs).  The fetch
+// offsets do not depend on the K tile, so they are computed once.
+template <class Tile, int THREADS, class T = float>
 struct DirectCopy {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 2, "4- or 2-byte elements");
+    static constexpr int PER_WORD = 4 / (int)sizeof(T);
     static_assert(Tile::pad == 0, "direct copies write whole rows contiguously");
     static constexpr int WAVES = THREADS / kWave;
     static constexpr int PIECE = kWave * 4;  // fp32 words per instruction per wavefront
@@ -285,15 +289,17 @@ struct DirectCopy {
         for (int i = 0; i < PER_WAVE; ++i) {
             int row = 0, col = 0;
             source((i * WAVES + wave_uniform) * PIECE + 4 * lane, row, col);
-            off[i] = (int64_t)row * ld + col;
+            off[i] = (int64_t)row * ld + (int64_t)col * PER_WORD;
         }
     }
 
     // Issue the copies of the tile at `origin` into `stage` of the LDS tile
     // at `lds`; they complete asynchronously (vector memory counter).
-    __device__ void issue(const float* origin, float* lds, int stage) const {
-        typedef __attribute__((address_space(3))) float lds_float;
-        const uint32_t base = (uint32_t)(uintptr_t)(lds_float*)lds + lds_piece + stage * (Tile::stage_elems * 4);
+    template <class W>
+    __device__ void issue(const T* origin, W* lds, int stage) const {
+        static_assert(sizeof(W) == 4, "LDS tiles are addressed in 4-byte words");
+        typedef __attribute__((address_space(3))) W lds_word;
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_word*)lds + lds_piece + stage * (Tile::stage_elems * 4);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) copy16_to_lds(origin + off[i], base + i * (WAVES * PIECE * 4));
     }
@@ -303,6 +309,31 @@ struct DirectCopy {
 // LDS copies included, have completed (s_waitcnt vmcnt(0); the expcnt and
 // lgkmcnt fields of the immediate are left at their no-wait maxima).
 __device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Store of a wavefront's MFMA accumulators: unmasked when the whole BM x BN
+// workgroup tile is in range (a uniform branch), else under the mask
+// rows < M and columns < N.  For a fixed result register, the MB lanes of a
+// k-group write consecutive floats of one row.
+template <class Op, int BM, int BN, int MI, int NI>
+__device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m0,
+                                          int64_t n0, int wm0, int wn0, int lane,
+                                          const typename Op::acc_t (&acc)[MI][NI]) {
+    const int r = lane % Op::MB;
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            const int64_t gn = n0 + wn0 + n * Op::NB + r;
+            const int64_t gm0 = m0 + wm0 + i * Op::MB;
+            float* cp = C + gm0 * ldc + gn;
+#pragma unroll
+            for (int v = 0; v < Op::ACC; ++v) {
+                const int dr = Op::out_row(lane, v);
+                if (full || (gm0 + dr < M && gn < N)) cp[dr * ldc] = acc[i][n][v];
+            }
+        }
+}
 
 template <class Cfg>
 __device__ inline TileCoord tile_of_block(int64_t tiles_m, int64_t tiles_n) {
@@ -477,24 +508,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         }
     }
 
-    // Store: unmasked when the whole BM x BN tile is in range (a uniform
-    // branch), else under the mask rows < M and columns < N.  For a fixed
-    // result register, the MB lanes of a k-group write consecutive floats of
-    // one row.
-    const bool full = m0 + BM <= M && n0 + BN <= N;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int n = 0; n < NI; ++n) {
-            const int64_t gn = n0 + wn0 + n * Op::NB + r;
-            const int64_t gm0 = m0 + wm0 + i * Op::MB;
-            float* cp = C + gm0 * ldc + gn;
-#pragma unroll
-            for (int v = 0; v < Op::ACC; ++v) {
-                const int dr = Op::out_row(lane, v);
-                if (full || (gm0 + dr < M && gn < N)) cp[dr * ldc] = acc[i][n][v];
-            }
-        }
+    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, wm0, wn0, lane, acc);
 }
 
 // --------------------------------------------------------------------------

@@ -1,0 +1,301 @@
+// mixed_kernels.hpp -- gfx950 kernel for C[M,N] = A[M,K] @ B[K,N] with 16-bit
+// inputs (bf16 or fp16, row-major, given as bit patterns) and fp32
+// accumulation and output.
+//
+// This is the mixed-precision step that "My Triton From Scratch, Part 18:
+// Shared Memory Optimization" announces as the next part: the same masked,
+// zero-filled tiling and two-stage LDS pipeline as the fp32 kernels
+// (gemm_kernels.hpp), with 16-bit operand tiles and the 16-bit matrix-core
+// instructions.  Products of two bf16 (or fp16) values are exact in fp32, so
+// the result differs from the exact sum only by the fp32 accumulation.
+//
+// Per wavefront and MFMA step (KB elements of k):
+//   A fragment: lane l of k-group g = l / MB holds A[row l % MB][8g .. 8g+7],
+//               16 consecutive bytes of an LDS row (one 16-byte read);
+//   B fragment: lane l holds B[8g .. 8g+7][column l % MB], a column segment
+//               of the row-major B tile, delivered by two transposing reads
+//               (ds_read_b64_tr_b16): in each group of 16 lanes, lane j gives
+//               the address of 4 consecutive elements of row j / 4 of a 4 x 16
+//               block, and lane i receives element i of each of the 4 rows.
+// Both layouts were checked on the device against a host model of the
+// instruction.  Tiles are filled by direct global->LDS copies (DirectCopy)
+// when in range, else through registers with zero fill.
+#pragma once
+
+#include "gemm_kernels.hpp"
+
+namespace dft {
+
+enum InputType { kInputBf16 = 0, kInputF16 = 1 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int TYPE, int MB>
+struct Mfma16Op;
+
+template <int TYPE>
+struct Mfma16Op<TYPE, 32> {
+    static constexpr int MB = 32, NB = 32, KB = 16, ACC = 16;
+    using acc_t = floatx16;
+    __device__ static acc_t mma(u32x4 a, u32x4 b, acc_t c) {
+        if constexpr (TYPE == kInputBf16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                           c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                          0, 0, 0);
+    }
+    __device__ static int out_row(int lane, int v) { return MfmaOp<32, 2>::out_row(lane, v); }
+    // k-group of a lane and first column of its 16-lane group within the block
+    __device__ static int kgroup(int lane) { return lane / 32; }
+    __device__ static int col_base(int lane) { return 16 * ((lane / 16) % 2); }
+};
+
+template <int TYPE>
+struct Mfma16Op<TYPE, 16> {
+    static constexpr int MB = 16, NB = 16, KB = 32, ACC = 4;
+    using acc_t = floatx4;
+    __device__ static acc_t mma(u32x4 a, u32x4 b, acc_t c) {
+        if constexpr (TYPE == kInputBf16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                           c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                          0, 0, 0);
+    }
+    __device__ static int out_row(int lane, int v) { return MfmaOp<16, 4>::out_row(lane, v); }
+    __device__ static int kgroup(int lane) { return lane / 16; }
+    __device__ static int col_base(int) { return 0; }
+};
+
+// A tile of a row-major 16-bit matrix, rows [row0, row0 + ROWS) and columns
+// [col0, col0 + COLS), read under the mask (row < row_bound) & (col <
+// col_bound) with zero fill, through registers; VEC = 8 (16-byte loads, when
+// aligned) or 1.  Threads map to VEC-wide column groups in row-major order.
+// Used for tiles the direct copy cannot take (edges) and for unaligned
+// operands.
+template <int ROWS, int COLS, int THREADS, int VEC>
+struct TileLoader16 {
+    static_assert(VEC == 1 || VEC == 8, "VEC must be 1 or 8");
+    static_assert(COLS % 8 == 0, "tile width must be a multiple of 8 elements");
+    static constexpr int VCOLS = COLS / VEC;
+    static constexpr int SLOTS = ROWS * VCOLS;
+    static_assert(SLOTS % THREADS == 0, "tile must split evenly over the threads");
+    static constexpr int PER_THREAD = SLOTS / THREADS;
+
+    uint16_t v[PER_THREAD][VEC];
+
+    __device__ static int slot_row(int tid, int i) { return (tid + i * THREADS) / VCOLS; }
+    __device__ static int slot_col(int tid, int i) { return ((tid + i * THREADS) % VCOLS) * VEC; }
+
+    __device__ void load(const uint16_t* __restrict__ tile, int64_t ld, int64_t rows_left, int64_t cols_left,
+                         int tid) {
+        if (rows_left >= ROWS && cols_left >= COLS) {
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                const uint16_t* p = tile + (int64_t)slot_row(tid, i) * ld + slot_col(tid, i);
+                if constexpr (VEC == 8) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[i][2 * e] = (uint16_t)(x[e] & 0xffffu);
+                        v[i][2 * e + 1] = (uint16_t)(x[e] >> 16);
+                    }
+                } else {
+                    v[i][0] = *p;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                const int r = slot_row(tid, i);
+                const int c = slot_col(tid, i);
+                const uint16_t* p = tile + (int64_t)r * ld + c;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[i][e] = (r < rows_left && c + e < cols_left) ? p[e] : (uint16_t)0;
+            }
+        }
+    }
+
+    // Element (r, c) -> 16-bit half (c % 2) of word Tile::offset(stage, r, c / 2).
+    template <class Tile>
+    __device__ void store(uint32_t* lds, int stage, int tid) const {
+        static_assert(Tile::rows == ROWS && 2 * Tile::cols == COLS, "LDS tile shape mismatch");
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int r = slot_row(tid, i), c = slot_col(tid, i);
+            if constexpr (VEC == 8) {
+                u32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (uint32_t)v[i][2 * e] | ((uint32_t)v[i][2 * e + 1] << 16);
+                *reinterpret_cast<u32x4*>(lds + Tile::offset(stage, r, c / 2)) = x;
+            } else {
+                reinterpret_cast<uint16_t*>(lds + Tile::offset(stage, r, c / 2))[c % 2] = v[i][0];
+            }
+        }
+    }
+};
+
+template <int TYPE_, int BM_, int BN_, int BK_, int WM_, int WN_, int MB_, class LayA, class LayB, int VEC_,
+          int MIN_WAVES_>
+struct MixedCfg {
+    using Op = Mfma16Op<TYPE_, MB_>;
+    static constexpr int TYPE = TYPE_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int VEC = VEC_;
+    static constexpr int MIN_WAVES = VEC == 1 && MIN_WAVES_ > 2 ? 2 : MIN_WAVES_;
+    static constexpr int ORDER = kXcdGroupedOrder;
+    static constexpr int LOAD = VEC == 8 ? kLoadDirect : kLoadRegisters;
+    static constexpr int STAGES = 2;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
+    static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
+    static constexpr int STEPS = BK / Op::KB;
+    using TileA = LdsTile<BM, BK / 2, LayA::pad, 2, LayA::unit, LayA::shift, LayA::mask>;  // 4-byte words
+    using TileB = LdsTile<BK, BN / 2, LayB::pad, 2, LayB::unit, LayB::shift, LayB::mask>;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
+    static_assert(BK % Op::KB == 0, "whole MFMA steps per K tile");
+    static_assert(LayA::pad == 0 && LayB::pad == 0, "direct copies need unpadded rows");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n) {
+    using Op = typename Cfg::Op;
+    using TileA = typename Cfg::TileA;
+    using TileB = typename Cfg::TileB;
+    using acc_t = typename Op::acc_t;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr int MI = Cfg::MI, NI = Cfg::NI, THREADS = Cfg::THREADS;
+
+    __shared__ __attribute__((aligned(16))) uint32_t lds_a[TileA::total_elems];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_b[TileB::total_elems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int g = lane / Op::MB, r = lane % Op::MB;
+    // transposing B reads: this lane's address within its 16-lane group
+    const int tr_row = 8 * Op::kgroup(lane) + (lane % 16) / 4;
+    const int tr_col = Op::col_base(lane) + 4 * (lane % 4);  // elements
+
+    const TileCoord tc = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const int64_t m0 = tc.m0, n0 = tc.n0;
+
+    acc_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
+
+    TileLoader16<BM, BK, THREADS, Cfg::VEC> ldr_a;
+    TileLoader16<BK, BN, THREADS, Cfg::VEC> ldr_b;
+    const uint16_t* a_tile = A + m0 * lda;
+    const uint16_t* b_tile = B + n0;
+    const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
+
+    auto load_tile = [&](int64_t t) {
+        const int64_t k0 = t * BK;
+        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, tid);
+        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, tid);
+    };
+    auto store_tile = [&](int stage) {
+        ldr_a.template store<TileA>(lds_a, stage, tid);
+        ldr_b.template store<TileB>(lds_b, stage, tid);
+    };
+    typedef __attribute__((address_space(3))) uint32_t lds_word;
+    typedef __attribute__((address_space(3))) shortx4 lds_short4;
+    auto multiply = [&](int stage) {
+#pragma unroll
+        for (int st = 0; st < Cfg::STEPS; ++st) {
+            u32x4 af[MI], bf[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                af[i] = *reinterpret_cast<const u32x4*>(
+                    lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, st * (Op::KB / 2) + 4 * g));
+#pragma unroll
+            for (int n = 0; n < NI; ++n) {
+                shortx4 half[2];
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int word = TileB::offset(stage, st * Op::KB + tr_row + 4 * rr, (wn0 + n * Op::NB + tr_col) / 2);
+                    half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_word*)lds_b + word));
+                }
+                const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
+                bf[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i], bf[n], acc[i][n]);
+        }
+    };
+
+    if constexpr (Cfg::LOAD == kLoadDirect) {
+        // As the fp32 direct kernel: the copies of tile t+1 are in flight
+        // during the multiply of tile t; tiles not wholly in range are loaded
+        // through registers with zero fill after the multiply.
+        const DirectCopy<TileA, THREADS, uint16_t> dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
+        const DirectCopy<TileB, THREADS, uint16_t> dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
+        const bool interior = M - m0 >= BM && N - n0 >= BN;
+        if (T > 0) {
+            if (interior && K >= BK) {
+                dma_a.issue(a_tile, lds_a, 0);
+                dma_b.issue(b_tile, lds_b, 0);
+            } else {
+                load_tile(0);
+                store_tile(0);
+            }
+        }
+        wait_vector_memory();
+        __syncthreads();
+        for (int64_t t = 0; t < T; ++t) {
+            const int s = (int)(t & 1);
+            const bool more = t + 1 < T;
+            const bool direct = more && interior && K - (t + 1) * BK >= BK;
+            if (direct) {
+                dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
+                dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+            }
+            multiply(s);
+            if (more && !direct) {
+                load_tile(t + 1);
+                store_tile(s ^ 1);
+            }
+            wait_vector_memory();
+            __syncthreads();
+        }
+    } else {
+        // Unaligned operands: 2-byte loads through registers, issued after
+        // the multiply so that the staged elements (one register each) are
+        // not live across it; the other workgroups on the CU hide the latency.
+        if (T > 0) {
+            load_tile(0);
+            store_tile(0);
+        }
+        __syncthreads();
+        for (int64_t t = 0; t < T; ++t) {
+            const int s = (int)(t & 1);
+            multiply(s);
+            if (t + 1 < T) {
+                load_tile(t + 1);
+                store_tile(s ^ 1);
+            }
+            __syncthreads();
+        }
+    }
+
+    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, wm0, wn0, lane, acc);
+}
+
+}  // namespace dft

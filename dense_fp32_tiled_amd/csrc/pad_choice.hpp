@@ -157,6 +157,68 @@ constexpr LayoutChoice mfma_layout_b(MfmaShape s, LdsGeometry g) {
     return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn, !s.direct);
 }
 
+// ---- matrix-core kernel with 16-bit inputs (bf16 / fp16) ------------------------
+// Tiles hold two elements per 4-byte word: A [BM][BK/2 words], B [BK][BN/2
+// words], both filled by direct copies (no LDS store instructions, no pad).
+// One MFMA step consumes KB elements of k: lane l of k-group g = l / MB reads
+// 8 consecutive k of A row l % MB (one 16-byte read at word column
+// step * KB/2 + 4g) and receives 8 consecutive k of B column l % MB through
+// two transposing 8-byte reads (ds_read_b64_tr_b16).  Measured lane mapping
+// of that read: in each group of 16 lanes, lane j supplies the address of
+// row (j / 4), columns 4 (j % 4) .. 4 (j % 4) + 3 of a 4 x 16 block, and lane
+// i receives column i of the block's four rows.  So for B, lane j of group
+// G = l / 16 addresses row step*KB + 8 kg + 4 rr + j / 4 (read rr = 0, 1) and
+// element column n_base(G) + 4 (j % 4), with kg = l / 32, n_base = 16 (G % 2)
+// for 32 x 32 blocks, and kg = G, n_base = 0 for 16 x 16 blocks.
+struct Mixed16Shape {
+    int bm, bn, bk, wm, wn, threads, mb;
+    constexpr int kb() const { return mb == 32 ? 16 : 32; }
+    constexpr int steps() const { return bk / kb(); }
+    constexpr int waves() const { return threads / kWaveLanes; }
+    constexpr int waves_n() const { return bn / wn; }
+};
+
+constexpr int mixed_a_cost(Mixed16Shape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    const int cols = s.bk / 2;
+    for (int w = 0; w < s.waves(); ++w) {
+        const int wm0 = (w / s.waves_n()) * s.wm;
+        for (int st = 0; st < s.steps(); ++st)
+            for (int mi = 0; mi < s.wm / s.mb; ++mi)
+                total += pattern_cost(c, cols, 4, g, [=](int l, int& row, int& col) {
+                    row = wm0 + mi * s.mb + l % s.mb;
+                    col = st * (s.kb() / 2) + 4 * (l / s.mb);
+                });
+    }
+    return total;
+}
+
+constexpr int mixed_b_cost(Mixed16Shape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    const int cols = s.bn / 2;
+    for (int w = 0; w < s.waves(); ++w) {
+        const int wn0 = (w % s.waves_n()) * s.wn;
+        for (int st = 0; st < s.steps(); ++st)
+            for (int ni = 0; ni < s.wn / s.mb; ++ni)
+                for (int rr = 0; rr < 2; ++rr)
+                    total += pattern_cost(c, cols, 2, g, [=](int l, int& row, int& col) {
+                        const int grp = l / 16, j = l % 16;
+                        const int kg = s.mb == 32 ? l / 32 : grp;
+                        const int nb = s.mb == 32 ? 16 * (grp % 2) : 0;
+                        row = st * s.kb() + 8 * kg + 4 * rr + j / 4;
+                        col = (wn0 + ni * s.mb + nb + 4 * (j % 4)) / 2;
+                    });
+    }
+    return total;
+}
+
+constexpr LayoutChoice mixed_layout_a(Mixed16Shape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return mixed_a_cost(s, c, g); }, s.bk / 2, false);
+}
+constexpr LayoutChoice mixed_layout_b(Mixed16Shape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return mixed_b_cost(s, c, g); }, s.bn / 2, false);
+}
+
 // ---- vector-ALU kernel: A k-major [BK][BM+pad], B row-major [BK][BN+pad] ----
 struct ValuShape {
     int bm, bn, bk, threads_n, threads, vec;

@@ -99,6 +99,9 @@ typedef struct {
     int32_t xcd_tile_order;      /* 1 if workgroups are mapped to tiles in the XCD-grouped order */
     int32_t direct_to_lds;       /* 1 if in-range tiles are copied global->LDS without registers (16 bytes
                                     per lane, LDS rows unpadded); edge tiles still go through registers */
+    int32_t elem_bytes;          /* bytes per A / B element: 4 (fp32), 2 (bf16 / fp16, gemm_mixed_f32);
+                                    LDS tile fields count 4-byte words, so a row of a 16-bit tile holds
+                                    2 * cols elements */
 } gemm_tile_config;
 
 /* C = A @ B with the default variant.  M, N, K >= 0; lda >= max(1,K),
@@ -227,6 +230,49 @@ int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, 
  * distinct = banks / gcd(columns, banks); pad = simultaneous_rows > distinct.
  * Returns -1 on bad arguments. */
 int32_t gemm_lds_page_pad(int32_t columns, int32_t simultaneous_rows, int32_t banks);
+
+/* ---- 16-bit inputs, fp32 accumulation ---------------------------------------
+ * The mixed-precision step that "My Triton From Scratch, Part 18: Shared
+ * Memory Optimization" announces as its next part: C (fp32) = A @ B with A
+ * and B in bf16 or fp16, products accumulated in fp32 on the matrix cores
+ * (v_mfma_f32_32x32x16_bf16 / _f16).  A product of two 16-bit values is
+ * exact in fp32, so C differs from the exact sum of products only by the fp32
+ * accumulation.  Same tiling, masking and zero fill as the fp32 kernels. */
+typedef enum {
+    GEMM_INPUT_BF16 = 0,  /* bfloat16 bit patterns (8-bit exponent, 7-bit fraction) */
+    GEMM_INPUT_F16 = 1    /* IEEE binary16 bit patterns */
+} gemm_input_type;
+
+typedef enum {
+    GEMM_MIXED_AUTO = 0,          /* picks one of the below from M, N (gemm_mixed_auto_variant) */
+    GEMM_MIXED_256x128 = 1,       /* 256x128x32 tile, 8 waves of 64x64, 4 waves per SIMD */
+    GEMM_MIXED_256x256 = 2,       /* 256x256x32 tile, 8 waves of 128x64, 2 waves per SIMD */
+    GEMM_MIXED_256x128_BK64 = 3,  /* 256x128x64 tile, 8 waves of 64x64 */
+    GEMM_MIXED_128x128_BK64 = 4,  /* 128x128x64 tile, 4 waves of 64x64 */
+    GEMM_MIXED_COUNT = 5
+} gemm_mixed_variant;
+
+/* C = A @ B, A and B of `input_type` (gemm_input_type), C fp32.  A, B, C are
+ * DEVICE pointers owned by the caller; M, N, K >= 0; lda >= max(1,K),
+ * ldb >= max(1,N), ldc >= max(1,N), in elements.  16-byte loads and direct
+ * copies need lda and ldb multiples of 8 and A, B 16-byte aligned; otherwise
+ * the 256x128x32 kernel runs with 2-byte loads (the same result up to the
+ * order of the fp32 additions).  Validation and
+ * asynchrony as gemm_f32.  Returns a gemm_status; GEMM_ERR_UNSUPPORTED for an
+ * unknown input type or variant. */
+int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda,
+                   const void *B, int64_t ldb,
+                   float *C, int64_t ldc,
+                   void *stream, int variant);
+
+/* Tile geometry of a gemm_mixed_variant (elem_bytes = 2).  Pure host call. */
+int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
+
+/* The variant GEMM_MIXED_AUTO runs: 256x256 when those tiles give at least
+ * one workgroup per CU, else 256x128 when those do, else 128x128_BK64.  Pure
+ * host call; GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
+int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
 #ifdef __cplusplus
 }

@@ -246,3 +246,47 @@ def test_every_binding_declares_its_full_signature(gemm_lib):
             for d, t in zip(decl, fn.argtypes):
                 if "*" in d:
                     assert t is ctypes.c_void_p or t is ctypes.c_char_p or hasattr(t, "contents"), (name, d, t)
+
+
+# ---- 16-bit inputs (gemm_mixed_f32) ----
+@pytest.mark.parametrize("variant", range(dft.MIXED_COUNT))
+def test_mixed_tile_config_is_consistent(variant, gemm_lib):
+    c = dft.gemm_mixed_tile_config(variant)
+    assert c["variant"] == variant and c["elem_bytes"] == 2 and c["direct_to_lds"] == 1
+    assert c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2
+    # LDS tiles in 4-byte words: a row of a 16-bit tile holds two elements per word
+    assert (c["a_rows"], 2 * c["a_cols"]) == (c["bm"], c["bk"])
+    assert (c["b_rows"], 2 * c["b_cols"]) == (c["bk"], c["bn"])
+    assert c["lds_bytes"] == 2 * (c["a_stage_elems"] + c["b_stage_elems"]) * 4 <= 160 * 1024
+    assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64
+    assert c["mfma_block"] == 32
+
+
+def test_mixed_argument_checks(gemm_lib):
+    def mixed(M, N, K, input_type=dft.INPUT_BF16, variant=0, A=FAKE_A, B=FAKE_B, C=FAKE_C, lda=None):
+        return dft.gemm_mixed_f32(input_type, M, N, K, A, lda or max(K, 1), B, max(N, 1), C, max(N, 1), None, variant)
+
+    assert mixed(4, 4, 4, input_type=2) == dft.GEMM_ERR_UNSUPPORTED
+    assert mixed(4, 4, 4, input_type=-1) == dft.GEMM_ERR_UNSUPPORTED
+    assert mixed(4, 4, 4, variant=dft.MIXED_COUNT) == dft.GEMM_ERR_UNSUPPORTED
+    assert mixed(-1, 4, 4) == dft.GEMM_ERR_INVALID_DIM
+    assert mixed(4, 4, 8, lda=7) == dft.GEMM_ERR_INVALID_LD
+    assert mixed(4, 4, 4, A=0) == dft.GEMM_ERR_NULL
+    assert mixed(0, 4, 4, A=0, B=0, C=0) == dft.GEMM_OK
+    # A spans (M - 1) * lda + K two-byte elements: C just past its end is legal, one element earlier aliases
+    M, K = 64, 64
+    end_a = FAKE_A + ((M - 1) * K + K) * 2
+    assert mixed(M, 8, K, C=end_a) != dft.GEMM_ERR_ALIAS
+    assert mixed(M, 8, K, C=end_a - 2) == dft.GEMM_ERR_ALIAS
+    with pytest.raises(dft.GemmError):
+        dft.gemm_mixed_tile_config(dft.MIXED_COUNT)
+    assert gemm_lib.gemm_mixed_tile_config(0, None) == dft.GEMM_ERR_NULL
+
+
+def test_mixed_auto_variant(gemm_lib):
+    av = dft.gemm_mixed_auto_variant
+    assert av(8192, 8192, 8192, 256) == dft.MIXED_256x256  # 1024 tiles of 256x256
+    assert av(4096, 4096, 4096, 256) == dft.MIXED_256x256  # 256 tiles
+    assert av(2048, 4096, 4096, 256) == dft.MIXED_256x128  # 128 tiles of 256x256, 256 of 256x128
+    assert av(2048, 256, 16384, 256) == dft.MIXED_128x128_BK64
+    assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM

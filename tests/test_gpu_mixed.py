@@ -1,0 +1,159 @@
+"""GPU parity of the 16-bit-input kernels (gemm_mixed_f32: bf16 or fp16 A and
+B, fp32 accumulation and C) against the fp64 oracle.
+
+The oracle multiplies the exact float32 widenings of the 16-bit inputs, so
+the GPU result differs from it only by fp32 accumulation: the fp32 bar
+applies (normalised error <= 1e-5), and integer-valued inputs must match bit
+for bit.  Buffers carry NaN in every ld gap and around C."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_fp32_tiled_amd as dft
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+SENTINEL_BITS = np.uint32(0x7FC0DEAD)
+NAN16 = {"bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00)}
+TYPES = {"bf16": dft.INPUT_BF16, "f16": dft.INPUT_F16}
+VARIANTS = list(range(dft.MIXED_COUNT))
+VARIANT_IDS = [dft.MIXED_NAMES[v] for v in VARIANTS]
+
+
+@pytest.fixture(scope="module")
+def torch_gpu(gemm_lib):
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+    return torch
+
+
+def embed16(bits: np.ndarray, ld: int, fill: np.uint16) -> np.ndarray:
+    rows, cols = bits.shape
+    out = np.full((max(rows, 1), ld), fill, dtype=np.uint16)
+    out[:rows, :cols] = bits
+    return out.reshape(-1)
+
+
+def run_mixed(torch, kind, a_bits, b_bits, variant, lda=None, ldb=None, ldc=None, offset=0):
+    M, K = a_bits.shape
+    N = b_bits.shape[1]
+    lda, ldb, ldc = lda or max(K, 1), ldb or max(N, 1), ldc or max(N, 1)
+    pad = np.full(offset, NAN16[kind], np.uint16)
+    abuf = np.concatenate([pad, embed16(a_bits, lda, NAN16[kind])]).view(np.int16)
+    bbuf = np.concatenate([pad, embed16(b_bits, ldb, NAN16[kind])]).view(np.int16)
+    cbuf = np.full((M + 1) * ldc, SENTINEL_BITS, np.uint32).view(np.float32)
+    da, db, dc = (torch.from_numpy(x).cuda() for x in (abuf, bbuf, cbuf))
+    st = dft.gemm_mixed_f32(TYPES[kind], M, N, K, da.data_ptr() + 2 * offset, lda, db.data_ptr() + 2 * offset, ldb,
+                            dc.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream, variant)
+    assert st == dft.GEMM_OK, dft.gemm_f32_status_string(st)
+    torch.cuda.synchronize()
+    full = dc.cpu().numpy().reshape(M + 1, ldc)
+    outside = np.ones(full.shape, bool)
+    outside[:M, :N] = False
+    assert np.all(full.view(np.uint32)[outside] == SENTINEL_BITS), "a write landed outside the M x N region"
+    return full[:M, :N].copy()
+
+
+def operands(kind, M, N, K, dist, seed):
+    a, b = workloads.make_operands(M, N, K, dist, seed)
+    (ab, af), (bb, bf) = workloads.to_16bit(a, kind), workloads.to_16bit(b, kind)
+    return ab, bb, af, bf
+
+
+_cache: dict = {}
+
+
+def reference(kind, cfg, integer):
+    key = (kind, cfg.name, integer)
+    if key not in _cache:
+        seed = cfg.seed + (workloads.INTEGER_SEED_OFFSET if integer else 0)
+        ab, bb, af, bf = operands(kind, cfg.M, cfg.N, cfg.K, "integer" if integer else cfg.dist, seed)
+        if cfg.sampled:
+            rows, cols = workloads.sample_rows_cols(cfg)
+            ref = (oracle.reference(af, bf, rows=rows), oracle.reference(af, bf, cols=cols), rows, cols)
+        else:
+            ref = (oracle.reference(af, bf),)
+        _cache[key] = (ab, bb, ref)
+    return _cache[key]
+
+
+def compare(cfg, c, ref, exact):
+    if cfg.sampled:
+        (cr, dr), (cc, dcol), rows, cols = ref
+        pairs = [(c[rows, :], cr, dr), (c[:, cols], cc, dcol)]
+    else:
+        (cf, df), = ref
+        pairs = [(c, cf, df)]
+    if exact:
+        for got, want, _ in pairs:
+            assert np.array_equal(got.astype(np.float64), want), "integer-valued product differs"
+        return 0.0
+    return max(oracle.normalised_error(got, want, den) for got, want, den in pairs)
+
+
+CONFIGS = ["small128", "ragged", "deepk", "shard8_4096", "square4096"]
+
+
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("cfg_name", CONFIGS)
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+def test_mixed_config_parity(kind, cfg_name, variant, torch_gpu):
+    cfg = workloads.CONFIG_BY_NAME[cfg_name]
+    ab, bb, ref = reference(kind, cfg, integer=False)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant)
+    err = compare(cfg, c, ref, exact=False)
+    print(f"{kind} {cfg_name} {dft.MIXED_NAMES[variant]}: normalised error {err:.3e}")
+    assert err <= TOL
+    abi, bbi, refi = reference(kind, cfg, integer=True)
+    compare(cfg, run_mixed(torch_gpu, kind, abi, bbi, variant), refi, exact=True)
+
+
+EDGE_SHAPES = [(1, 1, 1), (2, 3, 5), (31, 33, 15), (127, 129, 17), (256, 256, 32), (257, 255, 33), (300, 520, 100),
+               (520, 16, 64), (16, 520, 64), (600, 300, 1000)]
+
+
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+def test_mixed_edge_shapes(kind, shape, variant, torch_gpu):
+    """Ragged shapes, aligned (direct copies for in-range tiles) and shifted
+    by one element (2-byte loads), with padded leading dimensions."""
+    M, N, K = shape
+    ab, bb, af, bf = operands(kind, M, N, K, "uniform", M * 7 + N * 13 + K)
+    cref, den = oracle.reference(af, bf)
+    pad_a, pad_b = (8 - K % 8) % 8 + 8, (8 - N % 8) % 8 + 8
+    for offset, lda, ldb in ((0, K + pad_a, N + pad_b), (1, None, None)):
+        c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=lda, ldb=ldb, ldc=N + 3, offset=offset)
+        assert oracle.normalised_error(c, cref, den) <= TOL, (shape, offset)
+    abi, bbi, afi, bfi = operands(kind, M, N, K, "integer", M + N + K)
+    ci = run_mixed(torch_gpu, kind, abi, bbi, variant)
+    assert np.array_equal(ci.astype(np.float64), oracle.reference(afi, bfi)[0])
+
+
+@pytest.mark.parametrize("kind", list(TYPES))
+def test_mixed_k_zero_and_empty(kind, torch_gpu):
+    torch = torch_gpu
+    c = torch.full((7, 9), float("nan"), device="cuda")
+    st = dft.gemm_mixed_f32(TYPES[kind], 7, 9, 0, 0, 1, 0, 9, c.data_ptr(), 9, None, 0)
+    torch.cuda.synchronize()
+    assert st == dft.GEMM_OK and torch.all(c == 0)
+    assert dft.gemm_mixed_f32(TYPES[kind], 0, 9, 5, 0, 5, 0, 9, 0, 9, None, 0) == dft.GEMM_OK
+
+
+def test_matmul_mixed_wrapper(torch_gpu):
+    torch = torch_gpu
+    for dtype, kind in ((torch.bfloat16, "bf16"), (torch.float16, "f16")):
+        ab, bb, af, bf = operands(kind, 300, 260, 200, "uniform", 11)
+        a = torch.from_numpy(ab.view(np.int16)).cuda().view(dtype)
+        b = torch.from_numpy(bb.view(np.int16)).cuda().view(dtype)
+        c = dft.matmul_mixed(a, b).cpu().numpy()
+        cref, den = oracle.reference(af, bf)
+        assert oracle.normalised_error(c, cref, den) <= TOL
+    with pytest.raises(TypeError):
+        dft.matmul_mixed(torch.zeros(4, 4, device="cuda"), torch.zeros(4, 4, device="cuda"))

@@ -98,6 +98,38 @@ def config_operands(cfg: GemmConfig, integer: bool = False) -> tuple[np.ndarray,
     return make_operands(cfg.M, cfg.N, cfg.K, cfg.dist, cfg.seed)
 
 
+# ---- 16-bit inputs (the mixed-precision kernels) ----------------------------
+# Operands are drawn as above in float32 and then stored in a 16-bit format:
+# the GEMM's inputs ARE the 16-bit values, and their exact float32 values (a
+# widening, which loses nothing) are what the oracle multiplies.
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of float32 values, rounded to nearest, ties to
+    even (the upper 16 bits of the float32 pattern after adding half a unit
+    of the dropped part, plus one more when the kept part is odd).  Inputs
+    here are finite."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = bits + 0x7FFF + ((bits >> 16) & 1)
+    return (rounded >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bfloat16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_16bit(x: np.ndarray, input_type: str) -> tuple[np.ndarray, np.ndarray]:
+    """(16-bit patterns, their exact float32 values) of float32 operands, for
+    input_type "bf16" or "f16" (IEEE binary16, round to nearest even)."""
+    if input_type == "bf16":
+        bits = to_bf16_bits(x)
+        return bits, bf16_bits_to_f32(bits)
+    if input_type == "f16":
+        h = np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
+        return h.view(np.uint16), h.astype(np.float32)
+    raise ValueError(f"unknown 16-bit input type {input_type!r}")
+
+
 def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
     """Sorted distinct indices in [0, n): always 0 and n-1, the rest drawn
     without replacement from a seeded generator."""
