@@ -401,13 +401,19 @@ int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int spli
 // loads through registers, for unaligned operands.
 template <int TYPE, int VEC>
 using Mixed256x128 = MixedCfg<TYPE, 256, 128, 32, 64, 64, 32, layouts::x32_256x128x32::A, layouts::x32_256x128x32::B,
-                              VEC, 4>;
+                              VEC, 4, 2, false>;
 template <int TYPE, int VEC>
 using Mixed256x256 = MixedCfg<TYPE, 256, 256, 32, 128, 64, 32, layouts::x32_256x256x32::A, layouts::x32_256x256x32::B,
                               VEC, 2>;
 template <int TYPE, int VEC>
 using Mixed256x128Bk64 = MixedCfg<TYPE, 256, 128, 64, 64, 64, 32, layouts::x32_256x128x64::A,
                                   layouts::x32_256x128x64::B, VEC, 2>;
+template <int TYPE, int VEC>
+using Mixed256x256S3 = MixedCfg<TYPE, 256, 256, 32, 128, 64, 32, layouts::x32_256x256x32::A,
+                                layouts::x32_256x256x32::B, VEC, 2, 3>;
+template <int TYPE, int VEC>
+using Mixed256x256Bk64 = MixedCfg<TYPE, 256, 256, 64, 128, 64, 32, layouts::x32_256x256x64::A,
+                                  layouts::x32_256x256x64::B, VEC, 2, 2>;
 template <int TYPE, int VEC>
 using Mixed128x128Bk64 = MixedCfg<TYPE, 128, 128, 64, 64, 64, 32, layouts::x32_128x128x64::A,
                                   layouts::x32_128x128x64::B, VEC, 4>;
@@ -458,17 +464,19 @@ MixedVariant mixed_variant() {
 
 // Index = gemm_mixed_variant; AUTO's entry describes the large-problem choice.
 const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
-    /* AUTO           */ mixed_variant<Mixed256x256>(),
+    /* AUTO           */ mixed_variant<Mixed256x256Bk64>(),
     /* 256x128        */ mixed_variant<Mixed256x128>(),
     /* 256x256        */ mixed_variant<Mixed256x256>(),
     /* 256x128_BK64   */ mixed_variant<Mixed256x128Bk64>(),
     /* 128x128_BK64   */ mixed_variant<Mixed128x128Bk64>(),
+    /* 256x256_S3     */ mixed_variant<Mixed256x256S3>(),
+    /* 256x256_BK64   */ mixed_variant<Mixed256x256Bk64>(),
 };
 
 int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     (void)K;
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles >= num_cus) return GEMM_MIXED_256x256;
+    if (tiles >= num_cus) return GEMM_MIXED_256x256_BK64;
     const int64_t tiles128 = ((M + 255) / 256) * ((N + 127) / 128);
     return tiles128 >= num_cus ? GEMM_MIXED_256x128 : GEMM_MIXED_128x128_BK64;
 }

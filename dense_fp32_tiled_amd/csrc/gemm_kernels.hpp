@@ -281,12 +281,38 @@ struct DirectCopy {
     }
     static_assert(matches_layout(), "direct copies must fill the LDS tile in its own layout");
 
-    int64_t off[PER_WAVE];  // element offset of this lane's 16 bytes from the tile origin
-    uint32_t lds_piece;     // byte offset of this wavefront's first piece in a stage (uniform)
+    // Copy i of a lane fetches from row row_0 + i * ROUND_ROWS.  When a round
+    // of pieces covers whole rows and a whole number of swizzle periods, the
+    // column is the same for every i, so one offset per lane and a uniform
+    // row stride describe all copies (fewer registers); otherwise each copy
+    // keeps its own offset.
+    static constexpr int SWIZZLE_ROWS = Tile::swizzle.unit ? (Tile::swizzle.mask + 1) << Tile::swizzle.shift : 1;
+    static constexpr bool STRIDED = PIECE % Tile::cols == 0 && ((WAVES * PIECE / Tile::cols) % SWIZZLE_ROWS) == 0;
+    static constexpr int ROUND_ROWS = STRIDED ? WAVES * PIECE / Tile::cols : 0;
+    static constexpr bool strided_matches() {
+        if (!STRIDED) return true;
+        for (int w = 0; w < WAVES; ++w)
+            for (int lane = 0; lane < kWave; ++lane) {
+                int r0 = 0, c0 = 0;
+                source(w * PIECE + 4 * lane, r0, c0);
+                for (int i = 1; i < PER_WAVE; ++i) {
+                    int r = 0, c = 0;
+                    source((i * WAVES + w) * PIECE + 4 * lane, r, c);
+                    if (r != r0 + i * ROUND_ROWS || c != c0) return false;
+                }
+            }
+        return true;
+    }
+    static_assert(strided_matches(), "strided copies must fetch what the per-copy offsets would");
 
-    __device__ DirectCopy(int64_t ld, int wave_uniform, int lane) : lds_piece(wave_uniform * PIECE * 4) {
+    int64_t off[STRIDED ? 1 : PER_WAVE];  // element offset(s) of this lane's 16 bytes from the tile origin
+    int64_t round_stride;                 // elements between copy i and i+1 (strided form)
+    uint32_t lds_piece;                   // byte offset of this wavefront's first piece in a stage (uniform)
+
+    __device__ DirectCopy(int64_t ld, int wave_uniform, int lane)
+        : round_stride((int64_t)ROUND_ROWS * ld), lds_piece(wave_uniform * PIECE * 4) {
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
+        for (int i = 0; i < (STRIDED ? 1 : PER_WAVE); ++i) {
             int row = 0, col = 0;
             source((i * WAVES + wave_uniform) * PIECE + 4 * lane, row, col);
             off[i] = (int64_t)row * ld + (int64_t)col * PER_WORD;
@@ -301,7 +327,10 @@ struct DirectCopy {
         typedef __attribute__((address_space(3))) W lds_word;
         const uint32_t base = (uint32_t)(uintptr_t)(lds_word*)lds + lds_piece + stage * (Tile::stage_elems * 4);
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) copy16_to_lds(origin + off[i], base + i * (WAVES * PIECE * 4));
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const T* src = STRIDED ? origin + i * round_stride + off[0] : origin + off[i];
+            copy16_to_lds(src, base + i * (WAVES * PIECE * 4));
+        }
     }
 };
 
@@ -309,6 +338,16 @@ struct DirectCopy {
 // LDS copies included, have completed (s_waitcnt vmcnt(0); the expcnt and
 // lgkmcnt fields of the immediate are left at their no-wait maxima).
 __device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wavefront's vector memory operations are
+// outstanding (s_waitcnt vmcnt(N): N's low 4 bits in bits 3:0 of the
+// immediate, its high 2 bits in bits 15:14).  They complete in issue order,
+// so this waits for all but the N most recently issued.
+template <int N>
+__device__ inline void wait_vector_memory_at_most() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Store of a wavefront's MFMA accumulators: unmasked when the whole BM x BN
 // workgroup tile is in range (a uniform branch), else under the mask

@@ -141,7 +141,7 @@ struct TileLoader16 {
 };
 
 template <int TYPE_, int BM_, int BN_, int BK_, int WM_, int WN_, int MB_, class LayA, class LayB, int VEC_,
-          int MIN_WAVES_>
+          int MIN_WAVES_, int STAGES_ = 2, bool PIPELINE_ = true>
 struct MixedCfg {
     using Op = Mfma16Op<TYPE_, MB_>;
     static constexpr int TYPE = TYPE_;
@@ -150,13 +150,17 @@ struct MixedCfg {
     static constexpr int MIN_WAVES = VEC == 1 && MIN_WAVES_ > 2 ? 2 : MIN_WAVES_;
     static constexpr int ORDER = kXcdGroupedOrder;
     static constexpr int LOAD = VEC == 8 ? kLoadDirect : kLoadRegisters;
-    static constexpr int STAGES = 2;
+    static constexpr int STAGES = STAGES_;  // LDS stages of the direct-copy pipeline (register paths use two)
+    // Read the fragments of MFMA step st+1 during the MFMAs of step st (twice
+    // the fragment registers); off where the register budget has no room.
+    static constexpr bool PIPELINE = PIPELINE_;
+    static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
     static constexpr int STEPS = BK / Op::KB;
-    using TileA = LdsTile<BM, BK / 2, LayA::pad, 2, LayA::unit, LayA::shift, LayA::mask>;  // 4-byte words
-    using TileB = LdsTile<BK, BN / 2, LayB::pad, 2, LayB::unit, LayB::shift, LayB::mask>;
+    using TileA = LdsTile<BM, BK / 2, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;  // 4-byte words
+    using TileB = LdsTile<BK, BN / 2, LayB::pad, STAGES, LayB::unit, LayB::shift, LayB::mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
     static_assert(BK % Op::KB == 0, "whole MFMA steps per K tile");
@@ -215,70 +219,60 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     };
     typedef __attribute__((address_space(3))) uint32_t lds_word;
     typedef __attribute__((address_space(3))) shortx4 lds_short4;
-    auto multiply = [&](int stage) {
+    // Fragments of one MFMA step: A with 16-byte reads, B with two transposing
+    // 8-byte reads per block column.
+    auto read_fragments = [&](int stage, int st, u32x4 (&af)[MI], u32x4 (&bf)[NI]) {
 #pragma unroll
-        for (int st = 0; st < Cfg::STEPS; ++st) {
-            u32x4 af[MI], bf[NI];
+        for (int i = 0; i < MI; ++i)
+            af[i] = *reinterpret_cast<const u32x4*>(
+                lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, st * (Op::KB / 2) + 4 * g));
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(
-                    lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, st * (Op::KB / 2) + 4 * g));
+        for (int n = 0; n < NI; ++n) {
+            shortx4 half[2];
 #pragma unroll
-            for (int n = 0; n < NI; ++n) {
-                shortx4 half[2];
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int word = TileB::offset(stage, st * Op::KB + tr_row + 4 * rr, (wn0 + n * Op::NB + tr_col) / 2);
-                    half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_word*)lds_b + word));
-                }
-                const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
-                bf[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            for (int rr = 0; rr < 2; ++rr) {
+                const int word = TileB::offset(stage, st * Op::KB + tr_row + 4 * rr, (wn0 + n * Op::NB + tr_col) / 2);
+                half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_word*)lds_b + word));
             }
+            const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
+            bf[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    // Software-pipelined over the MFMA steps of a tile: the fragments of step
+    // st+1 are read while the MFMAs of step st run, so the LDS latency is
+    // hidden inside the wavefront instead of stalling the matrix pipe.  The
+    // scheduling barriers keep the compiler from sinking the reads back next
+    // to their MFMAs (which it does to save registers).
+    auto multiply = [&](int stage) {
+        if constexpr (Cfg::PIPELINE) {
+            u32x4 af[2][MI], bf[2][NI];
+            read_fragments(stage, 0, af[0], bf[0]);
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int st = 0; st < Cfg::STEPS; ++st) {
+                if (st + 1 < Cfg::STEPS) read_fragments(stage, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i], bf[n], acc[i][n]);
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[st & 1][i], bf[st & 1][n], acc[i][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < Cfg::STEPS; ++st) {
+                u32x4 af[MI], bf[NI];
+                read_fragments(stage, st, af, bf);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i], bf[n], acc[i][n]);
+            }
         }
     };
 
-    if constexpr (Cfg::LOAD == kLoadDirect) {
-        // As the fp32 direct kernel: the copies of tile t+1 are in flight
-        // during the multiply of tile t; tiles not wholly in range are loaded
-        // through registers with zero fill after the multiply.
-        const DirectCopy<TileA, THREADS, uint16_t> dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
-        const DirectCopy<TileB, THREADS, uint16_t> dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
-        const bool interior = M - m0 >= BM && N - n0 >= BN;
-        if (T > 0) {
-            if (interior && K >= BK) {
-                dma_a.issue(a_tile, lds_a, 0);
-                dma_b.issue(b_tile, lds_b, 0);
-            } else {
-                load_tile(0);
-                store_tile(0);
-            }
-        }
-        wait_vector_memory();
-        __syncthreads();
-        for (int64_t t = 0; t < T; ++t) {
-            const int s = (int)(t & 1);
-            const bool more = t + 1 < T;
-            const bool direct = more && interior && K - (t + 1) * BK >= BK;
-            if (direct) {
-                dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
-                dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
-            }
-            multiply(s);
-            if (more && !direct) {
-                load_tile(t + 1);
-                store_tile(s ^ 1);
-            }
-            wait_vector_memory();
-            __syncthreads();
-        }
-    } else {
-        // Unaligned operands: 2-byte loads through registers, issued after
-        // the multiply so that the staged elements (one register each) are
-        // not live across it; the other workgroups on the CU hide the latency.
+    // Two stages through registers, each refill issued after the multiply
+    // (edge workgroups, and unaligned operands below).
+    auto two_stage_registers = [&]() {
         if (T > 0) {
             load_tile(0);
             store_tile(0);
@@ -293,6 +287,67 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
             }
             __syncthreads();
         }
+    };
+
+    if constexpr (Cfg::LOAD == kLoadDirect) {
+        const bool interior = M - m0 >= BM && N - n0 >= BN;
+        if (interior) {
+            // S-stage pipeline of direct copies: during the multiply of tile t
+            // the copies of tiles t+1 .. t+S-1 are in flight, tile t+S-1 going
+            // into the stage tile t-1 used (every wave finished reading it
+            // before the barrier that ended iteration t-1).  Before the barrier
+            // that ends iteration t each wave waits until its copies of tile
+            // t+1 have landed, i.e. until at most the copies of tiles
+            // t+2 .. t+S-1 are outstanding.  A ragged last K tile (K % BK != 0)
+            // needs zero fill: it is loaded through registers instead, which
+            // makes that iteration wait for everything.
+            constexpr int S = Cfg::STAGES;
+            using DA = DirectCopy<TileA, THREADS, uint16_t>;
+            using DB = DirectCopy<TileB, THREADS, uint16_t>;
+            constexpr int COPIES = DA::PER_WAVE + DB::PER_WAVE;  // per wavefront and K tile
+            const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
+            const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
+            const int64_t TF = K / BK;  // K tiles wholly in range
+            for (int p = 0; p < S - 1 && p < T; ++p) {
+                if (p < TF) {
+                    dma_a.issue(a_tile + p * BK, lds_a, p);
+                    dma_b.issue(b_tile + p * BK * ldb, lds_b, p);
+                } else {
+                    load_tile(p);
+                    store_tile(p);
+                }
+            }
+            wait_vector_memory();
+            __syncthreads();
+            int s = 0;  // stage of tile t
+            for (int64_t t = 0; t < T; ++t) {
+                const int ps = s == 0 ? S - 1 : s - 1;  // stage of tile t + S - 1
+                const int64_t nt = t + S - 1;
+                const bool direct = nt < TF;
+                if (direct) {
+                    dma_a.issue(a_tile + nt * BK, lds_a, ps);
+                    dma_b.issue(b_tile + nt * BK * ldb, lds_b, ps);
+                }
+                multiply(s);
+                if (nt < T && !direct) {
+                    load_tile(nt);
+                    store_tile(ps);
+                }
+                if (direct)
+                    wait_vector_memory_at_most<(S - 2) * COPIES>();
+                else
+                    wait_vector_memory();
+                __syncthreads();
+                s = s + 1 == S ? 0 : s + 1;
+            }
+        } else {
+            two_stage_registers();
+        }
+    } else {
+        // Unaligned operands: 2-byte loads through registers, issued after
+        // the multiply so that the staged elements (one register each) are
+        // not live across it; the other workgroups on the CU hide the latency.
+        two_stage_registers();
     }
 
     store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, wm0, wn0, lane, acc);

@@ -249,7 +249,9 @@ typedef enum {
     GEMM_MIXED_256x256 = 2,       /* 256x256x32 tile, 8 waves of 128x64, 2 waves per SIMD */
     GEMM_MIXED_256x128_BK64 = 3,  /* 256x128x64 tile, 8 waves of 64x64 */
     GEMM_MIXED_128x128_BK64 = 4,  /* 128x128x64 tile, 4 waves of 64x64 */
-    GEMM_MIXED_COUNT = 5
+    GEMM_MIXED_256x256_S3 = 5,    /* as 256x256 with three LDS stages (copies two tiles ahead) */
+    GEMM_MIXED_256x256_BK64 = 6,  /* 256x256x64 tile, 8 waves of 128x64, two stages */
+    GEMM_MIXED_COUNT = 7
 } gemm_mixed_variant;
 
 /* C = A @ B, A and B of `input_type` (gemm_input_type), C fp32.  A, B, C are
@@ -269,8 +271,8 @@ int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K,
 /* Tile geometry of a gemm_mixed_variant (elem_bytes = 2).  Pure host call. */
 int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
 
-/* The variant GEMM_MIXED_AUTO runs: 256x256 when those tiles give at least
- * one workgroup per CU, else 256x128 when those do, else 128x128_BK64.  Pure
+/* The variant GEMM_MIXED_AUTO runs: 256x256_BK64 when 256x256 tiles give at
+ * least one workgroup per CU, else 256x128 when those do, else 128x128_BK64.  Pure
  * host call; GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 

@@ -253,11 +253,11 @@ def test_every_binding_declares_its_full_signature(gemm_lib):
 def test_mixed_tile_config_is_consistent(variant, gemm_lib):
     c = dft.gemm_mixed_tile_config(variant)
     assert c["variant"] == variant and c["elem_bytes"] == 2 and c["direct_to_lds"] == 1
-    assert c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2
+    assert c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] in (2, 3)
     # LDS tiles in 4-byte words: a row of a 16-bit tile holds two elements per word
     assert (c["a_rows"], 2 * c["a_cols"]) == (c["bm"], c["bk"])
     assert (c["b_rows"], 2 * c["b_cols"]) == (c["bk"], c["bn"])
-    assert c["lds_bytes"] == 2 * (c["a_stage_elems"] + c["b_stage_elems"]) * 4 <= 160 * 1024
+    assert c["lds_bytes"] == c["stages"] * (c["a_stage_elems"] + c["b_stage_elems"]) * 4 <= 160 * 1024
     assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64
     assert c["mfma_block"] == 32
 
@@ -285,8 +285,8 @@ def test_mixed_argument_checks(gemm_lib):
 
 def test_mixed_auto_variant(gemm_lib):
     av = dft.gemm_mixed_auto_variant
-    assert av(8192, 8192, 8192, 256) == dft.MIXED_256x256  # 1024 tiles of 256x256
-    assert av(4096, 4096, 4096, 256) == dft.MIXED_256x256  # 256 tiles
+    assert av(8192, 8192, 8192, 256) == dft.MIXED_256x256_BK64  # 1024 tiles of 256x256
+    assert av(4096, 4096, 4096, 256) == dft.MIXED_256x256_BK64  # 256 tiles
     assert av(2048, 4096, 4096, 256) == dft.MIXED_256x128  # 128 tiles of 256x256, 256 of 256x128
     assert av(2048, 256, 16384, 256) == dft.MIXED_128x128_BK64
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
