@@ -52,6 +52,12 @@ using Mfma128Bk32Direct = std::conditional_t<
             kXcdGroupedOrder, kLoadDirect>,
     MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
 template <int VEC>
+using Mfma64Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A, layouts::m32_64x64x16_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_v1::A, layouts::m32_64x64x16_v1::B, 1, kXcdGroupedOrder>>;
+template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
 // BK = 32 with 4-byte loads needs 32 staged values and their addresses per
@@ -190,12 +196,36 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_DIRECT   */ mfma_variant<Mfma256Direct<4>, Mfma256Direct<1>>(),
     /* MFMA_128_DIRECT      */ mfma_variant<Mfma128Direct<4>, Mfma128Direct<1>>(),
     /* MFMA_128_BK32_DIRECT */ mfma_variant<Mfma128Bk32Direct<4>, Mfma128Bk32Direct<1>>(),
+    /* MFMA_64_DIRECT       */ mfma_variant<Mfma64Direct<4>, Mfma64Direct<1>>(),
 };
 
+// AUTO picks the direct-copy variant with the highest estimated rate:
+// its measured full-chip rate at 4096^3-class sizes times the wave
+// quantisation of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the
+// fraction of CU-rounds that have work.  On 14 measured shapes from
+// 128^3 to 8192^3 (deep, flat and ragged) this picks the fastest variant.
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
-    const int64_t tiles256 = ((M + 255) / 256) * ((N + 127) / 128);
-    if (tiles256 >= num_cus) return GEMM_VARIANT_MFMA_DIRECT;
-    return K >= 4096 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT;
+    struct Candidate {
+        int variant, bm, bn;
+        double rate;  // TFLOP/s with every CU busy (relative weights only)
+    };
+    const Candidate candidates[] = {
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 137.0},
+        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 130.0},
+        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 110.0},
+    };
+    int best = GEMM_VARIANT_MFMA_DIRECT;
+    double best_rate = -1.0;
+    for (const Candidate& c : candidates) {
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
+        const double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
+        if (rate > best_rate * 1.02) {  // larger tiles win near-ties (listed first)
+            best = c.variant;
+            best_rate = rate;
+        }
+    }
+    return best;
 }
 
 // ---- per-device properties (cached) ---------------------------------------------

@@ -69,7 +69,8 @@ typedef enum {
     GEMM_VARIANT_MFMA_DIRECT = 9,   /* as MFMA with in-range tiles copied global->LDS directly (no registers) */
     GEMM_VARIANT_MFMA_128_DIRECT = 10,      /* as MFMA_128 with direct global->LDS copies */
     GEMM_VARIANT_MFMA_128_BK32_DIRECT = 11, /* as MFMA_128_BK32 with direct global->LDS copies */
-    GEMM_VARIANT_COUNT = 12
+    GEMM_VARIANT_MFMA_64_DIRECT = 12,       /* 64x64x16 tile, 4 waves of 32x32, direct copies (few output tiles) */
+    GEMM_VARIANT_COUNT = 13
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -174,9 +175,12 @@ int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
- * `num_cus` compute units: MFMA_DIRECT when its 256x128 tiles give at least
- * one workgroup per CU, else MFMA_128_BK32_DIRECT for K >= 4096, else
- * MFMA_128_DIRECT.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
+ * `num_cus` compute units: among MFMA_DIRECT (256x128 tiles), the 128x128
+ * direct variant (BK 32 when K >= 1024, else 16) and MFMA_64_DIRECT (64x64),
+ * the one with the highest rate estimate, its full-chip rate (137, 130, 110
+ * TFLOP/s) times the wave quantisation of its tile grid,
+ * tiles / (ceil(tiles / num_cus) * num_cus); a larger tile wins when within
+ * 2 %.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
  * sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
