@@ -81,6 +81,39 @@ def build_all() -> list[Path]:
     return [build(LIB, sources=SOURCES), build(PROBE_LIB, sources=PROBE_SOURCES)]
 
 
+def resource_report(source: Path | None = None) -> dict[str, dict[str, int]]:
+    """The compiler's per-kernel resource usage for the library's device code
+    (hipcc -Rpass-analysis=kernel-resource-usage): {mangled kernel name:
+    {"vgpr", "agpr", "scratch" (bytes per lane), "occupancy" (waves per SIMD),
+    "lds" (bytes per workgroup)}}.  Compiles device code only, to a
+    temporary object."""
+    import re
+    import tempfile
+
+    generate_layouts()
+    fields = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+              "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-c", f"-I{ROOT / 'include'}", f"-I{CSRC}",
+               str(source or SOURCES[0]), "-o", str(Path(tmp) / "device.o"), "-Rpass-analysis=kernel-resource-usage"]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stderr)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
+    report: dict[str, dict[str, int]] = {}
+    current = None
+    for line in proc.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            current = report.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(.+?): (\d+) \[-Rpass", line)
+        if m and current is not None and m.group(1) in fields:
+            current[fields[m.group(1)]] = int(m.group(2))
+    return report
+
+
 if __name__ == "__main__":
     for p in build_all():
         print(p)

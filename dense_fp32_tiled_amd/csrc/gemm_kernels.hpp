@@ -204,10 +204,15 @@ struct MfmaCfg {
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
     static constexpr int KG = BK / Op::KB;  // k values per lane group per tile
-    // Register budget: 4 waves per SIMD (<= 128 VGPRs) for the 16-byte load
-    // path, so that four 256-thread workgroups fit on a CU; the 4-byte load
-    // path holds 4x more load registers and is limited to 2 waves per SIMD.
-    static constexpr int MIN_WAVES = (VEC == 4 && WM * WN <= 64 * 64) ? 4 : 2;
+    // Register budget (waves per SIMD the compiler must fit): 4 (<= 128
+    // VGPRs) when the tile reaches LDS by direct copies, or through registers
+    // with at most 12 staged floats per thread; 3 for more staged floats
+    // (128x128 tiles through registers: 16 or 32, which spill at 4); 2 for
+    // 4-byte loads (four times the load registers).
+    static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
+    static constexpr int MIN_WAVES = VEC != 4 || WM * WN > 64 * 64 ? 2
+                                     : (LOAD == kLoadDirect || STAGED <= 12) ? 4
+                                                                             : 3;
     using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;
     using TileB = LdsTile<BK, BN, LayB::pad, STAGES, LayB::unit, LayB::shift, LayB::mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;

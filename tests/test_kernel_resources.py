@@ -1,0 +1,46 @@
+"""Register and LDS budgets of every kernel, from the compiler's own resource
+report (hipcc -Rpass-analysis=kernel-resource-usage on the library's device
+code).  CPU only: the code is cross-compiled for gfx950 here.
+
+A spill (scratch memory per lane) in a GEMM kernel turns register reads into
+memory traffic inside the K loop; none of the kernels may have one.  The
+default kernels must also keep the occupancy their tiling was designed for:
+it is what hides the latency of the LDS reads and the global->LDS copies."""
+
+from __future__ import annotations
+
+import pytest
+
+from dense_fp32_tiled_amd import build
+
+
+@pytest.fixture(scope="module")
+def report():
+    return build.resource_report()
+
+
+def kernels(report, fragment):
+    return {k: v for k, v in report.items() if fragment in k}
+
+
+def test_every_kernel_is_spill_free(report):
+    assert len(report) >= 30
+    spilled = {k: v["scratch"] for k, v in report.items() if v.get("scratch", 0) != 0}
+    assert not spilled, spilled
+
+
+def test_default_kernels_keep_their_occupancy(report):
+    # fp32 256x128 direct-copy kernel (AUTO for large problems): 4 waves per SIMD = two 8-wave workgroups
+    fp32_default = kernels(report, "MfmaCfgILi256ELi128ELi16ELi64ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
+                                   "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1EE")
+    assert len(fp32_default) == 1
+    (r,) = fp32_default.values()
+    assert r["occupancy"] == 4 and r["lds"] == 48 * 1024
+    # bf16 / fp16 256x256x64 (AUTO for large problems): 2 waves per SIMD, 128 KiB of LDS
+    mixed_default = kernels(report, "MixedCfgILi0ELi256ELi256ELi64E")
+    assert mixed_default and all(v["occupancy"] == 2 and v["lds"] == 128 * 1024 for v in mixed_default.values())
+
+
+def test_lds_fits_the_cu(report):
+    for name, v in report.items():
+        assert v.get("lds", 0) <= 160 * 1024, name
