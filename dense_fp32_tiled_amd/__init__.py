@@ -40,7 +40,8 @@ VARIANT_MFMA_DIRECT = 9
 VARIANT_MFMA_128_DIRECT = 10
 VARIANT_MFMA_128_BK32_DIRECT = 11
 VARIANT_MFMA_64_DIRECT = 12
-VARIANT_COUNT = 13
+VARIANT_MFMA_256x256_DIRECT = 13
+VARIANT_COUNT = 14
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -70,6 +71,7 @@ VARIANT_NAMES = {
     VARIANT_MFMA_128_DIRECT: "mfma_128_direct",
     VARIANT_MFMA_128_BK32_DIRECT: "mfma_128_bk32_direct",
     VARIANT_MFMA_64_DIRECT: "mfma_64_direct",
+    VARIANT_MFMA_256x256_DIRECT: "mfma_256x256_direct",
 }
 
 # Every symbol the public header declares.

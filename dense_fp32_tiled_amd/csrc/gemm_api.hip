@@ -52,6 +52,12 @@ using Mfma128Bk32Direct = std::conditional_t<
             kXcdGroupedOrder, kLoadDirect>,
     MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
 template <int VEC>
+using Mfma256x256Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 16, 128, 64, 2, 32, layouts::m32_256x256x16_direct::A, layouts::m32_256x256x16_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    Mfma256<2, 1>>;
+template <int VEC>
 using Mfma64Direct = std::conditional_t<
     VEC == 4,
     MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A, layouts::m32_64x64x16_direct::B, 4,
@@ -183,7 +189,7 @@ Variant mfma_variant() {
 // Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
 // to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO          */ mfma_variant<Mfma256Direct<4>, Mfma256Direct<1>>(),
+    /* AUTO          */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
     /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
     /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, valu_config<ValuT<1>>,
                          ValuT<4>::LDS_BYTES},
@@ -197,19 +203,22 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_128_DIRECT      */ mfma_variant<Mfma128Direct<4>, Mfma128Direct<1>>(),
     /* MFMA_128_BK32_DIRECT */ mfma_variant<Mfma128Bk32Direct<4>, Mfma128Bk32Direct<1>>(),
     /* MFMA_64_DIRECT       */ mfma_variant<Mfma64Direct<4>, Mfma64Direct<1>>(),
+    /* MFMA_256x256_DIRECT  */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate:
 // its measured full-chip rate at 4096^3-class sizes times the wave
 // quantisation of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the
-// fraction of CU-rounds that have work.  On 14 measured shapes from
-// 128^3 to 8192^3 (deep, flat and ragged) this picks the fastest variant.
+// fraction of CU-rounds that have work.  On 15 measured shapes from
+// 128^3 to 8192^3 (deep, flat and ragged) this picks the fastest variant
+// or one within 2.5 % of it.
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     struct Candidate {
         int variant, bm, bn;
         double rate;  // TFLOP/s with every CU busy (relative weights only)
     };
     const Candidate candidates[] = {
+        {GEMM_VARIANT_MFMA_256x256_DIRECT, 256, 256, 140.0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 137.0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 130.0},
         {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 110.0},

@@ -57,7 +57,7 @@ typedef enum {
 /* Kernel variants.  Every variant computes the same operation; they differ in
  * how (see gemm_f32_tile_config for each one's tile geometry). */
 typedef enum {
-    GEMM_VARIANT_AUTO = 0,          /* picks one of the direct-copy MFMA variants from M, N, K (gemm_f32_auto_variant) */
+    GEMM_VARIANT_AUTO = 0,          /* picks a direct-copy MFMA variant from M, N, K (gemm_f32_auto_variant) */
     GEMM_VARIANT_MFMA = 1,          /* v_mfma_f32_32x32x2_f32, 256x128x16 workgroup tile, 8 waves of 64x64 */
     GEMM_VARIANT_VALU = 2,          /* register-tiled vector-ALU fp32 FMA, 128x128x16, 8x8 per thread */
     GEMM_VARIANT_MFMA_STAGES1 = 3,  /* ablation of MFMA: one LDS stage, two barriers per K tile, no prefetch */
@@ -70,7 +70,8 @@ typedef enum {
     GEMM_VARIANT_MFMA_128_DIRECT = 10,      /* as MFMA_128 with direct global->LDS copies */
     GEMM_VARIANT_MFMA_128_BK32_DIRECT = 11, /* as MFMA_128_BK32 with direct global->LDS copies */
     GEMM_VARIANT_MFMA_64_DIRECT = 12,       /* 64x64x16 tile, 4 waves of 32x32, direct copies (few output tiles) */
-    GEMM_VARIANT_COUNT = 13
+    GEMM_VARIANT_MFMA_256x256_DIRECT = 13,  /* 256x256x16 tile, 8 waves of 128x64 (2 per SIMD), direct copies */
+    GEMM_VARIANT_COUNT = 14
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -175,12 +176,12 @@ int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
- * `num_cus` compute units: among MFMA_DIRECT (256x128 tiles), the 128x128
- * direct variant (BK 32 when K >= 1024, else 16) and MFMA_64_DIRECT (64x64),
- * the one with the highest rate estimate, its full-chip rate (137, 130, 110
- * TFLOP/s) times the wave quantisation of its tile grid,
- * tiles / (ceil(tiles / num_cus) * num_cus); a larger tile wins when within
- * 2 %.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
+ * `num_cus` compute units: among MFMA_256x256_DIRECT, MFMA_DIRECT (256x128),
+ * the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
+ * MFMA_64_DIRECT (64x64), the one with the highest rate estimate, its
+ * full-chip rate (140, 137, 130, 110 TFLOP/s) times the wave quantisation of
+ * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus); a larger tile
+ * wins when within 2 %.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
  * sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 

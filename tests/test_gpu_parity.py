@@ -26,7 +26,7 @@ SENTINEL = SENTINEL_BITS.view(np.float32)
 ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1,
                 dft.VARIANT_MFMA_NOPAD, dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128,
                 dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
-                dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT]
+                dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -122,7 +122,7 @@ def test_config_parity(cfg_name, variant, torch_gpu):
     assert err <= TOL
 
 
-FULL_CHECK_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU]
+FULL_CHECK_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA, dft.VARIANT_VALU]
 
 
 @pytest.mark.parametrize("variant", FULL_CHECK_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in FULL_CHECK_VARIANTS])
@@ -159,7 +159,8 @@ EDGE_SHAPES = [
 
 EDGE_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA16,
                  dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT,
-                 dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT]
+                 dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT,
+                 dft.VARIANT_MFMA_256x256_DIRECT]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
@@ -194,7 +195,7 @@ def test_pitched_operands(pitch, variant, torch_gpu):
 
 
 DIRECT_VARIANTS = [dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
-                   dft.VARIANT_MFMA_64_DIRECT]
+                   dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT]
 
 
 @pytest.mark.parametrize("variant", DIRECT_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in DIRECT_VARIANTS])

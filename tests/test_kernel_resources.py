@@ -30,7 +30,12 @@ def test_every_kernel_is_spill_free(report):
 
 
 def test_default_kernels_keep_their_occupancy(report):
-    # fp32 256x128 direct-copy kernel (AUTO for large problems): 4 waves per SIMD = two 8-wave workgroups
+    # fp32 256x256 direct-copy kernel (AUTO for large problems): one 8-wave workgroup per CU, 64 KiB of LDS
+    fp32_big = kernels(report, "MfmaCfgILi256ELi256ELi16ELi128ELi64E")
+    assert len(fp32_big) == 1
+    (r,) = fp32_big.values()
+    assert r["occupancy"] == 2 and r["lds"] == 64 * 1024
+    # fp32 256x128 direct-copy kernel (AUTO when 256x256 tiles round badly): 4 waves per SIMD = two workgroups
     fp32_default = kernels(report, "MfmaCfgILi256ELi128ELi16ELi64ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
                                    "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1EE")
     assert len(fp32_default) == 1
