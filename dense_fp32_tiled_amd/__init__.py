@@ -41,7 +41,8 @@ VARIANT_MFMA_128_DIRECT = 10
 VARIANT_MFMA_128_BK32_DIRECT = 11
 VARIANT_MFMA_64_DIRECT = 12
 VARIANT_MFMA_256x256_DIRECT = 13
-VARIANT_COUNT = 14
+VARIANT_MFMA_256x256_W4_DIRECT = 14
+VARIANT_COUNT = 15
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -72,6 +73,7 @@ VARIANT_NAMES = {
     VARIANT_MFMA_128_BK32_DIRECT: "mfma_128_bk32_direct",
     VARIANT_MFMA_64_DIRECT: "mfma_64_direct",
     VARIANT_MFMA_256x256_DIRECT: "mfma_256x256_direct",
+    VARIANT_MFMA_256x256_W4_DIRECT: "mfma_256x256_w4_direct",
 }
 
 # Every symbol the public header declares.

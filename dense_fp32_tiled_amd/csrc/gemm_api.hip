@@ -58,6 +58,12 @@ using Mfma256x256Direct = std::conditional_t<
             kXcdGroupedOrder, kLoadDirect>,
     Mfma256<2, 1>>;
 template <int VEC>
+using Mfma256x256W4Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 16, 128, 128, 2, 32, layouts::m32_256x256x16_w4_direct::A,
+            layouts::m32_256x256x16_w4_direct::B, 4, kXcdGroupedOrder, kLoadDirect>,
+    Mfma256<2, 1>>;
+template <int VEC>
 using Mfma64Direct = std::conditional_t<
     VEC == 4,
     MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A, layouts::m32_64x64x16_direct::B, 4,
@@ -204,6 +210,7 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_128_BK32_DIRECT */ mfma_variant<Mfma128Bk32Direct<4>, Mfma128Bk32Direct<1>>(),
     /* MFMA_64_DIRECT       */ mfma_variant<Mfma64Direct<4>, Mfma64Direct<1>>(),
     /* MFMA_256x256_DIRECT  */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
+    /* MFMA_256x256_W4_DIRECT */ mfma_variant<Mfma256x256W4Direct<4>, Mfma256x256W4Direct<1>>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate:

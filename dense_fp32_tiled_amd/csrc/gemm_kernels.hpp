@@ -209,8 +209,11 @@ struct MfmaCfg {
     // with at most 12 staged floats per thread; 3 for more staged floats
     // (128x128 tiles through registers: 16 or 32, which spill at 4); 2 for
     // 4-byte loads (four times the load registers).
+    // 1 for 128x128 wave tiles (256 accumulators: the whole register file
+    // at one wave per SIMD).
     static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
-    static constexpr int MIN_WAVES = VEC != 4 || WM * WN > 64 * 64 ? 2
+    static constexpr int MIN_WAVES = WM * WN >= 128 * 128           ? 1
+                                     : VEC != 4 || WM * WN > 64 * 64 ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
                                                                              : 3;
     using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;

@@ -71,7 +71,8 @@ typedef enum {
     GEMM_VARIANT_MFMA_128_BK32_DIRECT = 11, /* as MFMA_128_BK32 with direct global->LDS copies */
     GEMM_VARIANT_MFMA_64_DIRECT = 12,       /* 64x64x16 tile, 4 waves of 32x32, direct copies (few output tiles) */
     GEMM_VARIANT_MFMA_256x256_DIRECT = 13,  /* 256x256x16 tile, 8 waves of 128x64 (2 per SIMD), direct copies */
-    GEMM_VARIANT_COUNT = 14
+    GEMM_VARIANT_MFMA_256x256_W4_DIRECT = 14, /* 256x256x16 tile, 4 waves of 128x128 (1 per SIMD), direct copies */
+    GEMM_VARIANT_COUNT = 15
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of

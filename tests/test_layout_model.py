@@ -128,7 +128,7 @@ def degree(c, width, words):
 
 MFMA_LAYOUT_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32,
                         dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_64_DIRECT,
-                        dft.VARIANT_MFMA_256x256_DIRECT]
+                        dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT]
 
 
 @pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
