@@ -13,6 +13,10 @@
  * "Preserving shared dependencies").  Zero fill makes the tiled result equal
  * to the plain sum over k in [0, K) for every in-range element.
  *
+ * gemm_mixed_f32 (end of this header) computes the same product from bf16 or
+ * fp16 A and B with fp32 accumulation; the conventions below apply to it with
+ * 2-byte A and B elements.
+ *
  * Conventions for every entry point below
  *   - Matrices are row-major.  Element (i, k) of A is A[i*lda + k]; likewise
  *     B with ldb and C with ldc.  Leading dimensions are in elements and may
@@ -20,7 +24,8 @@
  *   - A, B and C are DEVICE pointers owned by the caller.  The library keeps no
  *     pointer after the call returns, allocates no device memory and holds no
  *     per-call state; it caches only per-device properties.
- *   - C = A @ B overwrites C (no alpha/beta).  C must not overlap A or B.
+ *   - C = A @ B overwrites C (no alpha/beta).  C must not overlap A or B (nor a
+ *     split-K workspace any operand).
  *   - M == 0 or N == 0: nothing is launched.  K == 0: the M x N region of C is
  *     set to zero (an empty sum).
  *   - Arguments are validated on the host before anything is launched, so an
@@ -47,7 +52,7 @@ typedef enum {
     GEMM_ERR_INVALID_LD = -2,   /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
     GEMM_ERR_NULL = -3,         /* a NULL pointer for an operand with non-zero extent */
     GEMM_ERR_ALIAS = -4,        /* the address range of C overlaps that of A or B */
-    GEMM_ERR_UNSUPPORTED = -5,  /* no gfx950 device current, or unknown variant */
+    GEMM_ERR_UNSUPPORTED = -5,  /* no gfx950 device current, or unknown variant or input type */
     GEMM_ERR_CONFIG = -6,       /* variant's LDS footprint exceeds the device limit */
     GEMM_ERR_HIP = -7,          /* a HIP runtime call or the launch failed */
     GEMM_ERR_TOO_LARGE = -8,    /* a size overflows the kernel's index range */
@@ -116,9 +121,12 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              void *stream);
 
 /* As gemm_f32 with an explicit gemm_variant.  When lda or ldb is not a
- * multiple of 4, or A or B is not 16-byte aligned, the variant's 16-byte
- * loads are illegal and the call runs the same variant with 4-byte masked
- * loads (a fallback, not an error; results are identical). */
+ * multiple of 4, or A or B is not 16-byte aligned, 16-byte loads and direct
+ * copies are illegal and the call runs the variant's 4-byte-load kernel
+ * instead (a fallback, not an error; the same result up to the order of the
+ * fp32 additions): the same tile for most variants, 128x128x16 for the BK = 32
+ * variants and 256x128x16 for the 256x256 variants, whose register-path
+ * versions would not fit their registers. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,
