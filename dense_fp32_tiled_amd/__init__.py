@@ -42,7 +42,11 @@ VARIANT_MFMA_128_BK32_DIRECT = 11
 VARIANT_MFMA_64_DIRECT = 12
 VARIANT_MFMA_256x256_DIRECT = 13
 VARIANT_MFMA_256x256_W4_DIRECT = 14
-VARIANT_COUNT = 15
+VARIANT_MFMA_256x256_PIPE = 15
+VARIANT_MFMA_256x256_BK32_PIPE = 16
+VARIANT_MFMA16_256x256_DIRECT = 17
+VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18
+VARIANT_COUNT = 19
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -74,6 +78,10 @@ VARIANT_NAMES = {
     VARIANT_MFMA_64_DIRECT: "mfma_64_direct",
     VARIANT_MFMA_256x256_DIRECT: "mfma_256x256_direct",
     VARIANT_MFMA_256x256_W4_DIRECT: "mfma_256x256_w4_direct",
+    VARIANT_MFMA_256x256_PIPE: "mfma_256x256_pipe",
+    VARIANT_MFMA_256x256_BK32_PIPE: "mfma_256x256_bk32_pipe",
+    VARIANT_MFMA16_256x256_DIRECT: "mfma16_256x256_direct",
+    VARIANT_MFMA16_256x256_W4_BK32_PIPE: "mfma16_256x256_w4_bk32_pipe",
 }
 
 # Every symbol the public header declares.

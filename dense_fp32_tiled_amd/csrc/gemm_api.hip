@@ -63,6 +63,32 @@ using Mfma256x256W4Direct = std::conditional_t<
     MfmaCfg<256, 256, 16, 128, 128, 2, 32, layouts::m32_256x256x16_w4_direct::A,
             layouts::m32_256x256x16_w4_direct::B, 4, kXcdGroupedOrder, kLoadDirect>,
     Mfma256<2, 1>>;
+// The 256x256 tile with the chunked, cross-barrier pipelined multiply, at
+// BK = 16 and BK = 32 (two 64 KiB stages: one workgroup per CU, as at BK = 16).
+template <int VEC>
+using Mfma256x256Pipe = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 16, 128, 64, 2, 32, layouts::m32_256x256x16_pipe::A, layouts::m32_256x256x16_pipe::B, 4,
+            kXcdGroupedOrder, kLoadDirect, true>,
+    Mfma256<2, 1>>;
+template <int VEC>
+using Mfma256x256Bk32Pipe = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 32, 128, 64, 2, 32, layouts::m32_256x256x32_pipe::A, layouts::m32_256x256x32_pipe::B, 4,
+            kXcdGroupedOrder, kLoadDirect, true>,
+    Mfma256<2, 1>>;
+template <int VEC>
+using Mfma16x256x256Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 16, 128, 64, 2, 16, layouts::m16_256x256x16_direct::A, layouts::m16_256x256x16_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    Mfma256<2, 1>>;
+template <int VEC>
+using Mfma16x256x256W4Bk32Pipe = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<256, 256, 32, 128, 128, 2, 16, layouts::m16_256x256x32_w4_pipe::A,
+            layouts::m16_256x256x32_w4_pipe::B, 4, kXcdGroupedOrder, kLoadDirect, true>,
+    Mfma256<2, 1>>;
 template <int VEC>
 using Mfma64Direct = std::conditional_t<
     VEC == 4,
@@ -165,6 +191,7 @@ gemm_tile_config mfma_config(int variant, int vec) {
     c.tm = Cfg::WM; c.tn = Cfg::WN;
     c.a_transposed = 0;
     c.mfma_block = Cfg::Op::MB;
+    if (Cfg::PIPE) c.direct_to_lds = 2;
     return c;
 }
 
@@ -195,7 +222,7 @@ Variant mfma_variant() {
 // Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
 // to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO          */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
+    /* AUTO          */ mfma_variant<Mfma256x256Bk32Pipe<4>, Mfma256x256Bk32Pipe<1>>(),
     /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
     /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, valu_config<ValuT<1>>,
                          ValuT<4>::LDS_BYTES},
@@ -211,31 +238,38 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_64_DIRECT       */ mfma_variant<Mfma64Direct<4>, Mfma64Direct<1>>(),
     /* MFMA_256x256_DIRECT  */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
     /* MFMA_256x256_W4_DIRECT */ mfma_variant<Mfma256x256W4Direct<4>, Mfma256x256W4Direct<1>>(),
+    /* MFMA_256x256_PIPE      */ mfma_variant<Mfma256x256Pipe<4>, Mfma256x256Pipe<1>>(),
+    /* MFMA_256x256_BK32_PIPE */ mfma_variant<Mfma256x256Bk32Pipe<4>, Mfma256x256Bk32Pipe<1>>(),
+    /* MFMA16_256x256_DIRECT  */ mfma_variant<Mfma16x256x256Direct<4>, Mfma16x256x256Direct<1>>(),
+    /* MFMA16_256x256_W4_BK32_PIPE   */ mfma_variant<Mfma16x256x256W4Bk32Pipe<4>, Mfma16x256x256W4Bk32Pipe<1>>(),
 };
 
-// AUTO picks the direct-copy variant with the highest estimated rate:
-// its measured full-chip rate at 4096^3-class sizes times the wave
-// quantisation of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the
-// fraction of CU-rounds that have work.  On 15 measured shapes from
-// 128^3 to 8192^3 (deep, flat and ragged) this picks the fastest variant
-// or one within 2.5 % of it.
+// AUTO picks the direct-copy variant with the highest estimated rate: its
+// measured full-chip rate at 4096^3-class sizes times the wave quantisation
+// of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the fraction of
+// CU-rounds that have work.  The 256x128 and 128x128 kernels are built to
+// run two workgroups per CU; with fewer tiles than two per CU they were
+// measured about 12 % slower, which the estimate applies.  On 15 measured
+// shapes from 512^2 x 16384 to 8192^3 (deep, flat and ragged) this picks
+// the fastest of these variants or one within 1.5 % of it.
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     struct Candidate {
-        int variant, bm, bn;
+        int variant, bm, bn, per_cu;
         double rate;  // TFLOP/s with every CU busy (relative weights only)
     };
     const Candidate candidates[] = {
-        {GEMM_VARIANT_MFMA_256x256_DIRECT, 256, 256, 140.0},
-        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 137.0},
-        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 130.0},
-        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 110.0},
+        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, 145.0},
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, 144.0},
+        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, 144.0},
+        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, 128.0},
     };
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
     for (const Candidate& c : candidates) {
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
-        const double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
+        double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
+        if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;
         if (rate > best_rate * 1.02) {  // larger tiles win near-ties (listed first)
             best = c.variant;
             best_rate = rate;
@@ -577,7 +611,7 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
 int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
                                 int32_t vec, int32_t direct, int32_t* out) {
     if (out == nullptr || (mb != 32 && mb != 16) || (vec != 1 && vec != 4)) return GEMM_ERR_INVALID_DIM;
-    if ((direct != 0 && direct != 1) || (direct && vec != 4)) return GEMM_ERR_INVALID_DIM;
+    if (direct < 0 || direct > 2 || (direct && vec != 4)) return GEMM_ERR_INVALID_DIM;
     if (bm < 1 || bn < 1 || bk < 1 || wm < mb || wn < mb || bm % wm || bn % wn || wm % mb || wn % mb)
         return GEMM_ERR_INVALID_DIM;
     const int kb = 64 / mb, threads = (bm / wm) * (bn / wn) * kWaveLanes;
@@ -585,7 +619,8 @@ int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, 
         (bk * bn / vec) % threads)
         return GEMM_ERR_INVALID_DIM;
     if (direct && ((bm * bk) % (threads * 4) || (bk * bn) % (threads * 4))) return GEMM_ERR_INVALID_DIM;
-    const MfmaShape shape{bm, bn, bk, wm, wn, threads, vec, mb, mb, kb, direct == 1};
+    if (direct == 2 && (bk / kb) % 8) return GEMM_ERR_INVALID_DIM;
+    const MfmaShape shape{bm, bn, bk, wm, wn, threads, vec, mb, mb, kb, direct != 0, direct == 2};
     const LayoutChoice a = mfma_layout_a(shape, kGfx950Lds), b = mfma_layout_b(shape, kGfx950Lds);
     const int32_t v[8] = {a.pad, a.swz.unit, a.swz.shift, a.swz.mask, b.pad, b.swz.unit, b.swz.shift, b.swz.mask};
     for (int i = 0; i < 8; ++i) out[i] = v[i];

@@ -104,6 +104,44 @@ struct TileLoader {
         }
     }
 
+    // Masked load and LDS store of the whole tile, at most MAX_CH slots at a
+    // time (the staging registers of those slots only), for kernels that
+    // cannot hold all PER_THREAD slots beside their other live registers.
+    template <class Tile, int MAX_CH>
+    __device__ static void copy_in_chunks(const float* __restrict__ tile, int64_t ld, int64_t rows_left,
+                                          int64_t cols_left, float* lds, int stage, int tid) {
+        static_assert(Tile::rows == ROWS && Tile::cols == COLS, "LDS tile shape mismatch");
+        constexpr int CH = MAX_CH < PER_THREAD ? MAX_CH : PER_THREAD;
+        static_assert(PER_THREAD % CH == 0, "chunks must split the slots evenly");
+        const bool full = rows_left >= ROWS && cols_left >= COLS;
+#pragma unroll 1
+        for (int i0 = 0; i0 < PER_THREAD; i0 += CH) {
+            float v[CH][VEC];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int r = slot_row(tid, i0 + i), c = slot_col(tid, i0 + i);
+                const float* p = tile + (int64_t)r * ld + c;
+                if (full && VEC == 4) {
+                    const floatx4 x = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[i][e] = x[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[i][e] = (r < rows_left && c + e < cols_left) ? p[e] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                float* q = lds + Tile::offset(stage, slot_row(tid, i0 + i), slot_col(tid, i0 + i));
+                if constexpr (VEC == 4) {
+                    *reinterpret_cast<floatx4*>(q) = floatx4{v[i][0], v[i][1], v[i][2], v[i][3]};
+                } else {
+                    *q = v[i][0];
+                }
+            }
+        }
+    }
+
     // Transposed LDS destination: element (r, c) -> Tile::offset(stage, c, r).
     template <class Tile>
     __device__ void store_transposed(float* lds, int stage, int tid) const {
@@ -194,12 +232,18 @@ enum TileOrder { kRowMajorOrder = 0, kXcdGroupedOrder = 1 };
 // by the direct global->LDS copy for in-range tiles (DirectCopy).
 enum LoadPath { kLoadRegisters = 0, kLoadDirect = 1 };
 
+// PIPE (direct copies only): the multiply of a K tile runs in chunks of four
+// k per lane group, the LDS fragments of chunk q+1 being read while chunk q
+// multiplies, and the last chunk of tile t multiplies after the barrier,
+// while the first fragments of tile t+1 are read; the matrix pipe then idles
+// only for the barrier itself, not for the LDS latency behind it.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MB_, class LayA, class LayB, int VEC_,
-          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters>
+          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters, bool PIPE_ = false>
 struct MfmaCfg {
     using Op = MfmaOp<MB_, 64 / MB_>;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_, LOAD = LOAD_;
+    static constexpr bool PIPE = PIPE_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
@@ -225,32 +269,61 @@ struct MfmaCfg {
     static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
     static_assert(LOAD == kLoadRegisters || (VEC == 4 && STAGES == 2 && LayA::pad == 0 && LayB::pad == 0),
                   "direct copies need 16-byte loads, two stages and unpadded rows");
+    static_assert(!PIPE || (LOAD == kLoadDirect && KG % 8 == 0),
+                  "the pipeline runs on direct copies, with an even number of 4-k chunks per tile");
+
+    // Pipelined fragment addressing: A block row i of chunk q at
+    // a_base(q) + i * MB rows; B step kk of block column n at
+    // b_base(n % PB) + kk rows + (n / PB) * PB * NB words.  Holds when the
+    // swizzle term of an address does not change along those strides.
+    static constexpr int Q = KG / 4, PB = NI < 2 ? NI : 2;
+    static constexpr bool pipelined_addressing() {
+        for (int w = 0; w < WAVES_M * WAVES_N; ++w)
+            for (int l = 0; l < kWave; ++l) {
+                const int g = l / Op::MB, r = l % Op::MB;
+                const int wm0 = (w / WAVES_N) * WM, wn0 = (w % WAVES_N) * WN;
+                for (int q = 0; q < Q; ++q)
+                    for (int i = 0; i < MI; ++i)
+                        if (TileA::offset(0, wm0 + i * Op::MB + r, g * KG + 4 * q) !=
+                            TileA::offset(0, wm0 + r, g * KG + 4 * q) + i * Op::MB * TileA::row_stride)
+                            return false;
+                for (int n = 0; n < NI; ++n)
+                    for (int kk = 0; kk < KG; ++kk)
+                        if (TileB::offset(0, g * KG + kk, wn0 + n * Op::NB + r) !=
+                            TileB::offset(0, g * KG, wn0 + (n % PB) * Op::NB + r) + kk * TileB::row_stride +
+                                (n / PB) * PB * Op::NB)
+                            return false;
+            }
+        return true;
+    }
+    static_assert(!PIPE || pipelined_addressing(), "layout does not admit pipelined fragment addressing");
 };
 
 // One direct global->LDS copy instruction (gfx950 global_load_lds_dwordx4):
-// each lane reads 16 bytes at its own global address `src`, and the wavefront
+// each lane reads 16 bytes at its own global address, and the wavefront
 // writes them to LDS at byte address lds_base + 16 * lane; lds_base must be
-// wave-uniform and is taken from M0, which the statement saves and restores
-// (one wait state is required between writing M0 and the copy).  Written as
-// an asm statement because the compiler's own form of this copy makes it wait
-// for every outstanding copy before any later LDS read, which would serialise
+// wave-uniform and is taken from M0 (one wait state is required between
+// writing M0 and the copy).  M0 is declared clobbered, so the compiler keeps
+// nothing of its own there across the statement.  Written as an asm
+// statement because the compiler's own form of this copy makes it wait for
+// every outstanding copy before any later LDS read, which would serialise
 // the copy of the next K tile with the multiply of the current one; as asm
 // the copy is invisible to the compiler's wait-count tracking, so completion
 // is waited for explicitly (wait_vector_memory) before the barrier that
 // publishes the stage.  The "memory" clobber keeps LDS accesses from being
 // moved across it.
-__device__ inline void copy16_to_lds(const void* src, uint32_t lds_base) {
-    uint32_t saved_m0;
+//
+// The address is a wave-uniform 64-bit base in scalar registers plus a
+// 32-bit byte offset per lane (no 64-bit address arithmetic per lane and
+// copy).
+__device__ inline void copy16_to_lds(const void* uniform_base, uint32_t byte_offset, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_nop 0\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved_m0)
-        : "v"(src), "s"(lds_base)
-        : "memory");
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(byte_offset), "s"(uniform_base), "s"(lds_base)
+        : "memory", "m0");
 }
 
 // Direct global->LDS copy of one operand tile.  A stage of an unpadded tile
@@ -313,9 +386,16 @@ struct DirectCopy {
     }
     static_assert(strided_matches(), "strided copies must fetch what the per-copy offsets would");
 
-    int64_t off[STRIDED ? 1 : PER_WAVE];  // element offset(s) of this lane's 16 bytes from the tile origin
-    int64_t round_stride;                 // elements between copy i and i+1 (strided form)
-    uint32_t lds_piece;                   // byte offset of this wavefront's first piece in a stage (uniform)
+    // Byte offsets from the tile origin must fit 31 bits: they are below
+    // Tile::rows * ld elements.  A kernel copies directly only when fits(ld)
+    // holds (a uniform condition) and loads through registers otherwise.
+    __host__ __device__ static constexpr bool fits(int64_t ld) {
+        return ld <= (((int64_t)1 << 31) - 1) / ((int64_t)Tile::rows * (int64_t)sizeof(T));
+    }
+
+    uint32_t off[STRIDED ? 1 : PER_WAVE];  // byte offset(s) of this lane's 16 bytes from the tile origin
+    int64_t round_stride;                  // elements between copy i and i+1 (strided form)
+    uint32_t lds_piece;                    // byte offset of this wavefront's first piece in a stage (uniform)
 
     __device__ DirectCopy(int64_t ld, int wave_uniform, int lane)
         : round_stride((int64_t)ROUND_ROWS * ld), lds_piece(wave_uniform * PIECE * 4) {
@@ -323,12 +403,13 @@ struct DirectCopy {
         for (int i = 0; i < (STRIDED ? 1 : PER_WAVE); ++i) {
             int row = 0, col = 0;
             source((i * WAVES + wave_uniform) * PIECE + 4 * lane, row, col);
-            off[i] = (int64_t)row * ld + (int64_t)col * PER_WORD;
+            off[i] = (uint32_t)(((int64_t)row * ld + (int64_t)col * PER_WORD) * (int64_t)sizeof(T));
         }
     }
 
     // Issue the copies of the tile at `origin` into `stage` of the LDS tile
     // at `lds`; they complete asynchronously (vector memory counter).
+    // Requires fits(ld).
     template <class W>
     __device__ void issue(const T* origin, W* lds, int stage) const {
         static_assert(sizeof(W) == 4, "LDS tiles are addressed in 4-byte words");
@@ -336,8 +417,8 @@ struct DirectCopy {
         const uint32_t base = (uint32_t)(uintptr_t)(lds_word*)lds + lds_piece + stage * (Tile::stage_elems * 4);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
-            const T* src = STRIDED ? origin + i * round_stride + off[0] : origin + off[i];
-            copy16_to_lds(src, base + i * (WAVES * PIECE * 4));
+            const T* row_base = STRIDED ? origin + i * round_stride : origin;
+            copy16_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
         }
     }
 };
@@ -507,9 +588,11 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         // when BK does not divide K) needs zero fill: it is loaded through
         // registers with masks after the multiply, so that no staging
         // registers are live across it.  Both choices are uniform.
-        const DirectCopy<TileA, THREADS> dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
-        const DirectCopy<TileB, THREADS> dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
-        const bool interior = M - m0 >= BM && N - n0 >= BN;
+        using DA = DirectCopy<TileA, THREADS>;
+        using DB = DirectCopy<TileB, THREADS>;
+        const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
+        const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
+        const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
         auto fill = [&](int64_t t, int stage) {
             const int64_t k0 = t * BK;
             if (interior && K - k0 >= BK) {
@@ -524,22 +607,109 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         if (T > 0) fill(0, 0);
         wait_vector_memory();
         __syncthreads();
-        for (int64_t t = 0; t < T; ++t) {
-            const int s = (int)(t & 1);
-            const bool more = t + 1 < T;
-            const bool direct = more && interior && K - (t + 1) * BK >= BK;
-            if (direct) {
-                dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
-                dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+        // Iteration t copies tile t+1 directly iff the workgroup is interior
+        // and tile t+1 is wholly in range (t + 1 < K / BK).
+        const int64_t t_direct = interior ? K / BK - 1 : 0;
+        if constexpr (Cfg::PIPE) {
+            // Software pipeline over the MFMA steps of a K tile (step kk
+            // consumes k = g * KG + kk for lane group g).  The B fragments of
+            // step kk+1 are read while step kk multiplies; the A fragments
+            // come in chunks of four steps (one 16-byte read per row block),
+            // chunk q+1 being read at the start of chunk q.  Steps and chunks
+            // alternate between two register buffers (KG and KG / 4 are
+            // even, so step 0 and chunk 0 of every tile use buffer 0).  The
+            // last step of tile t multiplies after the barrier, while the
+            // first fragments of tile t+1 are read, so the matrix pipe idles
+            // only for the barrier itself.  Every read of stage s completes
+            // before that barrier (it waits for them, and the last step's
+            // registers are needed after it anyway), so the copies issued
+            // after it may overwrite stage s.
+            constexpr int Q = Cfg::Q, PB = Cfg::PB;
+            int a_base[Q], b_base[PB];
+#pragma unroll
+            for (int q = 0; q < Q; ++q) a_base[q] = TileA::offset(0, wm0 + r, g * KG + 4 * q);
+#pragma unroll
+            for (int p = 0; p < PB; ++p) b_base[p] = TileB::offset(0, g * KG, wn0 + p * Op::NB + r);
+            floatx4 fa[2][MI];
+            float fb[2][NI];
+            auto read_a = [&](int buf, int stage, int q) {
+                const float* base = lds_a + stage * TileA::stage_elems + a_base[q];
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    fa[buf][i] = *reinterpret_cast<const floatx4*>(base + i * Op::MB * TileA::row_stride);
+            };
+            auto read_b = [&](int buf, int stage, int kk) {
+#pragma unroll
+                for (int n = 0; n < NI; ++n)
+                    fb[buf][n] = lds_b[stage * TileB::stage_elems + b_base[n % PB] + kk * TileB::row_stride +
+                                       (n / PB) * PB * Op::NB];
+            };
+            auto mma_step = [&](int abuf, int j, int bbuf) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(fa[abuf][i][j], fb[bbuf][n], acc[i][n]);
+            };
+            if (T > 0) {
+                read_a(0, 0, 0);
+                read_b(0, 0, 0);
             }
-            multiply(s);
-            if (more && !direct) {
-                load_tile(t + 1);
-                ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
-                ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
+            for (int64_t t = 0; t < T; ++t) {
+                const int s = (int)(t & 1);
+                const bool more = t + 1 < T;
+                const bool direct = t < t_direct;
+                if (direct) {
+                    dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
+                    dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+                }
+#pragma unroll
+                for (int kk = 0; kk + 1 < KG; ++kk) {
+                    const int q = kk / 4, j = kk % 4;
+                    if (j == 0 && q + 1 < Q) read_a((q + 1) & 1, s, q + 1);
+                    read_b((kk + 1) & 1, s, kk + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_step(q & 1, j, kk & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (more && !direct) {
+                    // Next tile through registers (zero fill), a few slots at
+                    // a time: the staging registers of whole tiles would not
+                    // fit beside the live fragment buffers.
+                    using LoaderA = TileLoader<BM, BK, THREADS, Cfg::VEC>;
+                    using LoaderB = TileLoader<BK, BN, THREADS, Cfg::VEC>;
+                    const int64_t k0 = (t + 1) * BK;
+                    LoaderA::template copy_in_chunks<TileA, 4>(a_tile + k0, lda, M - m0, K - k0, lds_a, s ^ 1, tid);
+                    LoaderB::template copy_in_chunks<TileB, 4>(b_tile + k0 * ldb, ldb, K - k0, N - n0, lds_b, s ^ 1,
+                                                               tid);
+                }
+                wait_vector_memory();
+                __syncthreads();
+                if (more) {
+                    read_a(0, s ^ 1, 0);
+                    read_b(0, s ^ 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mma_step(1, 3, 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            wait_vector_memory();
-            __syncthreads();
+        } else {
+            for (int64_t t = 0; t < T; ++t) {
+                const int s = (int)(t & 1);
+                const bool more = t + 1 < T;
+                const bool direct = t < t_direct;
+                if (direct) {
+                    dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
+                    dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+                }
+                multiply(s);
+                if (more && !direct) {
+                    load_tile(t + 1);
+                    ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
+                    ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
+                }
+                wait_vector_memory();
+                __syncthreads();
+            }
         }
     } else if constexpr (Cfg::STAGES == 2) {
         two_stage_registers();

@@ -290,7 +290,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     };
 
     if constexpr (Cfg::LOAD == kLoadDirect) {
-        const bool interior = M - m0 >= BM && N - n0 >= BN;
+        using DA = DirectCopy<TileA, THREADS, uint16_t>;
+        using DB = DirectCopy<TileB, THREADS, uint16_t>;
+        const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
         if (interior) {
             // S-stage pipeline of direct copies: during the multiply of tile t
             // the copies of tiles t+1 .. t+S-1 are in flight, tile t+S-1 going
@@ -302,8 +304,6 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
             // needs zero fill: it is loaded through registers instead, which
             // makes that iteration wait for everything.
             constexpr int S = Cfg::STAGES;
-            using DA = DirectCopy<TileA, THREADS, uint16_t>;
-            using DB = DirectCopy<TileB, THREADS, uint16_t>;
             constexpr int COPIES = DA::PER_WAVE + DB::PER_WAVE;  // per wavefront and K tile
             const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
             const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);

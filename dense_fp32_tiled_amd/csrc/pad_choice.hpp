@@ -57,14 +57,20 @@ constexpr int pattern_cost_pair(LayoutChoice c, int cols, LdsGeometry g, RowCol2
     return total;
 }
 
+struct AcceptAll {
+    constexpr bool operator()(LayoutChoice) const { return true; }
+};
+
 // Search pads 0, 4, ..., kMaxPad (only 0 unless allow_pad), then swizzles;
-// `cost(choice)` sums a tile's access costs.
-template <class Cost>
-constexpr LayoutChoice choose_layout(Cost cost, int cols, bool allow_pad = true) {
+// `cost(choice)` sums a tile's access costs; only layouts `accept` admits
+// are candidates (the plain layout always is).
+template <class Cost, class Accept = AcceptAll>
+constexpr LayoutChoice choose_layout(Cost cost, int cols, bool allow_pad = true, Accept accept = {}) {
     LayoutChoice best{0, kNoSwizzle};
     int best_cost = cost(best);
     for (int pad = 4; allow_pad && pad <= kMaxPad; pad += 4) {
         const LayoutChoice c{pad, kNoSwizzle};
+        if (!accept(c)) continue;
         const int v = cost(c);
         if (v < best_cost) { best = c; best_cost = v; }
     }
@@ -73,6 +79,7 @@ constexpr LayoutChoice choose_layout(Cost cost, int cols, bool allow_pad = true)
             for (int shift = 0; shift <= 4; ++shift) {
                 if (cols % (unit * (mask + 1)) != 0) continue;
                 const LayoutChoice c{0, Swizzle{unit, shift, mask}};
+                if (!accept(c)) continue;
                 const int v = cost(c);
                 if (v < best_cost) { best = c; best_cost = v; }
             }
@@ -87,13 +94,54 @@ constexpr LayoutChoice choose_layout(Cost cost, int cols, bool allow_pad = true)
 // wavefront instruction (no bank conflicts whatever the layout, and no room
 // for row padding), so only the fragment reads are costed and only unpadded
 // layouts are candidates.
+//
+// `pipelined` (direct copies only): the kernel addresses its fragments as a
+// per-lane base plus compile-time offsets, so that the addresses of a whole
+// K tile cost a few registers: A block row i of chunk q at
+// base_a(q) + i * MB rows, B step kk of block column n at
+// base_b(n % PB) + kk rows + (n / PB) * PB * NB words, PB = min(2, WN / NB).
+// Only layouts whose swizzle keeps that form are candidates
+// (pipelined_a_ok, pipelined_b_ok).
 struct MfmaShape {
     int bm, bn, bk, wm, wn, threads, vec, mb, nb, kb;
     bool direct = false;
+    bool pipelined = false;
     constexpr int kg() const { return bk / kb; }
     constexpr int waves() const { return threads / kWaveLanes; }
     constexpr int waves_n() const { return bn / wn; }
+    constexpr int pb() const { return wn / nb < 2 ? wn / nb : 2; }
 };
+
+constexpr bool pipelined_a_ok(MfmaShape s, LayoutChoice c) {
+    const int stride = s.bk + c.pad;
+    for (int w = 0; w < s.waves(); ++w)
+        for (int l = 0; l < kWaveLanes; ++l) {
+            const int row0 = (w / s.waves_n()) * s.wm + l % s.mb;
+            for (int q = 0; q < s.kg() / 4; ++q) {
+                const int col = (l / s.mb) * s.kg() + 4 * q;
+                const int64_t base = layout_word(c, s.bk, row0, col);
+                for (int i = 1; i < s.wm / s.mb; ++i)
+                    if (layout_word(c, s.bk, row0 + i * s.mb, col) != base + (int64_t)i * s.mb * stride) return false;
+            }
+        }
+    return true;
+}
+
+constexpr bool pipelined_b_ok(MfmaShape s, LayoutChoice c) {
+    const int stride = s.bn + c.pad, pb = s.pb();
+    for (int w = 0; w < s.waves(); ++w)
+        for (int l = 0; l < kWaveLanes; ++l) {
+            const int row0 = (l / s.nb) * s.kg(), col0 = (w % s.waves_n()) * s.wn + l % s.nb;
+            for (int n = 0; n < s.wn / s.nb; ++n) {
+                const int64_t base = layout_word(c, s.bn, row0, col0 + (n % pb) * s.nb);
+                for (int kk = 0; kk < s.kg(); ++kk)
+                    if (layout_word(c, s.bn, row0 + kk, col0 + n * s.nb) !=
+                        base + (int64_t)kk * stride + (int64_t)(n / pb) * pb * s.nb)
+                        return false;
+            }
+        }
+    return true;
+}
 
 // Every A access of one K tile: fragment reads (16-byte, KG/4 per block row
 // of every wavefront) and the cooperative stores (vec-wide).
@@ -151,10 +199,12 @@ constexpr int mfma_b_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
 }
 
 constexpr LayoutChoice mfma_layout_a(MfmaShape s, LdsGeometry g) {
-    return choose_layout([=](LayoutChoice c) { return mfma_a_cost(s, c, g); }, s.bk, !s.direct);
+    return choose_layout([=](LayoutChoice c) { return mfma_a_cost(s, c, g); }, s.bk, !s.direct,
+                         [=](LayoutChoice c) { return !s.pipelined || pipelined_a_ok(s, c); });
 }
 constexpr LayoutChoice mfma_layout_b(MfmaShape s, LdsGeometry g) {
-    return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn, !s.direct);
+    return choose_layout([=](LayoutChoice c) { return mfma_b_cost(s, c, g); }, s.bn, !s.direct,
+                         [=](LayoutChoice c) { return !s.pipelined || pipelined_b_ok(s, c); });
 }
 
 // ---- matrix-core kernel with 16-bit inputs (bf16 / fp16) ------------------------

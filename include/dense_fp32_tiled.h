@@ -77,7 +77,11 @@ typedef enum {
     GEMM_VARIANT_MFMA_64_DIRECT = 12,       /* 64x64x16 tile, 4 waves of 32x32, direct copies (few output tiles) */
     GEMM_VARIANT_MFMA_256x256_DIRECT = 13,  /* 256x256x16 tile, 8 waves of 128x64 (2 per SIMD), direct copies */
     GEMM_VARIANT_MFMA_256x256_W4_DIRECT = 14, /* 256x256x16 tile, 4 waves of 128x128 (1 per SIMD), direct copies */
-    GEMM_VARIANT_COUNT = 15
+    GEMM_VARIANT_MFMA_256x256_PIPE = 15,      /* as MFMA_256x256_DIRECT, multiply pipelined in 4-k chunks across the barrier */
+    GEMM_VARIANT_MFMA_256x256_BK32_PIPE = 16, /* as MFMA_256x256_PIPE with BK = 32 (128 KiB of LDS) */
+    GEMM_VARIANT_MFMA16_256x256_DIRECT = 17,  /* as MFMA_256x256_DIRECT with v_mfma_f32_16x16x4_f32 */
+    GEMM_VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18, /* 16x16x4, 256x256x32 tile, 4 waves of 128x128, pipelined */
+    GEMM_VARIANT_COUNT = 19
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of

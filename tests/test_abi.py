@@ -100,8 +100,9 @@ LAYOUT_KEYS = ("a_pad", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_pad", "b_s
 def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
     base = dft.gemm_f32_tile_config(dft.VARIANT_MFMA)
     auto = dft.gemm_f32_tile_config(dft.VARIANT_AUTO)  # AUTO describes its large-problem choice
-    big = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_256x256_DIRECT)
-    assert auto | {"variant": dft.VARIANT_MFMA_256x256_DIRECT} == big
+    big = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_256x256_BK32_PIPE)
+    assert auto | {"variant": dft.VARIANT_MFMA_256x256_BK32_PIPE} == big
+    assert big["bk"] == 32 and big["direct_to_lds"] == 2
     s1 = dft.gemm_f32_tile_config(dft.VARIANT_MFMA_STAGES1)
     assert s1["stages"] == 1 and s1["barriers_per_tile"] == 2
     assert s1 | {"variant": 1, "stages": 2, "barriers_per_tile": 1, "lds_bytes": base["lds_bytes"]} == base
@@ -120,13 +121,14 @@ def test_ablations_differ_from_the_default_in_one_choice(gemm_lib):
 
 def test_auto_variant_selection(gemm_lib):
     av = dft.gemm_f32_auto_variant
-    # measured fastest on one MI355X (256 CUs) for each of these shapes
-    assert av(4096, 4096, 4096, 256) == dft.VARIANT_MFMA_256x256_DIRECT   # 256 tiles of 256x256: 1 full round
-    assert av(8192, 8192, 8192, 256) == dft.VARIANT_MFMA_256x256_DIRECT
-    assert av(4096, 4096, 1024, 256) == dft.VARIANT_MFMA_256x256_DIRECT
-    assert av(4096, 2048, 4096, 256) == dft.VARIANT_MFMA_DIRECT           # 256 tiles of 256x128, 128 of 256x256
-    assert av(6144, 6144, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 1152 tiles: 4.5 rounds vs 2304 = 9
-    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 128 big tiles, 256 of 128x128
+    # measured fastest (or within 3 % of it) on one MI355X (256 CUs) for each of these shapes
+    assert av(4096, 4096, 4096, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 256 tiles of 256x256: 1 full round
+    assert av(8192, 8192, 8192, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE
+    assert av(4096, 4096, 1024, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE
+    assert av(4096, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 512 tiles of 128x128: two per CU
+    assert av(8192, 1024, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 256 tiles of 256x128: one per CU
+    assert av(6144, 6144, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2304 tiles: 9 full rounds
+    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 256 of 128x128 vs 1024 of 64x64
     assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_DIRECT
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_DIRECT         # 512 tiles of 64x64
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_64_DIRECT        # deep K, 128 small tiles

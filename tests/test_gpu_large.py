@@ -93,3 +93,75 @@ def test_splitk_offsets_beyond_2_31_elements(big):
     torch.cuda.synchronize()
     del ws
     check(torch, c, cref)
+
+
+# Leading dimensions so wide that a tile's byte span exceeds 31 bits: the
+# direct copies address a tile as a uniform base plus a 32-bit per-lane byte
+# offset, so such launches must load every tile through registers instead.
+# A: 8,388,612 floats per row (>= 2**31 bytes for any tile of 64 rows);
+# B: 33,554,436 floats per row (>= 2**31 bytes for a 16-row K tile).
+WIDE_LDA = (1 << 23) + 4
+WIDE_LDB = (1 << 25) + 4
+WIDE_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
+                 dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_PIPE,
+                 dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
+
+
+@pytest.fixture(scope="module")
+def torch_dev(gemm_lib):
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def wide_operands(torch, a, b, lda, ldb, dtype=None):
+    """Device copies of a and b embedded with leading dimensions lda / ldb
+    (NaN in the gaps), built on the device to keep host memory small."""
+    (M, K), N = a.shape, b.shape[1]
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    if dtype is not None:
+        ta, tb = ta.to(dtype), tb.to(dtype)
+    abuf = torch.full((M * lda,), float("nan"), device="cuda", dtype=ta.dtype)
+    bbuf = torch.full((K * ldb,), float("nan"), device="cuda", dtype=tb.dtype)
+    abuf.view(M, lda)[:, :K] = ta
+    bbuf.view(K, ldb)[:, :N] = tb
+    return abuf, bbuf
+
+
+@pytest.mark.parametrize("variant", WIDE_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in WIDE_VARIANTS])
+@pytest.mark.parametrize("wide", ["a", "b"])
+def test_wide_leading_dimension_falls_back_to_registers(wide, variant, torch_dev):
+    torch = torch_dev
+    M, N, K = 300, 260, 100  # the first 256 x 256 (and smaller) tiles are interior
+    a, b = workloads.make_operands(M, N, K, "integer", 515)
+    cref, _ = oracle.reference(a, b)
+    lda, ldb = (WIDE_LDA, N) if wide == "a" else (K, WIDE_LDB)
+    abuf, bbuf = wide_operands(torch, a, b, lda, ldb)
+    c = torch.full((M, N), float("nan"), device="cuda")
+    st = dft.gemm_f32_ex(M, N, K, abuf.data_ptr(), lda, bbuf.data_ptr(), ldb, c.data_ptr(), N,
+                         torch.cuda.current_stream().cuda_stream, variant)
+    assert st == dft.GEMM_OK, dft.gemm_f32_status_string(st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), cref)
+    del abuf, bbuf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wide", ["a", "b"])
+def test_wide_leading_dimension_bf16(wide, torch_dev):
+    torch = torch_dev
+    M, N, K = 300, 260, 136
+    a, b = workloads.make_operands(M, N, K, "integer", 516)
+    (abits, af), (bbits, bf) = workloads.to_16bit(a, "bf16"), workloads.to_16bit(b, "bf16")
+    cref, _ = oracle.reference(af, bf)
+    lda, ldb = (WIDE_LDA, N) if wide == "a" else (K, WIDE_LDB)
+    abuf, bbuf = wide_operands(torch, af, bf, lda, ldb, dtype=torch.bfloat16)
+    c = torch.full((M, N), float("nan"), device="cuda")
+    st = dft.gemm_mixed_f32(dft.INPUT_BF16, M, N, K, abuf.data_ptr(), lda, bbuf.data_ptr(), ldb, c.data_ptr(), N,
+                            torch.cuda.current_stream().cuda_stream, dft.MIXED_AUTO)
+    assert st == dft.GEMM_OK, dft.gemm_f32_status_string(st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), cref)
+    del abuf, bbuf
+    torch.cuda.empty_cache()

@@ -41,7 +41,8 @@ def random_cases(count: int, seed: int):
         yield M, N, K, pad, shift
 
 
-RANDOM_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_DIRECT,
+RANDOM_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_PIPE,
+                   dft.VARIANT_MFMA_256x256_BK32_PIPE, dft.VARIANT_MFMA_DIRECT,
                    dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA, dft.VARIANT_VALU]
 
 

@@ -30,14 +30,20 @@ def test_every_kernel_is_spill_free(report):
 
 
 def test_default_kernels_keep_their_occupancy(report):
-    # fp32 256x256 direct-copy kernel (AUTO for large problems): one 8-wave workgroup per CU, 64 KiB of LDS
-    fp32_big = kernels(report, "MfmaCfgILi256ELi256ELi16ELi128ELi64E")
+    # fp32 256x256x32 pipelined kernel (AUTO for large problems): one 8-wave workgroup per CU, 128 KiB of LDS
+    fp32_big = kernels(report, "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E")
     assert len(fp32_big) == 1
     (r,) = fp32_big.values()
+    assert r["occupancy"] == 2 and r["lds"] == 128 * 1024
+    # its non-pipelined 256x256x16 ablation: same occupancy, 64 KiB of LDS
+    fp32_plain = kernels(report, "MfmaCfgILi256ELi256ELi16ELi128ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
+                                 "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0E")
+    assert len(fp32_plain) == 1
+    (r,) = fp32_plain.values()
     assert r["occupancy"] == 2 and r["lds"] == 64 * 1024
     # fp32 256x128 direct-copy kernel (AUTO when 256x256 tiles round badly): 4 waves per SIMD = two workgroups
     fp32_default = kernels(report, "MfmaCfgILi256ELi128ELi16ELi64ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
-                                   "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1EE")
+                                   "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0EE")
     assert len(fp32_default) == 1
     (r,) = fp32_default.values()
     assert r["occupancy"] == 4 and r["lds"] == 48 * 1024

@@ -128,7 +128,9 @@ def degree(c, width, words):
 
 MFMA_LAYOUT_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32,
                         dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_64_DIRECT,
-                        dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT]
+                        dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT,
+                        dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
 
 
 @pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
@@ -164,7 +166,7 @@ def test_direct_copy_layouts_are_unpadded(gemm_lib):
     # 16x16x4 blocks: the search through registers pads B, the direct one cannot
     assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 16, 4, 0)[2][0] == 4
     assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 32, 1, 1)[0] == dft.GEMM_ERR_INVALID_DIM
-    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 32, 4, 2)[0] == dft.GEMM_ERR_INVALID_DIM
+    assert dft.gemm_lds_choose_mfma_layout(256, 128, 16, 64, 64, 32, 4, 3)[0] == dft.GEMM_ERR_INVALID_DIM
 
 
 def test_layout_search_rejects_bad_shapes(gemm_lib):
