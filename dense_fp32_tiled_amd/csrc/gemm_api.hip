@@ -481,22 +481,22 @@ int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int spli
 // loads through registers, for unaligned operands.
 template <int TYPE, int VEC>
 using Mixed256x128 = MixedCfg<TYPE, 256, 128, 32, 64, 64, 32, layouts::x32_256x128x32::A, layouts::x32_256x128x32::B,
-                              VEC, 4, 2, false>;
+                              VEC, 4, 2, kPipeNone>;
 template <int TYPE, int VEC>
 using Mixed256x256 = MixedCfg<TYPE, 256, 256, 32, 128, 64, 32, layouts::x32_256x256x32::A, layouts::x32_256x256x32::B,
                               VEC, 2>;
 template <int TYPE, int VEC>
 using Mixed256x128Bk64 = MixedCfg<TYPE, 256, 128, 64, 64, 64, 32, layouts::x32_256x128x64::A,
-                                  layouts::x32_256x128x64::B, VEC, 2>;
+                                  layouts::x32_256x128x64::B, VEC, 2, 2, kPipeAcrossTiles>;
 template <int TYPE, int VEC>
 using Mixed256x256S3 = MixedCfg<TYPE, 256, 256, 32, 128, 64, 32, layouts::x32_256x256x32::A,
-                                layouts::x32_256x256x32::B, VEC, 2, 3>;
+                                layouts::x32_256x256x32::B, VEC, 2, 3, kPipeAcrossTiles>;
 template <int TYPE, int VEC>
 using Mixed256x256Bk64 = MixedCfg<TYPE, 256, 256, 64, 128, 64, 32, layouts::x32_256x256x64::A,
-                                  layouts::x32_256x256x64::B, VEC, 2, 2>;
+                                  layouts::x32_256x256x64::B, VEC, 2, 2, kPipeAcrossTiles>;
 template <int TYPE, int VEC>
 using Mixed128x128Bk64 = MixedCfg<TYPE, 128, 128, 64, 64, 64, 32, layouts::x32_128x128x64::A,
-                                  layouts::x32_128x128x64::B, VEC, 4>;
+                                  layouts::x32_128x128x64::B, VEC, 4, 2, kPipeAcrossTiles>;
 
 template <class Cfg>
 hipError_t launch_mixed(const Args& a, hipStream_t stream) {

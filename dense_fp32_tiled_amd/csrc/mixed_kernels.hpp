@@ -51,8 +51,8 @@ struct Mfma16Op<TYPE, 32> {
     }
     __device__ static int out_row(int lane, int v) { return MfmaOp<32, 2>::out_row(lane, v); }
     // k-group of a lane and first column of its 16-lane group within the block
-    __device__ static int kgroup(int lane) { return lane / 32; }
-    __device__ static int col_base(int lane) { return 16 * ((lane / 16) % 2); }
+    __host__ __device__ static constexpr int kgroup(int lane) { return lane / 32; }
+    __host__ __device__ static constexpr int col_base(int lane) { return 16 * ((lane / 16) % 2); }
 };
 
 template <int TYPE>
@@ -68,8 +68,8 @@ struct Mfma16Op<TYPE, 16> {
                                                           0, 0, 0);
     }
     __device__ static int out_row(int lane, int v) { return MfmaOp<16, 4>::out_row(lane, v); }
-    __device__ static int kgroup(int lane) { return lane / 16; }
-    __device__ static int col_base(int) { return 0; }
+    __host__ __device__ static constexpr int kgroup(int lane) { return lane / 16; }
+    __host__ __device__ static constexpr int col_base(int) { return 0; }
 };
 
 // A tile of a row-major 16-bit matrix, rows [row0, row0 + ROWS) and columns
@@ -121,6 +121,54 @@ struct TileLoader16 {
         }
     }
 
+    // Masked load and LDS store of the whole tile, at most MAX_CH slots at a
+    // time (the staging registers of those slots only), for kernels that
+    // cannot hold all PER_THREAD slots beside their other live registers.
+    template <class Tile, int MAX_CH>
+    __device__ static void copy_in_chunks(const uint16_t* __restrict__ tile, int64_t ld, int64_t rows_left,
+                                          int64_t cols_left, uint32_t* lds, int stage, int tid) {
+        static_assert(Tile::rows == ROWS && 2 * Tile::cols == COLS, "LDS tile shape mismatch");
+        constexpr int CH = MAX_CH < PER_THREAD ? MAX_CH : PER_THREAD;
+        static_assert(PER_THREAD % CH == 0, "chunks must split the slots evenly");
+        const bool full = rows_left >= ROWS && cols_left >= COLS;
+#pragma unroll 1
+        for (int i0 = 0; i0 < PER_THREAD; i0 += CH) {
+            uint32_t w[CH][VEC == 8 ? 4 : 1];
+            uint16_t h[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int r = slot_row(tid, i0 + i), c = slot_col(tid, i0 + i);
+                const uint16_t* p = tile + (int64_t)r * ld + c;
+                if constexpr (VEC == 8) {
+                    if (full) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[i][e] = x[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t lo = (r < rows_left && c + 2 * e < cols_left) ? p[2 * e] : 0u;
+                            const uint32_t hi = (r < rows_left && c + 2 * e + 1 < cols_left) ? p[2 * e + 1] : 0u;
+                            w[i][e] = lo | (hi << 16);
+                        }
+                    }
+                } else {
+                    h[i] = (r < rows_left && c < cols_left) ? *p : (uint16_t)0;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int r = slot_row(tid, i0 + i), c = slot_col(tid, i0 + i);
+                if constexpr (VEC == 8) {
+                    *reinterpret_cast<u32x4*>(lds + Tile::offset(stage, r, c / 2)) =
+                        u32x4{w[i][0], w[i][1], w[i][2], w[i][3]};
+                } else {
+                    reinterpret_cast<uint16_t*>(lds + Tile::offset(stage, r, c / 2))[c % 2] = h[i];
+                }
+            }
+        }
+    }
+
     // Element (r, c) -> 16-bit half (c % 2) of word Tile::offset(stage, r, c / 2).
     template <class Tile>
     __device__ void store(uint32_t* lds, int stage, int tid) const {
@@ -140,8 +188,17 @@ struct TileLoader16 {
     }
 };
 
+// PIPELINE: 0, fragments read next to their MFMAs; 1, the fragments of MFMA
+// step st+1 read during the MFMAs of step st (twice the fragment
+// registers); 2, as 1 and across K tiles too: the last step of tile t
+// multiplies after the barrier, while the first fragments of tile t+1 are
+// read (direct-copy path; it shortens the time the copies of tile t+1 have
+// before the barrier waits for them, so it pays with four steps per tile or
+// three stages).
+enum PipelineLevel { kPipeNone = 0, kPipeSteps = 1, kPipeAcrossTiles = 2 };
+
 template <int TYPE_, int BM_, int BN_, int BK_, int WM_, int WN_, int MB_, class LayA, class LayB, int VEC_,
-          int MIN_WAVES_, int STAGES_ = 2, bool PIPELINE_ = true>
+          int MIN_WAVES_, int STAGES_ = 2, int PIPELINE_ = kPipeSteps>
 struct MixedCfg {
     using Op = Mfma16Op<TYPE_, MB_>;
     static constexpr int TYPE = TYPE_;
@@ -151,9 +208,7 @@ struct MixedCfg {
     static constexpr int ORDER = kXcdGroupedOrder;
     static constexpr int LOAD = VEC == 8 ? kLoadDirect : kLoadRegisters;
     static constexpr int STAGES = STAGES_;  // LDS stages of the direct-copy pipeline (register paths use two)
-    // Read the fragments of MFMA step st+1 during the MFMAs of step st (twice
-    // the fragment registers); off where the register budget has no room.
-    static constexpr bool PIPELINE = PIPELINE_;
+    static constexpr int PIPELINE = PIPELINE_;
     static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -165,6 +220,37 @@ struct MixedCfg {
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
     static_assert(BK % Op::KB == 0, "whole MFMA steps per K tile");
     static_assert(LayA::pad == 0 && LayB::pad == 0, "direct copies need unpadded rows");
+    static_assert(PIPELINE != kPipeAcrossTiles || STEPS % 2 == 0,
+                  "across tiles, steps alternate between two fragment buffers");
+
+    // Fragment addresses as per-lane bases plus compile-time offsets: A block
+    // row i of step st at a_base(st) + i * MB rows, B block column n at
+    // b_base(n) + (st * KB + 4 rr) rows for its two transposing reads rr.
+    static constexpr bool based_addressing() {
+        for (int w = 0; w < WAVES_M * WAVES_N; ++w)
+            for (int l = 0; l < kWave; ++l) {
+                const int g = l / Op::MB, r = l % Op::MB;
+                const int wm0 = (w / WAVES_N) * WM, wn0 = (w % WAVES_N) * WN;
+                const int tr_row = 8 * Op::kgroup(l) + (l % 16) / 4, tr_col = Op::col_base(l) + 4 * (l % 4);
+                for (int st = 0; st < STEPS; ++st) {
+                    const int col = st * (Op::KB / 2) + 4 * g;
+                    for (int i = 0; i < MI; ++i)
+                        if (TileA::offset(0, wm0 + i * Op::MB + r, col) !=
+                            TileA::offset(0, wm0 + r, col) + i * Op::MB * TileA::row_stride)
+                            return false;
+                }
+                for (int n = 0; n < NI; ++n) {
+                    const int col = (wn0 + n * Op::NB + tr_col) / 2;
+                    for (int st = 0; st < STEPS; ++st)
+                        for (int rr = 0; rr < 2; ++rr)
+                            if (TileB::offset(0, st * Op::KB + tr_row + 4 * rr, col) !=
+                                TileB::offset(0, tr_row, col) + (st * Op::KB + 4 * rr) * TileB::row_stride)
+                                return false;
+                }
+            }
+        return true;
+    }
+    static_assert(based_addressing(), "layout does not admit base-plus-offset fragment addressing");
 };
 
 template <class Cfg>
@@ -221,17 +307,21 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     typedef __attribute__((address_space(3))) shortx4 lds_short4;
     // Fragments of one MFMA step: A with 16-byte reads, B with two transposing
     // 8-byte reads per block column.
-    auto read_fragments = [&](int stage, int st, u32x4 (&af)[MI], u32x4 (&bf)[NI]) {
+    int a_base[Cfg::STEPS], b_base[NI];
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-            af[i] = *reinterpret_cast<const u32x4*>(
-                lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, st * (Op::KB / 2) + 4 * g));
+    for (int st = 0; st < Cfg::STEPS; ++st) a_base[st] = TileA::offset(0, wm0 + r, st * (Op::KB / 2) + 4 * g);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) b_base[n] = TileB::offset(0, tr_row, (wn0 + n * Op::NB + tr_col) / 2);
+    auto read_fragments = [&](int stage, int st, u32x4 (&af)[MI], u32x4 (&bf)[NI]) {
+        const uint32_t* a = lds_a + stage * TileA::stage_elems + a_base[st];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const u32x4*>(a + i * Op::MB * TileA::row_stride);
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
             shortx4 half[2];
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const int word = TileB::offset(stage, st * Op::KB + tr_row + 4 * rr, (wn0 + n * Op::NB + tr_col) / 2);
+                const int word = stage * TileB::stage_elems + b_base[n] + (st * Op::KB + 4 * rr) * TileB::row_stride;
                 half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_word*)lds_b + word));
             }
             const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
@@ -244,7 +334,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     // scheduling barriers keep the compiler from sinking the reads back next
     // to their MFMAs (which it does to save registers).
     auto multiply = [&](int stage) {
-        if constexpr (Cfg::PIPELINE) {
+        if constexpr (Cfg::PIPELINE != kPipeNone) {
             u32x4 af[2][MI], bf[2][NI];
             read_fragments(stage, 0, af[0], bf[0]);
 #pragma unroll
@@ -320,25 +410,76 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
             wait_vector_memory();
             __syncthreads();
             int s = 0;  // stage of tile t
-            for (int64_t t = 0; t < T; ++t) {
-                const int ps = s == 0 ? S - 1 : s - 1;  // stage of tile t + S - 1
-                const int64_t nt = t + S - 1;
-                const bool direct = nt < TF;
-                if (direct) {
-                    dma_a.issue(a_tile + nt * BK, lds_a, ps);
-                    dma_b.issue(b_tile + nt * BK * ldb, lds_b, ps);
+            if constexpr (Cfg::PIPELINE == kPipeAcrossTiles) {
+                // The last step of tile t multiplies after the barrier that
+                // ends iteration t, from registers read before it, while the
+                // fragments of step 0 of tile t+1 are read.  A ragged last
+                // K tile goes through registers a few slots at a time, the
+                // last step's fragments being live.
+                u32x4 af[2][MI], bf[2][NI];
+                auto mma_step = [&](const u32x4 (&a)[MI], const u32x4 (&b)[NI]) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+#pragma unroll
+                        for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(a[i], b[n], acc[i][n]);
+                };
+                if (T > 0) read_fragments(0, 0, af[0], bf[0]);
+                for (int64_t t = 0; t < T; ++t) {
+                    const int ps = s == 0 ? S - 1 : s - 1;  // stage of tile t + S - 1
+                    const int ns = s + 1 == S ? 0 : s + 1;  // stage of tile t + 1
+                    const int64_t nt = t + S - 1;
+                    const bool direct = nt < TF;
+                    if (direct) {
+                        dma_a.issue(a_tile + nt * BK, lds_a, ps);
+                        dma_b.issue(b_tile + nt * BK * ldb, lds_b, ps);
+                    }
+#pragma unroll
+                    for (int st = 0; st + 1 < Cfg::STEPS; ++st) {
+                        read_fragments(s, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma_step(af[st & 1], bf[st & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (nt < T && !direct) {
+                        // ragged last K tile through registers, a few slots at a time
+                        using LoaderA = TileLoader16<BM, BK, THREADS, Cfg::VEC>;
+                        using LoaderB = TileLoader16<BK, BN, THREADS, Cfg::VEC>;
+                        const int64_t k0 = nt * BK;
+                        LoaderA::template copy_in_chunks<TileA, 2>(a_tile + k0, lda, M - m0, K - k0, lds_a, ps, tid);
+                        LoaderB::template copy_in_chunks<TileB, 2>(b_tile + k0 * ldb, ldb, K - k0, N - n0, lds_b, ps, tid);
+                    }
+                    if (direct)
+                        wait_vector_memory_at_most<(S - 2) * COPIES>();
+                    else
+                        wait_vector_memory();
+                    __syncthreads();
+                    if (t + 1 < T) read_fragments(ns, 0, af[0], bf[0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_step(af[1], bf[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    s = ns;
                 }
-                multiply(s);
-                if (nt < T && !direct) {
-                    load_tile(nt);
-                    store_tile(ps);
+            } else {
+                for (int64_t t = 0; t < T; ++t) {
+                    const int ps = s == 0 ? S - 1 : s - 1;  // stage of tile t + S - 1
+                    const int64_t nt = t + S - 1;
+                    const bool direct = nt < TF;
+                    if (direct) {
+                        dma_a.issue(a_tile + nt * BK, lds_a, ps);
+                        dma_b.issue(b_tile + nt * BK * ldb, lds_b, ps);
+                    }
+                    multiply(s);
+                    if (nt < T && !direct) {
+                        load_tile(nt);
+                        store_tile(ps);
+                    }
+                    if (direct)
+                        wait_vector_memory_at_most<(S - 2) * COPIES>();
+                    else
+                        wait_vector_memory();
+                    __syncthreads();
+                    s = s + 1 == S ? 0 : s + 1;
                 }
-                if (direct)
-                    wait_vector_memory_at_most<(S - 2) * COPIES>();
-                else
-                    wait_vector_memory();
-                __syncthreads();
-                s = s + 1 == S ? 0 : s + 1;
             }
         } else {
             two_stage_registers();
