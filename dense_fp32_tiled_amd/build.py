@@ -81,6 +81,24 @@ def build_all() -> list[Path]:
     return [build(LIB, sources=SOURCES), build(PROBE_LIB, sources=PROBE_SOURCES)]
 
 
+def device_assembly(source: Path | None = None) -> str:
+    """The gfx950 assembly hipcc emits for the library's device code (the
+    same flags as the build), as text."""
+    import tempfile
+
+    generate_layouts()
+    with tempfile.TemporaryDirectory() as tmp:
+        out = Path(tmp) / "device.s"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-S", f"-I{ROOT / 'include'}", f"-I{CSRC}",
+               str(source or SOURCES[0]), "-o", str(out)]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            sys.stderr.write(proc.stderr)
+            raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
+        return out.read_text()
+
+
 def resource_report(source: Path | None = None) -> dict[str, dict[str, int]]:
     """The compiler's per-kernel resource usage for the library's device code
     (hipcc -Rpass-analysis=kernel-resource-usage): {mangled kernel name:

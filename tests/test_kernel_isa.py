@@ -1,0 +1,56 @@
+"""Properties of the compiled kernels read from their gfx950 assembly
+(hipcc -S on the library's device code).  CPU only: the code is
+cross-compiled for gfx950 here.
+
+* The VALU inner product is fully unrolled: one basic block holds all
+  BK x TM x TN = 16 x 8 x 8 fused multiply-adds of a K tile (the pages'
+  "Unrolling the inner dot loop", whose loop-control overhead this removes).
+* The default MFMA kernel's K tile is straight-line code: every MFMA of a
+  tile but the last step's (which runs after the barrier) sits in one block.
+* No packed fp32 instruction (v_pk_fma_f32, v_pk_mul_f32, v_pk_add_f32) is
+  emitted anywhere: the build disables them."""
+
+from __future__ import annotations
+
+import re
+
+import pytest
+
+from dense_fp32_tiled_amd import build
+
+
+@pytest.fixture(scope="module")
+def functions():
+    text = build.device_assembly()
+    labels = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w+):", text, re.M)]
+    out = {}
+    for k, (pos, name) in enumerate(labels):
+        end = labels[k + 1][0] if k + 1 < len(labels) else len(text)
+        out[name] = text[pos:end]
+    return text, out
+
+
+def max_per_block(body: str, pattern: str) -> int:
+    blocks = re.split(r"^\.LBB\d+_\d+:", body, flags=re.M)
+    return max(len(re.findall(pattern, b, re.M)) for b in blocks)
+
+
+def test_valu_inner_product_is_fully_unrolled(functions):
+    _, funcs = functions
+    valu = {n: b for n, b in funcs.items() if "gemm_valu_kernel" in n}
+    assert len(valu) == 2  # 16-byte and 4-byte load paths
+    for name, body in valu.items():
+        assert max_per_block(body, r"^\s+v_(?:fmac|fma)_f32") == 16 * 8 * 8, name
+
+
+def test_default_mfma_tile_is_straight_line(functions):
+    _, funcs = functions
+    # 256x256x32, 8 waves of 128x64: 4 x 2 blocks x 16 steps = 128 MFMAs per K tile
+    default = [b for n, b in funcs.items() if "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E" in n]
+    assert len(default) == 1
+    assert max_per_block(default[0], r"^\s+v_mfma_f32_32x32x2_f32") >= 128 - 8
+
+
+def test_no_packed_fp32_instructions(functions):
+    text, _ = functions
+    assert not re.search(r"v_pk_(?:fma|mul|add)_f32", text)

@@ -88,3 +88,20 @@ def test_oracle_builds_warning_free(tmp_path):
                           str(oracle._SRC), "-o", str(tmp_path / "lib.so"), "-lm"],
                          capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
+
+
+def test_config1_single_thread_is_well_under_a_second(oracle_lib):
+    """The 128^3 product on one host thread: the oracle's own speed bar (best
+    of three runs, so a busy host does not fail it)."""
+    import time
+
+    import workloads
+
+    cfg = workloads.CONFIG_BY_NAME["small128"]
+    a, b = workloads.config_operands(cfg)
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.reference(a, b, threads=1, lib=oracle_lib)
+        best = min(best, time.perf_counter() - t0)
+    assert best < 0.5, best
