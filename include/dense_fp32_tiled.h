@@ -77,8 +77,10 @@ typedef enum {
     GEMM_VARIANT_MFMA_64_DIRECT = 12,       /* 64x64x16 tile, 4 waves of 32x32, direct copies (few output tiles) */
     GEMM_VARIANT_MFMA_256x256_DIRECT = 13,  /* 256x256x16 tile, 8 waves of 128x64 (2 per SIMD), direct copies */
     GEMM_VARIANT_MFMA_256x256_W4_DIRECT = 14, /* 256x256x16 tile, 4 waves of 128x128 (1 per SIMD), direct copies */
-    GEMM_VARIANT_MFMA_256x256_PIPE = 15,      /* as MFMA_256x256_DIRECT, multiply pipelined in 4-k chunks across the barrier */
-    GEMM_VARIANT_MFMA_256x256_BK32_PIPE = 16, /* as MFMA_256x256_PIPE with BK = 32 (128 KiB of LDS) */
+    GEMM_VARIANT_MFMA_256x256_PIPE = 15,      /* as MFMA_256x256_DIRECT, multiply software-pipelined (fragments one
+                                                 MFMA step ahead, the last step after the K-tile barrier) */
+    GEMM_VARIANT_MFMA_256x256_BK32_PIPE = 16, /* as MFMA_256x256_PIPE with BK = 32 (128 KiB of LDS): AUTO's choice
+                                                 for large problems */
     GEMM_VARIANT_MFMA16_256x256_DIRECT = 17,  /* as MFMA_256x256_DIRECT with v_mfma_f32_16x16x4_f32 */
     GEMM_VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18, /* 16x16x4, 256x256x32 tile, 4 waves of 128x128, pipelined */
     GEMM_VARIANT_COUNT = 19
@@ -110,7 +112,10 @@ typedef struct {
     int32_t mfma_block;          /* MFMA block size (32 or 16), 0 for the VALU variant */
     int32_t xcd_tile_order;      /* 1 if workgroups are mapped to tiles in the XCD-grouped order */
     int32_t direct_to_lds;       /* 1 if in-range tiles are copied global->LDS without registers (16 bytes
-                                    per lane, LDS rows unpadded); edge tiles still go through registers */
+                                    per lane, LDS rows unpadded); edge tiles, and launches whose tile byte
+                                    span exceeds 31 bits (a very wide lda or ldb), still go through
+                                    registers; 2 if, in addition, the multiply is software-pipelined
+                                    across the K-tile barrier (fragments read one MFMA step ahead) */
     int32_t elem_bytes;          /* bytes per A / B element: 4 (fp32), 2 (bf16 / fp16, gemm_mixed_f32);
                                     LDS tile fields count 4-byte words, so a row of a 16-bit tile holds
                                     2 * cols elements */
@@ -189,13 +194,15 @@ int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
- * `num_cus` compute units: among MFMA_256x256_DIRECT, MFMA_DIRECT (256x128),
- * the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
+ * `num_cus` compute units: among MFMA_256x256_BK32_PIPE, MFMA_DIRECT
+ * (256x128), the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
  * MFMA_64_DIRECT (64x64), the one with the highest rate estimate, its
- * full-chip rate (140, 137, 130, 110 TFLOP/s) times the wave quantisation of
- * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus); a larger tile
- * wins when within 2 %.  Pure host call.  Returns a gemm_variant, or GEMM_ERR_INVALID_DIM for negative
- * sizes or num_cus < 1. */
+ * full-chip rate (145, 144, 144, 128 TFLOP/s) times the wave quantisation of
+ * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus), times 0.88 for
+ * the 256x128 and 128x128 kernels when there are fewer tiles than two per
+ * CU (they are built for two workgroups per CU); a larger tile wins when
+ * within 2 %.  Pure host call.  Returns a gemm_variant, or
+ * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
 /* ---- Host-side layout model -------------------------------------------------
@@ -237,7 +244,10 @@ int32_t gemm_lds_conflict_degree(const int64_t *lane_words, int32_t lanes,
  * 16) and global loads of `vec` floats (1 or 4) through registers, or, with
  * direct = 1 (vec must be 4), direct global->LDS copies: their LDS writes are
  * contiguous and cannot be padded, so only the fragment reads are costed and
- * only unpadded layouts are candidates.  Writes {pad, swz_unit, swz_shift,
+ * only unpadded layouts are candidates.  direct = 2 is the pipelined kernels'
+ * search (bk / (64 / mb) a multiple of 8): as 1, and only layouts whose
+ * fragment addresses are a per-lane base plus compile-time offsets (A block
+ * row i at base + i * mb rows, B step k at base + k rows) are candidates.  Writes {pad, swz_unit, swz_shift,
  * swz_mask} of A to out[0..3] and of B to out[4..7].  Returns GEMM_OK or
  * GEMM_ERR_INVALID_DIM. */
 int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,
