@@ -249,19 +249,23 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
 // of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the fraction of
 // CU-rounds that have work.  The 256x128 and 128x128 kernels are built to
 // run two workgroups per CU; with fewer tiles than two per CU they were
-// measured about 12 % slower, which the estimate applies.  On 15 measured
+// measured about 12 % slower, which the estimate applies.  When M or N is
+// not a multiple of the tile, a kernel whose edge workgroups load through
+// registers is charged an extra round (rounds / (rounds + 1)); the 64x64
+// kernel keeps direct copies on its edges and is not.  On 26 measured
 // shapes from 512^2 x 16384 to 8192^3 (deep, flat and ragged) this picks
-// the fastest of these variants or one within 1.5 % of it.
+// the fastest of these variants or one within 4.1 % of it.
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     struct Candidate {
         int variant, bm, bn, per_cu;
-        double rate;  // TFLOP/s with every CU busy (relative weights only)
+        bool edge_loop;  // edge workgroups keep direct copies for the operand in range
+        double rate;     // TFLOP/s with every CU busy (relative weights only)
     };
     const Candidate candidates[] = {
-        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, 145.0},
-        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, 144.0},
-        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, 144.0},
-        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, 128.0},
+        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, false, 145.0},
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, false, 144.0},
+        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, false, 144.0},
+        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, true, 128.0},
     };
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
@@ -270,6 +274,10 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
         double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
         if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;
+        // Edge workgroups of kernels without an edge loop load every tile
+        // through registers and take about twice as long; the last of them
+        // adds about a round.
+        if ((M % c.bm || N % c.bn) && !c.edge_loop) rate *= (double)rounds / (double)(rounds + 1);
         if (rate > best_rate * 1.02) {  // larger tiles win near-ties (listed first)
             best = c.variant;
             best_rate = rate;

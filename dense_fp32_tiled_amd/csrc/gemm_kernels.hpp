@@ -256,6 +256,10 @@ struct MfmaCfg {
     // 1 for 128x128 wave tiles (256 accumulators: the whole register file
     // at one wave per SIMD).
     static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
+    // Direct-copy kernels with this few staged floats per thread give edge
+    // workgroups a loop of their own: the operand in range is still copied
+    // directly, the other is prefetched through registers across the multiply.
+    static constexpr bool EDGE_PREFETCH = STAGED <= 8;
     static constexpr int MIN_WAVES = WM * WN >= 128 * 128           ? 1
                                      : VEC != 4 || WM * WN > 64 * 64 ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
@@ -592,25 +596,35 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         using DB = DirectCopy<TileB, THREADS>;
         const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
         const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
-        const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
+        // A's tiles are wholly in range when the workgroup's rows are (but for
+        // a ragged last K tile), B's when its columns are; an edge workgroup
+        // still copies the operand that is in range directly.
+        const bool rows_in = M - m0 >= BM && DA::fits(lda);
+        const bool cols_in = N - n0 >= BN && DB::fits(ldb);
+        const bool interior = rows_in && cols_in;
         auto fill = [&](int64_t t, int stage) {
             const int64_t k0 = t * BK;
-            if (interior && K - k0 >= BK) {
+            const bool k_in = K - k0 >= BK;
+            if (rows_in && k_in) {
                 dma_a.issue(a_tile + k0, lds_a, stage);
+            } else {
+                ldr_a.load(a_tile + k0, lda, M - m0, K - k0, tid);
+                ldr_a.template store<TileA>(lds_a, stage, tid);
+            }
+            if (cols_in && k_in) {
                 dma_b.issue(b_tile + k0 * ldb, lds_b, stage);
             } else {
-                load_tile(t);
-                ldr_a.template store<TileA>(lds_a, stage, tid);
+                ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, tid);
                 ldr_b.template store<TileB>(lds_b, stage, tid);
             }
         };
         if (T > 0) fill(0, 0);
         wait_vector_memory();
         __syncthreads();
-        // Iteration t copies tile t+1 directly iff the workgroup is interior
-        // and tile t+1 is wholly in range (t + 1 < K / BK).
-        const int64_t t_direct = interior ? K / BK - 1 : 0;
         if constexpr (Cfg::PIPE) {
+            // Iteration t copies tile t+1 directly iff the workgroup is
+            // interior and tile t+1 is wholly in range (t + 1 < K / BK).
+            const int64_t t_direct = interior ? K / BK - 1 : 0;
             // Software pipeline over the MFMA steps of a K tile (step kk
             // consumes k = g * KG + kk for lane group g).  The B fragments of
             // step kk+1 are read while step kk multiplies; the A fragments
@@ -692,7 +706,15 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                 mma_step(1, 3, 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else {
+        } else if (interior || !Cfg::EDGE_PREFETCH) {
+            // Interior workgroups, and every workgroup of kernels without
+            // EDGE_PREFETCH (the edge loop below would not fit their register
+            // budget beside this one).  Both operands copied directly when the
+            // workgroup is interior, else through registers; a ragged last K tile (K % BK)
+            // goes through registers after the multiply.  (Prefetching it
+            // across the multiply, as the edge loop below does, measured
+            // slower here: it costs every iteration a branch and registers.)
+            const int64_t t_direct = interior ? K / BK - 1 : 0;
             for (int64_t t = 0; t < T; ++t) {
                 const int s = (int)(t & 1);
                 const bool more = t + 1 < T;
@@ -707,6 +729,28 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                     ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
                     ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
                 }
+                wait_vector_memory();
+                __syncthreads();
+            }
+        } else if constexpr (Cfg::EDGE_PREFETCH) {
+            // Edge workgroup, per operand: a direct copy when that operand's
+            // next tile is in range, else a masked load through registers,
+            // issued before the multiply and stored after it (as in the
+            // register path; the staging registers are few).
+            const int64_t t_direct_a = rows_in ? K / BK - 1 : 0;
+            const int64_t t_direct_b = cols_in ? K / BK - 1 : 0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int s = (int)(t & 1);
+                const bool more = t + 1 < T;
+                const bool direct_a = t < t_direct_a, direct_b = t < t_direct_b;
+                const int64_t k1 = (t + 1) * BK;
+                if (direct_a) dma_a.issue(a_tile + k1, lds_a, s ^ 1);
+                if (direct_b) dma_b.issue(b_tile + k1 * ldb, lds_b, s ^ 1);
+                if (more && !direct_a) ldr_a.load(a_tile + k1, lda, M - m0, K - k1, tid);
+                if (more && !direct_b) ldr_b.load(b_tile + k1 * ldb, ldb, K - k1, N - n0, tid);
+                multiply(s);
+                if (more && !direct_a) ldr_a.template store<TileA>(lds_a, s ^ 1, tid);
+                if (more && !direct_b) ldr_b.template store<TileB>(lds_b, s ^ 1, tid);
                 wait_vector_memory();
                 __syncthreads();
             }

@@ -200,8 +200,10 @@ const char *gemm_f32_status_string(int status);
  * full-chip rate (145, 144, 144, 128 TFLOP/s) times the wave quantisation of
  * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus), times 0.88 for
  * the 256x128 and 128x128 kernels when there are fewer tiles than two per
- * CU (they are built for two workgroups per CU); a larger tile wins when
- * within 2 %.  Pure host call.  Returns a gemm_variant, or
+ * CU (they are built for two workgroups per CU), and times
+ * rounds / (rounds + 1) for the kernels whose edge workgroups load through
+ * registers when M or N is not a multiple of their tile (all but 64x64); a
+ * larger tile wins when within 2 %.  Pure host call.  Returns a gemm_variant, or
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 

@@ -133,6 +133,10 @@ def test_auto_variant_selection(gemm_lib):
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_DIRECT         # 512 tiles of 64x64
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_64_DIRECT        # deep K, 128 small tiles
     assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_DIRECT
+    # ragged grids: the 64x64 kernel keeps direct copies on its edge workgroups
+    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_DIRECT
+    assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_64_DIRECT
+    assert av(6000, 6000, 6000, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 9 rounds: one more costs 10 %
     assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_DIRECT       # many more CUs than big tiles
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
