@@ -1,0 +1,203 @@
+"""Host model of the K-loop synchronisation protocols, checked over every
+interleaving of a few abstract wavefronts.  CPU only.
+
+Each wavefront runs a list of events on a ring of LDS stages:
+
+* ("w", s, t): synchronous store of its piece of K tile t into stage s
+  (the register path: global load, then LDS store);
+* ("issue", s, t): an asynchronous direct copy of its piece of tile t into
+  stage s; the write lands at any later moment the model chooses;
+* ("wait", t): block until none of this wave's copies of tiles <= t is still
+  in flight (s_waitcnt on the copies; t = None waits for all);
+* ("r", s, t): read the whole stage s (every wave's piece), expecting tile t;
+* ("b",): workgroup barrier.
+
+A schedule is correct when every read, in every interleaving and for every
+landing time of every copy, sees tile t in all pieces of stage s, and no
+interleaving deadlocks.  The protocols are those of the kernels (two stages
+and one barrier per tile through registers or direct copies, the pipelined
+multiply whose last step runs after the barrier, the S-stage copy ring of
+the 16-bit-input kernels); the mutants (a barrier dropped, the stage parity
+flipped, the last step read after the barrier, the wait dropped or too
+weak) must each be caught.  The pages argue the one-barrier protocol in
+prose ("My Triton From Scratch, Part 18", section "What ping-pong changes
+about synchronization"); this is a machine check of that argument and of
+its pipelined extension.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import pytest
+
+
+def check(programs, stages: int):
+    """Explore every interleaving; return None, or a description of the
+    first violation or deadlock found."""
+    waves = len(programs)
+    sys.setrecursionlimit(100000)
+    seen = set()
+    # content[s][v]: tile in wave v's piece of stage s (-1: never written)
+    start = (tuple([0] * waves), tuple(tuple([-1] * waves) for _ in range(stages)),
+             tuple(frozenset() for _ in range(waves)))
+    stack = [start]
+    while stack:
+        state = stack.pop()
+        if state in seen:
+            continue
+        seen.add(state)
+        pcs, content, pending = state
+        if all(pcs[v] == len(programs[v]) for v in range(waves)):
+            continue
+        moves = []
+        # a copy in flight may land now
+        for v in range(waves):
+            for (s, t) in pending[v]:
+                c = [list(row) for row in content]
+                c[s][v] = t
+                p = list(pending)
+                p[v] = pending[v] - {(s, t)}
+                moves.append((pcs, tuple(tuple(row) for row in c), tuple(p)))
+        # barrier: all waves at a barrier together
+        if all(pcs[v] < len(programs[v]) and programs[v][pcs[v]][0] == "b" for v in range(waves)):
+            moves.append((tuple(pc + 1 for pc in pcs), content, pending))
+        for v in range(waves):
+            if pcs[v] == len(programs[v]):
+                continue
+            ev = programs[v][pcs[v]]
+            nxt = list(pcs)
+            nxt[v] += 1
+            nxt = tuple(nxt)
+            kind = ev[0]
+            if kind == "b":
+                continue
+            if kind == "w":
+                c = [list(row) for row in content]
+                c[ev[1]][v] = ev[2]
+                moves.append((nxt, tuple(tuple(row) for row in c), pending))
+            elif kind == "issue":
+                p = list(pending)
+                p[v] = pending[v] | {(ev[1], ev[2])}
+                moves.append((nxt, content, tuple(p)))
+            elif kind == "wait":
+                if all(ev[1] is not None and t > ev[1] for (_, t) in pending[v]):
+                    moves.append((nxt, content, pending))
+            elif kind == "r":
+                got = content[ev[1]]
+                if any(x != ev[2] for x in got):
+                    return f"wave {v} read stage {ev[1]} expecting tile {ev[2]}, pieces hold {got}"
+                moves.append((nxt, content, pending))
+        if not moves:
+            return f"deadlock at {pcs}"
+        stack.extend(moves)
+    return None
+
+
+# ---- the kernels' protocols (T K tiles) -------------------------------------------
+
+
+def one_stage_two_barriers(T):
+    ev = []
+    for t in range(T):
+        ev += [("w", 0, t), ("b",), ("r", 0, t), ("b",)]
+    return ev
+
+
+def two_stage_registers(T, parity_flip=False, drop_barrier=False):
+    ev = [("w", 0, 0), ("b",)]
+    for t in range(T):
+        ev.append(("r", t % 2, t))
+        if t + 1 < T:
+            ev.append(("w", (t if parity_flip else t + 1) % 2, t + 1))
+        if not drop_barrier:
+            ev.append(("b",))
+    return ev
+
+
+def two_stage_direct(T, drop_wait=False):
+    ev = [("issue", 0, 0), ("wait", None), ("b",)]
+    for t in range(T):
+        if t + 1 < T:
+            ev.append(("issue", (t + 1) % 2, t + 1))
+        ev.append(("r", t % 2, t))
+        if not drop_wait:
+            ev.append(("wait", None))
+        ev.append(("b",))
+    return ev
+
+
+def pipelined(T, steps=3, last_after_barrier=False):
+    """The MFMA kernel's PIPE loop: step 0 of tile t was read before the
+    loop or after the previous barrier; steps 1.. are read before the
+    barrier (the last one's registers are multiplied after it)."""
+    ev = [("issue", 0, 0), ("wait", None), ("b",), ("r", 0, 0)]
+    for t in range(T):
+        if t + 1 < T:
+            ev.append(("issue", (t + 1) % 2, t + 1))
+        body = [("r", t % 2, t)] * (steps - 1)
+        if last_after_barrier:
+            ev += body[:-1] + [("wait", None), ("b",), body[-1]]
+        else:
+            ev += body + [("wait", None), ("b",)]
+        if t + 1 < T:
+            ev.append(("r", (t + 1) % 2, t + 1))
+    return ev
+
+
+def ring(T, S, weak_wait=False):
+    """The 16-bit-input kernels' S-stage copy ring, pipelined across tiles:
+    the copies of tile t+S-1 go into the stage of tile t-1; before the
+    barrier each wave waits until its copies of tile t+1 have landed."""
+    ev = []
+    for p in range(min(S - 1, T)):
+        ev.append(("issue", p % S, p))
+    ev += [("wait", None), ("b",), ("r", 0, 0)]
+    for t in range(T):
+        nt = t + S - 1
+        if nt < T:
+            ev.append(("issue", nt % S, nt))
+        ev.append(("r", t % S, t))
+        ev.append(("wait", t if weak_wait else t + 1))
+        ev.append(("b",))
+        if t + 1 < T:
+            ev.append(("r", (t + 1) % S, t + 1))
+    return ev
+
+
+CORRECT = [
+    ("one stage, two barriers", lambda T: one_stage_two_barriers(T), 1),
+    ("two stages through registers", lambda T: two_stage_registers(T), 2),
+    ("two stages, direct copies", lambda T: two_stage_direct(T), 2),
+    ("pipelined multiply", lambda T: pipelined(T), 2),
+    ("three-stage copy ring", lambda T: ring(T, 3), 3),
+    ("four-stage copy ring", lambda T: ring(T, 4), 4),
+]
+
+MUTANTS = [
+    ("two stages without the barrier", lambda T: two_stage_registers(T, drop_barrier=True), 2),
+    ("stage parity flipped", lambda T: two_stage_registers(T, parity_flip=True), 2),
+    ("one stage with one barrier", lambda T: [e for i, e in enumerate(one_stage_two_barriers(T)) if i % 4 != 3], 1),
+    ("direct copies without the wait", lambda T: two_stage_direct(T, drop_wait=True), 2),
+    ("pipelined, last step read after the barrier", lambda T: pipelined(T, last_after_barrier=True), 2),
+    ("three-stage ring waiting one tile short", lambda T: ring(T, 3, weak_wait=True), 3),
+]
+
+
+@pytest.mark.parametrize("waves", [2, 3])
+@pytest.mark.parametrize("name,make,stages", CORRECT, ids=[c[0] for c in CORRECT])
+def test_protocol_is_race_free(name, make, stages, waves):
+    T = 4
+    assert check([make(T)] * waves, stages) is None
+
+
+@pytest.mark.parametrize("name,make,stages", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, make, stages):
+    T = 4
+    assert check([make(T)] * 2, stages) is not None
+
+
+def test_divergent_barrier_deadlocks():
+    prog = two_stage_registers(3)
+    short = prog[:-1]  # one wave skips the last barrier
+    assert "deadlock" in (check([prog, short], 2) or "")
