@@ -89,12 +89,11 @@ using Mfma16x256x256W4Bk32Pipe = std::conditional_t<
     MfmaCfg<256, 256, 32, 128, 128, 2, 16, layouts::m16_256x256x32_w4_pipe::A,
             layouts::m16_256x256x32_w4_pipe::B, 4, kXcdGroupedOrder, kLoadDirect, true>,
     Mfma256<2, 1>>;
+// The 64x64 kernel copies directly at both widths: 16 bytes per lane for
+// aligned operands, 4 bytes per lane (any row alignment) otherwise.
 template <int VEC>
-using Mfma64Direct = std::conditional_t<
-    VEC == 4,
-    MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A, layouts::m32_64x64x16_direct::B, 4,
-            kXcdGroupedOrder, kLoadDirect>,
-    MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_v1::A, layouts::m32_64x64x16_v1::B, 1, kXcdGroupedOrder>>;
+using Mfma64Direct = MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A,
+                             layouts::m32_64x64x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;

@@ -249,10 +249,11 @@ struct MfmaCfg {
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
     static constexpr int KG = BK / Op::KB;  // k values per lane group per tile
     // Register budget (waves per SIMD the compiler must fit): 4 (<= 128
-    // VGPRs) when the tile reaches LDS by direct copies, or through registers
-    // with at most 12 staged floats per thread; 3 for more staged floats
-    // (128x128 tiles through registers: 16 or 32, which spill at 4); 2 for
-    // 4-byte loads (four times the load registers).
+    // VGPRs) when the tile reaches LDS by direct copies (16- or 4-byte), or
+    // through registers with at most 12 staged floats per thread; 3 for more
+    // staged floats (128x128 tiles through registers: 16 or 32, which spill
+    // at 4); 2 for 4-byte loads through registers (four times the load
+    // registers).
     // 1 for 128x128 wave tiles (256 accumulators: the whole register file
     // at one wave per SIMD).
     static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
@@ -260,8 +261,8 @@ struct MfmaCfg {
     // workgroups a loop of their own: the operand in range is still copied
     // directly, the other is prefetched through registers across the multiply.
     static constexpr bool EDGE_PREFETCH = STAGED <= 8;
-    static constexpr int MIN_WAVES = WM * WN >= 128 * 128           ? 1
-                                     : VEC != 4 || WM * WN > 64 * 64 ? 2
+    static constexpr int MIN_WAVES = WM * WN >= 128 * 128 ? 1
+                                     : WM * WN > 64 * 64 || (VEC != 4 && LOAD == kLoadRegisters) ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
                                                                              : 3;
     using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;
@@ -271,8 +272,8 @@ struct MfmaCfg {
     static_assert(KG % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
     static_assert(TileB::row_stride % VEC == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
     static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
-    static_assert(LOAD == kLoadRegisters || (VEC == 4 && STAGES == 2 && LayA::pad == 0 && LayB::pad == 0),
-                  "direct copies need 16-byte loads, two stages and unpadded rows");
+    static_assert(LOAD == kLoadRegisters || (STAGES == 2 && LayA::pad == 0 && LayB::pad == 0),
+                  "direct copies need two stages and unpadded rows");
     static_assert(!PIPE || (LOAD == kLoadDirect && KG % 8 == 0),
                   "the pipeline runs on direct copies, with an even number of 4-k chunks per tile");
 
@@ -330,36 +331,52 @@ __device__ inline void copy16_to_lds(const void* uniform_base, uint32_t byte_off
         : "memory", "m0");
 }
 
+// The same copy moving 4 bytes per lane (global_load_lds_dword): LDS byte
+// address lds_base + 4 * lane; the global address needs only 4-byte
+// alignment, so it serves operands whose rows are not 16-byte aligned.
+__device__ inline void copy4_to_lds(const void* uniform_base, uint32_t byte_offset, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(byte_offset), "s"(uniform_base), "s"(lds_base)
+        : "memory", "m0");
+}
+
 // Direct global->LDS copy of one operand tile.  A stage of an unpadded tile
-// is cut into 1 KiB pieces (64 lanes x 16 bytes), piece i * WAVES + w being
-// written by wavefront w's i-th copy instruction, and the lane that writes
-// LDS word p fetches the elements the tile layout keeps there: row p / cols,
-// word column swizzle(row, p % cols) (the XOR swizzle is its own inverse).
-// The tile is laid out in 4-byte words; an element of type T is
-// 4 / sizeof(T) per word (1 for fp32, 2 for 16-bit inputs).  The fetch
-// offsets do not depend on the K tile, so they are computed once.
-template <class Tile, int THREADS, class T = float>
+// is cut into pieces of 64 lanes x BYTES (16: 1 KiB, or 4: 256 bytes),
+// piece i * WAVES + w being written by wavefront w's i-th copy instruction,
+// and the lane that writes LDS word p fetches the elements the tile layout
+// keeps there: row p / cols, word column swizzle(row, p % cols) (the XOR
+// swizzle is its own inverse, and moves groups of 4 words, so a lane's
+// BYTES stay contiguous).  The tile is laid out in 4-byte words; an element
+// of type T is 4 / sizeof(T) per word (1 for fp32, 2 for 16-bit inputs).
+// The fetch offsets do not depend on the K tile, so they are computed once.
+template <class Tile, int THREADS, class T = float, int BYTES = 16>
 struct DirectCopy {
     static_assert(sizeof(T) == 4 || sizeof(T) == 2, "4- or 2-byte elements");
+    static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte copies");
     static constexpr int PER_WORD = 4 / (int)sizeof(T);
+    static constexpr int LANE_WORDS = BYTES / 4;  // LDS words one lane writes per copy
     static_assert(Tile::pad == 0, "direct copies write whole rows contiguously");
     static constexpr int WAVES = THREADS / kWave;
-    static constexpr int PIECE = kWave * 4;  // fp32 words per instruction per wavefront
+    static constexpr int PIECE = kWave * LANE_WORDS;  // fp32 words per instruction per wavefront
     static_assert(Tile::stage_elems % (PIECE * WAVES) == 0, "tile must split evenly over the wavefronts");
     static constexpr int PER_WAVE = Tile::stage_elems / (PIECE * WAVES);
 
-    // Logical (row, col) of the four elements stored at LDS word `word` of a stage.
+    // Logical (row, col) of the element(s) stored at LDS word `word` of a stage.
     static constexpr void source(int word, int& row, int& col) {
         row = word / Tile::cols;
         col = Swizzle{Tile::swizzle.unit, Tile::swizzle.shift, Tile::swizzle.mask}.apply(row, word % Tile::cols);
     }
-    // Every 16-byte group of a stage is fetched from the element the tile
-    // layout (which the fragment reads use) places there.
+    // Every lane's group of LANE_WORDS words of a stage is fetched from the
+    // elements the tile layout (which the fragment reads use) places there.
     static constexpr bool matches_layout() {
-        for (int word = 0; word < Tile::stage_elems; word += 4) {
+        for (int word = 0; word < Tile::stage_elems; word += LANE_WORDS) {
             int row = 0, col = 0;
             source(word, row, col);
-            if (row >= Tile::rows || col % 4 != 0 || col >= Tile::cols || Tile::offset(0, row, col) != word)
+            if (row >= Tile::rows || col % LANE_WORDS != 0 || col >= Tile::cols || Tile::offset(0, row, col) != word)
                 return false;
         }
         return true;
@@ -379,10 +396,10 @@ struct DirectCopy {
         for (int w = 0; w < WAVES; ++w)
             for (int lane = 0; lane < kWave; ++lane) {
                 int r0 = 0, c0 = 0;
-                source(w * PIECE + 4 * lane, r0, c0);
+                source(w * PIECE + LANE_WORDS * lane, r0, c0);
                 for (int i = 1; i < PER_WAVE; ++i) {
                     int r = 0, c = 0;
-                    source((i * WAVES + w) * PIECE + 4 * lane, r, c);
+                    source((i * WAVES + w) * PIECE + LANE_WORDS * lane, r, c);
                     if (r != r0 + i * ROUND_ROWS || c != c0) return false;
                 }
             }
@@ -391,13 +408,18 @@ struct DirectCopy {
     static_assert(strided_matches(), "strided copies must fetch what the per-copy offsets would");
 
     // Byte offsets from the tile origin must fit 31 bits: they are below
-    // Tile::rows * ld elements.  A kernel copies directly only when fits(ld)
-    // holds (a uniform condition) and loads through registers otherwise.
+    // Tile::rows * ld elements.  A kernel copies directly only when
+    // fits(ld, origin) holds (a uniform condition) and loads through
+    // registers otherwise.  4-byte copies also need the operand 4-byte
+    // aligned (16-byte copies are only launched on 16-byte aligned operands).
     __host__ __device__ static constexpr bool fits(int64_t ld) {
         return ld <= (((int64_t)1 << 31) - 1) / ((int64_t)Tile::rows * (int64_t)sizeof(T));
     }
+    __device__ static bool fits(int64_t ld, const T* operand) {
+        return fits(ld) && (BYTES == 16 || ((uintptr_t)operand & 3) == 0);
+    }
 
-    uint32_t off[STRIDED ? 1 : PER_WAVE];  // byte offset(s) of this lane's 16 bytes from the tile origin
+    uint32_t off[STRIDED ? 1 : PER_WAVE];  // byte offset(s) of this lane's bytes from the tile origin
     int64_t round_stride;                  // elements between copy i and i+1 (strided form)
     uint32_t lds_piece;                    // byte offset of this wavefront's first piece in a stage (uniform)
 
@@ -406,7 +428,7 @@ struct DirectCopy {
 #pragma unroll
         for (int i = 0; i < (STRIDED ? 1 : PER_WAVE); ++i) {
             int row = 0, col = 0;
-            source((i * WAVES + wave_uniform) * PIECE + 4 * lane, row, col);
+            source((i * WAVES + wave_uniform) * PIECE + LANE_WORDS * lane, row, col);
             off[i] = (uint32_t)(((int64_t)row * ld + (int64_t)col * PER_WORD) * (int64_t)sizeof(T));
         }
     }
@@ -422,7 +444,10 @@ struct DirectCopy {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const T* row_base = STRIDED ? origin + i * round_stride : origin;
-            copy16_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
+            if constexpr (BYTES == 16)
+                copy16_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
+            else
+                copy4_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
         }
     }
 };
@@ -592,15 +617,15 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         // when BK does not divide K) needs zero fill: it is loaded through
         // registers with masks after the multiply, so that no staging
         // registers are live across it.  Both choices are uniform.
-        using DA = DirectCopy<TileA, THREADS>;
-        using DB = DirectCopy<TileB, THREADS>;
+        using DA = DirectCopy<TileA, THREADS, float, 4 * Cfg::VEC>;
+        using DB = DirectCopy<TileB, THREADS, float, 4 * Cfg::VEC>;
         const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
         const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
         // A's tiles are wholly in range when the workgroup's rows are (but for
         // a ragged last K tile), B's when its columns are; an edge workgroup
         // still copies the operand that is in range directly.
-        const bool rows_in = M - m0 >= BM && DA::fits(lda);
-        const bool cols_in = N - n0 >= BN && DB::fits(ldb);
+        const bool rows_in = M - m0 >= BM && DA::fits(lda, A);
+        const bool cols_in = N - n0 >= BN && DB::fits(ldb, B);
         const bool interior = rows_in && cols_in;
         auto fill = [&](int64_t t, int stage) {
             const int64_t k0 = t * BK;

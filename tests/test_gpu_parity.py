@@ -225,6 +225,24 @@ def test_direct_copy_paths(K, variant, torch_gpu):
     assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
+@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_AUTO],
+                         ids=["mfma_64_direct", "auto"])
+@pytest.mark.parametrize("K,pad,offset", [(513, 0, 0), (100, 1, 1), (257, 2, 3), (16, 1, 0), (33, 3, 1)])
+def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
+    """Operands whose rows are not 16-byte aligned (odd leading dimensions,
+    bases shifted by whole floats): the 64x64 kernel copies them into LDS 4
+    bytes per lane.  600 x 300 has interior and edge tiles of 64 x 64; NaN
+    fills every ld gap, so a copy that strays past column K or into a gap
+    shows up, as does any write outside C."""
+    M, N = 600, 300
+    lda, ldb, ldc = K + pad, N + 1 + pad, N + 3
+    a, b = workloads.make_operands(M, N, K, "integer", 500 + K)
+    cref, _ = oracle.reference(a, b)
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=ldc, offset=offset, c_rows_extra=2)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref)
+
+
 @pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
 def test_k_zero_writes_zeros(variant, torch_gpu):
     a = np.zeros((37, 0), np.float32)
