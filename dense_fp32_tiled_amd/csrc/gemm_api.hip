@@ -34,23 +34,20 @@ using Mfma16x256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m16_256x128x16_v
 // Direct global->LDS copies for in-range tiles (16-byte path only; the
 // 4-byte path of this variant loads through registers like MFMA).
 template <int VEC>
-using Mfma256Direct = std::conditional_t<
-    VEC == 4,
-    MfmaCfg<256, 128, 16, 64, 64, 2, 32, layouts::m32_256x128x16_direct::A, layouts::m32_256x128x16_direct::B, 4,
-            kXcdGroupedOrder, kLoadDirect>,
-    Mfma256<2, 1>>;
+using Mfma256Direct = MfmaCfg<256, 128, 16, 64, 64, 2, 32, layouts::m32_256x128x16_direct::A,
+                              layouts::m32_256x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
 template <int VEC>
-using Mfma128Direct = std::conditional_t<
-    VEC == 4,
-    MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A, layouts::m32_128x128x16_direct::B, 4,
-            kXcdGroupedOrder, kLoadDirect>,
-    MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
+using Mfma128Direct = MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A,
+                              layouts::m32_128x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
+// BK = 32 with 4-byte copies would need 32 staged floats per thread on edge
+// tiles beside the accumulators; the 4-byte form runs BK = 16.
 template <int VEC>
 using Mfma128Bk32Direct = std::conditional_t<
     VEC == 4,
     MfmaCfg<128, 128, 32, 64, 64, 2, 32, layouts::m32_128x128x32_direct::A, layouts::m32_128x128x32_direct::B, 4,
             kXcdGroupedOrder, kLoadDirect>,
-    MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
+    MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A, layouts::m32_128x128x16_direct::B, 1,
+            kXcdGroupedOrder, kLoadDirect>>;
 template <int VEC>
 using Mfma256x256Direct = std::conditional_t<
     VEC == 4,
@@ -72,11 +69,8 @@ using Mfma256x256Pipe = std::conditional_t<
             kXcdGroupedOrder, kLoadDirect, true>,
     Mfma256<2, 1>>;
 template <int VEC>
-using Mfma256x256Bk32Pipe = std::conditional_t<
-    VEC == 4,
-    MfmaCfg<256, 256, 32, 128, 64, 2, 32, layouts::m32_256x256x32_pipe::A, layouts::m32_256x256x32_pipe::B, 4,
-            kXcdGroupedOrder, kLoadDirect, true>,
-    Mfma256<2, 1>>;
+using Mfma256x256Bk32Pipe = MfmaCfg<256, 256, 32, 128, 64, 2, 32, layouts::m32_256x256x32_pipe::A,
+                                    layouts::m32_256x256x32_pipe::B, VEC, kXcdGroupedOrder, kLoadDirect, true>;
 template <int VEC>
 using Mfma16x256x256Direct = std::conditional_t<
     VEC == 4,

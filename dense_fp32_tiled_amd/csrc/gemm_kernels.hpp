@@ -249,11 +249,12 @@ struct MfmaCfg {
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
     static constexpr int KG = BK / Op::KB;  // k values per lane group per tile
     // Register budget (waves per SIMD the compiler must fit): 4 (<= 128
-    // VGPRs) when the tile reaches LDS by direct copies (16- or 4-byte), or
-    // through registers with at most 12 staged floats per thread; 3 for more
-    // staged floats (128x128 tiles through registers: 16 or 32, which spill
-    // at 4); 2 for 4-byte loads through registers (four times the load
-    // registers).
+    // VGPRs) when the tile reaches LDS by direct copies (16-byte, or 4-byte
+    // with 32x32 wave tiles), or through registers with at most 12 staged
+    // floats per thread; 3 for more staged floats (128x128 tiles through
+    // registers: 16 or 32, which spill at 4); 2 for 4-byte loads through
+    // registers (four times the load registers) and for 4-byte copies with
+    // 64x64 wave tiles, whose edge tiles load 4 bytes at a time.
     // 1 for 128x128 wave tiles (256 accumulators: the whole register file
     // at one wave per SIMD).
     static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
@@ -262,7 +263,7 @@ struct MfmaCfg {
     // directly, the other is prefetched through registers across the multiply.
     static constexpr bool EDGE_PREFETCH = STAGED <= 8;
     static constexpr int MIN_WAVES = WM * WN >= 128 * 128 ? 1
-                                     : WM * WN > 64 * 64 || (VEC != 4 && LOAD == kLoadRegisters) ? 2
+                                     : WM * WN > 64 * 64 || (VEC != 4 && (LOAD == kLoadRegisters || WM * WN >= 64 * 64)) ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
                                                                              : 3;
     using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;
@@ -334,13 +335,20 @@ __device__ inline void copy16_to_lds(const void* uniform_base, uint32_t byte_off
 // The same copy moving 4 bytes per lane (global_load_lds_dword): LDS byte
 // address lds_base + 4 * lane; the global address needs only 4-byte
 // alignment, so it serves operands whose rows are not 16-byte aligned.
+// The base is read from the first lane: it is wave-uniform by construction,
+// but in some of the kernels that use this form the compiler cannot prove
+// it, and a scalar operand must be.
 __device__ inline void copy4_to_lds(const void* uniform_base, uint32_t byte_offset, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)uniform_base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const void* base = (const void*)(uintptr_t)(lo | (hi << 32));
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dword %0, %1"
         :
-        : "v"(byte_offset), "s"(uniform_base), "s"(lds_base)
+        : "v"(byte_offset), "s"(base), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base))
         : "memory", "m0");
 }
 
@@ -384,12 +392,14 @@ struct DirectCopy {
     static_assert(matches_layout(), "direct copies must fill the LDS tile in its own layout");
 
     // Copy i of a lane fetches from row row_0 + i * ROUND_ROWS.  When a round
-    // of pieces covers whole rows and a whole number of swizzle periods, the
+    // of pieces (one per wavefront) covers whole rows and a whole number of
+    // swizzle periods, the
     // column is the same for every i, so one offset per lane and a uniform
     // row stride describe all copies (fewer registers); otherwise each copy
     // keeps its own offset.
     static constexpr int SWIZZLE_ROWS = Tile::swizzle.unit ? (Tile::swizzle.mask + 1) << Tile::swizzle.shift : 1;
-    static constexpr bool STRIDED = PIECE % Tile::cols == 0 && ((WAVES * PIECE / Tile::cols) % SWIZZLE_ROWS) == 0;
+    static constexpr bool STRIDED =
+        (WAVES * PIECE) % Tile::cols == 0 && ((WAVES * PIECE / Tile::cols) % SWIZZLE_ROWS) == 0;
     static constexpr int ROUND_ROWS = STRIDED ? WAVES * PIECE / Tile::cols : 0;
     static constexpr bool strided_matches() {
         if (!STRIDED) return true;
@@ -649,6 +659,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         if constexpr (Cfg::PIPE) {
             // Iteration t copies tile t+1 directly iff the workgroup is
             // interior and tile t+1 is wholly in range (t + 1 < K / BK).
+            // (Copying the in-range operand of an edge workgroup directly
+            // and only the other through registers measured 4% slower on
+            // interior workgroups too: the two conditions cost registers
+            // and scheduling freedom in the loop.)
             const int64_t t_direct = interior ? K / BK - 1 : 0;
             // Software pipeline over the MFMA steps of a K tile (step kk
             // consumes k = g * KG + kk for lane group g).  The B fragments of

@@ -225,15 +225,18 @@ def test_direct_copy_paths(K, variant, torch_gpu):
     assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
-@pytest.mark.parametrize("variant", [dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_AUTO],
-                         ids=["mfma_64_direct", "auto"])
+FOUR_BYTE_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
+                      dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_256x256_BK32_PIPE]
+
+
+@pytest.mark.parametrize("variant", FOUR_BYTE_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in FOUR_BYTE_VARIANTS])
 @pytest.mark.parametrize("K,pad,offset", [(513, 0, 0), (100, 1, 1), (257, 2, 3), (16, 1, 0), (33, 3, 1)])
 def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
     """Operands whose rows are not 16-byte aligned (odd leading dimensions,
-    bases shifted by whole floats): the 64x64 kernel copies them into LDS 4
-    bytes per lane.  600 x 300 has interior and edge tiles of 64 x 64; NaN
-    fills every ld gap, so a copy that strays past column K or into a gap
-    shows up, as does any write outside C."""
+    bases shifted by whole floats): the direct-copy kernels copy them into
+    LDS 4 bytes per lane.  600 x 300 has interior and edge tiles for every
+    tile size up to 256 x 256; NaN fills every ld gap, so a copy that strays
+    past column K or into a gap shows up, as does any write outside C."""
     M, N = 600, 300
     lda, ldb, ldc = K + pad, N + 1 + pad, N + 3
     a, b = workloads.make_operands(M, N, K, "integer", 500 + K)

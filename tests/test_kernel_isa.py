@@ -46,7 +46,8 @@ def test_valu_inner_product_is_fully_unrolled(functions):
 def test_default_mfma_tile_is_straight_line(functions):
     _, funcs = functions
     # 256x256x32, 8 waves of 128x64: 4 x 2 blocks x 16 steps = 128 MFMAs per K tile
-    default = [b for n, b in funcs.items() if "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E" in n]
+    default = [b for n, b in funcs.items()
+               if "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E" in n and "EEELi4ELi1ELi1ELb1E" in n]
     assert len(default) == 1
     assert max_per_block(default[0], r"^\s+v_mfma_f32_32x32x2_f32") >= 128 - 8
 
@@ -54,3 +55,20 @@ def test_default_mfma_tile_is_straight_line(functions):
 def test_no_packed_fp32_instructions(functions):
     text, _ = functions
     assert not re.search(r"v_pk_(?:fma|mul|add)_f32", text)
+
+
+def test_m0_is_used_only_by_the_direct_copies(functions):
+    """The copy statements write M0 without saving it (they declare it
+    clobbered, and the compiler does not preserve a reserved register across
+    inline asm).  That is safe only while no compiler-generated code keeps a
+    value in M0: every instruction that names m0 must be one of the copies'
+    own s_mov_b32 m0, sN, followed by the wait state and the copy."""
+    text, _ = functions
+    lines = [l.strip() for l in text.splitlines()]
+    code = [l for l in lines if l and not l.startswith((";", ".", "//")) and not l.endswith(":")]
+    uses = [i for i, l in enumerate(code) if re.search(r"\bm0\b", l)]
+    assert uses
+    for i in uses:
+        assert re.fullmatch(r"s_mov_b32 m0, s\d+", code[i]), code[i]
+        assert code[i + 1] == "s_nop 0", code[i + 1]
+        assert code[i + 2].startswith(("global_load_lds_dwordx4 ", "global_load_lds_dword ")), code[i + 2]
