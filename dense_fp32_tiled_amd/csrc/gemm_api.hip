@@ -258,7 +258,7 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
         {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, false, 145.0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, false, 144.0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, false, 144.0},
-        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, true, 128.0},
+        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, true, 132.0},
     };
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
@@ -267,10 +267,12 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
         double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
         if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;
-        // Edge workgroups of kernels without an edge loop load every tile
-        // through registers and take about twice as long; the last of them
-        // adds about a round.
-        if ((M % c.bm || N % c.bn) && !c.edge_loop) rate *= (double)rounds / (double)(rounds + 1);
+        // Edge tiles move back to end at M (N) and run like interior ones
+        // when M >= bm (N >= bn).  Otherwise the edge workgroups of kernels
+        // without an edge loop load every tile through registers and take
+        // about twice as long; the last of them adds about a round.
+        const bool edge_m = M % c.bm && M < c.bm, edge_n = N % c.bn && N < c.bn;
+        if ((edge_m || edge_n) && !c.edge_loop) rate *= (double)rounds / (double)(rounds + 1);
         if (rate > best_rate * 1.02) {  // larger tiles win near-ties (listed first)
             best = c.variant;
             best_rate = rate;

@@ -477,29 +477,49 @@ __device__ inline void wait_vector_memory_at_most() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Store of a wavefront's MFMA accumulators: unmasked when the whole BM x BN
-// workgroup tile is in range (a uniform branch), else under the mask
-// rows < M and columns < N.  For a fixed result register, the MB lanes of a
-// k-group write consecutive floats of one row.
+// Store of a wavefront's MFMA accumulators.  The accumulators hold the
+// BM x BN block whose first row and column are (ma, na); the workgroup owns
+// rows [m0, M) and columns [n0, N) of it (m0 >= ma and n0 >= na: a tile moved
+// back to end at M or N leaves the rows or columns before m0 or n0 to the
+// workgroup that owns them).  Unmasked when the block is the workgroup's own
+// and wholly in range (a uniform branch), else under the mask.  For a fixed
+// result register, the MB lanes of a k-group write consecutive floats of one
+// row.
 template <class Op, int BM, int BN, int MI, int NI>
-__device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m0,
-                                          int64_t n0, int wm0, int wn0, int lane,
+__device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t ma,
+                                          int64_t na, int64_t m0, int64_t n0, int wm0, int wn0, int lane,
                                           const typename Op::acc_t (&acc)[MI][NI]) {
     const int r = lane % Op::MB;
-    const bool full = m0 + BM <= M && n0 + BN <= N;
+    const bool full = ma == m0 && na == n0 && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
-            const int64_t gn = n0 + wn0 + n * Op::NB + r;
-            const int64_t gm0 = m0 + wm0 + i * Op::MB;
+            const int64_t gn = na + wn0 + n * Op::NB + r;
+            const int64_t gm0 = ma + wm0 + i * Op::MB;
             float* cp = C + gm0 * ldc + gn;
 #pragma unroll
             for (int v = 0; v < Op::ACC; ++v) {
                 const int dr = Op::out_row(lane, v);
-                if (full || (gm0 + dr < M && gn < N)) cp[dr * ldc] = acc[i][n][v];
+                if (full || (gm0 + dr >= m0 && gm0 + dr < M && gn >= n0 && gn < N)) cp[dr * ldc] = acc[i][n][v];
             }
         }
+}
+
+// Origin of the operand tiles of a workgroup whose output tile starts at
+// (m0, n0).  Direct-copy kernels move a tile that overhangs M (N) back so
+// that it ends at M (N), when M >= BM (N >= BN): an A row beyond M feeds only
+// outputs beyond M, and a B column beyond N only outputs beyond N, so the
+// moved tile's rows are all in range and need no zero fill (its copies run
+// like an interior tile's), and its outputs are the same sums; the rows and
+// columns that it recomputes before m0 and n0 are not stored.  Only the K
+// direction needs zero fill.
+template <class Cfg>
+__device__ inline TileCoord operand_origin(TileCoord own, int64_t M, int64_t N) {
+    if constexpr (Cfg::LOAD != kLoadDirect) return own;
+    const int64_t ma = own.m0 + Cfg::BM > M && M >= Cfg::BM ? M - Cfg::BM : own.m0;
+    const int64_t na = own.n0 + Cfg::BN > N && N >= Cfg::BN ? N - Cfg::BN : own.n0;
+    return TileCoord{ma, na};
 }
 
 template <class Cfg>
@@ -555,7 +575,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
     const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
     const int g = lane / Op::MB, r = lane % Op::MB;
 
-    const TileCoord tc = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord own = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord tc = operand_origin<Cfg>(own, M, N);
     const int64_t m0 = tc.m0, n0 = tc.n0;
 
     acc_t acc[MI][NI];
@@ -808,7 +829,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         }
     }
 
-    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, wm0, wn0, lane, acc);
+    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
 }
 
 // --------------------------------------------------------------------------

@@ -277,7 +277,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     const int tr_row = 8 * Op::kgroup(lane) + (lane % 16) / 4;
     const int tr_col = Op::col_base(lane) + 4 * (lane % 4);  // elements
 
-    const TileCoord tc = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord own = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord tc = operand_origin<Cfg>(own, M, N);
     const int64_t m0 = tc.m0, n0 = tc.n0;
 
     acc_t acc[MI][NI];
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
         two_stage_registers();
     }
 
-    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, wm0, wn0, lane, acc);
+    store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
 }
 
 }  // namespace dft

@@ -197,13 +197,15 @@ const char *gemm_f32_status_string(int status);
  * `num_cus` compute units: among MFMA_256x256_BK32_PIPE, MFMA_DIRECT
  * (256x128), the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
  * MFMA_64_DIRECT (64x64), the one with the highest rate estimate, its
- * full-chip rate (145, 144, 144, 128 TFLOP/s) times the wave quantisation of
+ * full-chip rate (145, 144, 144, 132 TFLOP/s) times the wave quantisation of
  * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus), times 0.88 for
  * the 256x128 and 128x128 kernels when there are fewer tiles than two per
  * CU (they are built for two workgroups per CU), and times
  * rounds / (rounds + 1) for the kernels whose edge workgroups load through
- * registers when M or N is not a multiple of their tile (all but 64x64); a
- * larger tile wins when within 2 %.  Pure host call.  Returns a gemm_variant, or
+ * registers (all but 64x64) when M or N is smaller than, and not a multiple
+ * of, their tile (when M >= BM and N >= BN an edge tile is moved back to end
+ * at M or N and runs as an interior one); a larger tile wins when within
+ * 2 %.  Pure host call.  Returns a gemm_variant, or
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 

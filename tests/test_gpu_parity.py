@@ -206,10 +206,10 @@ DIRECT_VARIANTS = [dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT, dft.VAR
 @pytest.mark.parametrize("K", [1, 15, 16, 17, 31, 32, 33, 100, 256])
 def test_direct_copy_paths(K, variant, torch_gpu):
     """Direct-copy variants on a grid with interior and edge tiles (600 x 300
-    is 3 x 3 tiles of 256 x 128, 5 x 3 of 128 x 128): interior workgroups copy
-    whole K tiles global->LDS directly and load a ragged last K tile through
-    registers with zero fill; edge workgroups load every tile through
-    registers.  Leading dimensions are
+    is 3 x 3 tiles of 256 x 128, 5 x 3 of 128 x 128): workgroups copy whole K
+    tiles global->LDS directly (edge tiles moved back to end at M or N) and
+    load a ragged last K tile through registers with zero fill.  Leading
+    dimensions are
     multiples of 4 with NaN in every gap, so a copy that strays past column K
     or into a gap shows up, as does any write outside C."""
     M, N = 600, 300
@@ -244,6 +244,35 @@ def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
     c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=ldc, offset=offset, c_rows_extra=2)
     check_sentinels(full, M, N)
     assert np.array_equal(c.astype(np.float64), cref)
+
+
+MOVED_SHAPES = [(65, 70, 64), (129, 250, 96), (257, 300, 64), (300, 257, 33), (511, 767, 100), (520, 260, 32),
+                (256, 257, 40), (257, 256, 40)]
+MOVED_VARIANTS = [dft.VARIANT_AUTO] + DIRECT_VARIANTS
+
+
+@pytest.mark.parametrize("variant", MOVED_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in MOVED_VARIANTS])
+@pytest.mark.parametrize("shape", MOVED_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in MOVED_SHAPES])
+def test_moved_edge_tiles(shape, variant, torch_gpu):
+    """Shapes a little past one or more whole tiles in M and/or N: a
+    direct-copy workgroup whose tile overhangs M (N) computes the tile that
+    ends at M (N) instead, overlapping its neighbour, and stores only the rows
+    and columns it owns.  Checked bit for bit on integer operands (a tile
+    moved by the wrong amount gives wrong sums) and to the tolerance on
+    uniform ones, with aligned and 4-byte-offset operands, a padded C and
+    NaN around every operand, so a stray copy or write shows up."""
+    M, N, K = shape
+    a, b = workloads.make_operands(M, N, K, "integer", 900 + M + N + K)
+    cref, _ = oracle.reference(a, b)
+    for offset in (0, 1):
+        c, full = run_gemm(torch_gpu, a, b, variant, lda=K + 4, ldb=N + 4, ldc=N + 5, offset=offset,
+                           c_rows_extra=2)
+        check_sentinels(full, M, N)
+        assert np.array_equal(c.astype(np.float64), cref), (shape, offset)
+    au, bu = workloads.make_operands(M, N, K, "uniform", 950 + M + N + K)
+    cu, _ = run_gemm(torch_gpu, au, bu, variant)
+    cref_u, den_u = oracle.reference(au, bu)
+    assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
 @pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
