@@ -46,7 +46,8 @@ VARIANT_MFMA_256x256_PIPE = 15
 VARIANT_MFMA_256x256_BK32_PIPE = 16
 VARIANT_MFMA16_256x256_DIRECT = 17
 VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18
-VARIANT_COUNT = 19
+VARIANT_MFMA_64_BK32_DIRECT = 19
+VARIANT_COUNT = 20
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -82,6 +83,7 @@ VARIANT_NAMES = {
     VARIANT_MFMA_256x256_BK32_PIPE: "mfma_256x256_bk32_pipe",
     VARIANT_MFMA16_256x256_DIRECT: "mfma16_256x256_direct",
     VARIANT_MFMA16_256x256_W4_BK32_PIPE: "mfma16_256x256_w4_bk32_pipe",
+    VARIANT_MFMA_64_BK32_DIRECT: "mfma_64_bk32_direct",
 }
 
 # Every symbol the public header declares.

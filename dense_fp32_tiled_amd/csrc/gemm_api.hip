@@ -88,6 +88,15 @@ using Mfma16x256x256W4Bk32Pipe = std::conditional_t<
 template <int VEC>
 using Mfma64Direct = MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A,
                              layouts::m32_64x64x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
+// BK = 32 halves the barriers per k of the 64x64 tile (one per 16 MFMAs per
+// wave instead of 8).  With 4-byte copies it would spill (8 copies per
+// operand and wave, and their offsets); that form runs BK = 16.
+template <int VEC>
+using Mfma64Bk32Direct = std::conditional_t<
+    VEC == 4,
+    MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A, layouts::m32_64x64x32_direct::B, 4,
+            kXcdGroupedOrder, kLoadDirect>,
+    Mfma64Direct<1>>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -235,6 +244,7 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_256x256_BK32_PIPE */ mfma_variant<Mfma256x256Bk32Pipe<4>, Mfma256x256Bk32Pipe<1>>(),
     /* MFMA16_256x256_DIRECT  */ mfma_variant<Mfma16x256x256Direct<4>, Mfma16x256x256Direct<1>>(),
     /* MFMA16_256x256_W4_BK32_PIPE   */ mfma_variant<Mfma16x256x256W4Bk32Pipe<4>, Mfma16x256x256W4Bk32Pipe<1>>(),
+    /* MFMA_64_BK32_DIRECT    */ mfma_variant<Mfma64Bk32Direct<4>, Mfma64Bk32Direct<1>>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate: its
@@ -242,12 +252,11 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
 // of its tile grid, tiles / (ceil(tiles / CUs) * CUs), the fraction of
 // CU-rounds that have work.  The 256x128 and 128x128 kernels are built to
 // run two workgroups per CU; with fewer tiles than two per CU they were
-// measured about 12 % slower, which the estimate applies.  When M or N is
-// not a multiple of the tile, a kernel whose edge workgroups load through
-// registers is charged an extra round (rounds / (rounds + 1)); the 64x64
-// kernel keeps direct copies on its edges and is not.  On 26 measured
-// shapes from 512^2 x 16384 to 8192^3 (deep, flat and ragged) this picks
-// the fastest of these variants or one within 4.1 % of it.
+// measured about 12 % slower, which the estimate applies.  An edge tile
+// moves back to end at M (N) when M >= BM (N >= BN) and then costs nothing
+// extra; when M or N is smaller than the tile, a kernel whose edge
+// workgroups load through registers is charged an extra round
+// (rounds / (rounds + 1)).
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     struct Candidate {
         int variant, bm, bn, per_cu;
@@ -258,7 +267,7 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
         {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, false, 145.0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, false, 144.0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, false, 144.0},
-        {GEMM_VARIANT_MFMA_64_DIRECT, 64, 64, 1, true, 132.0},
+        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, false, 134.0},
     };
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;

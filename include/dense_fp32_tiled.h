@@ -83,7 +83,9 @@ typedef enum {
                                                  for large problems */
     GEMM_VARIANT_MFMA16_256x256_DIRECT = 17,  /* as MFMA_256x256_DIRECT with v_mfma_f32_16x16x4_f32 */
     GEMM_VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18, /* 16x16x4, 256x256x32 tile, 4 waves of 128x128, pipelined */
-    GEMM_VARIANT_COUNT = 19
+    GEMM_VARIANT_MFMA_64_BK32_DIRECT = 19,    /* as MFMA_64_DIRECT with BK = 32 (half the barriers; its 4-byte-copy
+                                                 fallback uses BK = 16): AUTO's choice for few output tiles */
+    GEMM_VARIANT_COUNT = 20
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -196,14 +198,13 @@ const char *gemm_f32_status_string(int status);
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
  * `num_cus` compute units: among MFMA_256x256_BK32_PIPE, MFMA_DIRECT
  * (256x128), the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
- * MFMA_64_DIRECT (64x64), the one with the highest rate estimate, its
- * full-chip rate (145, 144, 144, 132 TFLOP/s) times the wave quantisation of
+ * MFMA_64_BK32_DIRECT (64x64), the one with the highest rate estimate, its
+ * full-chip rate (145, 144, 144, 134 TFLOP/s) times the wave quantisation of
  * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus), times 0.88 for
  * the 256x128 and 128x128 kernels when there are fewer tiles than two per
  * CU (they are built for two workgroups per CU), and times
- * rounds / (rounds + 1) for the kernels whose edge workgroups load through
- * registers (all but 64x64) when M or N is smaller than, and not a multiple
- * of, their tile (when M >= BM and N >= BN an edge tile is moved back to end
+ * rounds / (rounds + 1) when M or N is smaller than, and not a multiple
+ * of, the tile (its edge workgroups then load through registers) (when M >= BM and N >= BN an edge tile is moved back to end
  * at M or N and runs as an interior one); a larger tile wins when within
  * 2 %.  Pure host call.  Returns a gemm_variant, or
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */

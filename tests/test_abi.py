@@ -128,20 +128,20 @@ def test_auto_variant_selection(gemm_lib):
     assert av(4096, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 512 tiles of 128x128: two per CU
     assert av(8192, 1024, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 256 tiles of 256x128: one per CU
     assert av(6144, 6144, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2304 tiles: 9 full rounds
-    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_DIRECT        # 1024 of 64x64 vs 256 of 128x128
-    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_DIRECT
-    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_DIRECT         # 512 tiles of 64x64
-    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_64_DIRECT        # deep K, 128 small tiles
-    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_DIRECT
+    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 1024 of 64x64 vs 256 of 128x128
+    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT         # 512 tiles of 64x64
+    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # deep K, 128 small tiles
+    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
-    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_DIRECT
+    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 240 tiles of 256x256
     assert av(6000, 6000, 6000, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2209 tiles in 9 rounds
     assert av(4095, 4095, 4095, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE
-    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_DIRECT        # 6400 tiles: 25 full rounds
+    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 6400 tiles: 25 full rounds
     # a dimension below the tile: every workgroup of the big kernels is an edge one
-    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_DIRECT
-    assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_DIRECT       # many more CUs than big tiles
+    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_BK32_DIRECT       # many more CUs than big tiles
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
 

@@ -104,7 +104,7 @@ WIDE_LDA = (1 << 23) + 4
 WIDE_LDB = (1 << 25) + 4
 WIDE_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
                  dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_PIPE,
-                 dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
+                 dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
 
 
 @pytest.fixture(scope="module")

@@ -28,7 +28,7 @@ ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIAN
                 dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
                 dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT,
                 dft.VARIANT_MFMA_256x256_W4_DIRECT, dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
-    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -161,7 +161,7 @@ EDGE_SHAPES = [
 
 EDGE_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA16,
                  dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT,
-                 dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT,
+                 dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT,
                  dft.VARIANT_MFMA_256x256_DIRECT]
 
 
@@ -199,7 +199,7 @@ def test_pitched_operands(pitch, variant, torch_gpu):
 DIRECT_VARIANTS = [dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
                    dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT,
                    dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
-    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
 
 
 @pytest.mark.parametrize("variant", DIRECT_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in DIRECT_VARIANTS])
@@ -225,7 +225,7 @@ def test_direct_copy_paths(K, variant, torch_gpu):
     assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
-FOUR_BYTE_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
+FOUR_BYTE_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
                       dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_256x256_BK32_PIPE]
 
 

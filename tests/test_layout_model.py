@@ -130,7 +130,7 @@ MFMA_LAYOUT_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_1
                         dft.VARIANT_MFMA_SCALAR, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_64_DIRECT,
                         dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT,
                         dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
-    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE]
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
 
 
 @pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
