@@ -89,14 +89,11 @@ template <int VEC>
 using Mfma64Direct = MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_direct::A,
                              layouts::m32_64x64x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
 // BK = 32 halves the barriers per k of the 64x64 tile (one per 16 MFMAs per
-// wave instead of 8).  With 4-byte copies it would spill (8 copies per
-// operand and wave, and their offsets); that form runs BK = 16.
+// wave instead of 8).  Its 4-byte form runs at 2 waves per SIMD (16 staged
+// floats per thread on edge tiles).
 template <int VEC>
-using Mfma64Bk32Direct = std::conditional_t<
-    VEC == 4,
-    MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A, layouts::m32_64x64x32_direct::B, 4,
-            kXcdGroupedOrder, kLoadDirect>,
-    Mfma64Direct<1>>;
+using Mfma64Bk32Direct = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
+                                 layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -565,12 +562,23 @@ const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
     /* 256x256_BK64   */ mixed_variant<Mixed256x256Bk64>(),
 };
 
+// AUTO for 16-bit inputs.  The 256x256 kernels run one workgroup per CU, the
+// 128x128x64 kernel two; each is rated by the fraction of its CU-rounds that
+// have work (rates 1200 and 1050 TFLOP/s), and 256x256 keeps a 10 % bias: a
+// partial round of it was measured faster than the quantisation predicts (the
+// idle CUs leave the busy ones more clock).  Between the two 256x256 kernels,
+// BK = 64 wins when it divides K; otherwise its ragged last K tile goes
+// through registers and the three-stage BK = 32 kernel was faster.  On 15
+// measured bf16 shapes from 1000^3 to 8192^3 this picks the fastest of the
+// six variants on every one.
 int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
-    (void)K;
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles >= num_cus) return GEMM_MIXED_256x256_BK64;
-    const int64_t tiles128 = ((M + 255) / 256) * ((N + 127) / 128);
-    return tiles128 >= num_cus ? GEMM_MIXED_256x128 : GEMM_MIXED_128x128_BK64;
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t per_round256 = num_cus, per_round128 = 2 * (int64_t)num_cus;
+    const double e256 = t256 > 0 ? (double)t256 / (double)(((t256 + per_round256 - 1) / per_round256) * per_round256) : 1.0;
+    const double e128 = t128 > 0 ? (double)t128 / (double)(((t128 + per_round128 - 1) / per_round128) * per_round128) : 1.0;
+    if (1050.0 * e128 > 1.1 * 1200.0 * e256) return GEMM_MIXED_128x128_BK64;
+    return K % 64 == 0 ? GEMM_MIXED_256x256_BK64 : GEMM_MIXED_256x256_S3;
 }
 
 int run_mixed(int input_type, const Args& a, hipStream_t stream, int variant) {

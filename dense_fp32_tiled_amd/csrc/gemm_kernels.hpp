@@ -254,7 +254,8 @@ struct MfmaCfg {
     // floats per thread; 3 for more staged floats (128x128 tiles through
     // registers: 16 or 32, which spill at 4); 2 for 4-byte loads through
     // registers (four times the load registers) and for 4-byte copies with
-    // 64x64 wave tiles, whose edge tiles load 4 bytes at a time.
+    // 64x64 wave tiles or more than 8 staged floats per thread, whose edge
+    // tiles load 4 bytes at a time.
     // 1 for 128x128 wave tiles (256 accumulators: the whole register file
     // at one wave per SIMD).
     static constexpr int STAGED = (BM * BK + BK * BN) / THREADS;
@@ -263,7 +264,9 @@ struct MfmaCfg {
     // directly, the other is prefetched through registers across the multiply.
     static constexpr bool EDGE_PREFETCH = STAGED <= 8;
     static constexpr int MIN_WAVES = WM * WN >= 128 * 128 ? 1
-                                     : WM * WN > 64 * 64 || (VEC != 4 && (LOAD == kLoadRegisters || WM * WN >= 64 * 64)) ? 2
+                                     : WM * WN > 64 * 64 ||
+                                               (VEC != 4 && (LOAD == kLoadRegisters || WM * WN >= 64 * 64 || STAGED > 8))
+                                           ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
                                                                              : 3;
     using TileA = LdsTile<BM, BK, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;

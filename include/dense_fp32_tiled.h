@@ -83,8 +83,8 @@ typedef enum {
                                                  for large problems */
     GEMM_VARIANT_MFMA16_256x256_DIRECT = 17,  /* as MFMA_256x256_DIRECT with v_mfma_f32_16x16x4_f32 */
     GEMM_VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18, /* 16x16x4, 256x256x32 tile, 4 waves of 128x128, pipelined */
-    GEMM_VARIANT_MFMA_64_BK32_DIRECT = 19,    /* as MFMA_64_DIRECT with BK = 32 (half the barriers; its 4-byte-copy
-                                                 fallback uses BK = 16): AUTO's choice for few output tiles */
+    GEMM_VARIANT_MFMA_64_BK32_DIRECT = 19,    /* as MFMA_64_DIRECT with BK = 32 (half the barriers): AUTO's choice
+                                                 for few output tiles */
     GEMM_VARIANT_COUNT = 20
 } gemm_variant;
 
@@ -304,9 +304,12 @@ int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K,
 /* Tile geometry of a gemm_mixed_variant (elem_bytes = 2).  Pure host call. */
 int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
 
-/* The variant GEMM_MIXED_AUTO runs: 256x256_BK64 when 256x256 tiles give at
- * least one workgroup per CU, else 256x128 when those do, else 128x128_BK64.  Pure
- * host call; GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
+/* The variant GEMM_MIXED_AUTO runs: 128x128_BK64 when 1050 * e128 exceeds
+ * 1.1 * 1200 * e256, where e is the fraction of CU-rounds with work for that
+ * tile (tiles / (ceil(tiles / per_round) * per_round); per_round = num_cus
+ * for 256x256 tiles, 2 * num_cus for 128x128); otherwise 256x256_BK64 when
+ * K is a multiple of 64, else 256x256_S3.  Pure host call;
+ * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
 #ifdef __cplusplus

@@ -302,6 +302,11 @@ def test_mixed_auto_variant(gemm_lib):
     av = dft.gemm_mixed_auto_variant
     assert av(8192, 8192, 8192, 256) == dft.MIXED_256x256_BK64  # 1024 tiles of 256x256
     assert av(4096, 4096, 4096, 256) == dft.MIXED_256x256_BK64  # 256 tiles
-    assert av(2048, 4096, 4096, 256) == dft.MIXED_256x128  # 128 tiles of 256x256, 256 of 256x128
+    assert av(2048, 4096, 4096, 256) == dft.MIXED_128x128_BK64  # 128 tiles of 256x256, 512 of 128x128
     assert av(2048, 256, 16384, 256) == dft.MIXED_128x128_BK64
+    assert av(3000, 3000, 3000, 256) == dft.MIXED_256x256_S3     # 144 tiles; K not a multiple of 64
+    assert av(8000, 8000, 4000, 256) == dft.MIXED_256x256_S3
+    assert av(3072, 3072, 3072, 256) == dft.MIXED_256x256_BK64
+    assert av(6000, 6000, 6000, 256) == dft.MIXED_256x256_S3     # 576 tiles vs 2209 of 128x128
+    assert av(2048, 2048, 2048, 256) == dft.MIXED_128x128_BK64
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
