@@ -98,6 +98,7 @@ EXPORTS = (
     "gemm_f32_splitk_workspace_bytes",
     "gemm_f32_splitk_auto_splits",
     "gemm_f32_auto_variant",
+    "gemm_f32_auto_variant_ex",
     "gemm_mixed_f32",
     "gemm_mixed_tile_config",
     "gemm_mixed_auto_variant",
@@ -178,6 +179,8 @@ def library(path: Path | None = None):
     lib.gemm_f32_splitk_auto_splits.restype = ctypes.c_int
     lib.gemm_f32_auto_variant.argtypes = [i64, i64, i64, i32]
     lib.gemm_f32_auto_variant.restype = ctypes.c_int
+    lib.gemm_f32_auto_variant_ex.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.gemm_f32_auto_variant_ex.restype = ctypes.c_int
     lib.gemm_mixed_f32.argtypes = [ctypes.c_int] + gemm_args[:9] + [vp, ctypes.c_int]
     lib.gemm_mixed_f32.restype = ctypes.c_int
     lib.gemm_mixed_tile_config.argtypes = [ctypes.c_int, ctypes.POINTER(TileConfig)]
@@ -247,6 +250,10 @@ def gemm_f32_splitk_auto_splits(M: int, N: int, K: int, num_cus: int) -> int:
 
 def gemm_f32_auto_variant(M: int, N: int, K: int, num_cus: int) -> int:
     return library().gemm_f32_auto_variant(M, N, K, num_cus)
+
+
+def gemm_f32_auto_variant_ex(M: int, N: int, K: int, num_cus: int, a_rows_aligned: bool, b_rows_aligned: bool) -> int:
+    return library().gemm_f32_auto_variant_ex(M, N, K, num_cus, int(a_rows_aligned), int(b_rows_aligned))
 
 
 def gemm_mixed_f32(input_type, M, N, K, A, lda, B, ldb, C, ldc, stream=None, variant=MIXED_AUTO) -> int:

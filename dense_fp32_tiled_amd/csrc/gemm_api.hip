@@ -2,6 +2,8 @@
 // variant dispatch and kernel launches for the gfx950 fp32 GEMM kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <mutex>
 #include <stdint.h>
 #include <string.h>
@@ -33,21 +35,26 @@ using Mfma16x256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m16_256x128x16_v
                           2, VEC, 256, 128, 16, 16>;
 // Direct global->LDS copies for in-range tiles (16-byte path only; the
 // 4-byte path of this variant loads through registers like MFMA).
-template <int VEC>
+// The direct-copy variants that AUTO chooses from take a copy width per
+// operand (VEC for A, VEC_B for B): an operand whose rows are 16-byte
+// aligned keeps 16-byte copies when the other's are not.  VEC_B == VEC is
+// passed as 0 (MfmaCfg's default), so the uniform forms stay one type.
+template <int VEC, int VEC_B = VEC>
 using Mfma256Direct = MfmaCfg<256, 128, 16, 64, 64, 2, 32, layouts::m32_256x128x16_direct::A,
-                              layouts::m32_256x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
-template <int VEC>
+                              layouts::m32_256x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
+                              VEC_B == VEC ? 0 : VEC_B>;
+template <int VEC, int VEC_B = VEC>
 using Mfma128Direct = MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A,
-                              layouts::m32_128x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
+                              layouts::m32_128x128x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
+                              VEC_B == VEC ? 0 : VEC_B>;
 // BK = 32 with 4-byte copies would need 32 staged floats per thread on edge
-// tiles beside the accumulators; the 4-byte form runs BK = 16.
-template <int VEC>
+// tiles beside the accumulators; the forms with a 4-byte operand run BK = 16.
+template <int VEC, int VEC_B = VEC>
 using Mfma128Bk32Direct = std::conditional_t<
-    VEC == 4,
+    VEC == 4 && VEC_B == 4,
     MfmaCfg<128, 128, 32, 64, 64, 2, 32, layouts::m32_128x128x32_direct::A, layouts::m32_128x128x32_direct::B, 4,
             kXcdGroupedOrder, kLoadDirect>,
-    MfmaCfg<128, 128, 16, 64, 64, 2, 32, layouts::m32_128x128x16_direct::A, layouts::m32_128x128x16_direct::B, 1,
-            kXcdGroupedOrder, kLoadDirect>>;
+    Mfma128Direct<VEC, VEC_B>>;
 template <int VEC>
 using Mfma256x256Direct = std::conditional_t<
     VEC == 4,
@@ -68,9 +75,10 @@ using Mfma256x256Pipe = std::conditional_t<
     MfmaCfg<256, 256, 16, 128, 64, 2, 32, layouts::m32_256x256x16_pipe::A, layouts::m32_256x256x16_pipe::B, 4,
             kXcdGroupedOrder, kLoadDirect, true>,
     Mfma256<2, 1>>;
-template <int VEC>
+template <int VEC, int VEC_B = VEC>
 using Mfma256x256Bk32Pipe = MfmaCfg<256, 256, 32, 128, 64, 2, 32, layouts::m32_256x256x32_pipe::A,
-                                    layouts::m32_256x256x32_pipe::B, VEC, kXcdGroupedOrder, kLoadDirect, true>;
+                                    layouts::m32_256x256x32_pipe::B, VEC, kXcdGroupedOrder, kLoadDirect, true,
+                                    VEC_B == VEC ? 0 : VEC_B>;
 template <int VEC>
 using Mfma16x256x256Direct = std::conditional_t<
     VEC == 4,
@@ -91,9 +99,10 @@ using Mfma64Direct = MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_di
 // BK = 32 halves the barriers per k of the 64x64 tile (one per 16 MFMAs per
 // wave instead of 8).  Its 4-byte form runs at 2 waves per SIMD (16 staged
 // floats per thread on edge tiles).
-template <int VEC>
+template <int VEC, int VEC_B = VEC>
 using Mfma64Bk32Direct = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
-                                 layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
+                                 layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
+                                 VEC_B == VEC ? 0 : VEC_B>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -120,6 +129,11 @@ struct Args {
     float* C;
     int64_t ldc;
 };
+
+// Rows of A (B) start 16-byte aligned: the operand may be loaded or copied
+// 16 bytes per lane.
+inline bool a_aligned(const Args& a) { return a.lda % 4 == 0 && ((uintptr_t)a.A & 15) == 0; }
+inline bool b_aligned(const Args& a) { return a.ldb % 4 == 0 && ((uintptr_t)a.B & 15) == 0; }
 
 struct Split;
 using LaunchFn = hipError_t (*)(const Args&, Split, hipStream_t);
@@ -207,41 +221,48 @@ gemm_tile_config valu_config(int variant, int vec) {
 struct Variant {
     LaunchFn vec4;    // 16-byte global loads (needs aligned A/B and ld % 4 == 0)
     LaunchFn scalar;  // 4-byte masked loads, any alignment
+    LaunchFn a1b4;    // 4-byte loads of A, 16-byte of B (the scalar form where not built)
+    LaunchFn a4b1;    // 16-byte loads of A, 4-byte of B
     gemm_tile_config (*config4)(int variant, int vec);
     gemm_tile_config (*config1)(int variant, int vec);
     int lds_bytes;
 };
 
-template <class C4, class C1>
+template <class C4, class C1, class C14 = C1, class C41 = C1>
 Variant mfma_variant() {
-    return Variant{launch_mfma<C4>, launch_mfma<C1>, mfma_config<C4>, mfma_config<C1>,
-                   C4::LDS_BYTES > C1::LDS_BYTES ? C4::LDS_BYTES : C1::LDS_BYTES};
+    constexpr int lds = std::max({C4::LDS_BYTES, C1::LDS_BYTES, C14::LDS_BYTES, C41::LDS_BYTES});
+    return Variant{launch_mfma<C4>, launch_mfma<C1>, launch_mfma<C14>, launch_mfma<C41>, mfma_config<C4>,
+                   mfma_config<C1>, lds};
+}
+template <template <int, int> class V>
+Variant mfma_variant_per_operand() {
+    return mfma_variant<V<4, 4>, V<1, 1>, V<1, 4>, V<4, 1>>();
 }
 
 // Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
 // to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO          */ mfma_variant<Mfma256x256Bk32Pipe<4>, Mfma256x256Bk32Pipe<1>>(),
+    /* AUTO          */ mfma_variant_per_operand<Mfma256x256Bk32Pipe>(),
     /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
-    /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, valu_config<ValuT<4>>, valu_config<ValuT<1>>,
-                         ValuT<4>::LDS_BYTES},
+    /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, launch_valu<ValuT<1>>, launch_valu<ValuT<1>>,
+                         valu_config<ValuT<4>>, valu_config<ValuT<1>>, ValuT<4>::LDS_BYTES},
     /* MFMA_STAGES1  */ mfma_variant<Mfma256<1, 4>, Mfma256<1, 1>>(),
     /* MFMA_NOPAD    */ mfma_variant<Mfma256Plain<4>, Mfma256Plain<1>>(),
     /* MFMA_SCALAR   */ mfma_variant<Mfma256<2, 1>, Mfma256<2, 1>>(),
     /* MFMA16        */ mfma_variant<Mfma16x256<4>, Mfma16x256<1>>(),
     /* MFMA_128      */ mfma_variant<Mfma128<4>, Mfma128<1>>(),
     /* MFMA_128_BK32 */ mfma_variant<Mfma128Bk32<4>, Mfma128Bk32<1>>(),
-    /* MFMA_DIRECT   */ mfma_variant<Mfma256Direct<4>, Mfma256Direct<1>>(),
-    /* MFMA_128_DIRECT      */ mfma_variant<Mfma128Direct<4>, Mfma128Direct<1>>(),
-    /* MFMA_128_BK32_DIRECT */ mfma_variant<Mfma128Bk32Direct<4>, Mfma128Bk32Direct<1>>(),
+    /* MFMA_DIRECT   */ mfma_variant_per_operand<Mfma256Direct>(),
+    /* MFMA_128_DIRECT      */ mfma_variant_per_operand<Mfma128Direct>(),
+    /* MFMA_128_BK32_DIRECT */ mfma_variant_per_operand<Mfma128Bk32Direct>(),
     /* MFMA_64_DIRECT       */ mfma_variant<Mfma64Direct<4>, Mfma64Direct<1>>(),
     /* MFMA_256x256_DIRECT  */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
     /* MFMA_256x256_W4_DIRECT */ mfma_variant<Mfma256x256W4Direct<4>, Mfma256x256W4Direct<1>>(),
     /* MFMA_256x256_PIPE      */ mfma_variant<Mfma256x256Pipe<4>, Mfma256x256Pipe<1>>(),
-    /* MFMA_256x256_BK32_PIPE */ mfma_variant<Mfma256x256Bk32Pipe<4>, Mfma256x256Bk32Pipe<1>>(),
+    /* MFMA_256x256_BK32_PIPE */ mfma_variant_per_operand<Mfma256x256Bk32Pipe>(),
     /* MFMA16_256x256_DIRECT  */ mfma_variant<Mfma16x256x256Direct<4>, Mfma16x256x256Direct<1>>(),
     /* MFMA16_256x256_W4_BK32_PIPE   */ mfma_variant<Mfma16x256x256W4Bk32Pipe<4>, Mfma16x256x256W4Bk32Pipe<1>>(),
-    /* MFMA_64_BK32_DIRECT    */ mfma_variant<Mfma64Bk32Direct<4>, Mfma64Bk32Direct<1>>(),
+    /* MFMA_64_BK32_DIRECT    */ mfma_variant_per_operand<Mfma64Bk32Direct>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate: its
@@ -251,34 +272,38 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
 // run two workgroups per CU; with fewer tiles than two per CU they were
 // measured about 12 % slower, which the estimate applies.  An edge tile
 // moves back to end at M (N) when M >= BM (N >= BN) and then costs nothing
-// extra; when M or N is smaller than the tile, a kernel whose edge
-// workgroups load through registers is charged an extra round
-// (rounds / (rounds + 1)).
-int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
+// extra; when M or N is smaller than the tile, the edge workgroups load
+// through registers and are charged an extra round (rounds / (rounds + 1)).
+// The full-chip rates depend on which operands have 16-byte aligned rows
+// (a 4-byte operand costs each kernel differently: 4-byte copies of B are
+// cheap for 256x128 tiles, those of A less so); they were measured per
+// alignment class.
+int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = true, bool b_aligned = true) {
     struct Candidate {
         int variant, bm, bn, per_cu;
-        bool edge_loop;  // edge workgroups keep direct copies for the operand in range
-        double rate;     // TFLOP/s with every CU busy (relative weights only)
+        double rate[4];  // TFLOP/s with every CU busy, by alignment: both, A only, B only, neither
     };
     const Candidate candidates[] = {
-        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, false, 145.0},
-        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, false, 144.0},
-        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2, false, 144.0},
-        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, false, 134.0},
+        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}},
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}},
+        {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
+         {144.0, 124.0, 130.0, 118.0}},
+        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}},
     };
+    const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
     for (const Candidate& c : candidates) {
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
-        double rate = c.rate * (double)tiles / (double)(rounds * num_cus);
+        double rate = c.rate[cls] * (double)tiles / (double)(rounds * num_cus);
         if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;
         // Edge tiles move back to end at M (N) and run like interior ones
-        // when M >= bm (N >= bn).  Otherwise the edge workgroups of kernels
-        // without an edge loop load every tile through registers and take
-        // about twice as long; the last of them adds about a round.
+        // when M >= bm (N >= bn).  Otherwise the edge workgroups load every
+        // tile through registers and take about twice as long; the last of
+        // them adds about a round.
         const bool edge_m = M % c.bm && M < c.bm, edge_n = N % c.bn && N < c.bn;
-        if ((edge_m || edge_n) && !c.edge_loop) rate *= (double)rounds / (double)(rounds + 1);
+        if (edge_m || edge_n) rate *= (double)rounds / (double)(rounds + 1);
         if (rate > best_rate * 1.02) {  // larger tiles win near-ties (listed first)
             best = c.variant;
             best_rate = rate;
@@ -387,9 +412,8 @@ int launch_variant(const Args& a, int variant, int max_lds, Split sp, hipStream_
     const gemm_tile_config cfg = v.config4(variant, 4);
     const int64_t tiles = ((a.M + cfg.bm - 1) / cfg.bm) * ((a.N + cfg.bn - 1) / cfg.bn);
     if (tiles > (int64_t)0x7fffffff / cfg.threads) return GEMM_ERR_TOO_LARGE;
-    const bool aligned = (a.lda % 4 == 0) && (a.ldb % 4 == 0) && (((uintptr_t)a.A & 15) == 0) &&
-                         (((uintptr_t)a.B & 15) == 0);
-    const LaunchFn fn = aligned ? v.vec4 : v.scalar;
+    const bool a_al = a_aligned(a), b_al = b_aligned(a);
+    const LaunchFn fn = a_al ? (b_al ? v.vec4 : v.a4b1) : (b_al ? v.a1b4 : v.scalar);
     return fn(a, sp, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -399,7 +423,7 @@ int run(const Args& a, hipStream_t stream, int variant) {
     bool done = false;
     const int st = prologue(a, stream, &max_lds, &num_cus, &done);
     if (st != GEMM_OK || done) return st;
-    if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(a.M, a.N, a.K, num_cus);
+    if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(a.M, a.N, a.K, num_cus, a_aligned(a), b_aligned(a));
     return launch_variant(a, variant, max_lds, Split{}, stream);
 }
 
@@ -626,6 +650,12 @@ int gemm_f32_tile_config(int variant, gemm_tile_config* out) {
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
     if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
     return auto_variant(M, N, K, num_cus);
+}
+
+int gemm_f32_auto_variant_ex(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t a_rows_aligned,
+                             int32_t b_rows_aligned) {
+    if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+    return auto_variant(M, N, K, num_cus, a_rows_aligned != 0, b_rows_aligned != 0);
 }
 
 int gemm_lds_choose_mfma_layout(int32_t bm, int32_t bn, int32_t bk, int32_t wm, int32_t wn, int32_t mb,

@@ -238,11 +238,14 @@ enum LoadPath { kLoadRegisters = 0, kLoadDirect = 1 };
 // while the first fragments of tile t+1 are read; the matrix pipe then idles
 // only for the barrier itself, not for the LDS latency behind it.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MB_, class LayA, class LayB, int VEC_,
-          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters, bool PIPE_ = false>
+          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters, bool PIPE_ = false, int VEC_B_ = 0>
 struct MfmaCfg {
     using Op = MfmaOp<MB_, 64 / MB_>;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    // VEC: floats per global load or direct copy of A; VEC_B: the same for B
+    // (defaults to VEC).  4 needs 16-byte aligned rows, 1 takes any.
     static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_, LOAD = LOAD_;
+    static constexpr int VEC_B = VEC_B_ ? VEC_B_ : VEC_;
     static constexpr bool PIPE = PIPE_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -265,7 +268,8 @@ struct MfmaCfg {
     static constexpr bool EDGE_PREFETCH = STAGED <= 8;
     static constexpr int MIN_WAVES = WM * WN >= 128 * 128 ? 1
                                      : WM * WN > 64 * 64 ||
-                                               (VEC != 4 && (LOAD == kLoadRegisters || WM * WN >= 64 * 64 || STAGED > 8))
+                                               ((VEC != 4 || VEC_B != 4) &&
+                                                (LOAD == kLoadRegisters || WM * WN >= 64 * 64 || STAGED > 8))
                                            ? 2
                                      : (LOAD == kLoadDirect || STAGED <= 12) ? 4
                                                                              : 3;
@@ -274,7 +278,7 @@ struct MfmaCfg {
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
     static_assert(KG % 4 == 0 && TileA::row_stride % 4 == 0, "A fragments are read 16 bytes at a time");
-    static_assert(TileB::row_stride % VEC == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
+    static_assert(TileB::row_stride % VEC_B == 0 && TileA::row_stride % VEC == 0, "aligned LDS stores");
     static_assert(STAGES == 1 || STAGES == 2, "one or two stages");
     static_assert(LOAD == kLoadRegisters || (STAGES == 2 && LayA::pad == 0 && LayB::pad == 0),
                   "direct copies need two stages and unpadded rows");
@@ -324,34 +328,43 @@ struct MfmaCfg {
 //
 // The address is a wave-uniform 64-bit base in scalar registers plus a
 // 32-bit byte offset per lane (no 64-bit address arithmetic per lane and
-// copy).
+// copy).  The base and LDS address are wave-uniform by construction; where
+// the compiler cannot prove it (a scalar operand must be), READ_FIRST takes
+// them from the first lane.  That costs registers elsewhere in some kernels,
+// so it is used only where needed.
+__device__ inline const void* first_lane(const void* p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return (const void*)(uintptr_t)(lo | (hi << 32));
+}
+__device__ inline uint32_t first_lane(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
+template <bool READ_FIRST = false>
 __device__ inline void copy16_to_lds(const void* uniform_base, uint32_t byte_offset, uint32_t lds_base) {
+    const void* base = READ_FIRST ? first_lane(uniform_base) : uniform_base;
+    const uint32_t lds = READ_FIRST ? first_lane(lds_base) : lds_base;
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(byte_offset), "s"(uniform_base), "s"(lds_base)
+        : "v"(byte_offset), "s"(base), "s"(lds)
         : "memory", "m0");
 }
 
 // The same copy moving 4 bytes per lane (global_load_lds_dword): LDS byte
 // address lds_base + 4 * lane; the global address needs only 4-byte
 // alignment, so it serves operands whose rows are not 16-byte aligned.
-// The base is read from the first lane: it is wave-uniform by construction,
-// but in some of the kernels that use this form the compiler cannot prove
-// it, and a scalar operand must be.
+// The base and LDS address are always read from the first lane: in some of
+// the kernels that use this form the compiler cannot prove them uniform.
 __device__ inline void copy4_to_lds(const void* uniform_base, uint32_t byte_offset, uint32_t lds_base) {
-    const uint64_t b = (uint64_t)(uintptr_t)uniform_base;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const void* base = (const void*)(uintptr_t)(lo | (hi << 32));
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dword %0, %1"
         :
-        : "v"(byte_offset), "s"(base), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base))
+        : "v"(byte_offset), "s"(first_lane(uniform_base)), "s"(first_lane(lds_base))
         : "memory", "m0");
 }
 
@@ -364,7 +377,7 @@ __device__ inline void copy4_to_lds(const void* uniform_base, uint32_t byte_offs
 // BYTES stay contiguous).  The tile is laid out in 4-byte words; an element
 // of type T is 4 / sizeof(T) per word (1 for fp32, 2 for 16-bit inputs).
 // The fetch offsets do not depend on the K tile, so they are computed once.
-template <class Tile, int THREADS, class T = float, int BYTES = 16>
+template <class Tile, int THREADS, class T = float, int BYTES = 16, bool READ_FIRST = false>
 struct DirectCopy {
     static_assert(sizeof(T) == 4 || sizeof(T) == 2, "4- or 2-byte elements");
     static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte copies");
@@ -458,7 +471,7 @@ struct DirectCopy {
         for (int i = 0; i < PER_WAVE; ++i) {
             const T* row_base = STRIDED ? origin + i * round_stride : origin;
             if constexpr (BYTES == 16)
-                copy16_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
+                copy16_to_lds<READ_FIRST>(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
             else
                 copy4_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
         }
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
             for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
 
     TileLoader<BM, BK, THREADS, Cfg::VEC> ldr_a;
-    TileLoader<BK, BN, THREADS, Cfg::VEC> ldr_b;
+    TileLoader<BK, BN, THREADS, Cfg::VEC_B> ldr_b;
     const float* a_tile = A + m0 * lda;  // advances by BK columns per K tile
     const float* b_tile = B + n0;        // advances by BK rows per K tile
     const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
@@ -651,8 +664,11 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         // when BK does not divide K) needs zero fill: it is loaded through
         // registers with masks after the multiply, so that no staging
         // registers are live across it.  Both choices are uniform.
-        using DA = DirectCopy<TileA, THREADS, float, 4 * Cfg::VEC>;
-        using DB = DirectCopy<TileB, THREADS, float, 4 * Cfg::VEC>;
+        // Kernels with different copy widths for A and B lose the compiler's
+        // proof that the 16-byte copies' bases are uniform.
+        constexpr bool READ_FIRST = Cfg::VEC != Cfg::VEC_B;
+        using DA = DirectCopy<TileA, THREADS, float, 4 * Cfg::VEC, READ_FIRST>;
+        using DB = DirectCopy<TileB, THREADS, float, 4 * Cfg::VEC_B, READ_FIRST>;
         const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
         const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
         // A's tiles are wholly in range when the workgroup's rows are (but for
@@ -753,11 +769,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                     // a time: the staging registers of whole tiles would not
                     // fit beside the live fragment buffers.
                     using LoaderA = TileLoader<BM, BK, THREADS, Cfg::VEC>;
-                    using LoaderB = TileLoader<BK, BN, THREADS, Cfg::VEC>;
+                    using LoaderB = TileLoader<BK, BN, THREADS, Cfg::VEC_B>;
                     const int64_t k0 = (t + 1) * BK;
-                    LoaderA::template copy_in_chunks<TileA, 4>(a_tile + k0, lda, M - m0, K - k0, lds_a, s ^ 1, tid);
-                    LoaderB::template copy_in_chunks<TileB, 4>(b_tile + k0 * ldb, ldb, K - k0, N - n0, lds_b, s ^ 1,
-                                                               tid);
+                    LoaderA::template copy_in_chunks<TileA, Cfg::VEC == 4 ? 4 : 2>(a_tile + k0, lda, M - m0, K - k0,
+                                                                                    lds_a, s ^ 1, tid);
+                    LoaderB::template copy_in_chunks<TileB, Cfg::VEC_B == 4 ? 4 : 2>(b_tile + k0 * ldb, ldb, K - k0,
+                                                                                      N - n0, lds_b, s ^ 1, tid);
                 }
                 wait_vector_memory();
                 __syncthreads();

@@ -131,13 +131,19 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              float *C, int64_t ldc,
              void *stream);
 
-/* As gemm_f32 with an explicit gemm_variant.  When lda or ldb is not a
- * multiple of 4, or A or B is not 16-byte aligned, 16-byte loads and direct
- * copies are illegal and the call runs the variant's 4-byte-load kernel
- * instead (a fallback, not an error; the same result up to the order of the
- * fp32 additions): the same tile for most variants, 128x128x16 for the BK = 32
- * variants and 256x128x16 for the 256x256 variants, whose register-path
- * versions would not fit their registers. */
+/* As gemm_f32 with an explicit gemm_variant.  When lda (ldb) is not a
+ * multiple of 4, or A (B) is not 16-byte aligned, that operand cannot be
+ * loaded or copied 16 bytes per lane, and the call runs the variant's kernel
+ * that moves it 4 bytes per lane instead (a fallback, not an error; the same
+ * result up to the order of the fp32 additions).  The variants AUTO chooses
+ * from (MFMA_256x256_BK32_PIPE, MFMA_DIRECT, MFMA_128_DIRECT,
+ * MFMA_128_BK32_DIRECT, MFMA_64_BK32_DIRECT) decide per operand and keep
+ * 16-byte copies for an aligned one; the others move both operands 4 bytes
+ * at a time.  The fallback kernel has the variant's tile, except 128x128x16
+ * for the 128x128x32 variants and 256x128x16 through registers for
+ * MFMA_256x256_DIRECT, MFMA_256x256_W4_DIRECT, MFMA_256x256_PIPE and the
+ * MFMA16_256x256 variants, whose 4-byte versions would not fit their
+ * registers. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,
@@ -209,6 +215,19 @@ const char *gemm_f32_status_string(int status);
  * 2 %.  Pure host call.  Returns a gemm_variant, or
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
+
+/* As gemm_f32_auto_variant for operands whose rows may not be 16-byte
+ * aligned: a_rows_aligned (b_rows_aligned) nonzero when lda (ldb) is a
+ * multiple of 4 and A (B) is 16-byte aligned, the condition under which
+ * that operand is copied 16 bytes per lane; otherwise 4 bytes per lane.
+ * The rates (TFLOP/s with every CU busy, for 256x256 pipelined, 256x128,
+ * 128x128 and 64x64x32) are, for both aligned, 145, 144, 144, 134; only A
+ * aligned 134, 140, 124, 120; only B aligned 133, 130, 130, 128; neither
+ * 130, 121, 118, 110.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies
+ * this with the operands' actual alignment.  gemm_f32_auto_variant is this
+ * with both flags set.  Pure host call. */
+int gemm_f32_auto_variant_ex(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t a_rows_aligned,
+                             int32_t b_rows_aligned);
 
 /* ---- Host-side layout model -------------------------------------------------
  * The LDS layout and bank model the kernels are compiled from, exported so

@@ -146,6 +146,23 @@ def test_auto_variant_selection(gemm_lib):
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
 
 
+def test_auto_variant_by_operand_alignment(gemm_lib):
+    ax = dft.gemm_f32_auto_variant_ex
+    # both aligned: the same as gemm_f32_auto_variant
+    for shape in [(4096, 4096, 4096), (2048, 2048, 4096), (4096, 2048, 4096), (6000, 6000, 6000)]:
+        assert ax(*shape, 256, 1, 1) == dft.gemm_f32_auto_variant(*shape, 256)
+    # measured fastest on one MI355X for each alignment class (odd K: A's rows unaligned; odd N: B's)
+    assert ax(4096, 4096, 4095, 256, 0, 1) == dft.VARIANT_MFMA_256x256_BK32_PIPE
+    assert ax(4096, 4095, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT   # 4-byte B copies are cheap at 256x128
+    assert ax(8192, 8191, 8192, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
+    assert ax(4095, 4095, 4095, 256, 0, 0) == dft.VARIANT_MFMA_256x256_BK32_PIPE
+    assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
+    assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
+    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(-1, 4, 4, 256, 1, 1) == dft.GEMM_ERR_INVALID_DIM
+
+
 # ---- host-side argument validation: every case returns before any device call ----
 FAKE_A, FAKE_B, FAKE_C = 0x10000, 0x200000, 0x4000000  # never dereferenced
 

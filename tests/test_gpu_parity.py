@@ -246,6 +246,34 @@ def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
     assert np.array_equal(c.astype(np.float64), cref)
 
 
+PER_OPERAND_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_BK32_PIPE, dft.VARIANT_MFMA_DIRECT,
+                        dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT]
+
+
+@pytest.mark.parametrize("variant", PER_OPERAND_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in PER_OPERAND_VARIANTS])
+@pytest.mark.parametrize("which", ["a", "b"])
+@pytest.mark.parametrize("K", [16, 33, 100, 257])
+def test_one_operand_unaligned(K, which, variant, torch_gpu):
+    """Only A's rows (or only B's) are not 16-byte aligned: the variants
+    AUTO chooses from then copy that operand 4 bytes per lane and the other
+    16 bytes per lane.  600 x 520 spans interior and moved edge tiles of
+    every tile size; NaN fills every ld gap, so a copy that strays past
+    column K or N or into a gap shows up, as does any write outside C."""
+    M, N = 600, 520
+    lda = K + (4 - K % 4) % 4 + (1 if which == "a" else 4)
+    ldb = N + (1 if which == "b" else 4)
+    assert (lda % 4 != 0) == (which == "a") and (ldb % 4 != 0) == (which == "b")
+    a, b = workloads.make_operands(M, N, K, "integer", 1300 + K)
+    cref, _ = oracle.reference(a, b)
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=N + 3, c_rows_extra=2)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref)
+    au, bu = workloads.make_operands(M, N, K, "uniform", 1400 + K)
+    cu, _ = run_gemm(torch_gpu, au, bu, variant, lda=lda, ldb=ldb)
+    cref_u, den_u = oracle.reference(au, bu)
+    assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
+
+
 MOVED_SHAPES = [(65, 70, 64), (129, 250, 96), (257, 300, 64), (300, 257, 33), (511, 767, 100), (520, 260, 32),
                 (256, 257, 40), (257, 256, 40)]
 MOVED_VARIANTS = [dft.VARIANT_AUTO] + DIRECT_VARIANTS
