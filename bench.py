@@ -28,7 +28,8 @@ PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and packed vector): 256 CU
 PEAK_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak (no sparsity)
 METRIC = "fp32 GEMM TFLOP/s at 4096³ on 1 MI355X; % of fp32 peak"
 METRIC_16BIT = "{t}-input GEMM (fp32 accumulate) TFLOP/s on 1 MI355X; % of dense {t} peak"
-KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "lds_layout.hpp", "pad_choice.hpp", "layout_gen.cpp",
+KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "gemm_default.hip", "default_config.hpp", "launch.hpp",
+                  "lds_layout.hpp", "pad_choice.hpp", "layout_gen.cpp",
                   "mfma_shapes.def", "mixed_kernels.hpp", "mixed_shapes.def"]
 
 

@@ -22,7 +22,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libdense_fp32_tiled.so"
-SOURCES = [CSRC / "gemm_api.hip"]
+SOURCES = [CSRC / "gemm_api.hip", CSRC / "gemm_default.hip"]
 PROBE_LIB = PKG / "liblds_probe.so"
 PROBE_SOURCES = [CSRC / "lds_probe.hip"]
 ARCH = "gfx950"
@@ -51,21 +51,27 @@ LAYOUT_HEADER = GENERATED / "mfma_layouts.hpp"
 
 def generate_layouts() -> Path:
     """Compile and run the host layout search (layout_gen.cpp, plain C++17
-    with g++), writing csrc/generated/mfma_layouts.hpp for the kernels."""
+    with g++), writing csrc/generated/mfma_layouts.hpp for the kernels.
+    Safe to run from several processes at once: the search is built in a
+    private directory and the header replaced atomically."""
+    import tempfile
+
     GENERATED.mkdir(exist_ok=True)
-    exe = GENERATED / "layout_gen"
-    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", f"-I{CSRC}", str(LAYOUT_GEN_SRC), "-o", str(exe)],
-                   check=True)
-    text = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
-    tmp = LAYOUT_HEADER.with_suffix(".tmp")
-    tmp.write_text(text)
+    with tempfile.TemporaryDirectory() as work:
+        exe = Path(work) / "layout_gen"
+        subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", f"-I{CSRC}", str(LAYOUT_GEN_SRC), "-o", str(exe)],
+                       check=True)
+        text = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    fd, tmp = tempfile.mkstemp(dir=GENERATED, prefix=".mfma_layouts.", suffix=".tmp")
+    with os.fdopen(fd, "w") as f:
+        f.write(text)
     os.replace(tmp, LAYOUT_HEADER)
     return LAYOUT_HEADER
 
 
 def build(out: Path = LIB, extra: list[str] | None = None, sources: list[Path] | None = None) -> Path:
     """Compile the library (always recompiles)."""
-    tmp = out.with_name(out.name + ".tmp")
+    tmp = out.with_name(f"{out.name}.{os.getpid()}.tmp")
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{ROOT / 'include'}", f"-I{CSRC}",
            *[str(s) for s in (sources or SOURCES)], "-o", str(tmp)]
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,15 +89,18 @@ def build_all() -> list[Path]:
 
 def device_assembly(source: Path | None = None) -> str:
     """The gfx950 assembly hipcc emits for the library's device code (the
-    same flags as the build), as text."""
+    same flags as the build), as text: of `source`, or of every library
+    source concatenated."""
     import tempfile
 
+    if source is None:
+        return "\n".join(device_assembly(src) for src in SOURCES)
     generate_layouts()
     with tempfile.TemporaryDirectory() as tmp:
         out = Path(tmp) / "device.s"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
                "-packed-fp32-ops", "--cuda-device-only", "-S", f"-I{ROOT / 'include'}", f"-I{CSRC}",
-               str(source or SOURCES[0]), "-o", str(out)]
+               str(source), "-o", str(out)]
         proc = subprocess.run(cmd, capture_output=True, text=True)
         if proc.returncode != 0:
             sys.stderr.write(proc.stderr)
@@ -103,18 +112,23 @@ def resource_report(source: Path | None = None) -> dict[str, dict[str, int]]:
     """The compiler's per-kernel resource usage for the library's device code
     (hipcc -Rpass-analysis=kernel-resource-usage): {mangled kernel name:
     {"vgpr", "agpr", "scratch" (bytes per lane), "occupancy" (waves per SIMD),
-    "lds" (bytes per workgroup)}}.  Compiles device code only, to a
-    temporary object."""
+    "lds" (bytes per workgroup)}}, of `source` or of every library source.
+    Compiles device code only, to a temporary object."""
     import re
     import tempfile
 
+    if source is None:
+        merged: dict[str, dict[str, int]] = {}
+        for src in SOURCES:
+            merged.update(resource_report(src))
+        return merged
     generate_layouts()
     fields = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
               "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
     with tempfile.TemporaryDirectory() as tmp:
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
                "-packed-fp32-ops", "--cuda-device-only", "-c", f"-I{ROOT / 'include'}", f"-I{CSRC}",
-               str(source or SOURCES[0]), "-o", str(Path(tmp) / "device.o"), "-Rpass-analysis=kernel-resource-usage"]
+               str(source), "-o", str(Path(tmp) / "device.o"), "-Rpass-analysis=kernel-resource-usage"]
         proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stderr)

@@ -9,11 +9,42 @@
 #include <string.h>
 
 #include "dense_fp32_tiled.h"
+#include "default_config.hpp"
 #include "gemm_kernels.hpp"
+#include "launch.hpp"
 #include "mixed_kernels.hpp"
 #include "generated/mfma_layouts.hpp"
 #include "pad_choice.hpp"
 #include <type_traits>
+
+namespace dft {
+
+// --------------------------------------------------------------------------
+// Split-K reduction: C[i][j] = sum over s = 0, 1, ..., S-1 (in that order) of
+// W[s][i][j], where W holds S packed M x N partial products.  The fixed order
+// makes the result deterministic.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N, int64_t S,
+                                                            const float* __restrict__ W, float* __restrict__ C,
+                                                            int64_t ldc) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = W[i];
+        for (int64_t s = 1; s < S; ++s) acc += W[s * total + i];
+        C[(i / N) * ldc + (i % N)] = acc;
+    }
+}
+
+// --------------------------------------------------------------------------
+// K == 0: C's M x N region is an empty sum.
+__global__ void zero_fill_kernel(int64_t M, int64_t N, float* __restrict__ C, int64_t ldc) {
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x)
+        C[(i / N) * ldc + (i % N)] = 0.0f;
+}
+
+}  // namespace dft
 
 namespace {
 
@@ -75,10 +106,6 @@ using Mfma256x256Pipe = std::conditional_t<
     MfmaCfg<256, 256, 16, 128, 64, 2, 32, layouts::m32_256x256x16_pipe::A, layouts::m32_256x256x16_pipe::B, 4,
             kXcdGroupedOrder, kLoadDirect, true>,
     Mfma256<2, 1>>;
-template <int VEC, int VEC_B = VEC>
-using Mfma256x256Bk32Pipe = MfmaCfg<256, 256, 32, 128, 64, 2, 32, layouts::m32_256x256x32_pipe::A,
-                                    layouts::m32_256x256x32_pipe::B, VEC, kXcdGroupedOrder, kLoadDirect, true,
-                                    VEC_B == VEC ? 0 : VEC_B>;
 template <int VEC>
 using Mfma16x256x256Direct = std::conditional_t<
     VEC == 4,
@@ -119,59 +146,6 @@ constexpr int kValuPadB = valu_pad_b(kValuShape, kGfx950Lds);
 
 template <int VEC>
 using ValuT = ValuCfg<128, 128, 16, 8, 8, 2, kValuPadA, kValuPadB, VEC>;
-
-struct Args {
-    int64_t M, N, K;
-    const float* A;
-    int64_t lda;
-    const float* B;
-    int64_t ldb;
-    float* C;
-    int64_t ldc;
-};
-
-// Rows of A (B) start 16-byte aligned: the operand may be loaded or copied
-// 16 bytes per lane.
-inline bool a_aligned(const Args& a) { return a.lda % 4 == 0 && ((uintptr_t)a.A & 15) == 0; }
-inline bool b_aligned(const Args& a) { return a.ldb % 4 == 0 && ((uintptr_t)a.B & 15) == 0; }
-
-struct Split;
-using LaunchFn = hipError_t (*)(const Args&, Split, hipStream_t);
-
-// Launches go through hipLaunchKernel so that the returned status is this
-// launch's own (hipGetLastError would also report errors left by earlier,
-// unrelated runtime calls on the thread).
-// K slicing of one launch: `splits` slices of k_chunk (a multiple of BK)
-// along gridDim.y, slice s writing C + s * c_split_stride.  A plain launch is
-// one slice covering all of K.
-struct Split {
-    int64_t splits = 1, k_chunk = 0, c_split_stride = 0;
-};
-
-template <class Kernel>
-hipError_t launch_tiles(Kernel kernel, int bm, int bn, int threads, const Args& a, Split sp, hipStream_t stream) {
-    int64_t M = a.M, N = a.N, K = a.K, lda = a.lda, ldb = a.ldb, ldc = a.ldc;
-    const float* A = a.A;
-    const float* B = a.B;
-    float* C = a.C;
-    int64_t tiles_m = (M + bm - 1) / bm;
-    int64_t tiles_n = (N + bn - 1) / bn;
-    int64_t k_chunk = sp.splits > 1 ? sp.k_chunk : (K > 0 ? K : 1);
-    int64_t c_split_stride = sp.c_split_stride;
-    void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_m, &tiles_n, &k_chunk, &c_split_stride};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)(tiles_m * tiles_n), (unsigned)sp.splits),
-                           dim3(threads), args, 0, stream);
-}
-
-template <class Cfg>
-hipError_t launch_mfma(const Args& a, Split sp, hipStream_t stream) {
-    return launch_tiles(gemm_mfma_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
-}
-
-template <class Cfg>
-hipError_t launch_valu(const Args& a, Split sp, hipStream_t stream) {
-    return launch_tiles(gemm_valu_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
-}
 
 template <class Cfg>
 void describe_common(gemm_tile_config& c, int variant, int vec) {
@@ -238,11 +212,22 @@ template <template <int, int> class V>
 Variant mfma_variant_per_operand() {
     return mfma_variant<V<4, 4>, V<1, 1>, V<1, 4>, V<4, 1>>();
 }
+// The default kernel: its 16-byte form is launched from its own translation
+// unit (gemm_default.hip), so this one never instantiates it.
+Variant default_variant() {
+    using P4 = Mfma256x256Bk32Pipe<4>;
+    using P1 = Mfma256x256Bk32Pipe<1>;
+    using P14 = Mfma256x256Bk32Pipe<1, 4>;
+    using P41 = Mfma256x256Bk32Pipe<4, 1>;
+    constexpr int lds = std::max({P4::LDS_BYTES, P1::LDS_BYTES, P14::LDS_BYTES, P41::LDS_BYTES});
+    return Variant{launch_default_vec4, launch_mfma<P1>, launch_mfma<P14>, launch_mfma<P41>, mfma_config<P4>,
+                   mfma_config<P1>, lds};
+}
 
 // Index = gemm_variant.  AUTO's entry is never launched (run() resolves AUTO
 // to a concrete variant first); it describes the large-problem default.
 const Variant kVariants[GEMM_VARIANT_COUNT] = {
-    /* AUTO          */ mfma_variant_per_operand<Mfma256x256Bk32Pipe>(),
+    /* AUTO          */ default_variant(),
     /* MFMA          */ mfma_variant<Mfma256<2, 4>, Mfma256<2, 1>>(),
     /* VALU          */ {launch_valu<ValuT<4>>, launch_valu<ValuT<1>>, launch_valu<ValuT<1>>, launch_valu<ValuT<1>>,
                          valu_config<ValuT<4>>, valu_config<ValuT<1>>, ValuT<4>::LDS_BYTES},
@@ -259,7 +244,7 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_256x256_DIRECT  */ mfma_variant<Mfma256x256Direct<4>, Mfma256x256Direct<1>>(),
     /* MFMA_256x256_W4_DIRECT */ mfma_variant<Mfma256x256W4Direct<4>, Mfma256x256W4Direct<1>>(),
     /* MFMA_256x256_PIPE      */ mfma_variant<Mfma256x256Pipe<4>, Mfma256x256Pipe<1>>(),
-    /* MFMA_256x256_BK32_PIPE */ mfma_variant_per_operand<Mfma256x256Bk32Pipe>(),
+    /* MFMA_256x256_BK32_PIPE */ default_variant(),
     /* MFMA16_256x256_DIRECT  */ mfma_variant<Mfma16x256x256Direct<4>, Mfma16x256x256Direct<1>>(),
     /* MFMA16_256x256_W4_BK32_PIPE   */ mfma_variant<Mfma16x256x256W4Bk32Pipe<4>, Mfma16x256x256W4Bk32Pipe<1>>(),
     /* MFMA_64_BK32_DIRECT    */ mfma_variant_per_operand<Mfma64Bk32Direct>(),

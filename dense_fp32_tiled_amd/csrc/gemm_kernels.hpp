@@ -998,29 +998,4 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel
     }
 }
 
-// --------------------------------------------------------------------------
-// Split-K reduction: C[i][j] = sum over s = 0, 1, ..., S-1 (in that order) of
-// W[s][i][j], where W holds S packed M x N partial products.  The fixed order
-// makes the result deterministic.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(int64_t M, int64_t N, int64_t S,
-                                                            const float* __restrict__ W, float* __restrict__ C,
-                                                            int64_t ldc) {
-    const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        float acc = W[i];
-        for (int64_t s = 1; s < S; ++s) acc += W[s * total + i];
-        C[(i / N) * ldc + (i % N)] = acc;
-    }
-}
-
-// --------------------------------------------------------------------------
-// K == 0: C's M x N region is an empty sum.
-__global__ void zero_fill_kernel(int64_t M, int64_t N, float* __restrict__ C, int64_t ldc) {
-    const int64_t total = M * N;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x)
-        C[(i / N) * ldc + (i % N)] = 0.0f;
-}
-
 }  // namespace dft
