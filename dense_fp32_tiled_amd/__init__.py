@@ -47,7 +47,10 @@ VARIANT_MFMA_256x256_BK32_PIPE = 16
 VARIANT_MFMA16_256x256_DIRECT = 17
 VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18
 VARIANT_MFMA_64_BK32_DIRECT = 19
-VARIANT_COUNT = 20
+VARIANT_MFMA_64_KS4 = 20
+VARIANT_MFMA_32x64_KS4 = 21
+VARIANT_MFMA_32x32_KS8 = 22
+VARIANT_COUNT = 23
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -84,6 +87,9 @@ VARIANT_NAMES = {
     VARIANT_MFMA16_256x256_DIRECT: "mfma16_256x256_direct",
     VARIANT_MFMA16_256x256_W4_BK32_PIPE: "mfma16_256x256_w4_bk32_pipe",
     VARIANT_MFMA_64_BK32_DIRECT: "mfma_64_bk32_direct",
+    VARIANT_MFMA_64_KS4: "mfma_64_ks4",
+    VARIANT_MFMA_32x64_KS4: "mfma_32x64_ks4",
+    VARIANT_MFMA_32x32_KS8: "mfma_32x32_ks8",
 }
 
 # Every symbol the public header declares.
@@ -125,7 +131,7 @@ class TileConfig(ctypes.Structure):
         "b_rows", "b_cols", "b_pad", "b_row_stride", "b_stage_elems",
         "lds_bytes", "vec_width", "lds_banks_b32", "lds_lanes_b32", "lds_banks_b128", "lds_lanes_b128",
         "a_transposed", "a_swz_unit", "a_swz_shift", "a_swz_mask", "b_swz_unit", "b_swz_shift", "b_swz_mask",
-        "mfma_block", "xcd_tile_order", "direct_to_lds", "elem_bytes")]
+        "mfma_block", "xcd_tile_order", "direct_to_lds", "elem_bytes", "k_groups")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

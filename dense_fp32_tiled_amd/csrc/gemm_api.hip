@@ -130,6 +130,22 @@ template <int VEC, int VEC_B = VEC>
 using Mfma64Bk32Direct = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
                                  layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
                                  VEC_B == VEC ? 0 : VEC_B>;
+// Bases of the K-split variants (KsplitCfg): 32x64 and 32x32 tiles of
+// 32x32-wave blocks, BK = 32.
+template <int VEC, int VEC_B = VEC>
+using Mfma32x64Direct = MfmaCfg<32, 64, 32, 32, 32, 2, 32, layouts::m32_32x64x32_direct::A,
+                                layouts::m32_32x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
+                                VEC_B == VEC ? 0 : VEC_B>;
+template <int VEC, int VEC_B = VEC>
+using Mfma32x32Direct = MfmaCfg<32, 32, 32, 32, 32, 2, 32, layouts::m32_32x32x32_direct::A,
+                                layouts::m32_32x32x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
+                                VEC_B == VEC ? 0 : VEC_B>;
+template <int VEC, int VEC_B = VEC>
+using Mfma64Ks4 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 4>;
+template <int VEC, int VEC_B = VEC>
+using Mfma32x64Ks4 = KsplitCfg<Mfma32x64Direct<VEC, VEC_B>, 4>;
+template <int VEC, int VEC_B = VEC>
+using Mfma32x32Ks8 = KsplitCfg<Mfma32x32Direct<VEC, VEC_B>, 8>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -169,6 +185,7 @@ void describe_common(gemm_tile_config& c, int variant, int vec) {
     c.xcd_tile_order = Cfg::ORDER == kXcdGroupedOrder ? 1 : 0;
     c.direct_to_lds = Cfg::LOAD == kLoadDirect ? 1 : 0;
     c.elem_bytes = 4;
+    c.k_groups = 1;
 }
 
 template <class Cfg>
@@ -178,6 +195,8 @@ gemm_tile_config mfma_config(int variant, int vec) {
     c.tm = Cfg::WM; c.tn = Cfg::WN;
     c.a_transposed = 0;
     c.mfma_block = Cfg::Op::MB;
+    c.k_groups = Cfg::KSPLIT;
+    c.barriers_per_tile = Cfg::STAGES == 2 * Cfg::KSPLIT ? 1 : 2;  // per K tile of a group
     if (Cfg::PIPE) c.direct_to_lds = 2;
     return c;
 }
@@ -211,6 +230,12 @@ Variant mfma_variant() {
 template <template <int, int> class V>
 Variant mfma_variant_per_operand() {
     return mfma_variant<V<4, 4>, V<1, 1>, V<1, 4>, V<4, 1>>();
+}
+template <template <int, int> class V>
+Variant ksplit_variant() {
+    constexpr int lds = std::max({V<4, 4>::LDS_BYTES, V<1, 1>::LDS_BYTES, V<1, 4>::LDS_BYTES, V<4, 1>::LDS_BYTES});
+    return Variant{launch_ksplit<V<4, 4>>, launch_ksplit<V<1, 1>>, launch_ksplit<V<1, 4>>, launch_ksplit<V<4, 1>>,
+                   mfma_config<V<4, 4>>, mfma_config<V<1, 1>>, lds};
 }
 // The default kernel: its 16-byte form is launched from its own translation
 // unit (gemm_default.hip), so this one never instantiates it.
@@ -248,6 +273,9 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA16_256x256_DIRECT  */ mfma_variant<Mfma16x256x256Direct<4>, Mfma16x256x256Direct<1>>(),
     /* MFMA16_256x256_W4_BK32_PIPE   */ mfma_variant<Mfma16x256x256W4Bk32Pipe<4>, Mfma16x256x256W4Bk32Pipe<1>>(),
     /* MFMA_64_BK32_DIRECT    */ mfma_variant_per_operand<Mfma64Bk32Direct>(),
+    /* MFMA_64_KS4            */ ksplit_variant<Mfma64Ks4>(),
+    /* MFMA_32x64_KS4         */ ksplit_variant<Mfma32x64Ks4>(),
+    /* MFMA_32x32_KS8         */ ksplit_variant<Mfma32x32Ks8>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate: its
@@ -262,27 +290,39 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
 // The full-chip rates depend on which operands have 16-byte aligned rows
 // (a 4-byte operand costs each kernel differently: 4-byte copies of B are
 // cheap for 256x128 tiles, those of A less so); they were measured per
-// alignment class.
+// alignment class.  The 64x64 kernel's 4-wave workgroups reach its full
+// rate only at three or more per CU.  When few output tiles meet a deep K,
+// the K-split variants keep every CU's SIMDs busy with one workgroup.
 int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = true, bool b_aligned = true) {
     struct Candidate {
         int variant, bm, bn, per_cu;
-        double rate[4];  // TFLOP/s with every CU busy, by alignment: both, A only, B only, neither
+        double rate[4];   // TFLOP/s with every CU busy, by alignment: both, A only, B only, neither
+        bool small_wg;    // 4-wave workgroups: below full rate at one or two per CU
+        int64_t min_k;    // K-split variants: enough K tiles for every group (0: any K)
     };
     const Candidate candidates[] = {
-        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}},
-        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}},
+        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0},
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
-         {144.0, 124.0, 130.0, 118.0}},
-        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}},
+         {144.0, 124.0, 130.0, 118.0}, false, 0},
+        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0},
+        // K split inside the workgroup (16 K tiles of 32 per group at least);
+        // measured with both operands aligned only, so offered only then.
+        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 4},
+        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 4},
+        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 8},
     };
     const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
     for (const Candidate& c : candidates) {
+        if (c.rate[cls] <= 0.0 || K < c.min_k) continue;
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
         double rate = c.rate[cls] * (double)tiles / (double)(rounds * num_cus);
         if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;
+        // One 4-wave workgroup per CU measured 78 % of the full rate, two 89 %.
+        if (c.small_wg) rate *= tiles <= num_cus ? 0.78 : tiles <= 2 * (int64_t)num_cus ? 0.89 : 1.0;
         // Edge tiles move back to end at M (N) and run like interior ones
         // when M >= bm (N >= bn).  Otherwise the edge workgroups load every
         // tile through registers and take about twice as long; the last of

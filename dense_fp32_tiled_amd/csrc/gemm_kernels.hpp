@@ -247,6 +247,7 @@ struct MfmaCfg {
     static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_, LOAD = LOAD_;
     static constexpr int VEC_B = VEC_B_ ? VEC_B_ : VEC_;
     static constexpr bool PIPE = PIPE_;
+    static constexpr int KSPLIT = 1;  // wave groups splitting K inside the workgroup (KsplitCfg)
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
     static constexpr int MI = WM / Op::MB, NI = WN / Op::NB;
@@ -850,6 +851,184 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
     }
 
     store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
+}
+
+// --------------------------------------------------------------------------
+// K split inside the workgroup.  KSPLIT groups of waves share one output
+// tile: group q reduces the K tiles t = q, q + KSPLIT, q + 2 KSPLIT, ... in a
+// pair of LDS stages of its own, with Base's wave tiling, direct copies and
+// two-stage loop (the copy of its next tile in flight during the multiply of
+// the current one).  A grid of few output tiles (deep K, small M and N) then
+// still runs several waves per SIMD, without a workspace.  Every group runs
+// ceil(T / KSPLIT) iterations (a group past its last tile skips the
+// multiply), so all waves reach every barrier.  At the end groups 1 ..
+// KSPLIT-1 leave their partial sums in LDS; wave w of every group holds the
+// same outputs in the same lanes and registers, so they are written and read
+// back in lane order.  Group 0 adds them in group order (a fixed order: the
+// result is deterministic) and stores C.
+template <class Base, int KSPLIT_>
+struct KsplitCfg {
+    static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2 && !Base::PIPE,
+                  "groups run Base's two-stage direct-copy loop");
+    static_assert(KSPLIT_ >= 2, "at least two groups");
+    using Op = typename Base::Op;
+    static constexpr int KSPLIT = KSPLIT_;
+    static constexpr int BM = Base::BM, BN = Base::BN, BK = Base::BK, WM = Base::WM, WN = Base::WN;
+    static constexpr int VEC = Base::VEC, VEC_B = Base::VEC_B, ORDER = Base::ORDER, LOAD = kLoadDirect;
+    static constexpr bool PIPE = false;
+    static constexpr int WAVES_N = Base::WAVES_N, MI = Base::MI, NI = Base::NI, KG = Base::KG;
+    static constexpr int GROUP_THREADS = Base::THREADS, GROUP_WAVES = GROUP_THREADS / kWave;
+    static constexpr int THREADS = GROUP_THREADS * KSPLIT;
+    static constexpr int STAGES = 2 * KSPLIT;  // stages 2q, 2q+1 belong to group q
+    static constexpr int MIN_WAVES = Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES : THREADS / 256;
+    using TileA = LdsTile<BM, BK, 0, STAGES, Base::TileA::swizzle.unit, Base::TileA::swizzle.shift,
+                          Base::TileA::swizzle.mask>;
+    using TileB = LdsTile<BK, BN, 0, STAGES, Base::TileB::swizzle.unit, Base::TileB::swizzle.shift,
+                          Base::TileB::swizzle.mask>;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    // partial sums of groups 1 .. KSPLIT-1, over the stages' LDS
+    static constexpr int PARTIAL_VALUES = MI * NI * Op::ACC;  // per lane
+    static_assert((KSPLIT - 1) * GROUP_WAVES * PARTIAL_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
+                  "the partial sums fit in the stages");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit_kernel(
+    int64_t M, int64_t N, int64_t K_total, const float* __restrict__ A_in, int64_t lda,
+    const float* __restrict__ B_in, int64_t ldb, float* __restrict__ C_out, int64_t ldc, int64_t tiles_m,
+    int64_t tiles_n, int64_t k_chunk, int64_t c_split_stride) {
+    const KSlice ks = k_slice(A_in, B_in, C_out, K_total, ldb, k_chunk, c_split_stride);
+    const float* __restrict__ A = ks.A;
+    const float* __restrict__ B = ks.B;
+    float* __restrict__ C = ks.C;
+    const int64_t K = ks.K;
+    using Op = typename Cfg::Op;
+    using TileA = typename Cfg::TileA;
+    using TileB = typename Cfg::TileB;
+    using acc_t = typename Op::acc_t;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, KG = Cfg::KG, KS = Cfg::KSPLIT;
+    constexpr int MI = Cfg::MI, NI = Cfg::NI, GT = Cfg::GROUP_THREADS;
+
+    // One array: A's stages, then B's; the partial sums reuse all of it.
+    __shared__ __attribute__((aligned(16))) float lds[TileA::total_elems + TileB::total_elems];
+    float* const lds_a = lds;
+    float* const lds_b = lds + TileA::total_elems;
+
+    const int tid = threadIdx.x;
+    const int group = __builtin_amdgcn_readfirstlane(tid / GT);  // whole waves belong to one group
+    const int gtid = tid % GT;                                     // thread within the group
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(gtid / kWave);  // wave within the group
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int g = lane / Op::MB, r = lane % Op::MB;
+
+    const TileCoord own = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord tc = operand_origin<Cfg>(own, M, N);
+    const int64_t m0 = tc.m0, n0 = tc.n0;
+
+    acc_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
+
+    TileLoader<BM, BK, GT, Cfg::VEC> ldr_a;
+    TileLoader<BK, BN, GT, Cfg::VEC_B> ldr_b;
+    const float* a_tile = A + m0 * lda;
+    const float* b_tile = B + n0;
+    const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;  // K tiles
+    const int64_t TF = K / BK;                        // K tiles wholly in range
+    const int64_t ITERS = (T + KS - 1) / KS;          // per group
+
+    constexpr bool READ_FIRST = Cfg::VEC != Cfg::VEC_B;
+    using DA = DirectCopy<TileA, GT, float, 4 * Cfg::VEC, READ_FIRST>;
+    using DB = DirectCopy<TileB, GT, float, 4 * Cfg::VEC_B, READ_FIRST>;
+    const DA dma_a(lda, wave, lane);
+    const DB dma_b(ldb, wave, lane);
+    const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda, A) && DB::fits(ldb, B);
+
+    // Tile t of this group into stage `stage`: directly when in range, else
+    // through registers with zero fill (by the group's threads).
+    auto copy_direct = [&](int64_t t, int stage) {
+        dma_a.issue(a_tile + t * BK, lds_a, stage);
+        dma_b.issue(b_tile + t * BK * ldb, lds_b, stage);
+    };
+    auto copy_registers = [&](int64_t t, int stage) {
+        const int64_t k0 = t * BK;
+        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, gtid);
+        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, gtid);
+        ldr_a.template store<TileA>(lds_a, stage, gtid);
+        ldr_b.template store<TileB>(lds_b, stage, gtid);
+    };
+    auto multiply = [&](int stage) {
+        floatx4 af[MI][KG / 4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int q = 0; q < KG / 4; ++q)
+                af[i][q] = *reinterpret_cast<const floatx4*>(
+                    lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, g * KG + 4 * q));
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+            float bf[NI];
+#pragma unroll
+            for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, g * KG + j, wn0 + n * Op::NB + r)];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[n], acc[i][n]);
+        }
+    };
+
+    const int stage0 = 2 * group;
+    if (group < T) {
+        if (interior && group < TF)
+            copy_direct(group, stage0);
+        else
+            copy_registers(group, stage0);
+    }
+    wait_vector_memory();
+    __syncthreads();
+    for (int64_t it = 0; it < ITERS; ++it) {
+        const int s = stage0 + (int)(it & 1), ns = stage0 + (int)((it & 1) ^ 1);
+        const int64_t t = it * KS + group, tn = t + KS;
+        const bool direct = interior && tn < TF;
+        if (direct) copy_direct(tn, ns);
+        if (t < T) multiply(s);
+        if (tn < T && !direct) copy_registers(tn, ns);
+        wait_vector_memory();
+        __syncthreads();
+    }
+
+    // Every LDS read of the loop completed before its last barrier.
+    constexpr int PV = Cfg::PARTIAL_VALUES;
+    if (group > 0) {
+        float* dst = lds + ((group - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
+        int j = 0;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int n = 0; n < NI; ++n)
+#pragma unroll
+                for (int v = 0; v < Op::ACC; ++v) dst[(j++) * kWave] = acc[i][n][v];
+    }
+    __syncthreads();
+    if (group == 0) {
+        for (int q = 1; q < KS; ++q) {
+            const float* src = lds + ((q - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
+            int j = 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n)
+#pragma unroll
+                    for (int v = 0; v < Op::ACC; ++v) acc[i][n][v] += src[(j++) * kWave];
+        }
+        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
+    }
 }
 
 // --------------------------------------------------------------------------

@@ -58,6 +58,11 @@ hipError_t launch_mfma(const Args& a, Split sp, hipStream_t stream) {
 }
 
 template <class Cfg>
+hipError_t launch_ksplit(const Args& a, Split sp, hipStream_t stream) {
+    return launch_tiles(gemm_mfma_ksplit_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
+}
+
+template <class Cfg>
 hipError_t launch_valu(const Args& a, Split sp, hipStream_t stream) {
     return launch_tiles(gemm_valu_kernel<Cfg>, Cfg::BM, Cfg::BN, Cfg::THREADS, a, sp, stream);
 }

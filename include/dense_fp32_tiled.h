@@ -85,7 +85,11 @@ typedef enum {
     GEMM_VARIANT_MFMA16_256x256_W4_BK32_PIPE = 18, /* 16x16x4, 256x256x32 tile, 4 waves of 128x128, pipelined */
     GEMM_VARIANT_MFMA_64_BK32_DIRECT = 19,    /* as MFMA_64_DIRECT with BK = 32 (half the barriers): AUTO's choice
                                                  for few output tiles */
-    GEMM_VARIANT_COUNT = 20
+    GEMM_VARIANT_MFMA_64_KS4 = 20,    /* 64x64x32 tile, K split over 4 groups of 4 waves inside the workgroup
+                                         (partial sums added in LDS, in group order): deep K, few tiles */
+    GEMM_VARIANT_MFMA_32x64_KS4 = 21, /* 32x64x32 tile, 4 groups of 2 waves */
+    GEMM_VARIANT_MFMA_32x32_KS8 = 22, /* 32x32x32 tile, 8 groups of 1 wave */
+    GEMM_VARIANT_COUNT = 23
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -121,6 +125,9 @@ typedef struct {
     int32_t elem_bytes;          /* bytes per A / B element: 4 (fp32), 2 (bf16 / fp16, gemm_mixed_f32);
                                     LDS tile fields count 4-byte words, so a row of a 16-bit tile holds
                                     2 * cols elements */
+    int32_t k_groups;            /* groups of waves that split K inside the workgroup (1: none); each
+                                    group has 2 of the `stages`, `threads` counts all groups, tm x tn
+                                    is one wave's tile within a group */
 } gemm_tile_config;
 
 /* C = A @ B with the default variant.  M, N, K >= 0; lda >= max(1,K),
@@ -202,17 +209,22 @@ int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with
- * `num_cus` compute units: among MFMA_256x256_BK32_PIPE, MFMA_DIRECT
- * (256x128), the 128x128 direct variant (BK 32 when K >= 1024, else 16) and
- * MFMA_64_BK32_DIRECT (64x64), the one with the highest rate estimate, its
- * full-chip rate (145, 144, 144, 134 TFLOP/s) times the wave quantisation of
- * its tile grid, tiles / (ceil(tiles / num_cus) * num_cus), times 0.88 for
- * the 256x128 and 128x128 kernels when there are fewer tiles than two per
- * CU (they are built for two workgroups per CU), and times
- * rounds / (rounds + 1) when M or N is smaller than, and not a multiple
- * of, the tile (its edge workgroups then load through registers) (when M >= BM and N >= BN an edge tile is moved back to end
- * at M or N and runs as an interior one); a larger tile wins when within
- * 2 %.  Pure host call.  Returns a gemm_variant, or
+ * `num_cus` compute units, both operands' rows 16-byte aligned: the
+ * candidate with the highest rate estimate.  Candidates and full-chip rates:
+ * MFMA_256x256_BK32_PIPE 145 TFLOP/s, MFMA_DIRECT (256x128) 144, the 128x128
+ * direct variant (BK 32 when K >= 1024, else 16) 144, MFMA_64_BK32_DIRECT
+ * 134; when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
+ * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup).  Estimate:
+ * the rate times the wave quantisation of the tile grid,
+ * tiles / (ceil(tiles / num_cus) * num_cus); times 0.88 for the 256x128 and
+ * 128x128 kernels with fewer tiles than two per CU (they are built for two
+ * workgroups per CU); for the 64x64 kernel times 0.78 with at most one tile
+ * per CU and 0.89 with at most two (its 4-wave workgroups need several per
+ * CU); and times rounds / (rounds + 1) when M or N is smaller than, and not
+ * a multiple of, the tile (its edge workgroups then load through
+ * registers; when M >= BM and N >= BN an edge tile is moved back to end at
+ * M or N and runs as an interior one).  A candidate listed earlier wins
+ * within 2 %.  Pure host call.  Returns a gemm_variant, or
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
@@ -223,8 +235,9 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
  * The rates (TFLOP/s with every CU busy, for 256x256 pipelined, 256x128,
  * 128x128 and 64x64x32) are, for both aligned, 145, 144, 144, 134; only A
  * aligned 134, 140, 124, 120; only B aligned 133, 130, 130, 128; neither
- * 130, 121, 118, 110.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies
- * this with the operands' actual alignment.  gemm_f32_auto_variant is this
+ * 130, 121, 118, 110; the K-split variants are offered only with both
+ * aligned.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
+ * the operands' actual alignment.  gemm_f32_auto_variant is this
  * with both flags set.  Pure host call. */
 int gemm_f32_auto_variant_ex(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t a_rows_aligned,
                              int32_t b_rows_aligned);

@@ -64,19 +64,20 @@ def test_tile_config_is_consistent(variant, gemm_lib):
     # the pages' budget formula, on the physical (padded, staged) sizes
     assert c["lds_bytes"] == c["stages"] * (c["a_stage_elems"] + c["b_stage_elems"]) * 4
     assert c["lds_bytes"] <= 160 * 1024
-    assert c["barriers_per_tile"] == (1 if c["stages"] == 2 else 2)
+    assert c["k_groups"] >= 1
+    assert c["barriers_per_tile"] == (1 if c["stages"] == 2 * c["k_groups"] else 2)
     if c["a_transposed"]:
         assert (c["a_rows"], c["a_cols"]) == (c["bk"], c["bm"])
         assert c["mfma_block"] == 0
     else:
         assert (c["a_rows"], c["a_cols"]) == (c["bm"], c["bk"])
         assert c["mfma_block"] in (16, 32)
-        assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64
+        assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64 * c["k_groups"]
     assert (c["b_rows"], c["b_cols"]) == (c["bk"], c["bn"])
     assert c["vec_width"] in (1, 4)
     assert (c["a_row_stride"] % 4 == 0) and (c["b_row_stride"] % 4 == 0)
-    if c["direct_to_lds"]:  # 16-byte copies into unpadded rows, two stages, matrix cores
-        assert c["vec_width"] == 4 and c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2
+    if c["direct_to_lds"]:  # 16-byte copies into unpadded rows, two stages per group, matrix cores
+        assert c["vec_width"] == 4 and c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2 * c["k_groups"]
         assert c["mfma_block"] in (16, 32)
     for t in "ab":
         unit, mask = c[f"{t}_swz_unit"], c[f"{t}_swz_mask"]
@@ -131,7 +132,7 @@ def test_auto_variant_selection(gemm_lib):
     assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 1024 of 64x64 vs 256 of 128x128
     assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT         # 512 tiles of 64x64
-    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # deep K, 128 small tiles
+    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4  # deep K, 128 tiles of 64x64: split K
     assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
     assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
@@ -141,9 +142,26 @@ def test_auto_variant_selection(gemm_lib):
     assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 6400 tiles: 25 full rounds
     # a dimension below the tile: every workgroup of the big kernels is an edge one
     assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_BK32_DIRECT       # many more CUs than big tiles
+    assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_KS4  # many more CUs than big tiles
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
+
+
+def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
+    av = dft.gemm_f32_auto_variant
+    # measured fastest on one MI355X (256 CUs): K split inside the workgroup when few tiles meet a deep K
+    assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4   # 101 TF against 54 for 64x64x32
+    assert av(1024, 512, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4
+    assert av(1024, 1024, 8192, 256) == dft.VARIANT_MFMA_64_KS4      # 256 tiles: 118 against 105
+    assert av(4096, 256, 8192, 256) == dft.VARIANT_MFMA_64_KS4
+    assert av(512, 512, 16384, 256) == dft.VARIANT_MFMA_32x32_KS8    # 94 against 27
+    assert av(256, 256, 65536, 256) == dft.VARIANT_MFMA_32x32_KS8
+    # enough tiles, or too short a K: no split
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(2048, 256, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    # unaligned operands: the split variants were not measured there
+    assert dft.gemm_f32_auto_variant_ex(2048, 256, 16383, 256, 0, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
 
 
 def test_auto_variant_by_operand_alignment(gemm_lib):

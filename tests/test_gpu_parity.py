@@ -28,7 +28,8 @@ ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIAN
                 dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT,
                 dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT,
                 dft.VARIANT_MFMA_256x256_W4_DIRECT, dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
-    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT,
+    dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -162,7 +163,7 @@ EDGE_SHAPES = [
 EDGE_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA16,
                  dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT,
                  dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT,
-                 dft.VARIANT_MFMA_256x256_DIRECT]
+                 dft.VARIANT_MFMA_256x256_DIRECT] + [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
@@ -246,8 +247,34 @@ def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
     assert np.array_equal(c.astype(np.float64), cref)
 
 
+KSPLIT_VARIANTS = [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
 PER_OPERAND_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_BK32_PIPE, dft.VARIANT_MFMA_DIRECT,
-                        dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT]
+                        dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
+                        dft.VARIANT_MFMA_64_BK32_DIRECT] + KSPLIT_VARIANTS
+
+
+@pytest.mark.parametrize("variant", KSPLIT_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in KSPLIT_VARIANTS])
+@pytest.mark.parametrize("K", [1, 31, 32, 33, 64, 95, 96, 160, 255, 256, 257, 1000])
+def test_k_split_in_the_workgroup(K, variant, torch_gpu):
+    """Wave groups splitting K inside the workgroup: K tiles are dealt to the
+    groups in turn, so these K cover fewer tiles than groups, a count that
+    is not a multiple of the groups, and a ragged last tile falling to any
+    group; the partial sums are added in LDS.  130 x 100 spans interior and
+    moved edge tiles of every tile size; bit for bit on integer operands,
+    NaN in every ld gap and around C."""
+    M, N = 130, 100
+    lda, ldb, ldc = K + (4 - K % 4) % 4 + 4, N + 4, N + 3
+    a, b = workloads.make_operands(M, N, K, "integer", 1500 + K)
+    cref, _ = oracle.reference(a, b)
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=ldc, c_rows_extra=2)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref)
+    au, bu = workloads.make_operands(M, N, K, "uniform", 1600 + K)
+    for offset in (0, 1):  # 1: 4-byte copies of both operands
+        cu, full = run_gemm(torch_gpu, au, bu, variant, offset=offset)
+        check_sentinels(full, M, N)
+        cref_u, den_u = oracle.reference(au, bu)
+        assert oracle.normalised_error(cu, cref_u, den_u) <= TOL, offset
 
 
 @pytest.mark.parametrize("variant", PER_OPERAND_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in PER_OPERAND_VARIANTS])

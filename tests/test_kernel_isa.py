@@ -62,13 +62,13 @@ def test_m0_is_used_only_by_the_direct_copies(functions):
     clobbered, and the compiler does not preserve a reserved register across
     inline asm).  That is safe only while no compiler-generated code keeps a
     value in M0: every instruction that names m0 must be one of the copies'
-    own s_mov_b32 m0, sN, followed by the wait state and the copy."""
+    own s_mov_b32 m0 from a scalar register, followed by the wait state and the copy."""
     text, _ = functions
     lines = [l.strip() for l in text.splitlines()]
     code = [l for l in lines if l and not l.startswith((";", ".", "//")) and not l.endswith(":")]
     uses = [i for i, l in enumerate(code) if re.search(r"\bm0\b", l)]
     assert uses
     for i in uses:
-        assert re.fullmatch(r"s_mov_b32 m0, s\d+", code[i]), code[i]
+        assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", code[i]), code[i]
         assert code[i + 1] == "s_nop 0", code[i + 1]
         assert code[i + 2].startswith(("global_load_lds_dwordx4 ", "global_load_lds_dword ")), code[i + 2]

@@ -50,12 +50,17 @@ def test_default_kernels_keep_their_occupancy(report):
     assert r["occupancy"] == 4 and r["lds"] == 48 * 1024
     # fp32 64x64x32 direct-copy kernel (AUTO for small grids): at least 4 waves per SIMD with 16-byte copies,
     # at least 2 with 4-byte copies; 32 KiB of LDS
-    fp32_small = kernels(report, "MfmaCfgILi64ELi64ELi32ELi32ELi32ELi2ELi32E")
+    fp32_small = {k: v for k, v in kernels(report, "MfmaCfgILi64ELi64ELi32ELi32ELi32ELi2ELi32E").items()
+                  if "16gemm_mfma_kernel" in k}
     vec4 = [v for k, v in fp32_small.items() if "EEELi4ELi1ELi1ELb0ELi0EE" in k]
     vec1 = [v for k, v in fp32_small.items() if "EEELi1ELi1ELi1ELb0ELi0EE" in k]
     assert len(vec4) == 1 and len(vec1) == 1
     assert vec4[0]["occupancy"] >= 4 and vec1[0]["occupancy"] >= 2
     assert vec4[0]["lds"] == vec1[0]["lds"] == 32 * 1024
+    # K-split kernels: one workgroup (8 or 16 waves) per CU at least
+    ksplit = kernels(report, "gemm_mfma_ksplit_kernel")
+    assert len(ksplit) == 12  # 3 variants x 4 copy-width forms
+    assert all(v["occupancy"] >= 2 and v["lds"] <= 160 * 1024 for v in ksplit.values())
     # bf16 / fp16 256x256x64 (AUTO for large problems): 2 waves per SIMD, 128 KiB of LDS
     mixed_default = kernels(report, "MixedCfgILi0ELi256ELi256ELi64E")
     assert mixed_default and all(v["occupancy"] == 2 and v["lds"] == 128 * 1024 for v in mixed_default.values())
