@@ -5,11 +5,15 @@ Each wavefront runs a list of events on a ring of LDS stages:
 
 * ("w", s, t): synchronous store of its piece of K tile t into stage s
   (the register path: global load, then LDS store);
+* ("wall", s, t): synchronous store over the whole stage s (every piece:
+  data laid out without regard to the stages' pieces, like partial sums);
 * ("issue", s, t): an asynchronous direct copy of its piece of tile t into
   stage s; the write lands at any later moment the model chooses;
 * ("wait", t): block until none of this wave's copies of tiles <= t is still
   in flight (s_waitcnt on the copies; t = None waits for all);
 * ("r", s, t): read the whole stage s (every wave's piece), expecting tile t;
+  ("r", s, t, waves): read only the pieces of those waves (a stage that one
+  group of waves fills, or one wave's partial sums);
 * ("b",): workgroup barrier.
 
 A schedule is correct when every read, in every interleaving and for every
@@ -17,9 +21,11 @@ landing time of every copy, sees tile t in all pieces of stage s, and no
 interleaving deadlocks.  The protocols are those of the kernels (two stages
 and one barrier per tile through registers or direct copies, the pipelined
 multiply whose last step runs after the barrier, the S-stage copy ring of
-the 16-bit-input kernels); the mutants (a barrier dropped, the stage parity
-flipped, the last step read after the barrier, the wait dropped or too
-weak) must each be caught.  The pages argue the one-barrier protocol in
+the 16-bit-input kernels, the K split over groups of waves with its final
+exchange of partial sums through LDS); the mutants (a barrier dropped, the
+stage parity flipped, the last step read after the barrier, the wait
+dropped or too weak, the partial sums written before the loop's last
+barrier or read without a barrier) must each be caught.  The pages argue the one-barrier protocol in
 prose ("My Triton From Scratch, Part 18", section "What ping-pong changes
 about synchronization"); this is a machine check of that argument and of
 its pipelined extension.
@@ -72,9 +78,12 @@ def check(programs, stages: int):
             kind = ev[0]
             if kind == "b":
                 continue
-            if kind == "w":
+            if kind in ("w", "wall"):
                 c = [list(row) for row in content]
-                c[ev[1]][v] = ev[2]
+                if kind == "w":
+                    c[ev[1]][v] = ev[2]
+                else:
+                    c[ev[1]] = [ev[2]] * waves
                 moves.append((nxt, tuple(tuple(row) for row in c), pending))
             elif kind == "issue":
                 p = list(pending)
@@ -84,7 +93,7 @@ def check(programs, stages: int):
                 if all(ev[1] is not None and t > ev[1] for (_, t) in pending[v]):
                     moves.append((nxt, content, pending))
             elif kind == "r":
-                got = content[ev[1]]
+                got = content[ev[1]] if len(ev) == 3 else tuple(content[ev[1]][u] for u in ev[3])
                 if any(x != ev[2] for x in got):
                     return f"wave {v} read stage {ev[1]} expecting tile {ev[2]}, pieces hold {got}"
                 moves.append((nxt, content, pending))
@@ -163,6 +172,61 @@ def ring(T, S, weak_wait=False):
         if t + 1 < T:
             ev.append(("r", (t + 1) % S, t + 1))
     return ev
+
+
+def ksplit(T, groups, per_group, wave, drop_final_barrier=False, early_partials=False):
+    """The K-split kernel, as wave `wave` runs it: group q (per_group waves)
+    takes K tiles q, q + groups, ... through its own stages 2q and 2q + 1
+    (two-stage direct copies), every group running ceil(T / groups)
+    iterations and every barrier; then groups 1.. write their partial sums
+    over the LDS (group q's over all of stage q - 1, which another group
+    used), and
+    after a barrier group 0 reads them back (wave w of group 0 reads wave w
+    of each other group)."""
+    q, w = divmod(wave, per_group)
+    members = [q * per_group + i for i in range(per_group)]
+    ev = []
+    if q < T:
+        ev.append(("issue", 2 * q, q))
+    ev += [("wait", None), ("b",)]
+    iters = (T + groups - 1) // groups
+    for it in range(iters):
+        s, ns = 2 * q + it % 2, 2 * q + 1 - it % 2
+        t, tn = it * groups + q, it * groups + q + groups
+        if tn < T:
+            ev.append(("issue", ns, tn))
+        if t < T:
+            ev.append(("r", s, t, members))
+        ev.append(("wait", None))
+        if not (early_partials and it == iters - 1):
+            ev.append(("b",))
+    if q > 0:
+        ev.append(("wall", q - 1, f"P{q}"))
+    if early_partials:
+        ev.append(("b",))
+    if not drop_final_barrier:
+        ev.append(("b",))
+    if q == 0:
+        for g in range(1, groups):
+            ev.append(("r", g - 1, f"P{g}", [g * per_group + w]))
+    return ev
+
+
+def ksplit_programs(T, groups, per_group, **kw):
+    return [ksplit(T, groups, per_group, v, **kw) for v in range(groups * per_group)]
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5])
+@pytest.mark.parametrize("groups,per_group", [(2, 1), (2, 2), (3, 1)])
+def test_k_split_protocol_is_race_free(T, groups, per_group):
+    assert check(ksplit_programs(T, groups, per_group), 2 * groups) is None
+
+
+@pytest.mark.parametrize("mutant", ["drop_final_barrier", "early_partials"])
+def test_k_split_mutant_is_caught(mutant):
+    # T = 5 with 2 groups: group 0's last tile (4) is in its stage 0, the
+    # stage group 1's partial sums overwrite
+    assert check(ksplit_programs(5, 2, 1, **{mutant: True}), 4) is not None
 
 
 CORRECT = [
