@@ -64,8 +64,7 @@ using Mfma256Plain = MfmaCfg<256, 128, 16, 64, 64, 2, 32, TileLayout<0>, TileLay
 template <int VEC>
 using Mfma16x256 = MfmaAt<std::conditional_t<VEC == 4, layouts::m16_256x128x16_v4, layouts::m16_256x128x16_v1>,
                           2, VEC, 256, 128, 16, 16>;
-// Direct global->LDS copies for in-range tiles (16-byte path only; the
-// 4-byte path of this variant loads through registers like MFMA).
+// Direct global->LDS copies for in-range tiles, 16 or 4 bytes per lane.
 // The direct-copy variants that AUTO chooses from take a copy width per
 // operand (VEC for A, VEC_B for B): an operand whose rows are 16-byte
 // aligned keeps 16-byte copies when the other's are not.  VEC_B == VEC is

@@ -661,10 +661,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         // Two stages filled by direct copies: the copies of tile t+1 are in
         // flight during the multiply of tile t, and each wave waits for its
         // own copies before the barrier, after which the whole stage is in
-        // LDS.  A tile not wholly in range (edge workgroups; the last K tile
-        // when BK does not divide K) needs zero fill: it is loaded through
-        // registers with masks after the multiply, so that no staging
-        // registers are live across it.  Both choices are uniform.
+        // LDS.  A tile not wholly in range needs zero fill: the last K tile
+        // when BK does not divide K, and every tile of a workgroup whose
+        // tile cannot move back inside C (M < BM or N < BN) or whose
+        // operand is too wide for the copies' offsets.  It is loaded
+        // through registers with masks after the multiply, so that no
+        // staging registers are live across it.  Both choices are uniform.
         // Kernels with different copy widths for A and B lose the compiler's
         // proof that the 16-byte copies' bases are uniform.
         constexpr bool READ_FIRST = Cfg::VEC != Cfg::VEC_B;
@@ -673,8 +675,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
         const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
         // A's tiles are wholly in range when the workgroup's rows are (but for
-        // a ragged last K tile), B's when its columns are; an edge workgroup
-        // still copies the operand that is in range directly.
+        // a ragged last K tile), B's when its columns are.
         const bool rows_in = M - m0 >= BM && DA::fits(lda, A);
         const bool cols_in = N - n0 >= BN && DB::fits(ldb, B);
         const bool interior = rows_in && cols_in;

@@ -362,7 +362,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     };
 
     // Two stages through registers, each refill issued after the multiply
-    // (edge workgroups, and unaligned operands below).
+    // (workgroups whose tile cannot move back inside C, and unaligned
+    // operands below).
     auto two_stage_registers = [&]() {
         if (T > 0) {
             load_tile(0);
