@@ -305,11 +305,10 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
          {144.0, 124.0, 130.0, 118.0}, false, 0},
         {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0},
-        // K split inside the workgroup (16 K tiles of 32 per group at least);
-        // measured with both operands aligned only, so offered only then.
-        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 4},
-        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 4},
-        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 0.0, 0.0, 0.0}, false, 16 * 32 * 8},
+        // K split inside the workgroup (16 K tiles of 32 per group at least)
+        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4},
+        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4},
+        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8},
     };
     const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;

@@ -235,8 +235,9 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
  * The rates (TFLOP/s with every CU busy, for 256x256 pipelined, 256x128,
  * 128x128 and 64x64x32) are, for both aligned, 145, 144, 144, 134; only A
  * aligned 134, 140, 124, 120; only B aligned 133, 130, 130, 128; neither
- * 130, 121, 118, 110; the K-split variants are offered only with both
- * aligned.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
+ * 130, 121, 118, 110; for MFMA_64_KS4, MFMA_32x64_KS4 and MFMA_32x32_KS8
+ * (both aligned 117, 101, 96 as above) only A aligned 108, 79, 66; only B
+ * aligned 110, 95, 81; neither 103, 76, 63.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
  * the operands' actual alignment.  gemm_f32_auto_variant is this
  * with both flags set.  Pure host call. */
 int gemm_f32_auto_variant_ex(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t a_rows_aligned,

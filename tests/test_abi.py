@@ -160,8 +160,13 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(2048, 256, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    # unaligned operands: the split variants were not measured there
-    assert dft.gemm_f32_auto_variant_ex(2048, 256, 16383, 256, 0, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    # unaligned operands (odd K: A's rows; odd N: B's), measured per alignment class
+    ax = dft.gemm_f32_auto_variant_ex
+    assert ax(2048, 256, 16383, 256, 0, 1) == dft.VARIANT_MFMA_32x64_KS4   # 95 against 49
+    assert ax(2048, 255, 16384, 256, 1, 0) == dft.VARIANT_MFMA_32x64_KS4   # 79 against 43
+    assert ax(1024, 1023, 8192, 256, 1, 0) == dft.VARIANT_MFMA_64_KS4      # 108 against 85
+    assert ax(1023, 1023, 8191, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4
+    assert ax(512, 511, 16384, 256, 1, 0) == dft.VARIANT_MFMA_32x32_KS8    # 67 against 21
 
 
 def test_auto_variant_by_operand_alignment(gemm_lib):
