@@ -415,7 +415,7 @@ def run_splitk(torch, a, b, splits, ldc=None, ws_elems=None, variant=dft.VARIANT
 
 
 SPLITK_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_DIRECT,
-                   dft.VARIANT_VALU]
+                   dft.VARIANT_VALU, dft.VARIANT_MFMA_64_BK32_DIRECT, dft.VARIANT_MFMA_32x64_KS4]
 
 
 @pytest.mark.parametrize("variant", SPLITK_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in SPLITK_VARIANTS])
