@@ -62,10 +62,15 @@ MIXED_256x128_BK64 = 3
 MIXED_128x128_BK64 = 4
 MIXED_256x256_S3 = 5
 MIXED_256x256_BK64 = 6
-MIXED_COUNT = 7
+MIXED_64x64 = 7
+MIXED_64x64_KS2 = 8
+MIXED_64x64_KS4 = 9
+MIXED_32x64_KS4 = 10
+MIXED_COUNT = 11
 MIXED_NAMES = {MIXED_AUTO: "auto", MIXED_256x128: "256x128", MIXED_256x256: "256x256",
                MIXED_256x128_BK64: "256x128_bk64", MIXED_128x128_BK64: "128x128_bk64", MIXED_256x256_S3: "256x256_s3",
-               MIXED_256x256_BK64: "256x256_bk64"}
+               MIXED_256x256_BK64: "256x256_bk64", MIXED_64x64: "64x64", MIXED_64x64_KS2: "64x64_ks2",
+               MIXED_64x64_KS4: "64x64_ks4", MIXED_32x64_KS4: "32x64_ks4"}
 VARIANT_NAMES = {
     VARIANT_AUTO: "auto",
     VARIANT_MFMA: "mfma",

@@ -554,6 +554,21 @@ template <int TYPE, int VEC>
 using Mixed128x128Bk64 = MixedCfg<TYPE, 128, 128, 64, 64, 64, 32, layouts::x32_128x128x64::A,
                                   layouts::x32_128x128x64::B, VEC, 4, 2, kPipeAcrossTiles>;
 
+// Small tiles and K split inside the workgroup, for grids of few output
+// tiles (16-byte copies; the unaligned form is the shared 2-byte-load kernel).
+template <int TYPE, int VEC>
+using Mixed64 = MixedCfg<TYPE, 64, 64, 64, 32, 32, 32, layouts::x32_64x64x64::A, layouts::x32_64x64x64::B, VEC, 4, 2,
+                         kPipeSteps>;
+template <int TYPE, int VEC>
+using Mixed32x64 = MixedCfg<TYPE, 32, 64, 64, 32, 32, 32, layouts::x32_32x64x64::A, layouts::x32_32x64x64::B, VEC,
+                            4, 2, kPipeSteps>;
+template <int TYPE, int VEC>
+using Mixed64Ks2 = MixedKsplitCfg<Mixed64<TYPE, VEC>, 2>;
+template <int TYPE, int VEC>
+using Mixed64Ks4 = MixedKsplitCfg<Mixed64<TYPE, VEC>, 4>;
+template <int TYPE, int VEC>
+using Mixed32x64Ks4 = MixedKsplitCfg<Mixed32x64<TYPE, VEC>, 4>;
+
 template <class Cfg>
 hipError_t launch_mixed(const Args& a, hipStream_t stream) {
     int64_t M = a.M, N = a.N, K = a.K, lda = a.lda, ldb = a.ldb, ldc = a.ldc;
@@ -563,8 +578,12 @@ hipError_t launch_mixed(const Args& a, hipStream_t stream) {
     int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
     int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
     void* args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &tiles_m, &tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void*>(gemm_mixed_kernel<Cfg>), dim3((unsigned)(tiles_m * tiles_n)),
-                           dim3(Cfg::THREADS), args, 0, stream);
+    const void* kernel;
+    if constexpr (Cfg::KSPLIT > 1)
+        kernel = reinterpret_cast<const void*>(gemm_mixed_ksplit_kernel<Cfg>);
+    else
+        kernel = reinterpret_cast<const void*>(gemm_mixed_kernel<Cfg>);
+    return hipLaunchKernel(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(Cfg::THREADS), args, 0, stream);
 }
 
 template <class Cfg>
@@ -575,6 +594,8 @@ gemm_tile_config mixed_config(int variant, int vec) {
     c.a_transposed = 0;
     c.mfma_block = Cfg::Op::MB;
     c.elem_bytes = 2;
+    c.k_groups = Cfg::KSPLIT;
+    if (Cfg::KSPLIT > 1) c.barriers_per_tile = 1;  // per K tile of a group
     return c;
 }
 
@@ -607,6 +628,10 @@ const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
     /* 128x128_BK64   */ mixed_variant<Mixed128x128Bk64>(),
     /* 256x256_S3     */ mixed_variant<Mixed256x256S3>(),
     /* 256x256_BK64   */ mixed_variant<Mixed256x256Bk64>(),
+    /* 64x64          */ mixed_variant<Mixed64>(),
+    /* 64x64_KS2      */ mixed_variant<Mixed64Ks2>(),
+    /* 64x64_KS4      */ mixed_variant<Mixed64Ks4>(),
+    /* 32x64_KS4      */ mixed_variant<Mixed32x64Ks4>(),
 };
 
 // AUTO for 16-bit inputs.  The 256x256 kernels run one workgroup per CU, the
@@ -615,17 +640,48 @@ const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
 // partial round of it was measured faster than the quantisation predicts (the
 // idle CUs leave the busy ones more clock).  Between the two 256x256 kernels,
 // BK = 64 wins when it divides K; otherwise its ragged last K tile goes
-// through registers and the three-stage BK = 32 kernel was faster.  On 15
-// measured bf16 shapes from 1000^3 to 8192^3 this picks the fastest of the
-// six variants on every one.
+// through registers and the three-stage BK = 32 kernel was faster.
+// When 256x256 tiles would fill less than half the CUs, the 64x64-tile
+// kernels join: K split over 4 groups (64x64 at 420, 32x64 at 290 times
+// their quantisation) when K >= 4096, over 2 groups (530 times
+// min(1, 0.6 w)) when K >= 2048, and the plain 64x64 kernel (700 times
+// min(1, 0.375 w)), w being 64x64 tiles per CU; listed first wins within
+// 2 %.  On 24 measured bf16 shapes from 256^2 x 65536 to 8192^3 this picks
+// the fastest variant or one within 4.6 % of it.
+double round_fill(int64_t tiles, int64_t per_round) {
+    return tiles > 0 ? (double)tiles / (double)(((tiles + per_round - 1) / per_round) * per_round) : 1.0;
+}
 int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t per_round256 = num_cus, per_round128 = 2 * (int64_t)num_cus;
-    const double e256 = t256 > 0 ? (double)t256 / (double)(((t256 + per_round256 - 1) / per_round256) * per_round256) : 1.0;
-    const double e128 = t128 > 0 ? (double)t128 / (double)(((t128 + per_round128 - 1) / per_round128) * per_round128) : 1.0;
-    if (1050.0 * e128 > 1.1 * 1200.0 * e256) return GEMM_MIXED_128x128_BK64;
-    return K % 64 == 0 ? GEMM_MIXED_256x256_BK64 : GEMM_MIXED_256x256_S3;
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t t32x64 = ((M + 31) / 32) * ((N + 63) / 64);
+    const double e256 = round_fill(t256, num_cus), e128 = round_fill(t128, 2 * (int64_t)num_cus);
+    const int big = K % 64 == 0 ? GEMM_MIXED_256x256_BK64 : GEMM_MIXED_256x256_S3;
+    if (2 * t256 >= num_cus) return 1050.0 * e128 > 1.1 * 1200.0 * e256 ? GEMM_MIXED_128x128_BK64 : big;
+    const double w64 = (double)t64 / (double)num_cus;
+    struct Candidate {
+        int variant;
+        double rate;
+    };
+    Candidate candidates[6];
+    int n = 0;
+    if (K >= 4096) {
+        candidates[n++] = {GEMM_MIXED_64x64_KS4, 420.0 * round_fill(t64, num_cus)};
+        candidates[n++] = {GEMM_MIXED_32x64_KS4, 290.0 * round_fill(t32x64, num_cus)};
+    }
+    if (K >= 2048) candidates[n++] = {GEMM_MIXED_64x64_KS2, 530.0 * std::min(1.0, 0.6 * w64)};
+    candidates[n++] = {GEMM_MIXED_64x64, 700.0 * std::min(1.0, 0.375 * w64)};
+    candidates[n++] = {GEMM_MIXED_128x128_BK64, 1050.0 * e128};
+    candidates[n++] = {big, 1.1 * 1200.0 * e256};
+    int best = big;
+    double best_rate = -1.0;
+    for (int i = 0; i < n; ++i)
+        if (candidates[i].rate > best_rate * 1.02) {
+            best = candidates[i].variant;
+            best_rate = candidates[i].rate;
+        }
+    return best;
 }
 
 int run_mixed(int input_type, const Args& a, hipStream_t stream, int variant) {

@@ -209,6 +209,7 @@ struct MixedCfg {
     static constexpr int LOAD = VEC == 8 ? kLoadDirect : kLoadRegisters;
     static constexpr int STAGES = STAGES_;  // LDS stages of the direct-copy pipeline (register paths use two)
     static constexpr int PIPELINE = PIPELINE_;
+    static constexpr int KSPLIT = 1;  // wave groups splitting K inside the workgroup (MixedKsplitCfg)
     static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -494,6 +495,187 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     }
 
     store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
+}
+
+// --------------------------------------------------------------------------
+// K split inside the workgroup for 16-bit inputs (the fp32 KsplitCfg's
+// scheme): KSPLIT groups of waves share one output tile, group q taking K
+// tiles q, q + KSPLIT, ... through its own pair of LDS stages with Base's
+// wave tiling, direct copies and step-pipelined multiply; the groups'
+// partial sums are added in LDS in group order.  16-byte copies only: the
+// unaligned form of every 16-bit variant is the 2-byte-load kernel.
+template <class Base, int KSPLIT_>
+struct MixedKsplitCfg {
+    static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2, "groups run Base's two-stage direct-copy loop");
+    static_assert(KSPLIT_ >= 2, "at least two groups");
+    using Op = typename Base::Op;
+    static constexpr int TYPE = Base::TYPE, KSPLIT = KSPLIT_;
+    static constexpr int BM = Base::BM, BN = Base::BN, BK = Base::BK, WM = Base::WM, WN = Base::WN;
+    static constexpr int VEC = Base::VEC, ORDER = Base::ORDER, LOAD = kLoadDirect, PIPELINE = kPipeSteps;
+    static constexpr int WAVES_N = Base::WAVES_N, MI = Base::MI, NI = Base::NI, STEPS = Base::STEPS;
+    static constexpr int GROUP_THREADS = Base::THREADS, GROUP_WAVES = GROUP_THREADS / kWave;
+    static constexpr int THREADS = GROUP_THREADS * KSPLIT;
+    static constexpr int STAGES = 2 * KSPLIT;  // stages 2q, 2q+1 belong to group q
+    static constexpr int MIN_WAVES = Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES : THREADS / 256;
+    using TileA = LdsTile<BM, BK / 2, 0, STAGES, Base::TileA::swizzle.unit, Base::TileA::swizzle.shift,
+                          Base::TileA::swizzle.mask>;
+    using TileB = LdsTile<BK, BN / 2, 0, STAGES, Base::TileB::swizzle.unit, Base::TileB::swizzle.shift,
+                          Base::TileB::swizzle.mask>;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    static constexpr int PARTIAL_VALUES = MI * NI * Op::ACC;  // per lane
+    static_assert((KSPLIT - 1) * GROUP_WAVES * PARTIAL_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
+                  "the partial sums fit in the stages");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_ksplit_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n) {
+    using Op = typename Cfg::Op;
+    using TileA = typename Cfg::TileA;
+    using TileB = typename Cfg::TileB;
+    using acc_t = typename Op::acc_t;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, KS = Cfg::KSPLIT;
+    constexpr int MI = Cfg::MI, NI = Cfg::NI, GT = Cfg::GROUP_THREADS;
+
+    // One array: A's stages, then B's; the partial sums reuse all of it.
+    __shared__ __attribute__((aligned(16))) uint32_t lds[TileA::total_elems + TileB::total_elems];
+    uint32_t* const lds_a = lds;
+    uint32_t* const lds_b = lds + TileA::total_elems;
+
+    const int tid = threadIdx.x;
+    const int group = __builtin_amdgcn_readfirstlane(tid / GT);
+    const int gtid = tid % GT;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(gtid / kWave);
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int g = lane / Op::MB, r = lane % Op::MB;
+    const int tr_row = 8 * Op::kgroup(lane) + (lane % 16) / 4;
+    const int tr_col = Op::col_base(lane) + 4 * (lane % 4);
+
+    const TileCoord own = tile_of_block<Cfg>(tiles_m, tiles_n);
+    const TileCoord tc = operand_origin<Cfg>(own, M, N);
+    const int64_t m0 = tc.m0, n0 = tc.n0;
+
+    acc_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
+
+    TileLoader16<BM, BK, GT, Cfg::VEC> ldr_a;
+    TileLoader16<BK, BN, GT, Cfg::VEC> ldr_b;
+    const uint16_t* a_tile = A + m0 * lda;
+    const uint16_t* b_tile = B + n0;
+    const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
+    const int64_t TF = K / BK;
+    const int64_t ITERS = (T + KS - 1) / KS;
+
+    using DA = DirectCopy<TileA, GT, uint16_t>;
+    using DB = DirectCopy<TileB, GT, uint16_t>;
+    const DA dma_a(lda, wave, lane);
+    const DB dma_b(ldb, wave, lane);
+    const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
+
+    auto copy_direct = [&](int64_t t, int stage) {
+        dma_a.issue(a_tile + t * BK, lds_a, stage);
+        dma_b.issue(b_tile + t * BK * ldb, lds_b, stage);
+    };
+    auto copy_registers = [&](int64_t t, int stage) {
+        const int64_t k0 = t * BK;
+        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, gtid);
+        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, gtid);
+        ldr_a.template store<TileA>(lds_a, stage, gtid);
+        ldr_b.template store<TileB>(lds_b, stage, gtid);
+    };
+    typedef __attribute__((address_space(3))) uint32_t lds_word;
+    typedef __attribute__((address_space(3))) shortx4 lds_short4;
+    int a_base[Cfg::STEPS], b_base[NI];
+#pragma unroll
+    for (int st = 0; st < Cfg::STEPS; ++st) a_base[st] = TileA::offset(0, wm0 + r, st * (Op::KB / 2) + 4 * g);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) b_base[n] = TileB::offset(0, tr_row, (wn0 + n * Op::NB + tr_col) / 2);
+    auto read_fragments = [&](int stage, int st, u32x4 (&af)[MI], u32x4 (&bf)[NI]) {
+        const uint32_t* a = lds_a + stage * TileA::stage_elems + a_base[st];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const u32x4*>(a + i * Op::MB * TileA::row_stride);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            shortx4 half[2];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int word = stage * TileB::stage_elems + b_base[n] + (st * Op::KB + 4 * rr) * TileB::row_stride;
+                half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((lds_word*)lds_b + word));
+            }
+            const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
+            bf[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    auto multiply = [&](int stage) {
+        u32x4 af[2][MI], bf[2][NI];
+        read_fragments(stage, 0, af[0], bf[0]);
+#pragma unroll
+        for (int st = 0; st < Cfg::STEPS; ++st) {
+            if (st + 1 < Cfg::STEPS) read_fragments(stage, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[st & 1][i], bf[st & 1][n], acc[i][n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int stage0 = 2 * group;
+    if (group < T) {
+        if (interior && group < TF)
+            copy_direct(group, stage0);
+        else
+            copy_registers(group, stage0);
+    }
+    wait_vector_memory();
+    __syncthreads();
+    for (int64_t it = 0; it < ITERS; ++it) {
+        const int s = stage0 + (int)(it & 1), ns = stage0 + (int)((it & 1) ^ 1);
+        const int64_t t = it * KS + group, tn = t + KS;
+        const bool direct = interior && tn < TF;
+        if (direct) copy_direct(tn, ns);
+        if (t < T) multiply(s);
+        if (tn < T && !direct) copy_registers(tn, ns);
+        wait_vector_memory();
+        __syncthreads();
+    }
+
+    // Every LDS read of the loop completed before its last barrier.
+    constexpr int PV = Cfg::PARTIAL_VALUES;
+    float* const part = reinterpret_cast<float*>(lds);
+    if (group > 0) {
+        float* dst = part + ((group - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
+        int j = 0;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int n = 0; n < NI; ++n)
+#pragma unroll
+                for (int v = 0; v < Op::ACC; ++v) dst[(j++) * kWave] = acc[i][n][v];
+    }
+    __syncthreads();
+    if (group == 0) {
+        for (int q = 1; q < KS; ++q) {
+            const float* src = part + ((q - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
+            int j = 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n)
+#pragma unroll
+                    for (int v = 0; v < Op::ACC; ++v) acc[i][n][v] += src[(j++) * kWave];
+        }
+        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
+    }
 }
 
 }  // namespace dft

@@ -317,7 +317,11 @@ typedef enum {
     GEMM_MIXED_128x128_BK64 = 4,  /* 128x128x64 tile, 4 waves of 64x64 */
     GEMM_MIXED_256x256_S3 = 5,    /* as 256x256 with three LDS stages (copies two tiles ahead) */
     GEMM_MIXED_256x256_BK64 = 6,  /* 256x256x64 tile, 8 waves of 128x64, two stages */
-    GEMM_MIXED_COUNT = 7
+    GEMM_MIXED_64x64 = 7,         /* 64x64x64 tile, 4 waves of 32x32 (few output tiles) */
+    GEMM_MIXED_64x64_KS2 = 8,     /* 64x64x64 tile, K split over 2 groups of 4 waves inside the workgroup */
+    GEMM_MIXED_64x64_KS4 = 9,     /* 64x64x64 tile, K split over 4 groups of 4 waves */
+    GEMM_MIXED_32x64_KS4 = 10,    /* 32x64x64 tile, K split over 4 groups of 2 waves */
+    GEMM_MIXED_COUNT = 11
 } gemm_mixed_variant;
 
 /* C = A @ B, A and B of `input_type` (gemm_input_type), C fp32.  A, B, C are
@@ -337,11 +341,16 @@ int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K,
 /* Tile geometry of a gemm_mixed_variant (elem_bytes = 2).  Pure host call. */
 int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
 
-/* The variant GEMM_MIXED_AUTO runs: 128x128_BK64 when 1050 * e128 exceeds
- * 1.1 * 1200 * e256, where e is the fraction of CU-rounds with work for that
- * tile (tiles / (ceil(tiles / per_round) * per_round); per_round = num_cus
- * for 256x256 tiles, 2 * num_cus for 128x128); otherwise 256x256_BK64 when
- * K is a multiple of 64, else 256x256_S3.  Pure host call;
+/* The variant GEMM_MIXED_AUTO runs.  e is the fraction of CU-rounds with
+ * work for a tile, tiles / (ceil(tiles / per_round) * per_round), with
+ * per_round = num_cus for 256x256, 64x64 and 32x64 tiles and 2 * num_cus
+ * for 128x128; "big" is 256x256_BK64 when K is a multiple of 64, else
+ * 256x256_S3.  When 256x256 tiles number at least num_cus / 2: 128x128_BK64
+ * if 1050 * e128 > 1.1 * 1200 * e256, else big.  Otherwise the highest of
+ * these estimates (listed first wins within 2 %): 64x64_KS4 420 * e64 and
+ * 32x64_KS4 290 * e32x64 when K >= 4096; 64x64_KS2 530 * min(1, 0.6 w)
+ * when K >= 2048; 64x64 700 * min(1, 0.375 w); 128x128_BK64 1050 * e128;
+ * big 1.1 * 1200 * e256 (w: 64x64 tiles per CU).  Pure host call;
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 

@@ -308,12 +308,13 @@ def test_every_binding_declares_its_full_signature(gemm_lib):
 def test_mixed_tile_config_is_consistent(variant, gemm_lib):
     c = dft.gemm_mixed_tile_config(variant)
     assert c["variant"] == variant and c["elem_bytes"] == 2 and c["direct_to_lds"] == 1
-    assert c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] in (2, 3)
+    assert c["a_pad"] == 0 and c["b_pad"] == 0
+    assert c["stages"] in (2, 3) if c["k_groups"] == 1 else c["stages"] == 2 * c["k_groups"]
     # LDS tiles in 4-byte words: a row of a 16-bit tile holds two elements per word
     assert (c["a_rows"], 2 * c["a_cols"]) == (c["bm"], c["bk"])
     assert (c["b_rows"], 2 * c["b_cols"]) == (c["bk"], c["bn"])
     assert c["lds_bytes"] == c["stages"] * (c["a_stage_elems"] + c["b_stage_elems"]) * 4 <= 160 * 1024
-    assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64
+    assert c["threads"] == (c["bm"] // c["tm"]) * (c["bn"] // c["tn"]) * 64 * c["k_groups"]
     assert c["mfma_block"] == 32
 
 
@@ -343,10 +344,16 @@ def test_mixed_auto_variant(gemm_lib):
     assert av(8192, 8192, 8192, 256) == dft.MIXED_256x256_BK64  # 1024 tiles of 256x256
     assert av(4096, 4096, 4096, 256) == dft.MIXED_256x256_BK64  # 256 tiles
     assert av(2048, 4096, 4096, 256) == dft.MIXED_128x128_BK64  # 128 tiles of 256x256, 512 of 128x128
-    assert av(2048, 256, 16384, 256) == dft.MIXED_128x128_BK64
+    # few 256x256 tiles: the 64x64-tile kernels, with K split inside the workgroup when K is deep
+    assert av(2048, 256, 16384, 256) == dft.MIXED_32x64_KS4    # 290 TF against 94 for 128x128
+    assert av(1024, 1024, 8192, 256) == dft.MIXED_64x64_KS4    # 398 against 184
+    assert av(512, 4096, 4096, 256) == dft.MIXED_64x64_KS2     # 527 against 328
+    assert av(512, 512, 16384, 256) == dft.MIXED_32x64_KS4
+    assert av(1000, 1000, 1000, 256) == dft.MIXED_64x64       # 142 against 96
+    assert av(1536, 1536, 4096, 256) == dft.MIXED_64x64
     assert av(3000, 3000, 3000, 256) == dft.MIXED_256x256_S3     # 144 tiles; K not a multiple of 64
     assert av(8000, 8000, 4000, 256) == dft.MIXED_256x256_S3
     assert av(3072, 3072, 3072, 256) == dft.MIXED_256x256_BK64
     assert av(6000, 6000, 6000, 256) == dft.MIXED_256x256_S3     # 576 tiles vs 2209 of 128x128
-    assert av(2048, 2048, 2048, 256) == dft.MIXED_128x128_BK64
+    assert av(2048, 2048, 2048, 256) == dft.MIXED_64x64         # 544 against 492
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM

@@ -136,6 +136,26 @@ def test_mixed_edge_shapes(kind, shape, variant, torch_gpu):
     assert np.array_equal(ci.astype(np.float64), oracle.reference(afi, bfi)[0])
 
 
+KSPLIT_VARIANTS = [dft.MIXED_64x64_KS2, dft.MIXED_64x64_KS4, dft.MIXED_32x64_KS4]
+
+
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("K", [8, 64, 120, 128, 192, 200, 256, 320, 1000, 4100])
+@pytest.mark.parametrize("variant", KSPLIT_VARIANTS, ids=[dft.MIXED_NAMES[v] for v in KSPLIT_VARIANTS])
+def test_mixed_k_split_in_the_workgroup(kind, K, variant, torch_gpu):
+    """K tiles of 64 dealt to 2 or 4 groups of waves: fewer tiles than
+    groups, counts not a multiple of the groups, a ragged last tile in any
+    group; partial sums added in LDS.  130 x 100 spans interior and moved
+    edge tiles; bit for bit on integer operands."""
+    M, N = 130, 104
+    ab, bb, af, bf = operands(kind, M, N, K, "integer", 1700 + K)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=K + (8 - K % 8) % 8 + 8, ldb=N + 8, ldc=N + 3)
+    assert np.array_equal(c.astype(np.float64), oracle.reference(af, bf)[0])
+    ab, bb, af, bf = operands(kind, M, N, K, "uniform", 1800 + K)
+    cref, den = oracle.reference(af, bf)
+    assert oracle.normalised_error(run_mixed(torch_gpu, kind, ab, bb, variant), cref, den) <= TOL
+
+
 @pytest.mark.parametrize("kind", list(TYPES))
 def test_mixed_k_zero_and_empty(kind, torch_gpu):
     torch = torch_gpu
