@@ -601,17 +601,19 @@ gemm_tile_config mixed_config(int variant, int vec) {
 
 using MixedLaunchFn = hipError_t (*)(const Args&, hipStream_t);
 struct MixedVariant {
-    MixedLaunchFn vec8[2], scalar[2];  // by input type
+    MixedLaunchFn vec8[2], vec2[2], scalar[2];  // by input type: 16-byte, 4-byte copies; 2-byte loads
     gemm_tile_config (*config)(int variant, int vec);
     int lds_bytes;
 };
 
-// Unaligned operands of every variant run the 256x128x32 kernel with 2-byte
-// loads: it is the only shape whose register-path kernel fits its registers
-// without spilling (one staged element per register).
+// Operands whose rows are 4-byte aligned (even leading dimensions) run the
+// variant's own kernel with 4-byte copies.  Others run the 256x128x32
+// kernel with 2-byte loads: it is the only shape whose register-path kernel
+// fits its registers without spilling (one staged element per register).
 template <template <int, int> class Shape>
 MixedVariant mixed_variant() {
     return MixedVariant{{launch_mixed<Shape<kInputBf16, 8>>, launch_mixed<Shape<kInputF16, 8>>},
+                        {launch_mixed<Shape<kInputBf16, 2>>, launch_mixed<Shape<kInputF16, 2>>},
                         {launch_mixed<Mixed256x128<kInputBf16, 1>>, launch_mixed<Mixed256x128<kInputF16, 1>>},
                         mixed_config<Shape<kInputBf16, 8>>,
                         Shape<kInputBf16, 8>::LDS_BYTES > Mixed256x128<kInputBf16, 1>::LDS_BYTES
@@ -691,15 +693,19 @@ int run_mixed(int input_type, const Args& a, hipStream_t stream, int variant) {
     bool done = false;
     const int st = prologue(a, stream, &max_lds, &num_cus, &done, 2);
     if (st != GEMM_OK || done) return st;
+    // 16-byte copies need rows 16-byte aligned (ld % 8 == 0, 16-byte bases);
+    // 4-byte copies rows 4-byte aligned (even ld, 4-byte bases).
+    const bool rows16 = (a.lda % 8 == 0) && (a.ldb % 8 == 0) && (((uintptr_t)a.A & 15) == 0) &&
+                        (((uintptr_t)a.B & 15) == 0);
+    const bool rows4 = (a.lda % 2 == 0) && (a.ldb % 2 == 0) && (((uintptr_t)a.A & 3) == 0) &&
+                       (((uintptr_t)a.B & 3) == 0);
     if (variant == GEMM_MIXED_AUTO) variant = mixed_auto_variant(a.M, a.N, a.K, num_cus);
     const MixedVariant& v = kMixedVariants[variant];
     if (v.lds_bytes > max_lds) return GEMM_ERR_CONFIG;
     const gemm_tile_config cfg = v.config(variant, 8);
     const int64_t tiles = ((a.M + cfg.bm - 1) / cfg.bm) * ((a.N + cfg.bn - 1) / cfg.bn);
     if (tiles > (int64_t)0x7fffffff / cfg.threads) return GEMM_ERR_TOO_LARGE;
-    const bool aligned = (a.lda % 8 == 0) && (a.ldb % 8 == 0) && (((uintptr_t)a.A & 15) == 0) &&
-                         (((uintptr_t)a.B & 15) == 0);
-    const MixedLaunchFn fn = aligned ? v.vec8[input_type] : v.scalar[input_type];
+    const MixedLaunchFn fn = rows16 ? v.vec8[input_type] : rows4 ? v.vec2[input_type] : v.scalar[input_type];
     return fn(a, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 

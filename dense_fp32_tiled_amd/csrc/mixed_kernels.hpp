@@ -204,9 +204,13 @@ struct MixedCfg {
     static constexpr int TYPE = TYPE_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int VEC = VEC_;
-    static constexpr int MIN_WAVES = VEC == 1 && MIN_WAVES_ > 2 ? 2 : MIN_WAVES_;
+    static constexpr int MIN_WAVES = VEC != 8 && MIN_WAVES_ > 2 ? 2 : MIN_WAVES_;
     static constexpr int ORDER = kXcdGroupedOrder;
-    static constexpr int LOAD = VEC == 8 ? kLoadDirect : kLoadRegisters;
+    // VEC 8: 16-byte direct copies; 2: 4-byte direct copies (two elements,
+    // rows 4-byte aligned); 1: 2-byte loads through registers.
+    static_assert(VEC == 8 || VEC == 2 || VEC == 1, "16-byte, 4-byte or 2-byte operand access");
+    static constexpr int LOAD = VEC == 1 ? kLoadRegisters : kLoadDirect;
+    static constexpr int LOADER_VEC = VEC == 8 ? 8 : 1;  // register-path loads (edge and ragged tiles)
     static constexpr int STAGES = STAGES_;  // LDS stages of the direct-copy pipeline (register paths use two)
     static constexpr int PIPELINE = PIPELINE_;
     static constexpr int KSPLIT = 1;  // wave groups splitting K inside the workgroup (MixedKsplitCfg)
@@ -290,8 +294,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 #pragma unroll
             for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
 
-    TileLoader16<BM, BK, THREADS, Cfg::VEC> ldr_a;
-    TileLoader16<BK, BN, THREADS, Cfg::VEC> ldr_b;
+    TileLoader16<BM, BK, THREADS, Cfg::LOADER_VEC> ldr_a;
+    TileLoader16<BK, BN, THREADS, Cfg::LOADER_VEC> ldr_b;
     const uint16_t* a_tile = A + m0 * lda;
     const uint16_t* b_tile = B + n0;
     const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
@@ -362,29 +366,48 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
         }
     };
 
+    // Tile t into `stage` through registers, with zero fill, for kernels
+    // with 4-byte copies: 2 bytes per element (their rows need not be
+    // 16-byte aligned), a few slots at a time, since a whole tile's
+    // elements and addresses would not fit beside the accumulators.
+    auto fill_in_chunks = [&](int64_t t, int stage) {
+        const int64_t k0 = t * BK;
+        TileLoader16<BM, BK, THREADS, 1>::template copy_in_chunks<TileA, 2>(a_tile + k0, lda, M - m0, K - k0, lds_a,
+                                                                           stage, tid);
+        TileLoader16<BK, BN, THREADS, 1>::template copy_in_chunks<TileB, 2>(b_tile + k0 * ldb, ldb, K - k0, N - n0,
+                                                                           lds_b, stage, tid);
+    };
     // Two stages through registers, each refill issued after the multiply
     // (workgroups whose tile cannot move back inside C, and unaligned
     // operands below).
     auto two_stage_registers = [&]() {
         if (T > 0) {
-            load_tile(0);
-            store_tile(0);
+            if constexpr (Cfg::VEC == 2) {
+                fill_in_chunks(0, 0);
+            } else {
+                load_tile(0);
+                store_tile(0);
+            }
         }
         __syncthreads();
         for (int64_t t = 0; t < T; ++t) {
             const int s = (int)(t & 1);
             multiply(s);
             if (t + 1 < T) {
-                load_tile(t + 1);
-                store_tile(s ^ 1);
+                if constexpr (Cfg::VEC == 2) {
+                    fill_in_chunks(t + 1, s ^ 1);
+                } else {
+                    load_tile(t + 1);
+                    store_tile(s ^ 1);
+                }
             }
             __syncthreads();
         }
     };
 
     if constexpr (Cfg::LOAD == kLoadDirect) {
-        using DA = DirectCopy<TileA, THREADS, uint16_t>;
-        using DB = DirectCopy<TileB, THREADS, uint16_t>;
+        using DA = DirectCopy<TileA, THREADS, uint16_t, Cfg::VEC == 8 ? 16 : 4>;
+        using DB = DirectCopy<TileB, THREADS, uint16_t, Cfg::VEC == 8 ? 16 : 4>;
         const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
         if (interior) {
             // S-stage pipeline of direct copies: during the multiply of tile t
@@ -406,8 +429,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                     dma_a.issue(a_tile + p * BK, lds_a, p);
                     dma_b.issue(b_tile + p * BK * ldb, lds_b, p);
                 } else {
-                    load_tile(p);
-                    store_tile(p);
+                    if constexpr (Cfg::VEC == 2) {
+                        fill_in_chunks(p, p);
+                    } else {
+                        load_tile(p);
+                        store_tile(p);
+                    }
                 }
             }
             wait_vector_memory();
@@ -445,8 +472,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                     }
                     if (nt < T && !direct) {
                         // ragged last K tile through registers, a few slots at a time
-                        using LoaderA = TileLoader16<BM, BK, THREADS, Cfg::VEC>;
-                        using LoaderB = TileLoader16<BK, BN, THREADS, Cfg::VEC>;
+                        using LoaderA = TileLoader16<BM, BK, THREADS, Cfg::LOADER_VEC>;
+                        using LoaderB = TileLoader16<BK, BN, THREADS, Cfg::LOADER_VEC>;
                         const int64_t k0 = nt * BK;
                         LoaderA::template copy_in_chunks<TileA, 2>(a_tile + k0, lda, M - m0, K - k0, lds_a, ps, tid);
                         LoaderB::template copy_in_chunks<TileB, 2>(b_tile + k0 * ldb, ldb, K - k0, N - n0, lds_b, ps, tid);
@@ -473,8 +500,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                     }
                     multiply(s);
                     if (nt < T && !direct) {
-                        load_tile(nt);
-                        store_tile(ps);
+                        if constexpr (Cfg::VEC == 2) {
+                            fill_in_chunks(nt, ps);
+                        } else {
+                            load_tile(nt);
+                            store_tile(ps);
+                        }
                     }
                     if (direct)
                         wait_vector_memory_at_most<(S - 2) * COPIES>();
@@ -502,8 +533,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 // scheme): KSPLIT groups of waves share one output tile, group q taking K
 // tiles q, q + KSPLIT, ... through its own pair of LDS stages with Base's
 // wave tiling, direct copies and step-pipelined multiply; the groups'
-// partial sums are added in LDS in group order.  16-byte copies only: the
-// unaligned form of every 16-bit variant is the 2-byte-load kernel.
+// partial sums are added in LDS in group order.  Copies of 16 bytes
+// (VEC 8) or 4 bytes (VEC 2), as the base's.
 template <class Base, int KSPLIT_>
 struct MixedKsplitCfg {
     static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2, "groups run Base's two-stage direct-copy loop");
@@ -512,6 +543,7 @@ struct MixedKsplitCfg {
     static constexpr int TYPE = Base::TYPE, KSPLIT = KSPLIT_;
     static constexpr int BM = Base::BM, BN = Base::BN, BK = Base::BK, WM = Base::WM, WN = Base::WN;
     static constexpr int VEC = Base::VEC, ORDER = Base::ORDER, LOAD = kLoadDirect, PIPELINE = kPipeSteps;
+    static constexpr int LOADER_VEC = Base::LOADER_VEC;
     static constexpr int WAVES_N = Base::WAVES_N, MI = Base::MI, NI = Base::NI, STEPS = Base::STEPS;
     static constexpr int GROUP_THREADS = Base::THREADS, GROUP_WAVES = GROUP_THREADS / kWave;
     static constexpr int THREADS = GROUP_THREADS * KSPLIT;
@@ -566,16 +598,16 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kspli
 #pragma unroll
             for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
 
-    TileLoader16<BM, BK, GT, Cfg::VEC> ldr_a;
-    TileLoader16<BK, BN, GT, Cfg::VEC> ldr_b;
+    TileLoader16<BM, BK, GT, Cfg::LOADER_VEC> ldr_a;
+    TileLoader16<BK, BN, GT, Cfg::LOADER_VEC> ldr_b;
     const uint16_t* a_tile = A + m0 * lda;
     const uint16_t* b_tile = B + n0;
     const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
     const int64_t TF = K / BK;
     const int64_t ITERS = (T + KS - 1) / KS;
 
-    using DA = DirectCopy<TileA, GT, uint16_t>;
-    using DB = DirectCopy<TileB, GT, uint16_t>;
+    using DA = DirectCopy<TileA, GT, uint16_t, Cfg::VEC == 8 ? 16 : 4>;
+    using DB = DirectCopy<TileB, GT, uint16_t, Cfg::VEC == 8 ? 16 : 4>;
     const DA dma_a(lda, wave, lane);
     const DB dma_b(ldb, wave, lane);
     const bool interior = M - m0 >= BM && N - n0 >= BN && DA::fits(lda) && DB::fits(ldb);
@@ -586,10 +618,17 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kspli
     };
     auto copy_registers = [&](int64_t t, int stage) {
         const int64_t k0 = t * BK;
-        ldr_a.load(a_tile + k0, lda, M - m0, K - k0, gtid);
-        ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, gtid);
-        ldr_a.template store<TileA>(lds_a, stage, gtid);
-        ldr_b.template store<TileB>(lds_b, stage, gtid);
+        if constexpr (Cfg::VEC == 2) {  // 2-byte loads, a few slots at a time
+            TileLoader16<BM, BK, GT, 1>::template copy_in_chunks<TileA, 2>(a_tile + k0, lda, M - m0, K - k0, lds_a,
+                                                                          stage, gtid);
+            TileLoader16<BK, BN, GT, 1>::template copy_in_chunks<TileB, 2>(b_tile + k0 * ldb, ldb, K - k0, N - n0,
+                                                                          lds_b, stage, gtid);
+        } else {
+            ldr_a.load(a_tile + k0, lda, M - m0, K - k0, gtid);
+            ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, gtid);
+            ldr_a.template store<TileA>(lds_a, stage, gtid);
+            ldr_b.template store<TileB>(lds_b, stage, gtid);
+        }
     };
     typedef __attribute__((address_space(3))) uint32_t lds_word;
     typedef __attribute__((address_space(3))) shortx4 lds_short4;

@@ -326,10 +326,12 @@ typedef enum {
 
 /* C = A @ B, A and B of `input_type` (gemm_input_type), C fp32.  A, B, C are
  * DEVICE pointers owned by the caller; M, N, K >= 0; lda >= max(1,K),
- * ldb >= max(1,N), ldc >= max(1,N), in elements.  16-byte loads and direct
- * copies need lda and ldb multiples of 8 and A, B 16-byte aligned; otherwise
- * the 256x128x32 kernel runs with 2-byte loads (the same result up to the
- * order of the fp32 additions).  Validation and
+ * ldb >= max(1,N), ldc >= max(1,N), in elements.  16-byte direct copies
+ * need lda and ldb multiples of 8 and A, B 16-byte aligned; otherwise, with
+ * lda and ldb even and A, B 4-byte aligned, the variant's kernel runs with
+ * 4-byte copies (two elements per lane); otherwise the 256x128x32 kernel
+ * runs with 2-byte loads through registers (the same result up to the order
+ * of the fp32 additions).  Validation and
  * asynchrony as gemm_f32.  Returns a gemm_status; GEMM_ERR_UNSUPPORTED for an
  * unknown input type or variant. */
 int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K,
@@ -345,7 +347,7 @@ int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
  * work for a tile, tiles / (ceil(tiles / per_round) * per_round), with
  * per_round = num_cus for 256x256, 64x64 and 32x64 tiles and 2 * num_cus
  * for 128x128; "big" is 256x256_BK64 when K is a multiple of 64, else
- * 256x256_S3.  When 256x256 tiles number at least num_cus / 2: 128x128_BK64
+ * 256x256_S3 (with 16- or 4-byte copies alike).  When 256x256 tiles number at least num_cus / 2: 128x128_BK64
  * if 1050 * e128 > 1.1 * 1200 * e256, else big.  Otherwise the highest of
  * these estimates (listed first wins within 2 %): 64x64_KS4 420 * e64 and
  * 32x64_KS4 290 * e32x64 when K >= 4096; 64x64_KS2 530 * min(1, 0.6 w)

@@ -136,6 +136,26 @@ def test_mixed_edge_shapes(kind, shape, variant, torch_gpu):
     assert np.array_equal(ci.astype(np.float64), oracle.reference(afi, bfi)[0])
 
 
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("K,pad_a,pad_b,offset", [(130, 2, 4, 0), (64, 6, 2, 2), (200, 4, 6, 2), (1000, 2, 2, 0)])
+def test_mixed_four_byte_copies(kind, K, pad_a, pad_b, offset, variant, torch_gpu):
+    """Rows 4-byte but not 16-byte aligned (even leading dimensions not a
+    multiple of 8, bases shifted by two elements): the variants copy two
+    elements per lane.  Bit for bit on integer operands, within the bar on
+    uniform ones; NaN fills every ld gap."""
+    M, N = 300, 260
+    lda, ldb = K + pad_a, N + pad_b
+    assert lda % 2 == 0 and ldb % 2 == 0 and (lda % 8 or ldb % 8 or offset)
+    ab, bb, af, bf = operands(kind, M, N, K, "integer", 1900 + K)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=lda, ldb=ldb, ldc=N + 3, offset=offset)
+    assert np.array_equal(c.astype(np.float64), oracle.reference(af, bf)[0])
+    ab, bb, af, bf = operands(kind, M, N, K, "uniform", 2000 + K)
+    cref, den = oracle.reference(af, bf)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=lda, ldb=ldb, offset=offset)
+    assert oracle.normalised_error(c, cref, den) <= TOL
+
+
 KSPLIT_VARIANTS = [dft.MIXED_64x64_KS2, dft.MIXED_64x64_KS4, dft.MIXED_32x64_KS4]
 
 
