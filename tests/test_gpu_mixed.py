@@ -156,6 +156,28 @@ def test_mixed_four_byte_copies(kind, K, pad_a, pad_b, offset, variant, torch_gp
     assert oracle.normalised_error(c, cref, den) <= TOL
 
 
+_random_refs: dict = {}
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+def test_mixed_random_shapes(variant, torch_gpu):
+    """30 seeded random shapes (bf16), each with random leading-dimension
+    pads and a base offset of 0, 1 or 2 elements, so that calls take the
+    16-byte copies, the 4-byte copies or the 2-byte loads."""
+    rng = np.random.default_rng(4242)
+    for i in range(30):
+        M, N, K = (int(x) for x in rng.integers(1, 600, 3))
+        pa, pb, pc = (int(x) for x in rng.integers(0, 9, 3))
+        offset = int(rng.integers(0, 3))
+        if i not in _random_refs:
+            ab, bb, af, bf = operands("bf16", M, N, K, "uniform", 6000 + i)
+            _random_refs[i] = (ab, bb) + oracle.reference(af, bf)
+        ab, bb, cref, den = _random_refs[i]
+        c = run_mixed(torch_gpu, "bf16", ab, bb, variant, lda=K + pa, ldb=N + pb, ldc=N + pc, offset=offset)
+        err = oracle.normalised_error(c, cref, den)
+        assert err <= TOL, (M, N, K, pa, pb, pc, offset, err)
+
+
 KSPLIT_VARIANTS = [dft.MIXED_64x64_KS2, dft.MIXED_64x64_KS4, dft.MIXED_32x64_KS4]
 
 

@@ -43,7 +43,8 @@ def random_cases(count: int, seed: int):
 
 RANDOM_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_PIPE,
                    dft.VARIANT_MFMA_256x256_BK32_PIPE, dft.VARIANT_MFMA_DIRECT,
-                   dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT, dft.VARIANT_MFMA, dft.VARIANT_VALU]
+                   dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT, dft.VARIANT_MFMA, dft.VARIANT_VALU,
+                   dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
 
 
 _refs: dict = {}
