@@ -149,6 +149,10 @@ def test_auto_variant_selection(gemm_lib):
 
 def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     av = dft.gemm_f32_auto_variant
+
+    def ax_(M, N, K):  # row alignment as for packed operands (lda = K, ldb = N)
+        return dft.gemm_f32_auto_variant_ex(M, N, K, 256, int(K % 4 == 0), int(N % 4 == 0))
+
     # measured fastest on one MI355X (256 CUs): K split inside the workgroup when few tiles meet a deep K
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4   # 101 TF against 54 for 64x64x32
     assert av(1024, 512, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4
@@ -159,7 +163,16 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     # enough tiles, or too short a K: no split
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(2048, 256, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # split 56 against 59
+    # from K = 1024 when the split's grid has at most one tile per CU
+    assert av(512, 512, 1024, 256) == dft.VARIANT_MFMA_32x32_KS8         # 43 against 22
+    assert av(1000, 512, 1024, 256) == dft.VARIANT_MFMA_32x64_KS4        # 62 against 42
+    assert av(1000, 1000, 2000, 256) == dft.VARIANT_MFMA_64_KS4          # 92 against 87
+    assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT       # two rounds: split 41 against 52
+    assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    # a deep K still splits over several rounds of tiles
+    assert av(768, 768, 8192, 256) == dft.VARIANT_MFMA_32x32_KS8         # 68 against 57
     # unaligned operands (odd K: A's rows; odd N: B's), measured per alignment class
     ax = dft.gemm_f32_auto_variant_ex
     assert ax(2048, 256, 16383, 256, 0, 1) == dft.VARIANT_MFMA_32x64_KS4   # 95 against 49
