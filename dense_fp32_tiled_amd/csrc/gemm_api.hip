@@ -674,10 +674,13 @@ int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     };
     Candidate candidates[6];
     int n = 0;
-    if (K >= 4096) {
+    // The K split over four groups from K = 4096, or from K = 1024 when its
+    // grid has at most one tile per CU (bf16 on one box: 32x64_KS4 11-25 %
+    // ahead of the previous pick on 1-2k-row grids at K = 1024-3072).
+    if (K >= 4096 || (K >= 1024 && t64 <= num_cus))
         candidates[n++] = {GEMM_MIXED_64x64_KS4, 420.0 * round_fill(t64, num_cus)};
+    if (K >= 4096 || (K >= 1024 && t32x64 <= num_cus))
         candidates[n++] = {GEMM_MIXED_32x64_KS4, 290.0 * round_fill(t32x64, num_cus)};
-    }
     if (K >= 2048) candidates[n++] = {GEMM_MIXED_64x64_KS2, 530.0 * std::min(1.0, 0.6 * w64)};
     candidates[n++] = {GEMM_MIXED_64x64, 700.0 * std::min(1.0, 0.375 * w64)};
     candidates[n++] = {GEMM_MIXED_128x128_BK64, 1050.0 * e128};

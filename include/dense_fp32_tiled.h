@@ -351,7 +351,8 @@ int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
  * 256x256_S3 (with 16- or 4-byte copies alike).  When 256x256 tiles number at least num_cus / 2: 128x128_BK64
  * if 1050 * e128 > 1.1 * 1200 * e256, else big.  Otherwise the highest of
  * these estimates (listed first wins within 2 %): 64x64_KS4 420 * e64 and
- * 32x64_KS4 290 * e32x64 when K >= 4096; 64x64_KS2 530 * min(1, 0.6 w)
+ * 32x64_KS4 290 * e32x64, each when K >= 4096, or when K >= 1024 and its
+ * grid has at most num_cus tiles; 64x64_KS2 530 * min(1, 0.6 w)
  * when K >= 2048; 64x64 700 * min(1, 0.375 w); 128x128_BK64 1050 * e128;
  * big 1.1 * 1200 * e256 (w: 64x64 tiles per CU).  Pure host call;
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */

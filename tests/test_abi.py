@@ -369,4 +369,10 @@ def test_mixed_auto_variant(gemm_lib):
     assert av(3072, 3072, 3072, 256) == dft.MIXED_256x256_BK64
     assert av(6000, 6000, 6000, 256) == dft.MIXED_256x256_S3     # 576 tiles vs 2209 of 128x128
     assert av(2048, 2048, 2048, 256) == dft.MIXED_64x64         # 544 against 492
+    # from K = 1024 the split runs when its grid has at most one tile per CU
+    assert av(512, 512, 2048, 256) == dft.MIXED_32x64_KS4       # 103 against 85
+    assert av(1024, 512, 1024, 256) == dft.MIXED_32x64_KS4      # 120 against 108
+    assert av(1024, 1024, 3072, 256) == dft.MIXED_64x64_KS4     # 331 against 305
+    assert av(1536, 768, 2048, 256) == dft.MIXED_64x64_KS2      # 288 tiles of 64x64: no four-group split
+    assert av(512, 512, 512, 256) == dft.MIXED_64x64
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
