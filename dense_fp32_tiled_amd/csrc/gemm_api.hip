@@ -298,22 +298,24 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         double rate[4];   // TFLOP/s with every CU busy, by alignment: both, A only, B only, neither
         bool small_wg;    // 4-wave workgroups: below full rate at one or two per CU
         int64_t min_k;    // K-split variants: enough K tiles for every group (0: any K)
-                          // (1024 when the grid has at most one tile per CU)
+        int64_t min_k_one_round;  // the same when the grid has at most one tile per CU
     };
     const Candidate candidates[] = {
-        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0},
-        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0},
+        {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0, 0},
+        {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0, 0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
-         {144.0, 124.0, 130.0, 118.0}, false, 0},
-        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0},
+         {144.0, 124.0, 130.0, 118.0}, false, 0, 0},
+        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
         // K split inside the workgroup: 16 K tiles of 32 per group at
-        // least, or 8 (4 at eight groups) when the grid has at most one
-        // tile per CU.  Below K = 1024 (5-7 % under the 64x64 kernel at
-        // K = 512 on 1000^2 and 1024^2 grids) and on grids of two or more
-        // rounds at K = 1024-2048 (up to 22 % under it) the split loses.
-        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4},
-        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4},
-        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8},
+        // least; when the split's grid has at most one tile per CU, from
+        // K = 1024 for 64x64 tiles and K = 512 for the smaller ones (whose
+        // one-round grids leave the 64x64 kernel half the CUs or fewer).
+        // 64x64 KS4 measured 5-7 % under the 64x64 kernel at K = 512 on
+        // 1000^2 and 1024^2 grids, and any split up to 22 % under it on
+        // grids of two or more rounds at K = 1024-2048.
+        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4, 1024},
+        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 512},
+        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 512},
     };
     const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;
@@ -321,7 +323,7 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
     for (const Candidate& c : candidates) {
         if (c.rate[cls] <= 0.0) continue;
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        if (c.min_k > 0 && K < (tiles <= num_cus ? std::min<int64_t>(c.min_k, 1024) : c.min_k)) continue;
+        if (c.min_k > 0 && K < (tiles <= num_cus ? c.min_k_one_round : c.min_k)) continue;
         const int64_t rounds = tiles > 0 ? (tiles + num_cus - 1) / num_cus : 1;
         double rate = c.rate[cls] * (double)tiles / (double)(rounds * num_cus);
         if (tiles < (int64_t)c.per_cu * num_cus) rate *= c.per_cu > 1 ? 0.88 : 1.0;

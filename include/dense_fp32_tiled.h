@@ -214,8 +214,9 @@ const char *gemm_f32_status_string(int status);
  * MFMA_256x256_BK32_PIPE 145 TFLOP/s, MFMA_DIRECT (256x128) 144, the 128x128
  * direct variant (BK 32 when K >= 1024, else 16) 144, MFMA_64_BK32_DIRECT
  * 134; when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
- * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup; each of them
- * already from K >= 1024 when its grid has at most num_cus tiles).  Estimate:
+ * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup; when the
+ * split's grid has at most num_cus tiles, already from K >= 1024 for
+ * MFMA_64_KS4 and K >= 512 for the other two).  Estimate:
  * the rate times the wave quantisation of the tile grid,
  * tiles / (ceil(tiles / num_cus) * num_cus); times 0.88 for the 256x128 and
  * 128x128 kernels with fewer tiles than two per CU (they are built for two

@@ -163,12 +163,17 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     # enough tiles, or too short a K: no split
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # split 56 against 59
     # from K = 1024 when the split's grid has at most one tile per CU
     assert av(512, 512, 1024, 256) == dft.VARIANT_MFMA_32x32_KS8         # 43 against 22
     assert av(1000, 512, 1024, 256) == dft.VARIANT_MFMA_32x64_KS4        # 62 against 42
     assert av(1000, 1000, 2000, 256) == dft.VARIANT_MFMA_64_KS4          # 92 against 87
+    # and from K = 512 for the smaller split tiles
+    assert av(512, 512, 512, 256) == dft.VARIANT_MFMA_32x32_KS8          # 28 against 17
+    assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
+    assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
+    assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # no smaller split in one round
     assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT       # two rounds: split 41 against 52
     assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # a deep K still splits over several rounds of tiles
