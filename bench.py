@@ -9,6 +9,19 @@ Prints ONE JSON line with the whole-job TFLOP/s (wall clock over K steps
 bracketed by device synchronisation), the dominant kernel's roofline position
 (its average duration from HIP events on the launch stream) and the fp64 CPU
 oracle timed on a bounded sample of the same workload on the host cores.
+
+Before the W warmup steps the step is repeated for --settle-ms of wall time
+(untimed): an idle GPU raises its clock over the first tens of milliseconds
+of work (a kernel trace of 20 steps after 5 warmups shows the 4096^3 kernel
+taking 1.12 ms at first and 0.95 ms from about the 22nd launch on), so
+without it a short timed region measures the ramp, not the kernel.
+
+    python bench.py --sweep 1000x999x513,2048x256x16384 --sweep-variants auto,mfma_64_bk32_direct \
+        --sweep-out FILE [--sweep-reps 5] [--input bf16]
+
+instead times each listed variant on each shape (operands uniform[-1,1),
+packed leading dimensions), interleaved over --sweep-reps rounds, and writes
+one JSON line per shape and variant (median kernel TFLOP/s by HIP events).
 """
 
 from __future__ import annotations
@@ -59,6 +72,60 @@ def measured_traffic(variant_name: str, workload: str):
         return None
 
 
+def host_cpu_model() -> str | None:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sclk_mhz(props) -> float | None:
+    """The GPU's current engine clock level (MHz) from its pp_dpm_sclk sysfs
+    file (the line marked '*'), found by PCI address; None if unreadable."""
+    import re
+
+    candidates = []
+    try:
+        candidates.append(Path(f"/sys/bus/pci/devices/{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:"
+                               f"{props.pci_device_id:02x}.0/pp_dpm_sclk"))
+    except AttributeError:
+        pass
+    drm = sorted(Path("/sys/class/drm").glob("card*/device/pp_dpm_sclk"))
+    if len(drm) == 1:
+        candidates.append(drm[0])
+    for path in candidates:
+        try:
+            for line in path.read_text().splitlines():
+                m = re.search(r"(\d+)\s*Mhz\s*\*", line, re.IGNORECASE)
+                if m:
+                    return float(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def run_metadata(torch, dev) -> dict:
+    props = torch.cuda.get_device_properties(dev)
+    return {"device": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "host_cpu": host_cpu_model()}
+
+
+def settle(step, torch, ms: float) -> dict:
+    """Repeat `step` (untimed) for at least `ms` of wall time, in batches
+    ending with a device synchronisation."""
+    launches = 0
+    t0 = time.perf_counter()
+    while ms > 0 and (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        launches += 8
+        torch.cuda.synchronize()
+    return {"ms": (time.perf_counter() - t0) * 1e3, "launches": launches}
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,10 +151,87 @@ def parse_args(argv=None):
                          "many MiB to a scratch buffer, which evicts A and B from L2 and the 256 MB MALL "
                          "(reported as cold_cache; 0 = skip, the default, so that a kernel trace of the default "
                          "command holds only the warm launches the roofline figure averages)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="repeat the step for this long (wall ms, untimed) before the warmup steps, so that the "
+                         "GPU clock has left its idle level when the timed region starts (0 = skip)")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated MxNxK shapes: time --sweep-variants on each (see the module docstring) "
+                         "instead of the single-workload run")
+    ap.add_argument("--sweep-variants", default="auto", help="comma-separated variant names for --sweep")
+    ap.add_argument("--sweep-reps", type=int, default=5, help="interleaved rounds per shape for --sweep")
+    ap.add_argument("--sweep-out", default="", help="output file (JSON lines) for --sweep")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB (a "
                          "reference kernel of known traffic for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args(argv)
+
+
+def sweep(args, names: dict, mixed: bool) -> int:
+    """Kernel TFLOP/s of several variants on several shapes, interleaved:
+    each of --sweep-reps rounds times every variant once (--steps launches
+    by HIP events after --warmup), and each line reports the median round."""
+    import numpy as np
+    import torch
+
+    import dense_fp32_tiled_amd as dft
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    variants = [names[v] for v in args.sweep_variants.split(",")]
+    input_type = {"bf16": dft.INPUT_BF16, "f16": dft.INPUT_F16}.get(args.input)
+    meta = run_metadata(torch, dev)
+    out = open(args.sweep_out, "w") if args.sweep_out else sys.stdout
+    for shape in args.sweep.split(","):
+        M, N, K = (int(x) for x in shape.lower().split("x"))
+        a_np, b_np = workloads.make_operands(M, N, K, "uniform", 7)
+        if mixed:
+            a = torch.from_numpy(workloads.to_16bit(a_np, args.input)[0].view(np.int16)).to(dev)
+            b = torch.from_numpy(workloads.to_16bit(b_np, args.input)[0].view(np.int16)).to(dev)
+            auto = dft.gemm_mixed_auto_variant(M, N, K, cus)
+        else:
+            a, b = torch.from_numpy(a_np).to(dev), torch.from_numpy(b_np).to(dev)
+            auto = dft.gemm_f32_auto_variant_ex(M, N, K, cus, K % 4 == 0, N % 4 == 0)
+        c = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def step(v):
+            if mixed:
+                st = dft.gemm_mixed_f32(input_type, M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N,
+                                        handle, v)
+            else:
+                st = dft.gemm_f32_ex(M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N, handle, v)
+            if st != dft.GEMM_OK:
+                raise dft.GemmError(st, f"{shape} variant {v}")
+
+        settle(lambda: step(variants[0]), torch, args.settle_ms)
+        per_variant = {v: [] for v in variants}
+        for _ in range(args.sweep_reps):
+            for v in variants:
+                for _ in range(args.warmup):
+                    step(v)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.steps)]
+                for e0, e1 in ev:
+                    e0.record(stream)
+                    step(v)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                avg = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev) / 1e3
+                per_variant[v].append(2.0 * M * N * K / avg / 1e12)
+        for v in variants:
+            rates = sorted(per_variant[v])
+            vname = (dft.MIXED_NAMES if mixed else dft.VARIANT_NAMES)[v]
+            resolved = (dft.MIXED_NAMES if mixed else dft.VARIANT_NAMES)[auto] if v == 0 else vname
+            out.write(json.dumps({"shape": shape, "input": args.input, "variant": vname, "runs": resolved,
+                                  "tflops_median": rates[len(rates) // 2], "tflops_all": rates,
+                                  "device": meta["device"]}) + "\n")
+            out.flush()
+    if out is not sys.stdout:
+        out.close()
+    return 0
 
 
 def main(argv=None) -> int:
@@ -108,6 +252,8 @@ def main(argv=None) -> int:
         return 1
     mixed = args.input != "f32"
     names = {v: k for k, v in (dft.MIXED_NAMES if mixed else dft.VARIANT_NAMES).items()}
+    if args.sweep:
+        return sweep(args, names, mixed)
     variant = names[args.variant]
     if mixed and args.splits >= 0:
         print("--splits applies to fp32 inputs only", file=sys.stderr)
@@ -170,7 +316,12 @@ def main(argv=None) -> int:
         durs = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in ev)
         return wall_s, sum(durs) / len(durs), durs[len(durs) // 2], durs[0]
 
+    settled = settle(step, torch, args.settle_ms)
+    props = torch.cuda.get_device_properties(dev)
+    meta = run_metadata(torch, dev)
+    meta["sclk_mhz_before"] = sclk_mhz(props)
     wall_s, kern_avg_s, kern_med_s, kern_min_s = time_variant(variant, args.steps, args.warmup)
+    meta["sclk_mhz_after"] = sclk_mhz(props)
 
     # Cold caches: the timed region above re-reads A and B from L2 / MALL on
     # every launch after the first; here each launch follows a write of a
@@ -276,6 +427,8 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu_baseline,
         "cold_cache": cold,
         "parity_sample": parity,
+        "settle": settled,
+        "run": meta,
     }
 
     if args.ablations:

@@ -316,6 +316,10 @@ def gemm_lds_page_pad(columns: int, simultaneous_rows: int, banks: int = 32) -> 
 
 # ---- torch convenience -------------------------------------------------------------
 def _operand(t, name, dtype=None):
+    """(device pointer, row pitch in elements) of a 2-D tensor whose rows are
+    laid out one after another: unit column stride, and a row stride of at
+    least the row length (a tensor whose rows overlap, e.g. an expanded
+    view with row stride 0, has no such pitch and is rejected)."""
     import torch
 
     dtype = dtype or torch.float32
@@ -328,8 +332,35 @@ def _operand(t, name, dtype=None):
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return t.data_ptr(), max(ld, cols, 1)
+    if rows > 1 and cols > 0 and t.stride(0) < cols:
+        raise ValueError(f"{name} has overlapping rows (row stride {t.stride(0)} < {cols} columns)")
+    ld = t.stride(0) if rows > 1 and cols > 0 else max(cols, 1)
+    return t.data_ptr(), ld
+
+
+def _operands(a, b, out, dtype=None, out_dtype=None):
+    """Checks shared by the torch wrappers, all before any launch: operand
+    types and layouts, matching inner dimensions, every tensor on a's device
+    and `out` (allocated here when None) of shape (M, N).  Returns
+    (M, N, K, (pa, lda), (pb, ldb), (pc, ldc), out)."""
+    import torch
+
+    pa, lda = _operand(a, "a", dtype)
+    pb, ldb = _operand(b, "b", dtype)
+    M, K = a.shape
+    if b.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
+    N = b.shape[1]
+    if b.device != a.device:
+        raise ValueError(f"b is on {b.device}, a on {a.device}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    pc, ldc = _operand(out, "out", out_dtype)
+    if out.device != a.device:
+        raise ValueError(f"out is on {out.device}, a on {a.device}")
+    return M, N, K, (pa, lda), (pb, ldb), (pc, ldc), out
 
 
 def _stream_handle(stream, device):
@@ -346,21 +377,15 @@ def matmul_splitk(a, b, out=None, splits: int = 0, workspace=None, stream=None, 
     device) is allocated here when not given."""
     import torch
 
-    pa, lda = _operand(a, "a")
-    pb, ldb = _operand(b, "b")
-    M, K = a.shape
-    if b.shape[0] != K:
-        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
-    N = b.shape[1]
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    pc, ldc = _operand(out, "out")
+    M, N, K, (pa, lda), (pb, ldb), (pc, ldc), out = _operands(a, b, out)
     cus = torch.cuda.get_device_properties(a.device).multi_processor_count
     need = gemm_f32_splitk_workspace_bytes(M, N, K, splits, cus)
     if need < 0:
         raise GemmError(need, "gemm_f32_splitk_workspace_bytes")
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=a.device)
+    elif workspace is not None and workspace.device != a.device:
+        raise ValueError(f"workspace is on {workspace.device}, a on {a.device}")
     wp = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(a.device):
@@ -379,15 +404,7 @@ def matmul_mixed(a, b, out=None, variant: int = MIXED_AUTO, stream=None):
     types = {torch.bfloat16: INPUT_BF16, torch.float16: INPUT_F16}
     if a.dtype not in types or b.dtype != a.dtype:
         raise TypeError("a and b must both be bfloat16 or both float16")
-    pa, lda = _operand(a, "a", a.dtype)
-    pb, ldb = _operand(b, "b", a.dtype)
-    M, K = a.shape
-    if b.shape[0] != K:
-        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
-    N = b.shape[1]
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    pc, ldc = _operand(out, "out")
+    M, N, K, (pa, lda), (pb, ldb), (pc, ldc), out = _operands(a, b, out, a.dtype)
     with torch.cuda.device(a.device):
         st = gemm_mixed_f32(types[a.dtype], M, N, K, pa, lda, pb, ldb, pc, ldc, _stream_handle(stream, a.device),
                             variant)
@@ -402,17 +419,7 @@ def matmul(a, b, out=None, variant: int = VARIANT_AUTO, stream=None):
     (a torch.cuda.Stream or raw handle) or torch's current stream."""
     import torch
 
-    pa, lda = _operand(a, "a")
-    pb, ldb = _operand(b, "b")
-    M, K = a.shape
-    if b.shape[0] != K:
-        raise ValueError(f"inner dimensions differ: {K} vs {b.shape[0]}")
-    N = b.shape[1]
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    elif out.shape != (M, N):
-        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
-    pc, ldc = _operand(out, "out")
+    M, N, K, (pa, lda), (pb, ldb), (pc, ldc), out = _operands(a, b, out)
     if stream is None:
         handle = torch.cuda.current_stream(a.device).cuda_stream
     elif isinstance(stream, int):

@@ -705,10 +705,12 @@ int run_mixed(int input_type, const Args& a, hipStream_t stream, int variant) {
     const int st = prologue(a, stream, &max_lds, &num_cus, &done, 2);
     if (st != GEMM_OK || done) return st;
     // 16-byte copies need rows 16-byte aligned (ld % 8 == 0, 16-byte bases);
-    // 4-byte copies rows 4-byte aligned (even ld, 4-byte bases).
-    const bool rows16 = (a.lda % 8 == 0) && (a.ldb % 8 == 0) && (((uintptr_t)a.A & 15) == 0) &&
+    // 4-byte copies rows 4-byte aligned (even ld, 4-byte bases).  An edge
+    // tile moved back to end at N starts its B columns at N - BN, so B's
+    // copies also need N a multiple of the elements per copy.
+    const bool rows16 = (a.lda % 8 == 0) && (a.ldb % 8 == 0) && (a.N % 8 == 0) && (((uintptr_t)a.A & 15) == 0) &&
                         (((uintptr_t)a.B & 15) == 0);
-    const bool rows4 = (a.lda % 2 == 0) && (a.ldb % 2 == 0) && (((uintptr_t)a.A & 3) == 0) &&
+    const bool rows4 = (a.lda % 2 == 0) && (a.ldb % 2 == 0) && (a.N % 2 == 0) && (((uintptr_t)a.A & 3) == 0) &&
                        (((uintptr_t)a.B & 3) == 0);
     if (variant == GEMM_MIXED_AUTO) variant = mixed_auto_variant(a.M, a.N, a.K, num_cus);
     const MixedVariant& v = kMixedVariants[variant];

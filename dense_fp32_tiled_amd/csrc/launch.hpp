@@ -21,9 +21,13 @@ struct Args {
 };
 
 // Rows of A (B) start 16-byte aligned: the operand may be loaded or copied
-// 16 bytes per lane.
+// 16 bytes per lane.  A tile's columns of B start at a multiple of the tile
+// width, or at N - BN for an edge tile that the direct-copy kernels move back
+// to end at N; so B also needs N % 4 == 0 for every copy to start on a
+// 16-byte boundary.  (A's tiles start at whole rows and at multiples of BK
+// along K, so lda alone decides for A.)
 inline bool a_aligned(const Args& a) { return a.lda % 4 == 0 && ((uintptr_t)a.A & 15) == 0; }
-inline bool b_aligned(const Args& a) { return a.ldb % 4 == 0 && ((uintptr_t)a.B & 15) == 0; }
+inline bool b_aligned(const Args& a) { return a.ldb % 4 == 0 && a.N % 4 == 0 && ((uintptr_t)a.B & 15) == 0; }
 
 // K slicing of one launch: `splits` slices of k_chunk (a multiple of BK)
 // along gridDim.y, slice s writing C + s * c_split_stride.  A plain launch is

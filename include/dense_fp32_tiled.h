@@ -53,7 +53,13 @@ typedef enum {
     GEMM_ERR_NULL = -3,         /* a NULL pointer for an operand with non-zero extent */
     GEMM_ERR_ALIAS = -4,        /* the address range of C overlaps that of A or B */
     GEMM_ERR_UNSUPPORTED = -5,  /* no gfx950 device current, or unknown variant or input type */
-    GEMM_ERR_CONFIG = -6,       /* variant's LDS footprint exceeds the device limit */
+    GEMM_ERR_CONFIG = -6,       /* variant's LDS footprint (both operands' tiles, every stage and
+                                   its padding) exceeds the device's LDS per workgroup: the budget
+                                   check of "My Triton From Scratch, Part 18", section "Shared-memory
+                                   budget checks include stages and padding", and of Part 14, section
+                                   "Tracking the shared-memory budget"; as there, the check runs for
+                                   the operand pair before anything is launched, so a failure leaves
+                                   nothing half done */
     GEMM_ERR_HIP = -7,          /* a HIP runtime call or the launch failed */
     GEMM_ERR_TOO_LARGE = -8,    /* a size overflows the kernel's index range */
     GEMM_ERR_WORKSPACE = -9     /* split-K workspace missing or too small */
@@ -131,7 +137,12 @@ typedef struct {
 } gemm_tile_config;
 
 /* C = A @ B with the default variant.  M, N, K >= 0; lda >= max(1,K),
- * ldb >= max(1,N), ldc >= max(1,N).  Returns a gemm_status. */
+ * ldb >= max(1,N), ldc >= max(1,N).  Returns a gemm_status.
+ * One workgroup per BM x BN output tile, reducing over K tiles with masked,
+ * zero-filled operand tiles and a masked store: the program of "My Triton
+ * From Scratch, Part 14: Shared-Memory Tiles", section "The canonical source
+ * pattern", staged through LDS as in its sections "Cooperative copy mapping"
+ * and "Staging inside a runtime K loop". */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
              const float *B, int64_t ldb,
@@ -139,10 +150,15 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              void *stream);
 
 /* As gemm_f32 with an explicit gemm_variant.  When lda (ldb) is not a
- * multiple of 4, or A (B) is not 16-byte aligned, that operand cannot be
- * loaded or copied 16 bytes per lane, and the call runs the variant's kernel
- * that moves it 4 bytes per lane instead (a fallback, not an error; the same
- * result up to the order of the fp32 additions).  The variants AUTO chooses
+ * multiple of 4, or A (B) is not 16-byte aligned (for B also: N not a
+ * multiple of 4, since an edge tile moved back to end at N starts its
+ * columns at N - BN), that operand cannot be loaded or copied 16 bytes per
+ * lane, and the call runs the variant's kernel that moves it 4 bytes per
+ * lane instead: a fallback, not an error, with the same result up to the
+ * order of the fp32 additions.  This is the rule of "My Triton From Scratch,
+ * Part 18", section "Why a conservative matcher matters": a specialised
+ * lowering applies only where its preconditions hold, and otherwise the
+ * existing correct form runs.  The variants AUTO chooses
  * from (MFMA_256x256_BK32_PIPE, MFMA_DIRECT, MFMA_128_DIRECT,
  * MFMA_128_BK32_DIRECT, MFMA_64_BK32_DIRECT) decide per operand and keep
  * 16-byte copies for an aligned one; the others move both operands 4 bytes
@@ -201,11 +217,21 @@ int64_t gemm_f32_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int spl
  * least eight 16-deep K tiles per slice.  Pure host call. */
 int gemm_f32_splitk_auto_splits(int64_t M, int64_t N, int64_t K, int32_t num_cus);
 
-/* Fills *out with the tile geometry of `variant`.  Pure host call (touches no
- * device).  Returns GEMM_OK, GEMM_ERR_NULL or GEMM_ERR_UNSUPPORTED. */
+/* Fills *out with the tile geometry of `variant`: its BM x BN x BK tiles
+ * ("My Triton From Scratch, Part 14", section "A global tile description")
+ * and each operand's LDS tile with its row stride, stages and byte footprint
+ * (Part 18, sections "A shared buffer needs a physical row stride" and
+ * "Shared-memory budget checks include stages and padding").  Pure host call
+ * (touches no device).  Returns GEMM_OK, GEMM_ERR_NULL or
+ * GEMM_ERR_UNSUPPORTED. */
 int gemm_f32_tile_config(int variant, gemm_tile_config *out);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL).  Every
+ * failure is reported before anything is enqueued (argument and budget
+ * checks run first, as the LDS budget check of "My Triton From Scratch,
+ * Part 14", section "Tracking the shared-memory budget", makes a failure
+ * atomic), except GEMM_ERR_HIP for a launch the runtime refused.  Unknown
+ * codes give "unknown status". */
 const char *gemm_f32_status_string(int status);
 
 /* The variant GEMM_VARIANT_AUTO runs for an M x N x K problem on a device with

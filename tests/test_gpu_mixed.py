@@ -156,6 +156,21 @@ def test_mixed_four_byte_copies(kind, K, pad_a, pad_b, offset, variant, torch_gp
     assert oracle.normalised_error(c, cref, den) <= TOL
 
 
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("N", [250, 260, 262, 301])
+def test_mixed_moved_tiles_with_aligned_pitch(kind, N, variant, torch_gpu):
+    """ldb a multiple of 8 elements (16-byte rows) with N not a multiple of
+    8: an edge tile moved back to end at N starts its B columns at N - BN,
+    so the copies of B must be narrower than 16 bytes (4-byte copies for an
+    even N, 2-byte loads for an odd one).  Bit for bit on integer inputs."""
+    M, K = 300, 100
+    lda, ldb = K + (-K) % 8, N + (-N) % 8 + 8
+    ab, bb, af, bf = operands(kind, M, N, K, "integer", 2100 + N)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=lda, ldb=ldb, ldc=N + 1)
+    assert np.array_equal(c.astype(np.float64), oracle.reference(af, bf)[0])
+
+
 _random_refs: dict = {}
 
 

@@ -330,6 +330,27 @@ def test_moved_edge_tiles(shape, variant, torch_gpu):
     assert oracle.normalised_error(cu, cref_u, den_u) <= TOL
 
 
+PITCH_SHAPES = [(129, 250, 96), (257, 301, 40), (520, 263, 33), (300, 1003, 64)]
+
+
+@pytest.mark.parametrize("variant", MOVED_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in MOVED_VARIANTS])
+@pytest.mark.parametrize("shape", PITCH_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in PITCH_SHAPES])
+def test_moved_edge_tiles_with_aligned_pitch(shape, variant, torch_gpu):
+    """B's rows start 16-byte aligned (ldb a multiple of 4) but N is not a
+    multiple of 4: an edge tile moved back to end at N starts its B columns
+    at N - BN, off a 16-byte boundary, so B must be copied 4 bytes per lane.
+    Bit for bit on integer operands, NaN in every gap and around C."""
+    M, N, K = shape
+    assert N % 4
+    lda, ldb = K + (-K) % 4 + 4, N + (-N) % 4 + 4
+    assert lda % 4 == 0 and ldb % 4 == 0
+    a, b = workloads.make_operands(M, N, K, "integer", 1700 + M + N + K)
+    cref, _ = oracle.reference(a, b)
+    c, full = run_gemm(torch_gpu, a, b, variant, lda=lda, ldb=ldb, ldc=N + 3, c_rows_extra=2)
+    check_sentinels(full, M, N)
+    assert np.array_equal(c.astype(np.float64), cref), shape
+
+
 @pytest.mark.parametrize("variant", ALL_VARIANTS, ids=VARIANT_IDS)
 def test_k_zero_writes_zeros(variant, torch_gpu):
     a = np.zeros((37, 0), np.float32)
