@@ -26,6 +26,7 @@ GEMM_ERR_CONFIG = -6
 GEMM_ERR_HIP = -7
 GEMM_ERR_TOO_LARGE = -8
 GEMM_ERR_WORKSPACE = -9
+GEMM_ERR_SCRATCH = -10
 
 VARIANT_AUTO = 0
 VARIANT_MFMA = 1
@@ -105,6 +106,7 @@ EXPORTS = (
     "gemm_f32_status_string",
     "gemm_f32_splitk",
     "gemm_f32_splitk_ex",
+    "gemm_f32_splitk_noalloc",
     "gemm_f32_splitk_auto_variant",
     "gemm_f32_splitk_workspace_bytes",
     "gemm_f32_splitk_auto_splits",
@@ -182,6 +184,8 @@ def library(path: Path | None = None):
     lib.gemm_f32_splitk.restype = ctypes.c_int
     lib.gemm_f32_splitk_ex.argtypes = gemm_args[:9] + [vp, i64, ctypes.c_int, vp, ctypes.c_int]
     lib.gemm_f32_splitk_ex.restype = ctypes.c_int
+    lib.gemm_f32_splitk_noalloc.argtypes = gemm_args[:9] + [ctypes.c_int, vp]
+    lib.gemm_f32_splitk_noalloc.restype = ctypes.c_int
     lib.gemm_f32_splitk_auto_variant.argtypes = []
     lib.gemm_f32_splitk_auto_variant.restype = ctypes.c_int
     lib.gemm_f32_splitk_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, i32]
@@ -245,6 +249,10 @@ def gemm_f32_splitk_ex(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_byt
                        variant=VARIANT_AUTO) -> int:
     return library().gemm_f32_splitk_ex(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, splits, stream,
                                         variant)
+
+
+def gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, splits=0, stream=None) -> int:
+    return library().gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, splits, stream)
 
 
 def gemm_f32_splitk_auto_variant() -> int:

@@ -539,6 +539,67 @@ int run_splitk(const Args& a, void* workspace, int64_t workspace_bytes, int spli
                : GEMM_ERR_HIP;
 }
 
+// ---- split-K without allocation ----------------------------------------------------
+// gemm_f32_splitk_noalloc keeps the slices' partial products in a file-scope
+// device array instead of a caller's workspace: each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory; the device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is passed to kernels.  Every slice kernel stores its whole
+// M x N partial product (an empty slice stores zeros), so nothing needs
+// clearing between calls; calls that overlap on one GPU share the array and
+// race.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+struct ScratchSlot {
+    bool ready;
+    void* ptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchSlot& slot = g_scratch[dev];
+    if (!slot.ready) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GEMM_ERR_HIP;
+        slot.ptr = p;
+        slot.ready = true;
+    }
+    *out = slot.ptr;
+    return GEMM_OK;
+}
+
+// splits == 0: the split count of gemm_f32_splitk, lowered until the
+// partial products fit the array (down to 1, a plain launch).  An explicit
+// split count whose partial products do not fit is an error.
+int run_splitk_noalloc(const Args& a, int splits, hipStream_t stream) {
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_DIM;
+    int st = validate(a);
+    if (st != GEMM_OK) return st;
+    const bool work = a.M > 0 && a.N > 0 && a.K > 0;
+    if (work && splits > 1 && splitk_workspace_bytes(a.M, a.N, splits) > kScratchBytes) return GEMM_ERR_SCRATCH;
+    int max_lds = 0, num_cus = 0;
+    bool done = false;
+    st = prologue(a, stream, &max_lds, &num_cus, &done);
+    if (st != GEMM_OK || done) return st;
+    if (splits == 0) {
+        splits = splitk_auto_splits(a.M, a.N, a.K, num_cus);
+        while (splits > 1 && splitk_workspace_bytes(a.M, a.N, splits) > kScratchBytes) --splits;
+    }
+    void* ws = nullptr;
+    if (splits > 1) {
+        st = scratch_address(&ws);
+        if (st != GEMM_OK) return st;
+    }
+    return run_splitk(a, ws, splits > 1 ? kScratchBytes : 0, splits, stream, GEMM_VARIANT_AUTO);
+}
+
 // ---- 16-bit inputs, fp32 accumulation -----------------------------------------------
 // Tile shapes of the mixed-precision kernels (layouts from the host search,
 // mixed_shapes.def).  VEC 8: 16-byte loads and direct copies; VEC 1: 2-byte
@@ -788,6 +849,11 @@ int gemm_f32_splitk_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
                       variant);
 }
 
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                            int64_t ldb, float* C, int64_t ldc, int splits, void* stream) {
+    return run_splitk_noalloc(Args{M, N, K, A, lda, B, ldb, C, ldc}, splits, (hipStream_t)stream);
+}
+
 int gemm_f32_splitk_auto_variant(void) { return kSplitKVariant; }
 
 int gemm_mixed_f32(int input_type, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -834,6 +900,9 @@ const char* gemm_f32_status_string(int status) {
         case GEMM_ERR_HIP: return "HIP runtime error or launch failure";
         case GEMM_ERR_TOO_LARGE: return "problem too large for the kernel's index range";
         case GEMM_ERR_WORKSPACE: return "split-K workspace missing or smaller than gemm_f32_splitk_workspace_bytes";
+        case GEMM_ERR_SCRATCH:
+            return "split-K partial products (splits * M * N * 4 bytes) exceed the library's 64 MiB static scratch "
+                   "array";
         default: return "unknown status";
     }
 }

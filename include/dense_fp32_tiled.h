@@ -62,7 +62,8 @@ typedef enum {
                                    nothing half done */
     GEMM_ERR_HIP = -7,          /* a HIP runtime call or the launch failed */
     GEMM_ERR_TOO_LARGE = -8,    /* a size overflows the kernel's index range */
-    GEMM_ERR_WORKSPACE = -9     /* split-K workspace missing or too small */
+    GEMM_ERR_WORKSPACE = -9,    /* split-K workspace missing or too small */
+    GEMM_ERR_SCRATCH = -10      /* gemm_f32_splitk_noalloc: partial products exceed its static array */
 } gemm_status;
 
 /* Kernel variants.  Every variant computes the same operation; they differ in
@@ -203,6 +204,29 @@ int gemm_f32_splitk_ex(int64_t M, int64_t N, int64_t K,
                        const float *B, int64_t ldb,
                        float *C, int64_t ldc,
                        void *workspace, int64_t workspace_bytes, int splits, void *stream, int variant);
+
+/* Split-K for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * gemm_f32_splitk, with the partial products kept in a 64 MiB array that the
+ * library holds in device memory, one per GPU it runs on, until the process
+ * ends, instead of a caller's workspace.  Allocates nothing and calls no
+ * allocating routine; the array's device address is looked up on the first
+ * call on each device.
+ *   splits: 2..64 need splits * M * N * 4 <= 64 MiB, else GEMM_ERR_SCRATCH
+ *           (before anything is enqueued); 1 is a plain launch; 0 takes
+ *           gemm_f32_splitk_auto_splits, lowered until the partial products
+ *           fit (down to 1; on a 256-CU device the automatic count always
+ *           fits, its partial products stay near 32 MiB or below).
+ * The array keeps the last call's contents; nothing in it needs clearing
+ * (every slice writes its whole partial product).  Calls that overlap on one
+ * GPU (e.g. on two streams) share the array and race: serialise them.
+ * Other arguments, conventions and the result are gemm_f32_splitk's for the
+ * same split count. */
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            float *C, int64_t ldc,
+                            int splits, void *stream);
 
 /* The variant gemm_f32_splitk runs the slices with.  Pure host call. */
 int gemm_f32_splitk_auto_variant(void);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(gemm_lib):
 
 
 def test_status_strings(gemm_lib):
-    for st in range(-9, 1):
+    for st in range(-10, 1):
         s = dft.gemm_f32_status_string(st)
         assert s and s != "unknown status"
     assert dft.gemm_f32_status_string(12345) == "unknown status"
