@@ -208,8 +208,10 @@ def sweep(args, names: dict, mixed: bool) -> int:
 
         settle(lambda: step(variants[0]), torch, args.settle_ms)
         per_variant = {v: [] for v in variants}
-        for _ in range(args.sweep_reps):
-            for v in variants:
+        for rep in range(args.sweep_reps):
+            # rotate the order each round: a variant timed right after a slower
+            # one was seen to run a few percent faster (clock headroom)
+            for v in variants[rep % len(variants):] + variants[:rep % len(variants)]:
                 for _ in range(args.warmup):
                     step(v)
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -51,7 +51,8 @@ VARIANT_MFMA_64_BK32_DIRECT = 19
 VARIANT_MFMA_64_KS4 = 20
 VARIANT_MFMA_32x64_KS4 = 21
 VARIANT_MFMA_32x32_KS8 = 22
-VARIANT_COUNT = 23
+VARIANT_MFMA_64_BK32_PIPE = 23
+VARIANT_COUNT = 24
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -96,6 +97,7 @@ VARIANT_NAMES = {
     VARIANT_MFMA_64_KS4: "mfma_64_ks4",
     VARIANT_MFMA_32x64_KS4: "mfma_32x64_ks4",
     VARIANT_MFMA_32x32_KS8: "mfma_32x32_ks8",
+    VARIANT_MFMA_64_BK32_PIPE: "mfma_64_bk32_pipe",
 }
 
 # Every symbol the public header declares.

@@ -129,6 +129,11 @@ template <int VEC, int VEC_B = VEC>
 using Mfma64Bk32Direct = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
                                  layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
                                  VEC_B == VEC ? 0 : VEC_B>;
+// The 64x64x32 tile with the pipelined multiply.
+template <int VEC, int VEC_B = VEC>
+using Mfma64Bk32Pipe = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
+                               layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, true,
+                               VEC_B == VEC ? 0 : VEC_B>;
 // Bases of the K-split variants (KsplitCfg): 32x64 and 32x32 tiles of
 // 32x32-wave blocks, BK = 32.
 template <int VEC, int VEC_B = VEC>
@@ -195,7 +200,7 @@ gemm_tile_config mfma_config(int variant, int vec) {
     c.a_transposed = 0;
     c.mfma_block = Cfg::Op::MB;
     c.k_groups = Cfg::KSPLIT;
-    c.barriers_per_tile = Cfg::STAGES == 2 * Cfg::KSPLIT ? 1 : 2;  // per K tile of a group
+    c.barriers_per_tile = Cfg::STAGES == 1 ? 2 : 1;  // per K tile (of a group, with the K split)
     if (Cfg::PIPE) c.direct_to_lds = 2;
     return c;
 }
@@ -275,6 +280,7 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_64_KS4            */ ksplit_variant<Mfma64Ks4>(),
     /* MFMA_32x64_KS4         */ ksplit_variant<Mfma32x64Ks4>(),
     /* MFMA_32x32_KS8         */ ksplit_variant<Mfma32x32Ks8>(),
+    /* MFMA_64_BK32_PIPE      */ mfma_variant_per_operand<Mfma64Bk32Pipe>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate: its
@@ -300,12 +306,17 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         int64_t min_k;    // K-split variants: enough K tiles for every group (0: any K)
         int64_t min_k_one_round;  // the same when the grid has at most one tile per CU
     };
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     const Candidate candidates[] = {
         {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0, 0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0, 0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
          {144.0, 124.0, 130.0, 118.0}, false, 0, 0},
-        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
+        // 64x64x32: the pipelined multiply when the grid has more than one
+        // tile per CU (2-9 % ahead on multi-round grids), else the plain one
+        // (1-3 % ahead in a single round).
+        {t64 > num_cus ? GEMM_VARIANT_MFMA_64_BK32_PIPE : GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1,
+         {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
         // K split inside the workgroup: 16 K tiles of 32 per group at
         // least; when the split's grid has at most one tile per CU, from
         // K = 1024 for 64x64 tiles and K = 512 for the smaller ones (whose

@@ -141,6 +141,46 @@ __global__ __launch_bounds__(1024) void lds_probe_kernel(Pattern p, int reps, ui
     if (sink < -1.0f && never_written) never_written[threadIdx.x] = sink;
 }
 
+// Throughput of the direct global->LDS copy: every wave of every workgroup
+// issues reps x 16 copies of BYTES per lane (global_load_lds_dword or
+// _dwordx4) into its own LDS piece, waiting for all of them after each 16,
+// and reports the shader-clock cycles its loop took.  Lane l of wave w in
+// workgroup b reads src + off0 + (b * waves + w) * wave_stride
+// + (l / row_lanes) * ld_bytes + (l % row_lanes) * BYTES: a row-structured
+// piece as in a GEMM tile copy (row_lanes lanes per row, rows ld_bytes
+// apart).  The host checks that every byte read lies in the source buffer.
+template <int BYTES>
+__global__ __launch_bounds__(1024) void dma_probe_kernel(const char* src, uint32_t off0, uint32_t wave_stride,
+                                                         uint32_t ld_bytes, int row_lanes, int reps,
+                                                         uint64_t* cycles_out) {
+    __shared__ __attribute__((aligned(16))) float buf[16 * 64 * 4];  // 16 waves x 64 lanes x 16 bytes
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    typedef __attribute__((address_space(3))) float lds_float;
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)((uint32_t)(uintptr_t)((lds_float*)buf) + (uint32_t)(wave * 64 * BYTES)));
+    const uint32_t off = off0 + (uint32_t)(blockIdx.x * (blockDim.x / 64) + wave) * wave_stride +
+                         (uint32_t)(lane / row_lanes) * ld_bytes + (uint32_t)(lane % row_lanes) * BYTES;
+    const uint64_t t0 = clock64();
+    for (int r = 0; r < reps; ++r) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (BYTES == 16)
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                             :
+                             : "v"(off), "s"(src), "s"(lds)
+                             : "memory", "m0");
+            else
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                             :
+                             : "v"(off), "s"(src), "s"(lds)
+                             : "memory", "m0");
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    const uint64_t t1 = clock64();
+    if (lane == 0) cycles_out[blockIdx.x * (blockDim.x / 64) + wave] = t1 - t0;
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
                                                        int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
@@ -160,6 +200,33 @@ extern "C" int probe_xcc_ids(int32_t* out, int32_t blocks, int32_t threads, void
     void* args[] = {&out};
     return hipLaunchKernel(reinterpret_cast<const void*>(xcc_id_kernel), dim3((unsigned)blocks),
                            dim3((unsigned)threads), args, 0, (hipStream_t)stream) == hipSuccess
+               ? 0
+               : -2;
+}
+
+extern "C" int probe_dma_throughput(const void* src, int64_t src_bytes, int32_t bytes_per_lane, int32_t blocks,
+                                    int32_t waves, int32_t reps, int64_t off0, int64_t wave_stride, int64_t ld_bytes,
+                                    int32_t row_lanes, uint64_t* cycles_out, void* stream) {
+    if (src == nullptr || cycles_out == nullptr) return -1;
+    if (bytes_per_lane != 4 && bytes_per_lane != 16) return -1;
+    if (blocks < 1 || blocks > 4096 || waves < 1 || waves > 16 || reps < 1 || reps > 100000) return -1;
+    if (row_lanes < 1 || row_lanes > 64 || 64 % row_lanes != 0) return -1;
+    if (off0 < 0 || wave_stride < 0 || ld_bytes < 0) return -1;
+    if ((((uintptr_t)src + (uint64_t)off0) % (uint64_t)bytes_per_lane) != 0 || wave_stride % bytes_per_lane != 0 ||
+        ld_bytes % 4 != 0 || (bytes_per_lane == 16 && ld_bytes % 16 != 0))
+        return -1;
+    // the farthest byte any lane reads
+    const int64_t last = off0 + (int64_t)(blocks * waves - 1) * wave_stride + (int64_t)(64 / row_lanes - 1) * ld_bytes +
+                         (int64_t)row_lanes * bytes_per_lane;
+    if (last > src_bytes || last > 0x7fffffff) return -1;
+    const char* s = static_cast<const char*>(src);
+    uint32_t o = (uint32_t)off0, ws = (uint32_t)wave_stride, ld = (uint32_t)ld_bytes;
+    int rl = row_lanes, rp = reps;
+    void* args[] = {&s, &o, &ws, &ld, &rl, &rp, &cycles_out};
+    const void* kernel = bytes_per_lane == 16 ? reinterpret_cast<const void*>(dma_probe_kernel<16>)
+                                              : reinterpret_cast<const void*>(dma_probe_kernel<4>);
+    return hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), args, 0,
+                           (hipStream_t)stream) == hipSuccess
                ? 0
                : -2;
 }

@@ -45,7 +45,50 @@ def load():
     lib.probe_xcc_ids.restype = ctypes.c_int
     lib.probe_copy_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.probe_copy_f32.restype = ctypes.c_int
+    lib.probe_dma_throughput.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_dma_throughput.restype = ctypes.c_int
     return lib
+
+
+# Direct-copy pieces as the 64x64x32 fp32 kernel issues them: (label, bytes per
+# lane, lanes per row, row pitch in bytes, byte offset of the first row).
+DMA_CASES = [
+    ("16-byte, A tile rows (8 lanes per 128-byte row, pitch 2048 B)", 16, 8, 2048, 0),
+    ("4-byte, A tile rows (32 lanes per row, pitch 2048 B)", 4, 32, 2048, 0),
+    ("4-byte, A tile rows (32 lanes per row, pitch 2052 B, odd lda)", 4, 32, 2052, 4),
+    ("4-byte, B tile rows (64 lanes per row, pitch 3996 B, odd ldb)", 4, 64, 3996, 4),
+    ("16-byte, B tile rows (16 lanes per row, pitch 4096 B)", 16, 16, 4096, 0),
+]
+
+
+def dma_throughput(reps: int = 200, blocks: int = 256, waves_list=(1, 2, 4, 8, 16)):
+    """Copies per CU per 1000 cycles for each DMA_CASES piece and wave count
+    (one workgroup per CU: `blocks` no larger than the CU count)."""
+    import torch
+
+    lib = load()
+    src_bytes = 128 << 20
+    src = torch.zeros(src_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    rows = []
+    for label, width, row_lanes, ld, off0 in DMA_CASES:
+        for waves in waves_list:
+            # each wave reads its own 64 rows' worth of a window that stays in L2 and MALL
+            wave_stride = ((64 // row_lanes) * ld + 15) // 16 * 16
+            st = lib.probe_dma_throughput(src.data_ptr(), src_bytes, width, blocks, waves, reps, off0, wave_stride,
+                                          ld, row_lanes, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"probe_dma_throughput failed ({st}) for {label}, {waves} waves")
+            torch.cuda.synchronize()
+            cyc = out[:blocks * waves].cpu().tolist()
+            worst = max(cyc)
+            rows.append({"case": label, "bytes_per_lane": width, "waves": waves,
+                         "cycles_per_copy_per_wave": worst / (reps * 16),
+                         "copies_per_kcycle_per_cu": 1000.0 * waves * reps * 16 / worst,
+                         "bytes_per_cycle_per_cu": waves * reps * 16 * 64 * width / worst})
+    return rows
 
 
 def patterns():
@@ -227,7 +270,22 @@ def main(argv=None) -> int:
     ap.add_argument("--kernels", action="store_true",
                     help="also replay every LDS access pattern of the MFMA variants")
     ap.add_argument("--xcc", action="store_true", help="also report the XCD of each workgroup of a 512-block launch")
+    ap.add_argument("--dma", action="store_true",
+                    help="time the direct global->LDS copies instead (probe_dma_throughput, one workgroup per CU)")
     args = ap.parse_args(argv)
+    if args.dma:
+        rows = dma_throughput()
+        lines = ["# direct global->LDS copy throughput: 256 workgroups (one per CU), each wave 200 x 16 copies, "
+                 "waiting after each 16; worst wave",
+                 "case | waves | cycles/copy/wave | copies per 1000 cycles per CU | bytes/cycle/CU"]
+        for r in rows:
+            lines.append(f"{r['case']} | {r['waves']} | {r['cycles_per_copy_per_wave']:.1f} | "
+                         f"{r['copies_per_kcycle_per_cu']:.1f} | {r['bytes_per_cycle_per_cu']:.1f}")
+        text = "\n".join(lines)
+        print(text)
+        if args.out:
+            Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+        return 0
     import dense_fp32_tiled_amd as dft
 
     variants = (dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128_BK32) if args.kernels else ()

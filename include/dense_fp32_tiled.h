@@ -96,7 +96,8 @@ typedef enum {
                                          (partial sums added in LDS, in group order): deep K, few tiles */
     GEMM_VARIANT_MFMA_32x64_KS4 = 21, /* 32x64x32 tile, 4 groups of 2 waves */
     GEMM_VARIANT_MFMA_32x32_KS8 = 22, /* 32x32x32 tile, 8 groups of 1 wave */
-    GEMM_VARIANT_COUNT = 23
+    GEMM_VARIANT_MFMA_64_BK32_PIPE = 23, /* as MFMA_64_BK32_DIRECT with the pipelined multiply */
+    GEMM_VARIANT_COUNT = 24
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -262,8 +263,9 @@ const char *gemm_f32_status_string(int status);
  * `num_cus` compute units, both operands' rows 16-byte aligned: the
  * candidate with the highest rate estimate.  Candidates and full-chip rates:
  * MFMA_256x256_BK32_PIPE 145 TFLOP/s, MFMA_DIRECT (256x128) 144, the 128x128
- * direct variant (BK 32 when K >= 1024, else 16) 144, MFMA_64_BK32_DIRECT
- * 134; when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
+ * direct variant (BK 32 when K >= 1024, else 16) 144, the 64x64x32 kernel
+ * 134 (MFMA_64_BK32_PIPE when its grid has more than num_cus tiles, else
+ * MFMA_64_BK32_DIRECT); when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
  * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup; when the
  * split's grid has at most num_cus tiles, already from K >= 1024 for
  * MFMA_64_KS4 and K >= 512 for the other two).  Estimate:

@@ -53,6 +53,28 @@ int lds_probe_run(const int32_t *lane_words, int32_t width_words, int32_t waves,
 int probe_xcc_ids(int32_t *out, int32_t blocks, int32_t threads, void *stream);
 
 /*
+ * Throughput of the direct global->LDS copy (global_load_lds_dword for
+ * bytes_per_lane 4, _dwordx4 for 16), as the GEMM kernels use it to fill
+ * their LDS tiles: `blocks` workgroups of `waves` wavefronts; every wave
+ * issues reps x 16 copies into an LDS piece of its own, waiting for them
+ * after each 16, and writes the shader-clock cycles its loop took to
+ * cycles_out[block * waves + wave] (DEVICE buffer of blocks * waves uint64,
+ * owned by the caller).  Lane l of wave w of workgroup b reads
+ * src + off0 + (b * waves + w) * wave_stride + (l / row_lanes) * ld_bytes
+ * + (l % row_lanes) * bytes_per_lane: row_lanes lanes per row, rows ld_bytes
+ * apart, like the copy of one piece of a tile of a matrix with that pitch.
+ * src: DEVICE buffer of src_bytes bytes, owned by the caller; every byte read
+ * must lie inside it (checked), src + off0 aligned to bytes_per_lane,
+ * wave_stride a multiple of it, ld_bytes a multiple of 4 (16 for 16-byte
+ * copies).  blocks 1..4096, waves 1..16, reps 1..100000, row_lanes a
+ * divisor of 64.  Returns 0, -1 for invalid arguments (nothing is
+ * launched), -2 if the launch failed.  Asynchronous.
+ */
+int probe_dma_throughput(const void *src, int64_t src_bytes, int32_t bytes_per_lane, int32_t blocks,
+                         int32_t waves, int32_t reps, int64_t off0, int64_t wave_stride, int64_t ld_bytes,
+                         int32_t row_lanes, uint64_t *cycles_out, void *stream);
+
+/*
  * Reference kernel for calibrating the HBM traffic counters: dst[i] = src[i]
  * for i < n, 16-byte loads and stores, grid-stride.  It reads and writes
  * exactly 4*n bytes.  src and dst are DEVICE pointers owned by the caller,

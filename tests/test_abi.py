@@ -30,7 +30,8 @@ def exported(lib: Path) -> set[str]:
 def test_probe_library_exports_its_header(gemm_lib):
     from dense_fp32_tiled_amd import lds_probe
 
-    assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32", "probe_xcc_ids"}
+    assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32", "probe_xcc_ids",
+                                                "probe_dma_throughput"}
     assert declared_functions(PROBE_HEADER) <= exported(lds_probe.PROBE_LIB)
 
 
@@ -65,7 +66,7 @@ def test_tile_config_is_consistent(variant, gemm_lib):
     assert c["lds_bytes"] == c["stages"] * (c["a_stage_elems"] + c["b_stage_elems"]) * 4
     assert c["lds_bytes"] <= 160 * 1024
     assert c["k_groups"] >= 1
-    assert c["barriers_per_tile"] == (1 if c["stages"] == 2 * c["k_groups"] else 2)
+    assert c["barriers_per_tile"] == (2 if c["stages"] == 1 else 1)
     if c["a_transposed"]:
         assert (c["a_rows"], c["a_cols"]) == (c["bk"], c["bm"])
         assert c["mfma_block"] == 0
@@ -76,8 +77,9 @@ def test_tile_config_is_consistent(variant, gemm_lib):
     assert (c["b_rows"], c["b_cols"]) == (c["bk"], c["bn"])
     assert c["vec_width"] in (1, 4)
     assert (c["a_row_stride"] % 4 == 0) and (c["b_row_stride"] % 4 == 0)
-    if c["direct_to_lds"]:  # 16-byte copies into unpadded rows, two stages per group, matrix cores
-        assert c["vec_width"] == 4 and c["a_pad"] == 0 and c["b_pad"] == 0 and c["stages"] == 2 * c["k_groups"]
+    if c["direct_to_lds"]:  # 16-byte copies into unpadded rows, two or more stages per group, matrix cores
+        assert c["vec_width"] == 4 and c["a_pad"] == 0 and c["b_pad"] == 0
+        assert c["stages"] == 2 * c["k_groups"]
         assert c["mfma_block"] in (16, 32)
     for t in "ab":
         unit, mask = c[f"{t}_swz_unit"], c[f"{t}_swz_mask"]
@@ -129,19 +131,19 @@ def test_auto_variant_selection(gemm_lib):
     assert av(4096, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 512 tiles of 128x128: two per CU
     assert av(8192, 1024, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 256 tiles of 256x128: one per CU
     assert av(6144, 6144, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2304 tiles: 9 full rounds
-    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 1024 of 64x64 vs 256 of 128x128
-    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT         # 512 tiles of 64x64
+    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 1024 of 64x64 vs 256 of 128x128: 126 vs 121
+    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 108 (plain 64x64: 112)
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE   # 512 tiles of 64x64: 111 vs 109 plain
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4  # deep K, 128 tiles of 64x64: split K
     assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
-    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
     assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 240 tiles of 256x256
     assert av(6000, 6000, 6000, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2209 tiles in 9 rounds
     assert av(4095, 4095, 4095, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE
-    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT        # 6400 tiles: 25 full rounds
+    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 6400 tiles: 25 full rounds, 135
     # a dimension below the tile: every workgroup of the big kernels is an edge one
-    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
     assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_KS4  # many more CUs than big tiles
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
@@ -161,7 +163,7 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(512, 512, 16384, 256) == dft.VARIANT_MFMA_32x32_KS8    # 94 against 27
     assert av(256, 256, 65536, 256) == dft.VARIANT_MFMA_32x32_KS8
     # enough tiles, or too short a K: no split
-    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # split 56 against 59
@@ -174,8 +176,8 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
     assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
     assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # no smaller split in one round
-    assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT       # two rounds: split 41 against 52
-    assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE         # two rounds: split 44 against 51
+    assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE
     # a deep K still splits over several rounds of tiles
     assert av(768, 768, 8192, 256) == dft.VARIANT_MFMA_32x32_KS8         # 68 against 57
     # unaligned operands (odd K: A's rows; odd N: B's), measured per alignment class
@@ -199,7 +201,7 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(4095, 4095, 4095, 256, 0, 0) == dft.VARIANT_MFMA_256x256_BK32_PIPE
     assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
-    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_PIPE
     assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert ax(-1, 4, 4, 256, 1, 1) == dft.GEMM_ERR_INVALID_DIM
 

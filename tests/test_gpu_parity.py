@@ -29,7 +29,8 @@ ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIAN
                 dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT,
                 dft.VARIANT_MFMA_256x256_W4_DIRECT, dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
     dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT,
-    dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
+    dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8,
+    dft.VARIANT_MFMA_64_BK32_PIPE]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -200,7 +201,8 @@ def test_pitched_operands(pitch, variant, torch_gpu):
 DIRECT_VARIANTS = [dft.VARIANT_MFMA_DIRECT, dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
                    dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_256x256_DIRECT, dft.VARIANT_MFMA_256x256_W4_DIRECT,
                    dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
-    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT]
+    dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT,
+    dft.VARIANT_MFMA_64_BK32_PIPE]
 
 
 @pytest.mark.parametrize("variant", DIRECT_VARIANTS, ids=[dft.VARIANT_NAMES[v] for v in DIRECT_VARIANTS])
