@@ -7,7 +7,8 @@ One step is one C = A @ B call through the C ABI on operands already resident
 in device memory (4096 x 4096 x 4096, entries normal(0,1), seed 3, by default).
 Prints ONE JSON line with the whole-job TFLOP/s (wall clock over K steps
 bracketed by device synchronisation), the dominant kernel's roofline position
-(its average duration from HIP events on the launch stream) and the fp64 CPU
+(its average duration from two HIP events on the launch stream around the
+timed launches) and the fp64 CPU
 oracle timed on a bounded sample of the same workload on the host cores.
 
 Before the W warmup steps the step is repeated for --settle-ms of wall time
@@ -21,7 +22,8 @@ without it a short timed region measures the ramp, not the kernel.
 
 instead times each listed variant on each shape (operands uniform[-1,1),
 packed leading dimensions), interleaved over --sweep-reps rounds, and writes
-one JSON line per shape and variant (median kernel TFLOP/s by HIP events).
+one JSON line per shape and variant (median over the rounds of the kernel
+TFLOP/s, from two HIP events around --steps back-to-back launches).
 """
 
 from __future__ import annotations
@@ -168,8 +170,9 @@ def parse_args(argv=None):
 
 def sweep(args, names: dict, mixed: bool) -> int:
     """Kernel TFLOP/s of several variants on several shapes, interleaved:
-    each of --sweep-reps rounds times every variant once (--steps launches
-    by HIP events after --warmup), and each line reports the median round."""
+    each of --sweep-reps rounds times every variant once (--steps
+    back-to-back launches between two HIP events, after --warmup), and each
+    line reports the median round."""
     import numpy as np
     import torch
 
@@ -214,14 +217,13 @@ def sweep(args, names: dict, mixed: bool) -> int:
             for v in variants[rep % len(variants):] + variants[:rep % len(variants)]:
                 for _ in range(args.warmup):
                     step(v)
-                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(args.steps)]
-                for e0, e1 in ev:
-                    e0.record(stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.steps):
                     step(v)
-                    e1.record(stream)
+                e1.record(stream)
                 torch.cuda.synchronize()
-                avg = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev) / 1e3
+                avg = e0.elapsed_time(e1) / args.steps / 1e3
                 per_variant[v].append(2.0 * M * N * K / avg / 1e12)
         for v in variants:
             rates = sorted(per_variant[v])
@@ -300,15 +302,25 @@ def main(argv=None) -> int:
             raise dft.GemmError(st, "gemm")
 
     def time_variant(v, steps, warmup):
+        """(wall seconds per step, kernel seconds per launch, median and min
+        of single launches).  The timed region is bracketed by device
+        synchronisation for the wall clock and by two HIP events on the launch
+        stream for the kernel time: the launches run back to back, so the
+        events' span over `steps` is the kernels' own time (a pair of events
+        around each launch adds a few microseconds to a short kernel; those
+        single-launch figures are taken afterwards, for the median and min)."""
         for _ in range(warmup):
             step(v)
         torch.cuda.synchronize()
+        span0, span1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        span0.record(stream)
         for _ in range(steps):
             step(v)
+        span1.record(stream)
         torch.cuda.synchronize()
         wall_s = (time.perf_counter() - t0) / steps
-        # per-launch durations from HIP events recorded on the launch stream
+        kernel_s = span0.elapsed_time(span1) / 1e3 / steps
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for e0, e1 in ev:
             e0.record(stream)
@@ -316,7 +328,7 @@ def main(argv=None) -> int:
             e1.record(stream)
         torch.cuda.synchronize()
         durs = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in ev)
-        return wall_s, sum(durs) / len(durs), durs[len(durs) // 2], durs[0]
+        return wall_s, kernel_s, durs[len(durs) // 2], durs[0]
 
     settled = settle(step, torch, args.settle_ms)
     props = torch.cuda.get_device_properties(dev)
