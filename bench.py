@@ -41,6 +41,12 @@ if str(ROOT) not in sys.path:
 
 PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and packed vector): 256 CUs x 256 flop/clk x 2.4 GHz
 PEAK_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak (no sparsity)
+# The vector-ALU kernel's ceiling: the library is built without packed fp32, so
+# it runs one-product v_fmac_f32; the probe (lds_probe --valu) and its
+# SQ_INSTS_VALU / GRBM_GUI_ACTIVE counters measure 0.42 of them per cycle per
+# SIMD with two or more waves alternating: 0.42 x 64 lanes x 2 flop x 1024
+# SIMDs x 2.4 GHz.
+PEAK_VALU_FMA_TFLOPS = 132.1
 METRIC = "fp32 GEMM TFLOP/s at 4096³ on 1 MI355X; % of fp32 peak"
 METRIC_16BIT = "{t}-input GEMM (fp32 accumulate) TFLOP/s on 1 MI355X; % of dense {t} peak"
 KERNEL_SOURCES = ["gemm_kernels.hpp", "gemm_api.hip", "gemm_default.hip", "default_config.hpp", "launch.hpp",
@@ -373,7 +379,7 @@ def main(argv=None) -> int:
             resolved = variant
         tile = dft.gemm_f32_tile_config(resolved)
         run_name = dft.VARIANT_NAMES[resolved] + (f"+splitk{splits_used}" if args.splits >= 0 else "")
-    peak = PEAK_16BIT_TFLOPS if mixed else PEAK_FP32_TFLOPS
+    peak = PEAK_16BIT_TFLOPS if mixed else PEAK_FP32_TFLOPS if tile["mfma_block"] else PEAK_VALU_FMA_TFLOPS
 
     # correctness spot check and CPU baseline: the oracle on a bounded row sample
     cpu_baseline = None

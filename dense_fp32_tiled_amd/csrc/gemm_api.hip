@@ -160,12 +160,9 @@ template <int VEC>
 using Mfma128Bk32 = std::conditional_t<VEC == 4, MfmaAt<layouts::m32_128x128x32_v4, 2, 4, 128, 128, 32, 32>,
                                        MfmaAt<layouts::m32_128x128x16_v1, 2, 1, 128, 128, 16, 32>>;
 
-constexpr ValuShape kValuShape{128, 128, 16, 16, 256, 4};
-constexpr int kValuPadA = valu_pad_a(kValuShape, kGfx950Lds);
-constexpr int kValuPadB = valu_pad_b(kValuShape, kGfx950Lds);
-
+// LDS layouts of the vector-ALU kernel from the host layout search.
 template <int VEC>
-using ValuT = ValuCfg<128, 128, 16, 8, 8, 2, kValuPadA, kValuPadB, VEC>;
+using ValuT = ValuCfg<128, 128, 16, 8, 8, 2, layouts::valu_128x128x16::A, layouts::valu_128x128x16::B, VEC>;
 
 template <class Cfg>
 void describe_common(gemm_tile_config& c, int variant, int vec) {

@@ -1039,17 +1039,17 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
 // read neighbouring 16-byte LDS words.  A is stored k-major in LDS (At[k][m]),
 // B row-major (B[k][n]); per k each thread reads TM + TN values with 16-byte
 // loads and issues TM * TN FMAs.
-template <int BM_, int BN_, int BK_, int TM_, int TN_, int STAGES_, int PADA_, int PADB_, int VEC_>
+template <int BM_, int BN_, int BK_, int TM_, int TN_, int STAGES_, class LayA, class LayB, int VEC_>
 struct ValuCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, TM = TM_, TN = TN_;
-    static constexpr int STAGES = STAGES_, PADA = PADA_, PADB = PADB_, VEC = VEC_;
+    static constexpr int STAGES = STAGES_, VEC = VEC_;
     static constexpr int THREADS_M = BM / TM, THREADS_N = BN / TN;
     static constexpr int THREADS = THREADS_M * THREADS_N;
     static constexpr int MIN_WAVES = 2;
     static constexpr int ORDER = kRowMajorOrder;
     static constexpr int LOAD = kLoadRegisters;
-    using TileA = LdsTile<BK, BM, PADA, STAGES>;  // k-major
-    using TileB = LdsTile<BK, BN, PADB, STAGES>;
+    using TileA = LdsTile<BK, BM, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;  // k-major
+    using TileB = LdsTile<BK, BN, LayB::pad, STAGES, LayB::unit, LayB::shift, LayB::mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
     static_assert(TM == 8 && TN == 8, "register tile is two 4-wide halves per axis");
     static_assert(TileA::row_stride % 4 == 0 && TileB::row_stride % 4 == 0, "16-byte LDS reads");

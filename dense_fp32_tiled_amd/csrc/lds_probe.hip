@@ -181,6 +181,32 @@ __global__ __launch_bounds__(1024) void dma_probe_kernel(const char* src, uint32
     if (lane == 0) cycles_out[blockIdx.x * (blockDim.x / 64) + wave] = t1 - t0;
 }
 
+// Throughput of the vector ALU's fp32 FMA (v_fmac_f32, one product per lane,
+// no packed forms): every lane runs reps x 64 FMAs over 8 independent
+// accumulators, with no memory access in the loop, and each wave reports
+// the shader-clock cycles its loop took.  The accumulators are stored only
+// under a condition that the data never meets, so the FMAs stay live.
+__global__ __launch_bounds__(1024) void valu_fma_probe_kernel(int reps, float x, float y, uint64_t* cycles_out,
+                                                              float* never_written) {
+    float a0 = (float)threadIdx.x, a1 = a0 + 1.0f, a2 = a0 + 2.0f, a3 = a0 + 3.0f;
+    float a4 = a0 + 4.0f, a5 = a0 + 5.0f, a6 = a0 + 6.0f, a7 = a0 + 7.0f;
+    const uint64_t t0 = clock64();
+    for (int r = 0; r < reps; ++r) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            asm volatile(
+                "v_fmac_f32 %0, %8, %9\n\tv_fmac_f32 %1, %8, %9\n\tv_fmac_f32 %2, %8, %9\n\t"
+                "v_fmac_f32 %3, %8, %9\n\tv_fmac_f32 %4, %8, %9\n\tv_fmac_f32 %5, %8, %9\n\t"
+                "v_fmac_f32 %6, %8, %9\n\tv_fmac_f32 %7, %8, %9"
+                : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7)
+                : "v"(x), "v"(y));
+    }
+    const uint64_t t1 = clock64();
+    if (threadIdx.x % 64 == 0) cycles_out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = t1 - t0;
+    const float sum = a0 + a1 + a2 + a3 + a4 + a5 + a6 + a7;
+    if (sum != sum && never_written) never_written[blockIdx.x * blockDim.x + threadIdx.x] = sum;  // NaN only
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
                                                        int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
@@ -227,6 +253,20 @@ extern "C" int probe_dma_throughput(const void* src, int64_t src_bytes, int32_t 
                                               : reinterpret_cast<const void*>(dma_probe_kernel<4>);
     return hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), args, 0,
                            (hipStream_t)stream) == hipSuccess
+               ? 0
+               : -2;
+}
+
+extern "C" int probe_valu_fma(int32_t blocks, int32_t waves, int32_t reps, uint64_t* cycles_out, void* stream) {
+    if (cycles_out == nullptr || blocks < 1 || blocks > 4096 || waves < 1 || waves > 16 || reps < 1 ||
+        reps > 1000000)
+        return -1;
+    int rp = reps;
+    float x = 0.5f, y = 0.25f;  // finite accumulators: the store below never happens
+    float* never_written = nullptr;
+    void* args[] = {&rp, &x, &y, &cycles_out, &never_written};
+    return hipLaunchKernel(reinterpret_cast<const void*>(valu_fma_probe_kernel), dim3((unsigned)blocks),
+                           dim3((unsigned)(64 * waves)), args, 0, (hipStream_t)stream) == hipSuccess
                ? 0
                : -2;
 }

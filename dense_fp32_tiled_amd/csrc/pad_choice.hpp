@@ -269,56 +269,62 @@ constexpr LayoutChoice mixed_layout_b(Mixed16Shape s, LdsGeometry g) {
     return choose_layout([=](LayoutChoice c) { return mixed_b_cost(s, c, g); }, s.bn / 2, false);
 }
 
-// ---- vector-ALU kernel: A k-major [BK][BM+pad], B row-major [BK][BN+pad] ----
+// ---- vector-ALU kernel: A k-major [BK][BM], B row-major [BK][BN] ----
+// Thread t (of `threads`) owns rows (t / threads_n) * 4 (+ BM / 2) and columns
+// (t % threads_n) * 4 (+ BN / 2) of the output tile.  Per k it reads 4 + 4
+// consecutive words of row k of At and of B (16-byte reads); the tiles are
+// stored by the cooperative copy: B row-major with `vec`-wide stores, A
+// transposed with one 4-byte store per element.  Every wavefront's accesses
+// are costed (the swizzle makes them differ by wavefront).
 struct ValuShape {
     int bm, bn, bk, threads_n, threads, vec;
+    constexpr int waves() const { return threads / kWaveLanes; }
 };
 
-// At read (16-byte): lane l of wave 0 reads At[k][(l/threads_n)*4].
-constexpr int valu_a_read_degree(ValuShape s, int pad, LdsGeometry g) {
-    (void)pad;
-    return conflict_degree([=](int l) { return (int64_t)(l / s.threads_n) * 4; }, kWaveLanes, 4,
-                           g.banks_for_width(4), g.group_for_width(4));
-}
-// Transposed store of A: slot l holds A[l/(BK/vec)][vec*(l%(BK/vec)) + e]; element e goes to
-// At[vec*(l%(BK/vec)) + e][l/(BK/vec)] with a 4-byte store.
-constexpr int valu_a_write_degree(ValuShape s, int pad, LdsGeometry g) {
-    const int stride = s.bm + pad, vcols = s.bk / s.vec;
-    return conflict_degree([=](int l) { return (int64_t)(s.vec * (l % vcols)) * stride + l / vcols; },
-                           kWaveLanes, 1, g.banks_for_width(1), g.group_for_width(1));
-}
-constexpr int valu_b_read_degree(ValuShape s, int pad, LdsGeometry g) {
-    (void)pad;
-    return conflict_degree([=](int l) { return (int64_t)(l % s.threads_n) * 4; }, kWaveLanes, 4,
-                           g.banks_for_width(4), g.group_for_width(4));
-}
-constexpr int valu_b_write_degree(ValuShape s, int pad, LdsGeometry g) {
-    const int stride = s.bn + pad, vcols = s.bn / s.vec;
-    return conflict_degree([=](int l) { return (int64_t)(l / vcols) * stride + s.vec * (l % vcols); },
-                           kWaveLanes, s.vec, g.banks_for_width(s.vec), g.group_for_width(s.vec));
-}
-
-template <class Cost>
-constexpr int argmin_pad(Cost cost) {
-    int best_pad = 0, best = cost(0);
-    for (int pad = 4; pad <= kMaxPad; pad += 4) {
-        const int c = cost(pad);
-        if (c < best) { best = c; best_pad = pad; }
+constexpr int valu_a_cost(ValuShape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    const int vcols = s.bk / s.vec;
+    for (int w = 0; w < s.waves(); ++w) {
+        for (int k = 0; k < s.bk; ++k)
+            for (int half = 0; half < 2; ++half)
+                total += pattern_cost(c, s.bm, 4, g, [=](int l, int& row, int& col) {
+                    row = k;
+                    col = half * (s.bm / 2) + ((w * kWaveLanes + l) / s.threads_n) * 4;
+                });
+        for (int i = 0; i < s.bm * vcols / s.threads; ++i)
+            for (int e = 0; e < s.vec; ++e)
+                total += pattern_cost(c, s.bm, 1, g, [=](int l, int& row, int& col) {
+                    const int slot = w * kWaveLanes + l + i * s.threads;
+                    row = s.vec * (slot % vcols) + e;
+                    col = slot / vcols;
+                });
     }
-    return best_pad;
+    return total;
 }
-
-constexpr int valu_pad_a(ValuShape s, LdsGeometry g) {
-    return argmin_pad([=](int pad) {
-        return 2 * s.bk * access_cost(valu_a_read_degree(s, pad, g), 4, g) +
-               (s.bm * s.bk / s.threads) * access_cost(valu_a_write_degree(s, pad, g), 1, g);
-    });
+constexpr int valu_b_cost(ValuShape s, LayoutChoice c, LdsGeometry g) {
+    int total = 0;
+    const int vcols = s.bn / s.vec;
+    for (int w = 0; w < s.waves(); ++w) {
+        for (int k = 0; k < s.bk; ++k)
+            for (int half = 0; half < 2; ++half)
+                total += pattern_cost(c, s.bn, 4, g, [=](int l, int& row, int& col) {
+                    row = k;
+                    col = half * (s.bn / 2) + ((w * kWaveLanes + l) % s.threads_n) * 4;
+                });
+        for (int i = 0; i < s.bk * vcols / s.threads; ++i)
+            total += pattern_cost(c, s.bn, s.vec, g, [=](int l, int& row, int& col) {
+                const int slot = w * kWaveLanes + l + i * s.threads;
+                row = slot / vcols;
+                col = s.vec * (slot % vcols);
+            });
+    }
+    return total;
 }
-constexpr int valu_pad_b(ValuShape s, LdsGeometry g) {
-    return argmin_pad([=](int pad) {
-        return 2 * s.bk * access_cost(valu_b_read_degree(s, pad, g), 4, g) +
-               (s.bk * s.bn / (s.vec * s.threads)) * access_cost(valu_b_write_degree(s, pad, g), s.vec, g);
-    });
+constexpr LayoutChoice valu_layout_a(ValuShape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return valu_a_cost(s, c, g); }, s.bm);
+}
+constexpr LayoutChoice valu_layout_b(ValuShape s, LdsGeometry g) {
+    return choose_layout([=](LayoutChoice c) { return valu_b_cost(s, c, g); }, s.bn);
 }
 
 }  // namespace dft

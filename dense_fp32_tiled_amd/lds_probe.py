@@ -49,7 +49,30 @@ def load():
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_dma_throughput.restype = ctypes.c_int
+    lib.probe_valu_fma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_valu_fma.restype = ctypes.c_int
     return lib
+
+
+def valu_fma_throughput(reps: int = 20000, blocks: int = 256, waves_list=(4, 8, 16)):
+    """v_fmac_f32 instructions per cycle per SIMD (one workgroup per CU, its
+    waves spread over the CU's 4 SIMDs) and the fp32 rate that implies at
+    2.4 GHz on 256 CUs."""
+    import torch
+
+    lib = load()
+    out = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    rows = []
+    for waves in waves_list:
+        st = lib.probe_valu_fma(blocks, waves, reps, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"probe_valu_fma failed ({st}), {waves} waves")
+        torch.cuda.synchronize()
+        worst = max(out[:blocks * waves].cpu().tolist())
+        ipc = (waves / 4) * reps * 64 / worst  # per SIMD
+        rows.append({"waves_per_cu": waves, "cycles": worst, "fma_instr_per_cycle_per_simd": ipc,
+                     "cycles_per_fma_instr": 1.0 / ipc, "tflops_at_2400mhz_256cu": ipc * 64 * 2 * 1024 * 2.4e9 / 1e12})
+    return rows
 
 
 # Direct-copy pieces as the 64x64x32 fp32 kernel issues them: (label, bytes per
@@ -272,7 +295,23 @@ def main(argv=None) -> int:
     ap.add_argument("--xcc", action="store_true", help="also report the XCD of each workgroup of a 512-block launch")
     ap.add_argument("--dma", action="store_true",
                     help="time the direct global->LDS copies instead (probe_dma_throughput, one workgroup per CU)")
+    ap.add_argument("--valu", action="store_true",
+                    help="time the vector ALU's v_fmac_f32 instead (probe_valu_fma, one workgroup per CU)")
     args = ap.parse_args(argv)
+    if args.valu:
+        rows = valu_fma_throughput()
+        lines = ["# v_fmac_f32 throughput: 256 workgroups (one per CU), each lane 20000 x 64 FMAs on 8 independent "
+                 "accumulators; worst wave",
+                 "waves per CU | cycles | FMA instructions per cycle per SIMD | cycles per instruction | "
+                 "fp32 TFLOP/s at 2.4 GHz, 256 CUs"]
+        for r in rows:
+            lines.append(f"{r['waves_per_cu']} | {r['cycles']} | {r['fma_instr_per_cycle_per_simd']:.3f} | "
+                         f"{r['cycles_per_fma_instr']:.2f} | {r['tflops_at_2400mhz_256cu']:.1f}")
+        text = "\n".join(lines)
+        print(text)
+        if args.out:
+            Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+        return 0
     if args.dma:
         rows = dma_throughput()
         lines = ["# direct global->LDS copy throughput: 256 workgroups (one per CU), each wave 200 x 16 copies, "

@@ -75,6 +75,18 @@ int probe_dma_throughput(const void *src, int64_t src_bytes, int32_t bytes_per_l
                          int32_t row_lanes, uint64_t *cycles_out, void *stream);
 
 /*
+ * Throughput of the vector ALU's fp32 fused multiply-add in its one-product
+ * form (v_fmac_f32; the library is built without packed fp32): `blocks`
+ * workgroups of `waves` wavefronts; every lane runs reps x 64 FMAs over 8
+ * independent accumulators with no memory access, and each wave writes the
+ * shader-clock cycles of its loop to cycles_out[block * waves + wave]
+ * (DEVICE buffer of blocks * waves uint64, owned by the caller).  blocks
+ * 1..4096, waves 1..16, reps 1..1000000.  Returns 0, -1 for invalid
+ * arguments (nothing is launched), -2 if the launch failed.  Asynchronous.
+ */
+int probe_valu_fma(int32_t blocks, int32_t waves, int32_t reps, uint64_t *cycles_out, void *stream);
+
+/*
  * Reference kernel for calibrating the HBM traffic counters: dst[i] = src[i]
  * for i < n, 16-byte loads and stores, grid-stride.  It reads and writes
  * exactly 4*n bytes.  src and dst are DEVICE pointers owned by the caller,
