@@ -2,10 +2,12 @@
 
     python -m dense_fp32_tiled_amd.build
 
-first runs the host LDS layout search (csrc/layout_gen.cpp -> 
+first runs the host LDS layout search (csrc/layout_gen.cpp ->
 csrc/generated/mfma_layouts.hpp), then produces
-dense_fp32_tiled_amd/libdense_fp32_tiled.so from csrc/gemm_api.hip and the
-LDS bank-geometry probe liblds_probe.so from csrc/lds_probe.hip.
+dense_fp32_tiled_amd/libdense_fp32_tiled.so from csrc/gemm_api.hip and
+csrc/gemm_default.hip, the same library built with DFT_LDS_POISON=1
+(libdense_fp32_tiled_poison.so, for the LDS-poison parity tests), and the
+measurement probes liblds_probe.so from csrc/lds_probe.hip.
 Packed fp32 VALU instructions are disabled for all device code
 (-packed-fp32-ops); hipcc's host pass warns that it does not know that
 feature, which is harmless.
@@ -22,6 +24,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libdense_fp32_tiled.so"
+POISON_LIB = PKG / "libdense_fp32_tiled_poison.so"
 SOURCES = [CSRC / "gemm_api.hip", CSRC / "gemm_default.hip"]
 PROBE_LIB = PKG / "liblds_probe.so"
 PROBE_SOURCES = [CSRC / "lds_probe.hip"]
@@ -69,22 +72,37 @@ def generate_layouts() -> Path:
     return LAYOUT_HEADER
 
 
-def build(out: Path = LIB, extra: list[str] | None = None, sources: list[Path] | None = None) -> Path:
-    """Compile the library (always recompiles)."""
+def _start(out: Path, extra: list[str] | None, sources: list[Path] | None):
     tmp = out.with_name(f"{out.name}.{os.getpid()}.tmp")
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{ROOT / 'include'}", f"-I{CSRC}",
            *[str(s) for s in (sources or SOURCES)], "-o", str(tmp)]
-    proc = subprocess.run(cmd, capture_output=True, text=True)
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    return proc, tmp, out, cmd
+
+
+def _finish(job) -> Path:
+    proc, tmp, out, cmd = job
+    _, err = proc.communicate()
     if proc.returncode != 0:
-        sys.stderr.write(proc.stderr)
+        sys.stderr.write(err)
         raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd)}")
     os.replace(tmp, out)
     return out
 
 
+def build(out: Path = LIB, extra: list[str] | None = None, sources: list[Path] | None = None) -> Path:
+    """Compile the library (always recompiles)."""
+    return _finish(_start(out, extra, sources))
+
+
 def build_all() -> list[Path]:
+    """The library, its LDS-poison debug build (every kernel fills its LDS
+    with NaN before the first copy: DFT_LDS_POISON=1) and the probe library,
+    compiled concurrently."""
     generate_layouts()
-    return [build(LIB, sources=SOURCES), build(PROBE_LIB, sources=PROBE_SOURCES)]
+    jobs = [_start(LIB, None, SOURCES), _start(POISON_LIB, ["-DDFT_LDS_POISON=1"], SOURCES),
+            _start(PROBE_LIB, None, PROBE_SOURCES)]
+    return [_finish(j) for j in jobs]
 
 
 def device_assembly(source: Path | None = None) -> str:

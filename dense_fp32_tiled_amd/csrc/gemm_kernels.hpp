@@ -31,7 +31,28 @@
 
 #include "lds_layout.hpp"
 
+// Debug build (DFT_LDS_POISON=1): every kernel fills its LDS with a NaN
+// pattern before its first copy, so that a read of a word that no copy or
+// store of the tile wrote puts a NaN into the result instead of stale data.
+// Every consumed LDS word must hold a defined value ("My Triton From Scratch,
+// Part 14: Shared-Memory Tiles", section "Zero-filled boundary tiles"); the
+// parity tests run once against a library built this way.
+#ifndef DFT_LDS_POISON
+#define DFT_LDS_POISON 0
+#endif
+
 namespace dft {
+
+// Fill `words` 4-byte LDS words from `lds` with a quiet NaN and wait for the
+// whole workgroup (no-op unless DFT_LDS_POISON).
+__device__ inline void poison_lds(void* lds, int words) {
+    if constexpr (DFT_LDS_POISON) {
+        uint32_t* w = static_cast<uint32_t*>(lds);
+        // a NaN as fp32, and in both halves as bf16 or fp16
+        for (int i = threadIdx.x; i < words; i += blockDim.x) w[i] = 0x7FC07FC0u;
+        __syncthreads();
+    }
+}
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -584,6 +605,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
 
     __shared__ __attribute__((aligned(16))) float lds_a[TileA::total_elems];
     __shared__ __attribute__((aligned(16))) float lds_b[TileB::total_elems];
+    poison_lds(lds_a, TileA::total_elems);
+    poison_lds(lds_b, TileB::total_elems);
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -912,6 +935,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
 
     // One array: A's stages, then B's; the partial sums reuse all of it.
     __shared__ __attribute__((aligned(16))) float lds[TileA::total_elems + TileB::total_elems];
+    poison_lds(lds, TileA::total_elems + TileB::total_elems);
     float* const lds_a = lds;
     float* const lds_b = lds + TileA::total_elems;
 
@@ -1071,6 +1095,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_valu_kernel
 
     __shared__ __attribute__((aligned(16))) float lds_a[TileA::total_elems];
     __shared__ __attribute__((aligned(16))) float lds_b[TileB::total_elems];
+    poison_lds(lds_a, TileA::total_elems);
+    poison_lds(lds_b, TileB::total_elems);
 
     const int tid = threadIdx.x;
     const int ty = tid / Cfg::THREADS_N, tx = tid % Cfg::THREADS_N;

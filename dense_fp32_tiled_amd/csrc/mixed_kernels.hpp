@@ -271,6 +271,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 
     __shared__ __attribute__((aligned(16))) uint32_t lds_a[TileA::total_elems];
     __shared__ __attribute__((aligned(16))) uint32_t lds_b[TileB::total_elems];
+    poison_lds(lds_a, TileA::total_elems);
+    poison_lds(lds_b, TileB::total_elems);
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -572,6 +574,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kspli
 
     // One array: A's stages, then B's; the partial sums reuse all of it.
     __shared__ __attribute__((aligned(16))) uint32_t lds[TileA::total_elems + TileB::total_elems];
+    poison_lds(lds, TileA::total_elems + TileB::total_elems);
     uint32_t* const lds_a = lds;
     uint32_t* const lds_b = lds + TileA::total_elems;
 

@@ -25,6 +25,6 @@ def gemm_lib():
     """The HIP library (built in-tree if it is not there yet)."""
     import dense_fp32_tiled_amd as dft
     from dense_fp32_tiled_amd import build, lds_probe
-    if not dft.LIB_PATH.exists() or not lds_probe.PROBE_LIB.exists():
+    if not all(p.exists() for p in (dft.LIB_PATH, build.POISON_LIB, lds_probe.PROBE_LIB)):
         build.build_all()
     return dft.library()

@@ -46,6 +46,14 @@ def test_library_exports_every_declared_symbol(gemm_lib):
         assert hasattr(gemm_lib, name)
 
 
+def test_poison_build_exports_every_declared_symbol(gemm_lib):
+    """The LDS-poison debug build is the same library: same entry points."""
+    from dense_fp32_tiled_amd import build
+
+    missing = declared_functions() - exported(build.POISON_LIB)
+    assert not missing, f"declared but not exported by the poison build: {missing}"
+
+
 def test_status_strings(gemm_lib):
     for st in range(-10, 1):
         s = dft.gemm_f32_status_string(st)
