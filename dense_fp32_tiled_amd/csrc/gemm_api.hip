@@ -610,8 +610,9 @@ int run_splitk_noalloc(const Args& a, int splits, hipStream_t stream) {
 
 // ---- 16-bit inputs, fp32 accumulation -----------------------------------------------
 // Tile shapes of the mixed-precision kernels (layouts from the host search,
-// mixed_shapes.def).  VEC 8: 16-byte loads and direct copies; VEC 1: 2-byte
-// loads through registers, for unaligned operands.
+// mixed_shapes.def).  VEC 8: 16-byte direct copies; VEC 2: 4-byte direct
+// copies; VEC 1: shifted 16-byte loads through registers, for rows only
+// 2-byte aligned.
 template <int TYPE, int VEC>
 using Mixed256x128 = MixedCfg<TYPE, 256, 128, 32, 64, 64, 32, layouts::x32_256x128x32::A, layouts::x32_256x128x32::B,
                               VEC, 4, 2, kPipeNone>;
@@ -678,39 +679,41 @@ gemm_tile_config mixed_config(int variant, int vec) {
 
 using MixedLaunchFn = hipError_t (*)(const Args&, hipStream_t);
 struct MixedVariant {
-    MixedLaunchFn vec8[2], vec2[2], scalar[2];  // by input type: 16-byte, 4-byte copies; 2-byte loads
+    MixedLaunchFn vec8[2], vec2[2], scalar[2];  // by input type: 16-byte, 4-byte copies; registers
     gemm_tile_config (*config)(int variant, int vec);
     int lds_bytes;
 };
 
 // Operands whose rows are 4-byte aligned (even leading dimensions) run the
-// variant's own kernel with 4-byte copies.  Others run the 256x128x32
-// kernel with 2-byte loads: it is the only shape whose register-path kernel
-// fits its registers without spilling (one staged element per register).
-template <template <int, int> class Shape>
+// variant's own kernel with 4-byte copies.  Rows only 2-byte aligned run
+// `Unaligned` with VEC 1: raw 4-byte copies realigned in LDS where its
+// tiles leave room for them (the 256x256x32 kernel for every 256x256
+// variant: the three-stage and BK = 64 ones have none), else shifted 16-byte
+// loads through registers; K-split variants use their base shape.
+template <template <int, int> class Shape, template <int, int> class Unaligned = Shape>
 MixedVariant mixed_variant() {
     return MixedVariant{{launch_mixed<Shape<kInputBf16, 8>>, launch_mixed<Shape<kInputF16, 8>>},
                         {launch_mixed<Shape<kInputBf16, 2>>, launch_mixed<Shape<kInputF16, 2>>},
-                        {launch_mixed<Mixed256x128<kInputBf16, 1>>, launch_mixed<Mixed256x128<kInputF16, 1>>},
+                        {launch_mixed<Unaligned<kInputBf16, 1>>, launch_mixed<Unaligned<kInputF16, 1>>},
                         mixed_config<Shape<kInputBf16, 8>>,
-                        Shape<kInputBf16, 8>::LDS_BYTES > Mixed256x128<kInputBf16, 1>::LDS_BYTES
+                        Shape<kInputBf16, 8>::LDS_BYTES > Unaligned<kInputBf16, 1>::LDS_BYTES
                             ? Shape<kInputBf16, 8>::LDS_BYTES
-                            : Mixed256x128<kInputBf16, 1>::LDS_BYTES};
+                            : Unaligned<kInputBf16, 1>::LDS_BYTES};
 }
 
 // Index = gemm_mixed_variant; AUTO's entry describes the large-problem choice.
 const MixedVariant kMixedVariants[GEMM_MIXED_COUNT] = {
-    /* AUTO           */ mixed_variant<Mixed256x256Bk64>(),
+    /* AUTO           */ mixed_variant<Mixed256x256Bk64, Mixed256x256>(),
     /* 256x128        */ mixed_variant<Mixed256x128>(),
     /* 256x256        */ mixed_variant<Mixed256x256>(),
     /* 256x128_BK64   */ mixed_variant<Mixed256x128Bk64>(),
     /* 128x128_BK64   */ mixed_variant<Mixed128x128Bk64>(),
-    /* 256x256_S3     */ mixed_variant<Mixed256x256S3>(),
-    /* 256x256_BK64   */ mixed_variant<Mixed256x256Bk64>(),
+    /* 256x256_S3     */ mixed_variant<Mixed256x256S3, Mixed256x256>(),
+    /* 256x256_BK64   */ mixed_variant<Mixed256x256Bk64, Mixed256x256>(),
     /* 64x64          */ mixed_variant<Mixed64>(),
-    /* 64x64_KS2      */ mixed_variant<Mixed64Ks2>(),
-    /* 64x64_KS4      */ mixed_variant<Mixed64Ks4>(),
-    /* 32x64_KS4      */ mixed_variant<Mixed32x64Ks4>(),
+    /* 64x64_KS2      */ mixed_variant<Mixed64Ks2, Mixed64>(),
+    /* 64x64_KS4      */ mixed_variant<Mixed64Ks4, Mixed64>(),
+    /* 32x64_KS4      */ mixed_variant<Mixed32x64Ks4, Mixed32x64>(),
 };
 
 // AUTO for 16-bit inputs.  The 256x256 kernels run one workgroup per CU, the

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lds_layout.hpp"
 
 // Debug build (DFT_LDS_POISON=1): every kernel fills its LDS with a NaN
@@ -544,8 +546,17 @@ __device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, in
         }
 }
 
+// Whether a kernel moves its overhanging edge tiles back inside C (below):
+// the direct-copy kernels, and any configuration that says so.
+template <class Cfg, class = void>
+struct moves_edge_tiles : std::bool_constant<Cfg::LOAD == kLoadDirect> {};
+template <class Cfg>
+struct moves_edge_tiles<Cfg, std::void_t<decltype(Cfg::MOVE_EDGE_TILES)>>
+    : std::bool_constant<Cfg::LOAD == kLoadDirect || Cfg::MOVE_EDGE_TILES> {};
+
 // Origin of the operand tiles of a workgroup whose output tile starts at
-// (m0, n0).  Direct-copy kernels move a tile that overhangs M (N) back so
+// (m0, n0).  Direct-copy kernels (and the register kernels for 16-bit rows
+// that are only 2-byte aligned) move a tile that overhangs M (N) back so
 // that it ends at M (N), when M >= BM (N >= BN): an A row beyond M feeds only
 // outputs beyond M, and a B column beyond N only outputs beyond N, so the
 // moved tile's rows are all in range and need no zero fill (its copies run
@@ -554,7 +565,7 @@ __device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, in
 // direction needs zero fill.
 template <class Cfg>
 __device__ inline TileCoord operand_origin(TileCoord own, int64_t M, int64_t N) {
-    if constexpr (Cfg::LOAD != kLoadDirect) return own;
+    if constexpr (!moves_edge_tiles<Cfg>::value) return own;
     const int64_t ma = own.m0 + Cfg::BM > M && M >= Cfg::BM ? M - Cfg::BM : own.m0;
     const int64_t na = own.n0 + Cfg::BN > N && N >= Cfg::BN ? N - Cfg::BN : own.n0;
     return TileCoord{ma, na};

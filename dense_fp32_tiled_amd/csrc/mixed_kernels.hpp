@@ -22,6 +22,8 @@
 // when in range, else through registers with zero fill.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_kernels.hpp"
 
 namespace dft {
@@ -188,6 +190,238 @@ struct TileLoader16 {
     }
 };
 
+// A tile of a row-major 16-bit matrix whose rows are only 2-byte aligned
+// (an odd leading dimension or base), read 16 bytes per slot through
+// registers.  A slot's 8 elements are fetched as the five 4-byte-aligned
+// words that hold them (a 16-byte load from the word holding the first
+// element, and a 4-byte load of the word after those four), then moved down
+// by 0 or 2 bytes (v_alignbyte) as they are stored to LDS, so the loads can
+// be issued well before the store.  Every word read holds an element of the
+// slot (when the slot starts word-aligned the fifth load repeats the fourth
+// word), so no read leaves the pages of the operand.  In a tile that
+// overhangs the matrix (the last K tile when BK does not divide K; edge
+// tiles move back inside C) the slots not wholly in range take masked
+// 2-byte loads with zero fill.
+template <int ROWS, int COLS, int THREADS>
+struct TileLoaderShifted16 {
+    static constexpr int VCOLS = COLS / 8;
+    static constexpr int SLOTS = ROWS * VCOLS;
+    static_assert(COLS % 8 == 0 && SLOTS % THREADS == 0, "tile must split evenly over the threads");
+    static constexpr int PER_THREAD = SLOTS / THREADS;
+
+    static_assert(PER_THREAD <= 32, "one shift bit per slot");
+    uint32_t w[PER_THREAD][5];
+    uint32_t shifted;  // bit i: slot i's elements start 2 bytes into its first word
+
+    __device__ static int slot_row(int tid, int i) { return (tid + i * THREADS) / VCOLS; }
+    __device__ static int slot_col(int tid, int i) { return ((tid + i * THREADS) % VCOLS) * 8; }
+
+    // The 8 elements of the slot at (r, c) of a tile whose rows_left x
+    // cols_left corner is in range, from p (2-byte aligned) at that slot:
+    // the five words, and whether they start 2 bytes early.  A slot not
+    // wholly in range is read element by element with zero fill (shift 0).
+    __device__ static void fetch_whole(const uint16_t* p, uint32_t (&w)[5], uint32_t& s) {
+        s = (uint32_t)(uintptr_t)p & 2u;
+        // pointer arithmetic (not an integer round trip) keeps the loads in
+        // the global address space
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(p) - s);
+        u32x4 x;
+        __builtin_memcpy(&x, q, sizeof(x));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = x[e];
+        w[4] = q[s ? 4 : 3];
+    }
+    __device__ static void fetch(const uint16_t* p, int r, int c, int64_t rows_left, int64_t cols_left,
+                                 uint32_t (&w)[5], uint32_t& s) {
+        if (r < rows_left && c + 8 <= cols_left) {
+            fetch_whole(p, w, s);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = (r < rows_left && c + 2 * e < cols_left) ? p[2 * e] : 0u;
+                const uint32_t hi = (r < rows_left && c + 2 * e + 1 < cols_left) ? p[2 * e + 1] : 0u;
+                w[e] = lo | (hi << 16);
+            }
+            w[4] = 0;
+            s = 0;
+        }
+    }
+    __device__ static u32x4 shifted_words(const uint32_t (&w)[5], uint32_t s) {
+        return u32x4{__builtin_amdgcn_alignbyte(w[1], w[0], s), __builtin_amdgcn_alignbyte(w[2], w[1], s),
+                     __builtin_amdgcn_alignbyte(w[3], w[2], s), __builtin_amdgcn_alignbyte(w[4], w[3], s)};
+    }
+
+    __device__ void load(const uint16_t* __restrict__ tile, int64_t ld, int64_t rows_left, int64_t cols_left,
+                         int tid) {
+        shifted = 0;
+        if (rows_left >= ROWS && cols_left >= COLS) {  // whole tile in range: no per-slot test
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                uint32_t s = 0;
+                fetch_whole(tile + (int64_t)slot_row(tid, i) * ld + slot_col(tid, i), w[i], s);
+                shifted |= (s >> 1) << i;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_THREAD; ++i) {
+                const int r = slot_row(tid, i), c = slot_col(tid, i);
+                uint32_t s = 0;
+                fetch(tile + (int64_t)r * ld + c, r, c, rows_left, cols_left, w[i], s);
+                shifted |= (s >> 1) << i;
+            }
+        }
+    }
+
+    // Masked load and LDS store of the whole tile, CH slots at a time (the
+    // staging registers of those slots only), for a tile loaded while the
+    // multiply's registers are live.
+    template <class Tile, int CH>
+    __device__ static void copy_in_chunks(const uint16_t* __restrict__ tile, int64_t ld, int64_t rows_left,
+                                          int64_t cols_left, uint32_t* lds, int stage, int tid) {
+        static_assert(Tile::rows == ROWS && 2 * Tile::cols == COLS, "LDS tile shape mismatch");
+        static_assert(PER_THREAD % CH == 0, "chunks must split the slots evenly");
+#pragma unroll 1
+        for (int i0 = 0; i0 < PER_THREAD; i0 += CH) {
+            uint32_t w[CH][5], s[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int r = slot_row(tid, i0 + i), c = slot_col(tid, i0 + i);
+                fetch(tile + (int64_t)r * ld + c, r, c, rows_left, cols_left, w[i], s[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int r = slot_row(tid, i0 + i), c = slot_col(tid, i0 + i);
+                *reinterpret_cast<u32x4*>(lds + Tile::offset(stage, r, c / 2)) = shifted_words(w[i], s[i]);
+            }
+        }
+    }
+
+    // Element (r, c) -> 16-bit half (c % 2) of word Tile::offset(stage, r, c / 2).
+    template <class Tile>
+    __device__ void store(uint32_t* lds, int stage, int tid) const {
+        static_assert(Tile::rows == ROWS && 2 * Tile::cols == COLS, "LDS tile shape mismatch");
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int r = slot_row(tid, i), c = slot_col(tid, i);
+            *reinterpret_cast<u32x4*>(lds + Tile::offset(stage, r, c / 2)) =
+                shifted_words(w[i], ((shifted >> i) & 1u) * 2u);
+        }
+    }
+};
+
+// Direct 4-byte copies of a tile of a row-major 16-bit matrix whose rows are
+// only 2-byte aligned (ROWS rows of COLS elements).  A row whose first
+// element is the upper half of a 4-byte word (shift 2) has its elements in
+// COLS / 2 + 1 words.  The main copies fetch, for every row, the COLS / 2
+// words from the one holding its first element into a plain row-major main
+// area.  The word after those is, for a tile of A followed by another whole
+// K tile, the first main word of the same row in that tile, which the
+// realignment reads from that tile's main area; otherwise (B, whose tile
+// rows are K indices, and A's last whole tile) the extra copies fetch it
+// into an extra area (one word per row, 64 rows per copy instruction; for a
+// row that starts word-aligned, a second copy of its last word, so that no
+// read leaves the row's own words).  realign() then
+// moves each row down by its shift, 4 words at a time, into the kernel's LDS
+// tile layout: output word c of a row is bytes shift .. shift+3 of raw
+// words c, c+1.  A round of main copies covers an even number of whole rows,
+// so the shift of the row a lane fetches, and its column, are the same in
+// every round: one offset per lane and a uniform row stride describe all
+// main copies.  Tile origins advance by whole words along K, so the shifts
+// and offsets hold for every K tile.
+template <int ROWS, int COLS, int THREADS>
+struct RawCopy16 {
+    static constexpr int WAVES = THREADS / kWave;
+    static constexpr int RW = COLS / 2;  // main words per row
+    static constexpr int MAIN = ROWS * RW;
+    static constexpr int ROUND = WAVES * kWave;  // words per round of main copies
+    static constexpr int ROUND_ROWS = RW > 0 && ROUND % RW == 0 ? ROUND / RW : 0;
+    static constexpr int PER_WAVE = MAIN / ROUND;
+    static constexpr int EXTRA_COPIES = (ROWS + kWave - 1) / kWave;
+    static constexpr int EXTRA_WORDS = EXTRA_COPIES * kWave;
+    static constexpr int GROUPS = MAIN / 4;  // realign groups of 4 words
+    // Every thread realigns (REALIGNERS: measured no faster when only one
+    // of the two waves on each SIMD did, the other multiplying meanwhile).
+    static constexpr int REALIGNERS = THREADS;
+    static constexpr int REALIGN_GROUPS = GROUPS / REALIGNERS;
+    static constexpr bool OK = COLS % 8 == 0 && ROUND_ROWS > 0 && ROUND_ROWS % 2 == 0 && MAIN % ROUND == 0 &&
+                               EXTRA_COPIES <= WAVES && GROUPS % REALIGNERS == 0 && REALIGN_GROUPS <= 32;
+
+    // Byte offsets from the tile origin fit 31 bits.
+    __host__ __device__ static constexpr bool fits(int64_t ld) {
+        return ld <= (((int64_t)1 << 31) - 4 * RW - 8) / (2 * (int64_t)ROWS);
+    }
+    // Shift (bytes) of row `row` of a tile whose origin is `lead` bytes past a word boundary.
+    __device__ static uint32_t row_shift(uint32_t lead, int64_t row, int64_t ld) {
+        return (lead + 2u * ((uint32_t)(row * ld) & 1u)) & 2u;
+    }
+    // Byte offset of the word holding row `row`'s first element from the word holding the origin.
+    __device__ static uint32_t row_start(uint32_t lead, int64_t row, int64_t ld) {
+        return (uint32_t)(lead + 2 * row * ld) - row_shift(lead, row, ld);
+    }
+
+    uint32_t main_off;    // this lane's main copy in round 0
+    uint32_t extra_off;   // this lane's extra copy (the wave that makes one)
+    uint32_t lead;        // origin & 2
+    int64_t round_bytes;  // ROUND_ROWS rows
+    int wave;             // wave-uniform
+    uint32_t shifted;     // bit i: realign group i of this thread has shift 2
+
+    __device__ RawCopy16(int64_t ld, uint32_t lead_, int wave_uniform, int lane, int tid)
+        : lead(lead_), round_bytes((int64_t)ROUND_ROWS * ld * 2), wave(wave_uniform) {
+        const int word = wave * kWave + lane;
+        main_off = row_start(lead, word / RW, ld) + 4u * (uint32_t)(word % RW);
+        const int64_t row = wave * kWave + lane < ROWS ? wave * kWave + lane : ROWS - 1;
+        extra_off = row_start(lead, row, ld) + 4u * (uint32_t)(row_shift(lead, row, ld) ? RW : RW - 1);
+        shifted = 0;
+#pragma unroll
+        for (int i = 0; i < REALIGN_GROUPS; ++i)
+            shifted |= (row_shift(lead, (tid + i * REALIGNERS) / (RW / 4), ld) >> 1) << i;
+    }
+
+    // Issue the main copies of the tile at `origin` into `main` (MAIN
+    // words); they complete asynchronously (vector memory counter).
+    __device__ void issue_main(const uint16_t* origin, uint32_t* main) const {
+        static_assert(OK, "tile shape unsuited to raw copies");
+        typedef __attribute__((address_space(3))) uint32_t lds_word;
+        const char* base = reinterpret_cast<const char*>(origin) - lead;
+        const uint32_t lds = (uint32_t)(uintptr_t)(lds_word*)main;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i)
+            copy4_to_lds(base + i * round_bytes, main_off, lds + 4u * (uint32_t)((i * WAVES + wave) * kWave));
+    }
+    // The extra copies (waves below EXTRA_COPIES) into `extra` (EXTRA_WORDS words).
+    __device__ void issue_extra(const uint16_t* origin, uint32_t* extra) const {
+        typedef __attribute__((address_space(3))) uint32_t lds_word;
+        if (wave < EXTRA_COPIES)
+            copy4_to_lds(reinterpret_cast<const char*>(origin) - lead, extra_off,
+                         (uint32_t)(uintptr_t)(lds_word*)extra + 4u * (uint32_t)(wave * kWave));
+    }
+
+    // Rows of the landed tile at `main`, shifted into place, to `stage` of
+    // the LDS tile at `lds` (threads below REALIGNERS).  The word after row
+    // r's main words is after[r * after_stride]: in the next K tile's main
+    // area (stride RW) or in an extra area (stride 1).
+    template <class Tile>
+    __device__ void realign(const uint32_t* main, const uint32_t* after, int after_stride, uint32_t* lds, int stage,
+                            int tid) const {
+        static_assert(Tile::rows == ROWS && Tile::cols == RW, "LDS tile shape mismatch");
+#pragma unroll
+        for (int i = 0; i < REALIGN_GROUPS; ++i) {
+            const int g = tid + i * REALIGNERS;
+            const int row = g / (RW / 4), j = g % (RW / 4);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(main + row * RW + 4 * j);
+            const uint32_t next = j + 1 < RW / 4 ? main[row * RW + 4 * j + 4] : after[row * after_stride];
+            const uint32_t sh = ((shifted >> i) & 1u) * 2u;
+            const u32x4 y{__builtin_amdgcn_alignbyte(x[1], x[0], sh), __builtin_amdgcn_alignbyte(x[2], x[1], sh),
+                          __builtin_amdgcn_alignbyte(x[3], x[2], sh), __builtin_amdgcn_alignbyte(next, x[3], sh)};
+            *reinterpret_cast<u32x4*>(lds + Tile::offset(stage, row, 4 * j)) = y;
+            // two groups at a time: bounds the registers live beside the
+            // multiply's accumulators and fragments
+            if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
 // PIPELINE: 0, fragments read next to their MFMAs; 1, the fragments of MFMA
 // step st+1 read during the MFMAs of step st (twice the fragment
 // registers); 2, as 1 and across K tiles too: the last step of tile t
@@ -211,6 +445,9 @@ struct MixedCfg {
     static_assert(VEC == 8 || VEC == 2 || VEC == 1, "16-byte, 4-byte or 2-byte operand access");
     static constexpr int LOAD = VEC == 1 ? kLoadRegisters : kLoadDirect;
     static constexpr int LOADER_VEC = VEC == 8 ? 8 : 1;  // register-path loads (edge and ragged tiles)
+    // The register kernels (VEC 1) also move edge tiles back inside C, so
+    // that only the K direction takes masked loads.
+    static constexpr bool MOVE_EDGE_TILES = true;
     static constexpr int STAGES = STAGES_;  // LDS stages of the direct-copy pipeline (register paths use two)
     static constexpr int PIPELINE = PIPELINE_;
     static constexpr int KSPLIT = 1;  // wave groups splitting K inside the workgroup (MixedKsplitCfg)
@@ -221,7 +458,24 @@ struct MixedCfg {
     static constexpr int STEPS = BK / Op::KB;
     using TileA = LdsTile<BM, BK / 2, LayA::pad, STAGES, LayA::unit, LayA::shift, LayA::mask>;  // 4-byte words
     using TileB = LdsTile<BK, BN / 2, LayB::pad, STAGES, LayB::unit, LayB::shift, LayB::mask>;
-    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    // VEC 1: raw 4-byte copies of both operands (RawCopy16) realigned in
+    // LDS, when the shape suits them and they fit beside the tiles; shifted
+    // loads through registers otherwise (and for tiles that cannot move
+    // inside C).
+    // A's main copies in three stages (a tile's realignment reads the next
+    // tile's), one A extra area (A's last whole K tile), B's main copies in
+    // two stages and B's extra copies in three (issued a tile ahead of B's
+    // main copies, since each fetches words of 64 different rows).
+    using RawA = RawCopy16<BM, BK, THREADS>;
+    using RawB = RawCopy16<BK, BN, THREADS>;
+    static constexpr int RAW_A_OFF = 0, RAW_AX_OFF = 3 * RawA::MAIN, RAW_B_OFF = RAW_AX_OFF + RawA::EXTRA_WORDS,
+                         RAW_BX_OFF = RAW_B_OFF + 2 * RawB::MAIN;
+    static constexpr int RAW_WORDS = RAW_BX_OFF + 3 * RawB::EXTRA_WORDS;
+    // (Eight-wave kernels only: the raw stages would cost the smaller
+    // kernels their second workgroup per CU, measured slower.)
+    static constexpr bool RAW = VEC == 1 && RawA::OK && RawB::OK && STAGES == 2 && THREADS >= 512 &&
+                                TileA::bytes + TileB::bytes + RAW_WORDS * 4 <= 160 * 1024;
+    static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes + (RAW ? RAW_WORDS * 4 : 0);
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % Op::MB == 0 && WN % Op::NB == 0, "wave tiling");
     static_assert(BK % Op::KB == 0, "whole MFMA steps per K tile");
     static_assert(LayA::pad == 0 && LayB::pad == 0, "direct copies need unpadded rows");
@@ -271,8 +525,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 
     __shared__ __attribute__((aligned(16))) uint32_t lds_a[TileA::total_elems];
     __shared__ __attribute__((aligned(16))) uint32_t lds_b[TileB::total_elems];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_raw[Cfg::RAW ? Cfg::RAW_WORDS : 4];
     poison_lds(lds_a, TileA::total_elems);
     poison_lds(lds_b, TileB::total_elems);
+    if constexpr (Cfg::RAW) poison_lds(lds_raw, Cfg::RAW_WORDS);
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -296,8 +552,11 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 #pragma unroll
             for (int v = 0; v < Op::ACC; ++v) acc[i][j][v] = 0.0f;
 
-    TileLoader16<BM, BK, THREADS, Cfg::LOADER_VEC> ldr_a;
-    TileLoader16<BK, BN, THREADS, Cfg::LOADER_VEC> ldr_b;
+    // Rows only 2-byte aligned (VEC 1): shifted 16-byte loads.
+    std::conditional_t<Cfg::VEC == 1, TileLoaderShifted16<BM, BK, THREADS>,
+                       TileLoader16<BM, BK, THREADS, Cfg::LOADER_VEC>> ldr_a;
+    std::conditional_t<Cfg::VEC == 1, TileLoaderShifted16<BK, BN, THREADS>,
+                       TileLoader16<BK, BN, THREADS, Cfg::LOADER_VEC>> ldr_b;
     const uint16_t* a_tile = A + m0 * lda;
     const uint16_t* b_tile = B + n0;
     const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;
@@ -341,10 +600,18 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
     // hidden inside the wavefront instead of stalling the matrix pipe.  The
     // scheduling barriers keep the compiler from sinking the reads back next
     // to their MFMAs (which it does to save registers).
-    auto multiply = [&](int stage) {
+    // `early` runs before the MFMAs of step 0 and `mid` after those of the
+    // first half of the steps: the kernels for 2-byte-aligned rows move the
+    // next tile into LDS there, while the matrix pipe works through MFMAs
+    // already issued.
+    constexpr int MID_STEP = Cfg::STEPS / 2 - 1;
+    auto multiply_with = [&](int stage, auto&& early, auto&& mid) {
         if constexpr (Cfg::PIPELINE != kPipeNone) {
             u32x4 af[2][MI], bf[2][NI];
             read_fragments(stage, 0, af[0], bf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            early();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int st = 0; st < Cfg::STEPS; ++st) {
                 if (st + 1 < Cfg::STEPS) read_fragments(stage, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
@@ -354,8 +621,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 #pragma unroll
                     for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[st & 1][i], bf[st & 1][n], acc[i][n]);
                 __builtin_amdgcn_sched_barrier(0);
+                if (st == MID_STEP) {
+                    mid();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
+            early();
 #pragma unroll
             for (int st = 0; st < Cfg::STEPS; ++st) {
                 u32x4 af[MI], bf[NI];
@@ -364,9 +636,11 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i], bf[n], acc[i][n]);
+                if (st == MID_STEP) mid();
             }
         }
     };
+    auto multiply = [&](int stage) { multiply_with(stage, [] {}, [] {}); };
 
     // Tile t into `stage` through registers, with zero fill, for kernels
     // with 4-byte copies: 2 bytes per element (their rows need not be
@@ -521,10 +795,100 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
             two_stage_registers();
         }
     } else {
-        // Unaligned operands: 2-byte loads through registers, issued after
-        // the multiply so that the staged elements (one register each) are
-        // not live across it; the other workgroups on the CU hide the latency.
-        two_stage_registers();
+        // Rows only 2-byte aligned.
+        bool raw_done = false;
+        if constexpr (Cfg::RAW) {
+            using RA = typename Cfg::RawA;
+            using RB = typename Cfg::RawB;
+            if (M - m0 >= BM && N - n0 >= BN && RA::fits(lda) && RB::fits(ldb)) {
+                // Tile u (each K tile wholly in range) is realigned halfway
+                // through the multiply of tile u-1, into the tile stage that
+                // multiply does not read (every wave finished reading it
+                // before the barrier that ended iteration u-2).  It reads A's
+                // main copies of tiles u and u+1 (A's extra copies for the
+                // last whole tile) and B's main and extra copies of tile u;
+                // iteration t issues A's main and B's extra copies of tile
+                // t+3 and B's main copies of tile t+2, so each has landed
+                // (waited for before the barrier that ends iteration t) an
+                // iteration or more before it is read, and goes into a stage
+                // whose previous tile was realigned before that barrier; A's
+                // extra copies (of the last whole tile) are issued first.  A
+                // ragged last K tile goes through registers.
+                const int wv = __builtin_amdgcn_readfirstlane(wave);
+                const RA raw_a(lda, (uint32_t)(uintptr_t)a_tile & 2u, wv, lane, tid);
+                const RB raw_b(ldb, (uint32_t)(uintptr_t)b_tile & 2u, wv, lane, tid);
+                const int64_t TF = K / BK;  // K tiles wholly in range
+                static_assert(RA::REALIGNERS == RB::REALIGNERS, "one set of realigning waves");
+                const bool realigner = wv < RA::REALIGNERS / kWave;
+                uint32_t* const a_main = lds_raw + Cfg::RAW_A_OFF;
+                uint32_t* const a_extra = lds_raw + Cfg::RAW_AX_OFF;
+                uint32_t* const b_main = lds_raw + Cfg::RAW_B_OFF;
+                uint32_t* const b_extra = lds_raw + Cfg::RAW_BX_OFF;
+                auto issue3 = [&](int64_t u, int r3) {  // A main, B extra of tile u into ring slot r3
+                    raw_a.issue_main(a_tile + u * BK, a_main + r3 * RA::MAIN);
+                    raw_b.issue_extra(b_tile + u * BK * ldb, b_extra + r3 * RB::EXTRA_WORDS);
+                };
+                auto issue2 = [&](int64_t u, int r2) { raw_b.issue_main(b_tile + u * BK * ldb, b_main + r2 * RB::MAIN); };
+                auto fill_tile = [&](int64_t u, int stage, int r3, int r2) {
+                    if (u < TF) {
+                        if (!realigner) return;
+                        const bool last = u + 1 == TF;
+                        const uint32_t* a_after = last ? a_extra : a_main + (r3 == 2 ? 0 : r3 + 1) * RA::MAIN;
+                        raw_a.template realign<TileA>(a_main + r3 * RA::MAIN, a_after, last ? 1 : RA::RW, lds_a,
+                                                      stage, tid);
+                        raw_b.template realign<TileB>(b_main + r2 * RB::MAIN, b_extra + r3 * RB::EXTRA_WORDS, 1,
+                                                      lds_b, stage, tid);
+                    } else {
+                        fill_in_chunks(u, stage);
+                    }
+                };
+                if (TF > 0) raw_a.issue_extra(a_tile + (TF - 1) * BK, a_extra);  // for the last whole tile
+                for (int p = 0; p < 3 && p < TF; ++p) issue3(p, p);
+                for (int p = 0; p < 2 && p < TF; ++p) issue2(p, p);
+                wait_vector_memory();
+                __syncthreads();
+                if (T > 0) fill_tile(0, 0, 0, 0);
+                __syncthreads();
+                int r3 = 0, r2 = 0;  // ring slots of tile t
+                for (int64_t t = 0; t < T; ++t) {
+                    const int s = (int)(t & 1);
+                    const int n3 = r3 == 2 ? 0 : r3 + 1, n2 = r2 ^ 1;  // slots of tile t+1
+                    if (t + 3 < TF) issue3(t + 3, r3);
+                    if (t + 2 < TF) issue2(t + 2, r2);
+                    multiply_with(s, [] {}, [&] {
+                        if (t + 1 < T) fill_tile(t + 1, s ^ 1, n3, n2);
+                    });
+                    wait_vector_memory();
+                    __syncthreads();
+                    r3 = n3;
+                    r2 = n2;
+                }
+                raw_done = true;
+            }
+        }
+        if (!raw_done) {
+            // Two LDS stages filled through registers.  Halfway through the
+            // multiply of tile t (stage s) each thread stores tile t+1,
+            // loaded during the iteration before, to the other stage (every
+            // wave finished reading it before the barrier that ended
+            // iteration t-1), then issues the loads of tile t+2 into the
+            // registers just freed: a load has a whole iteration to land,
+            // and the stores run beside MFMAs already issued.
+            if (T > 0) {
+                load_tile(0);
+                store_tile(0);
+            }
+            if (T > 1) load_tile(1);
+            __syncthreads();
+            for (int64_t t = 0; t < T; ++t) {
+                const int s = (int)(t & 1);
+                multiply_with(s, [] {}, [&] {
+                    if (t + 1 < T) store_tile(s ^ 1);
+                    if (t + 2 < T) load_tile(t + 2);
+                });
+                __syncthreads();
+            }
+        }
     }
 
     store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);

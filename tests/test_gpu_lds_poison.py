@@ -49,6 +49,9 @@ MIXED_CASES = [
     (300, 520, 100, 4, 8, 0),   # aligned rows, moved edge tiles
     (130, 100, 1000, 8, 4, 0),  # K-split groups
     (300, 250, 100, 4, 6, 0),   # ldb aligned, N not: narrow copies of moved B
+    (300, 260, 33, 1, 1, 0),    # rows 2-byte aligned: raw copies realigned in LDS
+    (520, 300, 64, 3, 1, 1),
+    (256, 256, 1, 1, 1, 0),
 ]
 
 _refs: dict = {}

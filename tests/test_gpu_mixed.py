@@ -171,6 +171,32 @@ def test_mixed_moved_tiles_with_aligned_pitch(kind, N, variant, torch_gpu):
     assert np.array_equal(c.astype(np.float64), oracle.reference(af, bf)[0])
 
 
+TWO_BYTE_SHAPES = [(256, 256, 1), (300, 260, 15), (257, 300, 32), (300, 257, 33), (520, 300, 64), (300, 520, 65),
+                   (256, 512, 100), (513, 257, 1000)]
+
+
+@pytest.mark.parametrize("kind", list(TYPES))
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("shape", TWO_BYTE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in TWO_BYTE_SHAPES])
+def test_mixed_two_byte_rows(kind, shape, variant, torch_gpu):
+    """Rows only 2-byte aligned (odd leading dimensions, bases shifted by
+    one element), M and N at least one large tile, so the raw 4-byte copies
+    realigned in LDS run for the interior and moved edge tiles: K of one
+    partial tile, one whole tile, a whole tile and a ragged one, many tiles.
+    Bit for bit on integer inputs (each row's shift must be right), within
+    the bar on uniform ones; NaN in every ld gap and around C."""
+    M, N, K = shape
+    ab, bb, af, bf = operands(kind, M, N, K, "integer", 2300 + M + N + K)
+    want = oracle.reference(af, bf)[0]
+    for lda, ldb, offset in ((K + 1, N + 1, 0), (K + 3, N + 5, 1), (K + 1, N + 2, 1), (K + 2, N + 1, 0)):
+        c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=lda, ldb=ldb, ldc=N + 3, offset=offset)
+        assert np.array_equal(c.astype(np.float64), want), (lda, ldb, offset)
+    ab, bb, af, bf = operands(kind, M, N, K, "uniform", 2400 + M + N + K)
+    cref, den = oracle.reference(af, bf)
+    c = run_mixed(torch_gpu, kind, ab, bb, variant, lda=K + 1, ldb=N + 1, offset=1)
+    assert oracle.normalised_error(c, cref, den) <= TOL
+
+
 _random_refs: dict = {}
 
 
