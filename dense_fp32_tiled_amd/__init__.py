@@ -122,6 +122,7 @@ EXPORTS = (
     "gemm_lds_offset",
     "gemm_lds_bank",
     "gemm_lds_conflict_degree",
+    "gemm_lds_access_cycles",
     "gemm_lds_page_pad",
 )
 
@@ -215,6 +216,8 @@ def library(path: Path | None = None):
     lib.gemm_lds_bank.restype = i32
     lib.gemm_lds_conflict_degree.argtypes = [ctypes.POINTER(i64), i32, i32, i32, i32]
     lib.gemm_lds_conflict_degree.restype = i32
+    lib.gemm_lds_access_cycles.argtypes = [ctypes.POINTER(i64), i32]
+    lib.gemm_lds_access_cycles.restype = i32
     lib.gemm_lds_page_pad.argtypes = [i32, i32, i32]
     lib.gemm_lds_page_pad.restype = i32
     if path is None:
@@ -318,6 +321,14 @@ def gemm_lds_bank(word_offset: int, banks: int) -> int:
 def gemm_lds_conflict_degree(lane_words, width: int, banks: int, group: int) -> int:
     arr = (ctypes.c_int64 * len(lane_words))(*lane_words)
     return library().gemm_lds_conflict_degree(arr, len(lane_words), width, banks, group)
+
+
+def gemm_lds_access_cycles(lane_words, mode: int) -> int:
+    """LDS cycles of one 64-lane access under the gfx950 bank model (see the header)."""
+    words = list(lane_words)
+    if len(words) != 64:
+        raise ValueError("64 lane offsets")
+    return library().gemm_lds_access_cycles((ctypes.c_int64 * 64)(*words), mode)
 
 
 def gemm_lds_page_pad(columns: int, simultaneous_rows: int, banks: int = 32) -> int:

@@ -950,6 +950,26 @@ int32_t gemm_lds_conflict_degree(const int64_t* lane_words, int32_t lanes, int32
     return conflict_degree([=](int l) { return lane_words[l]; }, lanes, width, banks, group);
 }
 
+int32_t gemm_lds_access_cycles(const int64_t* lane_words, int32_t mode) {
+    if (lane_words == nullptr) return -1;
+    for (int l = 0; l < kWaveLanes; ++l)
+        if (lane_words[l] < 0) return -1;
+    auto at = [=](int l) { return lane_words[l]; };
+    switch (mode) {
+        case 1: case 2: case 4:
+            return access_cycles(at, mode, false, kGfx950Lds);
+        case 101: case 102: case 104:
+            return access_cycles(at, mode - 100, true, kGfx950Lds);
+        case -16: case -32: {  // ds_read2_b32: the second dword -mode words after the first
+            const int off = -mode;
+            return access_cycles(at, 1, false, kGfx950Lds) +
+                   access_cycles([=](int l) { return lane_words[l] + off; }, 1, false, kGfx950Lds);
+        }
+        default:
+            return -1;
+    }
+}
+
 int32_t gemm_lds_page_pad(int32_t columns, int32_t simultaneous_rows, int32_t banks) {
     if (columns < 1 || simultaneous_rows < 0 || banks < 1) return -1;
     return page_pad(columns, simultaneous_rows, banks);

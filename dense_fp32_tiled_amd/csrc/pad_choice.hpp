@@ -5,7 +5,8 @@
 // For every LDS access a kernel issues on a tile (fragment reads by every
 // wavefront, cooperative stores by every thread) the conflict degree is
 // computed from the exact addresses the lanes touch; a layout's cost is the
-// sum over those accesses of passes x degree, per K tile.  Candidates are row
+// sum over those accesses of their LDS cycles (access_cycles: per pass, its
+// conflict degree), per K tile.  Candidates are row
 // pads that keep 16-byte alignment and XOR swizzles of 16-byte column groups
 // (no pad); the cheapest wins, ties going to no change, then to a pad, then to
 // a swizzle.  This replaces the pages' one-pattern rule ("My Triton From
@@ -28,22 +29,17 @@ constexpr int64_t layout_word(LayoutChoice c, int cols, int row, int col) {
     return (int64_t)row * (cols + c.pad) + c.swz.apply(row, col);
 }
 
-// LDS passes one access of `width_words` costs at conflict degree `degree`.
-constexpr int access_cost(int degree, int width_words, LdsGeometry g) {
-    return degree * (kWaveLanes / g.group_for_width(width_words));
-}
-
-// Cost of one wavefront-wide access: lane l touches (row(l), col(l)) .. +width.
+// Cost (LDS cycles, access_cycles) of one wavefront-wide access: lane l
+// touches (row(l), col(l)) .. +width; `store` selects the store geometry.
 template <class RowCol>
-constexpr int pattern_cost(LayoutChoice c, int cols, int width, LdsGeometry g, RowCol rc) {
-    const int d = conflict_degree(
+constexpr int pattern_cost(LayoutChoice c, int cols, int width, LdsGeometry g, RowCol rc, bool store = false) {
+    return access_cycles(
         [=](int l) {
             int row = 0, col = 0;
             rc(l, row, col);
             return layout_word(c, cols, row, col);
         },
-        kWaveLanes, width, g.banks_for_width(width), g.group_for_width(width));
-    return access_cost(d, width, g);
+        width, store, g);
 }
 
 // Cost of a two-address access (ds_read2_b32): lane l touches (row(l, e),
@@ -157,11 +153,14 @@ constexpr int mfma_a_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
                 });
         const int vcols = s.bk / s.vec;
         for (int i = 0; !s.direct && i < (s.bm * vcols) / s.threads; ++i)
-            total += pattern_cost(c, s.bk, s.vec, g, [=](int l, int& row, int& col) {
-                const int idx = w * kWaveLanes + l + i * s.threads;
-                row = idx / vcols;
-                col = (idx % vcols) * s.vec;
-            });
+            total += pattern_cost(
+                c, s.bk, s.vec, g,
+                [=](int l, int& row, int& col) {
+                    const int idx = w * kWaveLanes + l + i * s.threads;
+                    row = idx / vcols;
+                    col = (idx % vcols) * s.vec;
+                },
+                true);
     }
     return total;
 }
@@ -189,11 +188,14 @@ constexpr int mfma_b_cost(MfmaShape s, LayoutChoice c, LdsGeometry g) {
         }
         const int vcols = s.bn / s.vec;
         for (int i = 0; !s.direct && i < (s.bk * vcols) / s.threads; ++i)
-            total += pattern_cost(c, s.bn, s.vec, g, [=](int l, int& row, int& col) {
-                const int idx = w * kWaveLanes + l + i * s.threads;
-                row = idx / vcols;
-                col = (idx % vcols) * s.vec;
-            });
+            total += pattern_cost(
+                c, s.bn, s.vec, g,
+                [=](int l, int& row, int& col) {
+                    const int idx = w * kWaveLanes + l + i * s.threads;
+                    row = idx / vcols;
+                    col = (idx % vcols) * s.vec;
+                },
+                true);
     }
     return total;
 }
@@ -293,11 +295,14 @@ constexpr int valu_a_cost(ValuShape s, LayoutChoice c, LdsGeometry g) {
                 });
         for (int i = 0; i < s.bm * vcols / s.threads; ++i)
             for (int e = 0; e < s.vec; ++e)
-                total += pattern_cost(c, s.bm, 1, g, [=](int l, int& row, int& col) {
-                    const int slot = w * kWaveLanes + l + i * s.threads;
-                    row = s.vec * (slot % vcols) + e;
-                    col = slot / vcols;
-                });
+                total += pattern_cost(
+                    c, s.bm, 1, g,
+                    [=](int l, int& row, int& col) {
+                        const int slot = w * kWaveLanes + l + i * s.threads;
+                        row = s.vec * (slot % vcols) + e;
+                        col = slot / vcols;
+                    },
+                    true);
     }
     return total;
 }
@@ -312,11 +317,14 @@ constexpr int valu_b_cost(ValuShape s, LayoutChoice c, LdsGeometry g) {
                     col = half * (s.bn / 2) + ((w * kWaveLanes + l) % s.threads_n) * 4;
                 });
         for (int i = 0; i < s.bk * vcols / s.threads; ++i)
-            total += pattern_cost(c, s.bn, s.vec, g, [=](int l, int& row, int& col) {
-                const int slot = w * kWaveLanes + l + i * s.threads;
-                row = slot / vcols;
-                col = s.vec * (slot % vcols);
-            });
+            total += pattern_cost(
+                c, s.bn, s.vec, g,
+                [=](int l, int& row, int& col) {
+                    const int slot = w * kWaveLanes + l + i * s.threads;
+                    row = slot / vcols;
+                    col = s.vec * (slot % vcols);
+                },
+                true);
     }
     return total;
 }

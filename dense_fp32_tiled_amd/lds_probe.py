@@ -2,12 +2,13 @@
 
     python -m dense_fp32_tiled_amd.lds_probe [--out FILE]
 
-Times a fixed set of one-instruction LDS read patterns (strided 4/8/16-byte
-reads, and the exact fragment-read patterns of the GEMM kernels at their
-candidate paddings) and prints cycles per instruction next to the conflict
-degree the bank model predicts for each candidate geometry.  The geometry
-whose predictions track the measurements is the one the kernels' padding is
-derived for.
+Times a fixed set of one-instruction LDS access patterns (strided 4/8/16-byte
+reads and stores, two-address reads, patterns that isolate which lanes share
+a pass, and with --kernels every fragment read and store of the MFMA
+kernels with their built layouts) and prints the LDS cycles per instruction
+next to what the bank model the layout search uses predicts for it
+(gemm_lds_access_cycles, or the issue floor of a conflict-free
+instruction).
 """
 
 from __future__ import annotations
@@ -20,13 +21,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 PROBE_LIB = PKG / "liblds_probe.so"
+LDS_PROBE_WORDS = 16384  # the probe kernel's LDS buffer (include/lds_probe.h)
 
-# candidate geometries: access width in dwords -> (banks, lanes serviced per pass)
-GEOMETRIES = {
-    "32 banks x 128 B/pass": {1: (32, 32), 2: (32, 16), 4: (32, 8)},
-    "64 banks x 256 B/pass": {1: (64, 64), 2: (64, 32), 4: (64, 16)},
-    "b32 32x32, b64 64x32, b128 64x16": {1: (32, 32), 2: (64, 32), 4: (64, 16)},
-}
 
 
 def load():
@@ -162,6 +158,29 @@ def patterns():
         pats.append((f"b128 rows x groups, lanes {label} (g = l / 16)", 4,
                      [quad(l % 16, l // 16) if l in lanes else 0 for l in range(64)]))
     pats.append(("b128 rows x groups, all lanes (g = l / 32, rows 0..31)", 4, [quad(l % 32, l // 32) for l in range(64)]))
+    # One pass alone (lanes 0-15; the others read lane 0's address): 16
+    # distinct 16-byte bank quads, spread over 256-byte rows in different ways.
+    def one_pass(words16):
+        return [words16[l] if l < 16 else words16[0] for l in range(64)]
+    mfma16_quad = [4 * (l % 4) + l // 4 for l in range(16)]
+    for label, words16 in (
+            ("quads in order, one row", [4 * l for l in range(16)]),
+            ("quads in order, row per lane", [4 * l + 64 * l for l in range(16)]),
+            ("quads 4(l%4)+l/4, one row", [4 * q for q in mfma16_quad]),
+            ("quads 4(l%4)+l/4, row per lane", [4 * q + 64 * l for l, q in enumerate(mfma16_quad)]),
+            ("quads in order, row l/4", [4 * l + 64 * (l // 4) for l in range(16)]),
+            ("quads in order, row l%4", [4 * l + 64 * (l % 4) for l in range(16)]),
+            ("quads in order, row l/8", [4 * l + 64 * (l // 8) for l in range(16)]),
+            ("quads in order, row l%2", [4 * l + 64 * (l % 2) for l in range(16)]),
+            ("mfma16 A rows (16-word rows, swizzle 4,2,3)",
+             [16 * r + 4 * (0 ^ ((r >> 2) & 3)) for r in range(16)])):
+        pats.append((f"b128 one pass, {label}", 4, one_pass(words16)))
+    # Two passes whose quads coincide: lanes 0-15 and lanes 16k..16k+15 at
+    # another row, one pair of passes at a time.
+    for other in (1, 2, 3):
+        pats.append((f"b128 passes 0 and {other} on the same quads", 4,
+                     [4 * (l % 16) + (1024 if l // 16 == other else 0) if l // 16 in (0, other) else 0
+                      for l in range(64)]))
     pats.append(("valu A read (broadcast groups of 16)", 4, [(l // 16) * 4 for l in range(64)]))
     pats.append(("valu B read", 4, [(l % 16) * 4 for l in range(64)]))
     return pats
@@ -169,8 +188,9 @@ def patterns():
 
 def kernel_patterns(variant: int):
     """Every distinct LDS access pattern one K tile of an MFMA variant issues
-    (fragment reads, ds_read2 pairs, cooperative stores), A tile at dword 0
-    and B tile at dword 8192 as in the kernel's stage-0 layout."""
+    (fragment reads, ds_read2 pairs, and the cooperative stores of the
+    register-path kernels), A tile at dword 0 and B tile at dword 8192 as in
+    the kernel's stage-0 layout."""
     import dense_fp32_tiled_amd as dft
 
     c = dft.gemm_f32_tile_config(variant)
@@ -205,6 +225,8 @@ def kernel_patterns(variant: int):
                 add(f"B read2 w{w} j{j} n{ni}", -mb,
                     [word("b", (l // mb) * kg + j, wn0 + ni * mb + l % mb) for l in range(64)])
         for tile, rows, cols in (("a", c["bm"], c["bk"]), ("b", c["bk"], c["bn"])):
+            if c["direct_to_lds"]:
+                break  # direct copies: no LDS store instructions
             vcols = cols // vec
             for i in range(rows * vcols // c["threads"]):
                 idx = [w * 64 + l + i * c["threads"] for l in range(64)]
@@ -212,42 +234,18 @@ def kernel_patterns(variant: int):
     return out
 
 
-def predicted(words, width, geom):
+# Issue time of a conflict-free instruction (LDS cycles, measured with 4
+# waves): the bank model's cycles (gemm_lds_access_cycles) exclude it, so a
+# timing is predicted as the larger of the two.
+ISSUE_FLOOR = {1: 3.4, 2: 3.4, 4: 4.0, -16: 4.0, -32: 4.0, 101: 4.0, 102: 4.0, 104: 13.1}
+
+
+def model_cycles(words, mode) -> float:
+    """Cycles per instruction the gfx950 bank model predicts (bank cycles or
+    the issue floor, whichever is larger)."""
     import dense_fp32_tiled_amd as dft
 
-    if width > 100:  # a store: modelled with the read geometry of its width
-        width -= 100
-    if width < 0:  # ds_read2_b32: two 4-byte accesses, one per address; report the worse
-        banks, group = geom[1]
-        return max(dft.gemm_lds_conflict_degree(words, 1, banks, group),
-                   dft.gemm_lds_conflict_degree([w - width for w in words], 1, banks, group))
-    banks, group = geom[width]
-    return dft.gemm_lds_conflict_degree(words, width, banks, group)
-
-
-def measured_degree(cycles_per_instr: float, width: int, waves: int, geom, issue_floor: float) -> int:
-    """Conflict degree implied by a timing.  An instruction occupies the LDS
-    for (64 / lanes per pass) passes of one cycle per unit of degree, and
-    `waves` wavefronts share it, so cycles = waves * passes * degree unless
-    that is below the issue floor (the time of a broadcast read), where every
-    degree-1 access lands."""
-    if cycles_per_instr < 1.1 * issue_floor:
-        return 1
-    width = width - 100 if width > 100 else width
-    passes = 64 // geom[width][1] if width > 0 else 2 * (64 // geom[1][1])
-    return max(1, round(cycles_per_instr / (waves * passes)))
-
-
-def fit(rows, waves):
-    """Patterns whose measured degree equals each geometry's prediction."""
-    floor = next(r["cycles_per_instr_per_wave"] for r in rows if r["pattern"] == "b32 stride 0")
-    score = {}
-    for g, geom in GEOMETRIES.items():
-        score[g] = sum(1 for r in rows
-                       if measured_degree(r["cycles_per_instr_per_wave"], r.get("mode", r["width_bytes"] // 4), waves,
-                                          geom, floor)
-                       == r["predicted_degree"][g])
-    return score
+    return max(ISSUE_FLOOR[mode], dft.gemm_lds_access_cycles(words, mode))
 
 
 def xcc_map(blocks: int = 512, threads: int = 512):
@@ -273,6 +271,8 @@ def run(reps: int = 2000, waves: int = 4, variants=()):
         pats += kernel_patterns(v)
     for name, width, words in pats:
         arr = (ctypes.c_int32 * 64)(*words)
+        if max(words) + 4 + (-width if width < 0 else 0) > LDS_PROBE_WORDS:
+            continue  # beyond the probe's LDS buffer (tiles of the largest kernels)
         st = lib.lds_probe_run(arr, width, waves, reps, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise RuntimeError(f"lds_probe_run failed ({st}) for {name}")
@@ -280,9 +280,28 @@ def run(reps: int = 2000, waves: int = 4, variants=()):
         cyc = out[:waves].cpu().tolist()
         per_instr = max(cyc) / (reps * 16)
         rows.append({"pattern": name, "width_bytes": 4 * (width % 100) if width > 0 else 8, "mode": width,
-                     "cycles_per_instr_per_wave": per_instr,
-                     "predicted_degree": {g: predicted(words, width, v) for g, v in GEOMETRIES.items()}})
+                     "words": list(words), "cycles_per_instr_per_wave": per_instr,
+                     "cycles_per_instr": per_instr / waves,  # the waves share the LDS
+                     "model_cycles": model_cycles(words, width)})
     return rows
+
+
+def unique_patterns(rows):
+    """Rows whose (mode, words) differ only by a whole number of 64-dword
+    lines share bank behaviour: keep the first of each (its name, the median
+    timing, how many there were)."""
+    import statistics
+
+    groups = {}
+    for r in rows:
+        base = (min(r["words"]) // 64) * 64
+        groups.setdefault((r["mode"], tuple(w - base for w in r["words"])), []).append(r)
+    out = []
+    for (mode, words), rs in groups.items():
+        out.append({"pattern": rs[0]["pattern"], "count": len(rs), "mode": mode, "words": list(words),
+                    "cycles_per_instr": round(statistics.median(x["cycles_per_instr"] for x in rs), 3),
+                    "model_cycles": rs[0]["model_cycles"]})
+    return out
 
 
 def main(argv=None) -> int:
@@ -327,28 +346,34 @@ def main(argv=None) -> int:
         return 0
     import dense_fp32_tiled_amd as dft
 
-    variants = (dft.VARIANT_MFMA, dft.VARIANT_MFMA16, dft.VARIANT_MFMA_128_BK32) if args.kernels else ()
-    rows = run(args.reps, args.waves, variants)
-    lines = [f"# LDS probe: {args.waves} waves x {args.reps} x 16 reads per pattern; cycles per instruction per wave",
-             "pattern | bytes/lane | cycles/instr | " + " | ".join(f"degree[{g}]" for g in GEOMETRIES)]
+    variants = [v for v in range(1, dft.VARIANT_COUNT)
+                if dft.gemm_f32_tile_config(v)["mfma_block"] > 0] if args.kernels else ()
+    rows = unique_patterns(run(args.reps, args.waves, variants))
+    lines = ["# command: python -m dense_fp32_tiled_amd.lds_probe" + (" --kernels" if args.kernels else "") +
+             " --out <file>",
+             f"# LDS probe: {args.waves} waves x {args.reps} x 16 accesses per pattern; patterns that differ only "
+             "by a whole number of 64-dword lines are timed once (count = how many the run had)",
+             "# cycles per instruction of the LDS (per wave / waves); model = gemm_lds_access_cycles or the "
+             "issue floor, whichever is larger",
+             "pattern | count | mode | LDS cycles/instr | model"]
     for r in rows:
-        lines.append(f"{r['pattern']} | {r['width_bytes']} | {r['cycles_per_instr_per_wave']:.2f} | " +
-                     " | ".join(str(r["predicted_degree"][g]) for g in GEOMETRIES))
+        lines.append(f"{r['pattern']} | {r['count']} | {r['mode']} | {r['cycles_per_instr']:.2f} | "
+                     f"{r['model_cycles']:.1f}")
     if args.xcc:
         ids = xcc_map()
         rr = sum(1 for b, x in enumerate(ids) if x == b % 8)
         lines.append("")
         lines.append(f"XCD of workgroups 0..{len(ids) - 1} (512 threads each): {ids[:32]} ...")
         lines.append(f"workgroups with XCD == index % 8: {rr} of {len(ids)}")
-    score = fit(rows, args.waves)
+    close = [r for r in rows if abs(r["model_cycles"] - r["cycles_per_instr"]) <= 0.15 * r["cycles_per_instr"]]
     lines.append("")
-    lines.append("patterns whose timing matches the predicted degree (of %d):" % len(rows))
-    for g, ok in score.items():
-        lines.append(f"  {g}: {ok}")
+    lines.append(f"patterns the bank model times within 15 %: {len(close)} of {len(rows)} "
+                 f"({sum(r['count'] for r in close)} of {sum(r['count'] for r in rows)} counting repeats)")
+    lines.append("not within 15 %: " + "; ".join(r["pattern"] for r in rows if r not in close))
     text = "\n".join(lines)
     print(text)
     if args.out:
-        Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+        Path(args.out).write_text(text + "\n\n" + json.dumps(rows, separators=(",", ":")) + "\n")
     return 0
 
 
