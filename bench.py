@@ -374,7 +374,8 @@ def main(argv=None) -> int:
         if args.splits >= 0:
             resolved = dft.gemm_f32_splitk_auto_variant() if variant == dft.VARIANT_AUTO else variant
         elif variant == dft.VARIANT_AUTO:
-            resolved = dft.gemm_f32_auto_variant(M, N, K, cus)
+            # the library's own choice for these operands: packed rows (lda = K, ldb = N) on aligned bases
+            resolved = dft.gemm_f32_auto_variant_ex(M, N, K, cus, K % 4 == 0, N % 4 == 0)
         else:
             resolved = variant
         tile = dft.gemm_f32_tile_config(resolved)

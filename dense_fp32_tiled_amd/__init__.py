@@ -52,7 +52,8 @@ VARIANT_MFMA_64_KS4 = 20
 VARIANT_MFMA_32x64_KS4 = 21
 VARIANT_MFMA_32x32_KS8 = 22
 VARIANT_MFMA_64_BK32_PIPE = 23
-VARIANT_COUNT = 24
+VARIANT_MFMA_64_KS2 = 24
+VARIANT_COUNT = 25
 # 16-bit inputs with fp32 accumulation (gemm_mixed_f32)
 INPUT_BF16 = 0
 INPUT_F16 = 1
@@ -98,6 +99,7 @@ VARIANT_NAMES = {
     VARIANT_MFMA_32x64_KS4: "mfma_32x64_ks4",
     VARIANT_MFMA_32x32_KS8: "mfma_32x32_ks8",
     VARIANT_MFMA_64_BK32_PIPE: "mfma_64_bk32_pipe",
+    VARIANT_MFMA_64_KS2: "mfma_64_ks2",
 }
 
 # Every symbol the public header declares.

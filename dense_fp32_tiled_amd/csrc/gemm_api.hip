@@ -150,6 +150,8 @@ template <int VEC, int VEC_B = VEC>
 using Mfma32x64Ks4 = KsplitCfg<Mfma32x64Direct<VEC, VEC_B>, 4>;
 template <int VEC, int VEC_B = VEC>
 using Mfma32x32Ks8 = KsplitCfg<Mfma32x32Direct<VEC, VEC_B>, 8>;
+template <int VEC, int VEC_B>
+using Mfma64Ks2 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 2>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -278,6 +280,7 @@ const Variant kVariants[GEMM_VARIANT_COUNT] = {
     /* MFMA_32x64_KS4         */ ksplit_variant<Mfma32x64Ks4>(),
     /* MFMA_32x32_KS8         */ ksplit_variant<Mfma32x32Ks8>(),
     /* MFMA_64_BK32_PIPE      */ mfma_variant_per_operand<Mfma64Bk32Pipe>(),
+    /* MFMA_64_KS2            */ ksplit_variant<Mfma64Ks2>(),
 };
 
 // AUTO picks the direct-copy variant with the highest estimated rate: its
@@ -324,6 +327,11 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4, 1024},
         {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 512},
         {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 512},
+        // Two groups: two waves per SIMD on a one-round 64x64 grid.  Measured
+        // 6 % ahead of the 64x64x32 kernel with neither operand's rows
+        // aligned (1000 x 999 x 513), 3 % behind with both (1024^2 x 512),
+        // 10 % behind on multi-round grids.
+        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {101.0, 94.0, 100.0, 91.0}, false, 16 * 32 * 2, 512},
     };
     const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;

@@ -97,7 +97,8 @@ typedef enum {
     GEMM_VARIANT_MFMA_32x64_KS4 = 21, /* 32x64x32 tile, 4 groups of 2 waves */
     GEMM_VARIANT_MFMA_32x32_KS8 = 22, /* 32x32x32 tile, 8 groups of 1 wave */
     GEMM_VARIANT_MFMA_64_BK32_PIPE = 23, /* as MFMA_64_BK32_DIRECT with the pipelined multiply */
-    GEMM_VARIANT_COUNT = 24
+    GEMM_VARIANT_MFMA_64_KS2 = 24,    /* 64x64x32 tile, K split over 2 groups of 4 waves (two waves per SIMD) */
+    GEMM_VARIANT_COUNT = 25
 } gemm_variant;
 
 /* Tile geometry of one variant.  The LDS tiles follow the layout of
@@ -291,7 +292,10 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
  * aligned 134, 140, 124, 120; only B aligned 133, 130, 130, 128; neither
  * 130, 121, 118, 110; for MFMA_64_KS4, MFMA_32x64_KS4 and MFMA_32x32_KS8
  * (both aligned 117, 101, 96 as above) only A aligned 108, 79, 66; only B
- * aligned 110, 95, 81; neither 103, 76, 63.  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
+ * aligned 110, 95, 81; neither 103, 76, 63; MFMA_64_KS2 (from K >= 1024, or
+ * K >= 512 when its grid has at most num_cus tiles) 101, 94, 100, 91: it
+ * wins only with neither operand aligned, in one round of tiles (1000 x 999
+ * x 513: 58 TFLOP/s against 55 for the 64x64x32 kernel).  GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
  * the operands' actual alignment.  gemm_f32_auto_variant is this
  * with both flags set.  Pure host call. */
 int gemm_f32_auto_variant_ex(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t a_rows_aligned,

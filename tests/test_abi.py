@@ -210,7 +210,10 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
     assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_PIPE
-    assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 58 against 55
+    assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(1000, 999, 1025, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4      # 73 against 73 (KS2) and 65
+    assert ax(2000, 1999, 1025, 256, 0, 0) != dft.VARIANT_MFMA_64_KS2     # multi-round: no two-group split
     assert ax(-1, 4, 4, 256, 1, 1) == dft.GEMM_ERR_INVALID_DIM
 
 

@@ -30,7 +30,7 @@ ALL_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIAN
                 dft.VARIANT_MFMA_256x256_W4_DIRECT, dft.VARIANT_MFMA_256x256_PIPE, dft.VARIANT_MFMA_256x256_BK32_PIPE,
     dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE, dft.VARIANT_MFMA_64_BK32_DIRECT,
     dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8,
-    dft.VARIANT_MFMA_64_BK32_PIPE]
+    dft.VARIANT_MFMA_64_BK32_PIPE, dft.VARIANT_MFMA_64_KS2]
 VARIANT_IDS = [dft.VARIANT_NAMES[v] for v in ALL_VARIANTS]
 
 
@@ -164,7 +164,8 @@ EDGE_SHAPES = [
 EDGE_VARIANTS = [dft.VARIANT_MFMA, dft.VARIANT_VALU, dft.VARIANT_MFMA_STAGES1, dft.VARIANT_MFMA16,
                  dft.VARIANT_MFMA_128, dft.VARIANT_MFMA_128_BK32, dft.VARIANT_MFMA_DIRECT,
                  dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT, dft.VARIANT_MFMA_64_DIRECT, dft.VARIANT_MFMA_64_BK32_DIRECT,
-                 dft.VARIANT_MFMA_256x256_DIRECT] + [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
+                 dft.VARIANT_MFMA_256x256_DIRECT] + [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8,
+                                                     dft.VARIANT_MFMA_64_KS2]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
@@ -249,7 +250,8 @@ def test_four_byte_direct_copies(K, pad, offset, variant, torch_gpu):
     assert np.array_equal(c.astype(np.float64), cref)
 
 
-KSPLIT_VARIANTS = [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8]
+KSPLIT_VARIANTS = [dft.VARIANT_MFMA_64_KS4, dft.VARIANT_MFMA_32x64_KS4, dft.VARIANT_MFMA_32x32_KS8,
+                   dft.VARIANT_MFMA_64_KS2]
 PER_OPERAND_VARIANTS = [dft.VARIANT_AUTO, dft.VARIANT_MFMA_256x256_BK32_PIPE, dft.VARIANT_MFMA_DIRECT,
                         dft.VARIANT_MFMA_128_DIRECT, dft.VARIANT_MFMA_128_BK32_DIRECT,
                         dft.VARIANT_MFMA_64_BK32_DIRECT] + KSPLIT_VARIANTS
