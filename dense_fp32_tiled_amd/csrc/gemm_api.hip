@@ -326,7 +326,9 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         // grids of two or more rounds at K = 1024-2048.
         {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4, 1024},
         {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 512},
-        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 512},
+        // (32x32 KS8 from K = 256 on a one-round grid: at 256^3 5.3 TFLOP/s
+        // against 3.7 for the 64x64 kernel.)
+        {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 256},
         // Two groups: two waves per SIMD on a one-round 64x64 grid.  Measured
         // 6 % ahead of the 64x64x32 kernel with neither operand's rows
         // aligned (1000 x 999 x 513), 3 % behind with both (1024^2 x 512),
@@ -756,14 +758,18 @@ int mixed_auto_variant(int64_t M, int64_t N, int64_t K, int num_cus) {
     };
     Candidate candidates[6];
     int n = 0;
-    // The K split over four groups from K = 4096, or from K = 1024 when its
-    // grid has at most one tile per CU (bf16 on one box: 32x64_KS4 11-25 %
-    // ahead of the previous pick on 1-2k-row grids at K = 1024-3072).
-    if (K >= 4096 || (K >= 1024 && t64 <= num_cus))
+    // The K split over four groups from K = 4096, or when its grid has at
+    // most one tile per CU from K = 1024 for 32x64 tiles and K = 2048 for
+    // 64x64 (bf16 on one box: 32x64_KS4 11-25 % ahead of the previous pick
+    // on 1-2k-row grids at K = 1024-3072; at 1024^3 64x64_KS4 ran 10 %
+    // behind 64x64_KS2, four K tiles of 64 per group being too few).  Two
+    // groups from K = 2048, or K = 1024 on a one-round grid.
+    if (K >= 4096 || (K >= 2048 && t64 <= num_cus))
         candidates[n++] = {GEMM_MIXED_64x64_KS4, 420.0 * round_fill(t64, num_cus)};
     if (K >= 4096 || (K >= 1024 && t32x64 <= num_cus))
         candidates[n++] = {GEMM_MIXED_32x64_KS4, 290.0 * round_fill(t32x64, num_cus)};
-    if (K >= 2048) candidates[n++] = {GEMM_MIXED_64x64_KS2, 530.0 * std::min(1.0, 0.6 * w64)};
+    if (K >= 2048 || (K >= 1024 && t64 <= num_cus))
+        candidates[n++] = {GEMM_MIXED_64x64_KS2, 530.0 * std::min(1.0, 0.6 * w64)};
     candidates[n++] = {GEMM_MIXED_64x64, 700.0 * std::min(1.0, 0.375 * w64)};
     candidates[n++] = {GEMM_MIXED_128x128_BK64, 1050.0 * e128};
     candidates[n++] = {big, 1.1 * 1200.0 * e256};

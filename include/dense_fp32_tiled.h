@@ -269,7 +269,8 @@ const char *gemm_f32_status_string(int status);
  * MFMA_64_BK32_DIRECT); when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
  * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup; when the
  * split's grid has at most num_cus tiles, already from K >= 1024 for
- * MFMA_64_KS4 and K >= 512 for the other two).  Estimate:
+ * MFMA_64_KS4, K >= 512 for MFMA_32x64_KS4 and K >= 256 for
+ * MFMA_32x32_KS8).  Estimate:
  * the rate times the wave quantisation of the tile grid,
  * tiles / (ceil(tiles / num_cus) * num_cus); times 0.88 for the 256x128 and
  * 128x128 kernels with fewer tiles than two per CU (they are built for two
@@ -426,9 +427,10 @@ int gemm_mixed_tile_config(int variant, gemm_tile_config *out);
  * 256x256_S3 (with 16- or 4-byte copies alike).  When 256x256 tiles number at least num_cus / 2: 128x128_BK64
  * if 1050 * e128 > 1.1 * 1200 * e256, else big.  Otherwise the highest of
  * these estimates (listed first wins within 2 %): 64x64_KS4 420 * e64 and
- * 32x64_KS4 290 * e32x64, each when K >= 4096, or when K >= 1024 and its
- * grid has at most num_cus tiles; 64x64_KS2 530 * min(1, 0.6 w)
- * when K >= 2048; 64x64 700 * min(1, 0.375 w); 128x128_BK64 1050 * e128;
+ * 32x64_KS4 290 * e32x64, each when K >= 4096, or when its grid has at most
+ * num_cus tiles and K >= 2048 (64x64) or K >= 1024 (32x64); 64x64_KS2
+ * 530 * min(1, 0.6 w) when K >= 2048, or K >= 1024 with at most num_cus
+ * 64x64 tiles; 64x64 700 * min(1, 0.375 w); 128x128_BK64 1050 * e128;
  * big 1.1 * 1200 * e256 (w: 64x64 tiles per CU).  Pure host call;
  * GEMM_ERR_INVALID_DIM for negative sizes or num_cus < 1. */
 int gemm_mixed_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);

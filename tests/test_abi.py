@@ -181,6 +181,7 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(1000, 1000, 2000, 256) == dft.VARIANT_MFMA_64_KS4          # 92 against 87
     # and from K = 512 for the smaller split tiles
     assert av(512, 512, 512, 256) == dft.VARIANT_MFMA_32x32_KS8          # 28 against 17
+    assert av(256, 256, 256, 256) == dft.VARIANT_MFMA_32x32_KS8          # 5.3 against 3.7
     assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
     assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
     assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # no smaller split in one round
@@ -393,4 +394,5 @@ def test_mixed_auto_variant(gemm_lib):
     assert av(1024, 1024, 3072, 256) == dft.MIXED_64x64_KS4     # 331 against 305
     assert av(1536, 768, 2048, 256) == dft.MIXED_64x64_KS2      # 288 tiles of 64x64: no four-group split
     assert av(512, 512, 512, 256) == dft.MIXED_64x64
+    assert av(1024, 1024, 1024, 256) == dft.MIXED_64x64_KS2     # 266 against 240 for 64x64_KS4
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
