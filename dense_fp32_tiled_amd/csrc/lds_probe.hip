@@ -207,6 +207,48 @@ __global__ __launch_bounds__(1024) void valu_fma_probe_kernel(int reps, float x,
     if (sum != sum && never_written) never_written[blockIdx.x * blockDim.x + threadIdx.x] = sum;  // NaN only
 }
 
+// Matrix-pipe throughput of v_mfma_f32_32x32x2_f32 (4096 flops per wave
+// instruction): every wave runs reps x 16 MFMAs round-robin over 4
+// independent 32x32 accumulators, with no memory access in the loop, and
+// reports the shader-clock cycles its loop took.  ACC_AGPR keeps the
+// accumulators in AGPRs (inline asm with the "a" constraint, the register
+// file the compiler uses for accumulators beyond 256 registers a lane);
+// otherwise the compiler's builtin keeps them in VGPRs.  The results are
+// stored only under a condition that the data never meets.
+template <bool ACC_AGPR>
+__global__ __launch_bounds__(1024) void mfma_probe_kernel(int reps, float x, float y, uint64_t* cycles_out,
+                                                          float* never_written) {
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const float a = x + (float)(threadIdx.x % 7), b = y;
+    const uint64_t t0 = clock64();
+    for (int r = 0; r < reps; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (ACC_AGPR) {
+                asm volatile(
+                    "v_mfma_f32_32x32x2_f32 %0, %4, %5, %0\n\t"
+                    "v_mfma_f32_32x32x2_f32 %1, %4, %5, %1\n\t"
+                    "v_mfma_f32_32x32x2_f32 %2, %4, %5, %2\n\t"
+                    "v_mfma_f32_32x32x2_f32 %3, %4, %5, %3"
+                    : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+                    : "v"(a), "v"(b));
+            } else {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c3, 0, 0, 0);
+            }
+        }
+    }
+    const uint64_t t1 = clock64();
+    if (threadIdx.x % 64 == 0) cycles_out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = t1 - t0;
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c0[i] + c1[i] + c2[i] + c3[i];
+    if (sum != sum && never_written) never_written[blockIdx.x * blockDim.x + threadIdx.x] = sum;  // NaN only
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
                                                        int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
@@ -267,6 +309,23 @@ extern "C" int probe_valu_fma(int32_t blocks, int32_t waves, int32_t reps, uint6
     void* args[] = {&rp, &x, &y, &cycles_out, &never_written};
     return hipLaunchKernel(reinterpret_cast<const void*>(valu_fma_probe_kernel), dim3((unsigned)blocks),
                            dim3((unsigned)(64 * waves)), args, 0, (hipStream_t)stream) == hipSuccess
+               ? 0
+               : -2;
+}
+
+extern "C" int probe_mfma_f32(int32_t blocks, int32_t waves, int32_t reps, int32_t acc_agpr, uint64_t* cycles_out,
+                              void* stream) {
+    if (cycles_out == nullptr || blocks < 1 || blocks > 4096 || waves < 1 || waves > 16 || reps < 1 ||
+        reps > 1000000 || (acc_agpr != 0 && acc_agpr != 1))
+        return -1;
+    int rp = reps;
+    float x = 0.5f, y = 0.25f;  // finite products: the store below never happens
+    float* never_written = nullptr;
+    void* args[] = {&rp, &x, &y, &cycles_out, &never_written};
+    const void* kernel = acc_agpr ? reinterpret_cast<const void*>(mfma_probe_kernel<true>)
+                                  : reinterpret_cast<const void*>(mfma_probe_kernel<false>);
+    return hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), args, 0,
+                           (hipStream_t)stream) == hipSuccess
                ? 0
                : -2;
 }

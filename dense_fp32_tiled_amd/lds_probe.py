@@ -47,6 +47,9 @@ def load():
     lib.probe_dma_throughput.restype = ctypes.c_int
     lib.probe_valu_fma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_valu_fma.restype = ctypes.c_int
+    lib.probe_mfma_f32.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.probe_mfma_f32.restype = ctypes.c_int
     return lib
 
 
@@ -68,6 +71,58 @@ def valu_fma_throughput(reps: int = 20000, blocks: int = 256, waves_list=(4, 8, 
         ipc = (waves / 4) * reps * 64 / worst  # per SIMD
         rows.append({"waves_per_cu": waves, "cycles": worst, "fma_instr_per_cycle_per_simd": ipc,
                      "cycles_per_fma_instr": 1.0 / ipc, "tflops_at_2400mhz_256cu": ipc * 64 * 2 * 1024 * 2.4e9 / 1e12})
+    return rows
+
+
+def mfma_throughput(reps: int = 4000, blocks: int = 256, waves_list=(4, 8, 16)):
+    """v_mfma_f32_32x32x2_f32 instructions per cycle per SIMD (one workgroup
+    per CU, its waves spread over the CU's 4 SIMDs), accumulators in VGPRs
+    and in AGPRs, and the fp32 rate that implies at 2.4 GHz on 256 CUs."""
+    import torch
+
+    lib = load()
+    out = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    rows = []
+    for agpr in (0, 1):
+        for waves in waves_list:
+            st = lib.probe_mfma_f32(blocks, waves, reps, agpr, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"probe_mfma_f32 failed ({st}), {waves} waves")
+            torch.cuda.synchronize()
+            worst = max(out[:blocks * waves].cpu().tolist())
+            ipc = (waves / 4) * reps * 16 / worst  # per SIMD
+            rows.append({"accumulators": "AGPR" if agpr else "VGPR", "waves_per_cu": waves, "cycles": worst,
+                         "mfma_instr_per_cycle_per_simd": ipc, "cycles_per_mfma_instr": 1.0 / ipc,
+                         "tflops_at_2400mhz_256cu": ipc * 4096 * 1024 * 2.4e9 / 1e12})
+    return rows
+
+
+def platform_gemm(shapes=((4096, 4096, 4096), (8192, 8192, 8192)), reps: int = 20):
+    """Context only, not part of the library: the platform's own GEMM
+    (torch.matmul on the GPU, fp32 with TF32 off, then bf16 inputs) timed
+    with HIP events over `reps` launches after 5 untimed ones."""
+    import torch
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    rows = []
+    for dtype in (torch.float32, torch.bfloat16):
+        for M, N, K in shapes:
+            g = torch.Generator(device="cuda").manual_seed(M + N + K)
+            a = torch.rand(M, K, device="cuda", dtype=torch.float32, generator=g).to(dtype)
+            b = torch.rand(K, N, device="cuda", dtype=torch.float32, generator=g).to(dtype)
+            for _ in range(5):
+                torch.matmul(a, b)
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(reps):
+                torch.matmul(a, b)
+            stop.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(stop) / reps
+            rows.append({"dtype": str(dtype).replace("torch.", ""), "shape": f"{M}x{N}x{K}", "ms": ms,
+                         "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12})
+            del a, b
     return rows
 
 
@@ -316,7 +371,40 @@ def main(argv=None) -> int:
                     help="time the direct global->LDS copies instead (probe_dma_throughput, one workgroup per CU)")
     ap.add_argument("--valu", action="store_true",
                     help="time the vector ALU's v_fmac_f32 instead (probe_valu_fma, one workgroup per CU)")
+    ap.add_argument("--mfma", action="store_true",
+                    help="time the matrix pipe's v_mfma_f32_32x32x2_f32 instead (probe_mfma_f32, one workgroup per CU)")
+    ap.add_argument("--platform-gemm", action="store_true",
+                    help="time torch.matmul (fp32 with TF32 off, and bf16) at 4096^3 and 8192^3, for context")
     args = ap.parse_args(argv)
+    if args.mfma:
+        rows = mfma_throughput()
+        lines = ["# command: python -m dense_fp32_tiled_amd.lds_probe --mfma --out <file>",
+                 "# v_mfma_f32_32x32x2_f32 throughput: 256 workgroups (one per CU), each wave 4000 x 16 MFMAs on "
+                 "4 independent accumulators, register operands; worst wave",
+                 "accumulators | waves per CU | cycles | MFMA instructions per cycle per SIMD | "
+                 "cycles per instruction | fp32 TFLOP/s at 2.4 GHz, 256 CUs"]
+        for r in rows:
+            lines.append(f"{r['accumulators']} | {r['waves_per_cu']} | {r['cycles']} | "
+                         f"{r['mfma_instr_per_cycle_per_simd']:.4f} | {r['cycles_per_mfma_instr']:.2f} | "
+                         f"{r['tflops_at_2400mhz_256cu']:.1f}")
+        text = "\n".join(lines)
+        print(text)
+        if args.out:
+            Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+        return 0
+    if args.platform_gemm:
+        rows = platform_gemm()
+        lines = ["# command: python -m dense_fp32_tiled_amd.lds_probe --platform-gemm --out <file>",
+                 "# torch.matmul on the GPU (context only; not part of the library), TF32 off; 20 timed launches "
+                 "after 5 untimed, HIP events",
+                 "dtype | M x N x K | ms per launch | TFLOP/s"]
+        for r in rows:
+            lines.append(f"{r['dtype']} | {r['shape']} | {r['ms']:.4f} | {r['tflops']:.1f}")
+        text = "\n".join(lines)
+        print(text)
+        if args.out:
+            Path(args.out).write_text(text + "\n\n" + json.dumps(rows) + "\n")
+        return 0
     if args.valu:
         rows = valu_fma_throughput()
         lines = ["# v_fmac_f32 throughput: 256 workgroups (one per CU), each lane 20000 x 64 FMAs on 8 independent "

@@ -87,6 +87,20 @@ int probe_dma_throughput(const void *src, int64_t src_bytes, int32_t bytes_per_l
 int probe_valu_fma(int32_t blocks, int32_t waves, int32_t reps, uint64_t *cycles_out, void *stream);
 
 /*
+ * Throughput of the matrix pipe on v_mfma_f32_32x32x2_f32 (2*32*32*2 = 4096
+ * flops per wave instruction) with register operands: `blocks` workgroups of
+ * `waves` wavefronts; every wave runs reps x 16 MFMAs over 4 independent
+ * accumulators with no memory access, and writes the shader-clock cycles of
+ * its loop to cycles_out[block * waves + wave] (DEVICE buffer of
+ * blocks * waves uint64, owned by the caller).  acc_agpr = 1 keeps the
+ * accumulators in AGPRs, 0 in VGPRs.  blocks 1..4096, waves 1..16, reps
+ * 1..1000000.  Returns 0, -1 for invalid arguments (nothing is launched),
+ * -2 if the launch failed.  Asynchronous.
+ */
+int probe_mfma_f32(int32_t blocks, int32_t waves, int32_t reps, int32_t acc_agpr, uint64_t *cycles_out,
+                   void *stream);
+
+/*
  * Reference kernel for calibrating the HBM traffic counters: dst[i] = src[i]
  * for i < n, 16-byte loads and stores, grid-stride.  It reads and writes
  * exactly 4*n bytes.  src and dst are DEVICE pointers owned by the caller,

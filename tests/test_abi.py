@@ -31,7 +31,8 @@ def test_probe_library_exports_its_header(gemm_lib):
     from dense_fp32_tiled_amd import lds_probe
 
     assert declared_functions(PROBE_HEADER) == {"lds_probe_run", "probe_copy_f32", "probe_xcc_ids",
-                                                "probe_dma_throughput", "probe_valu_fma"}
+                                                "probe_dma_throughput", "probe_valu_fma",
+                                                "probe_mfma_f32"}
     assert declared_functions(PROBE_HEADER) <= exported(lds_probe.PROBE_LIB)
 
 
