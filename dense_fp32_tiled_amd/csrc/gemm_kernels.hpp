@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "lds_layout.hpp"
 
@@ -525,10 +526,21 @@ __device__ inline void wait_vector_memory_at_most() {
 // and wholly in range (a uniform branch), else under the mask.  For a fixed
 // result register, the MB lanes of a k-group write consecutive floats of one
 // row.
+// f(std::integral_constant<int, I>{}) for I = 0, 1, ..., N - 1, in order.
+template <class F, int... I>
+__device__ inline void static_for_each(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ inline void static_for(F&& f) {
+    static_for_each(f, std::make_integer_sequence<int, N>{});
+}
+
 template <class Op, int BM, int BN, int MI, int NI>
 __device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t ma,
                                           int64_t na, int64_t m0, int64_t n0, int wm0, int wn0, int lane,
-                                          const typename Op::acc_t (&acc)[MI][NI]) {
+                                          const typename Op::acc_t (&acc)[MI][NI], int j_lo = 0,
+                                          int j_hi = MI * NI * Op::ACC) {
     const int r = lane % Op::MB;
     const bool full = ma == m0 && na == n0 && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
@@ -540,6 +552,8 @@ __device__ inline void store_accumulators(float* __restrict__ C, int64_t ldc, in
             float* cp = C + gm0 * ldc + gn;
 #pragma unroll
             for (int v = 0; v < Op::ACC; ++v) {
+                const int j = (i * NI + n) * Op::ACC + v;  // flat index of the value
+                if (j < j_lo || j >= j_hi) continue;
                 const int dr = Op::out_row(lane, v);
                 if (full || (gm0 + dr >= m0 && gm0 + dr < M && gn >= n0 && gn < N)) cp[dr * ldc] = acc[i][n][v];
             }
@@ -896,11 +910,16 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
 // the current one).  A grid of few output tiles (deep K, small M and N) then
 // still runs several waves per SIMD, without a workspace.  Every group runs
 // ceil(T / KSPLIT) iterations (a group past its last tile skips the
-// multiply), so all waves reach every barrier.  At the end groups 1 ..
-// KSPLIT-1 leave their partial sums in LDS; wave w of every group holds the
-// same outputs in the same lanes and registers, so they are written and read
-// back in lane order.  Group 0 adds them in group order (a fixed order: the
-// result is deterministic) and stores C.
+// multiply), so all waves reach every barrier.  A ragged last K tile goes
+// through registers, stored to LDS after the multiply of the group's
+// previous tile (its global loads issued before that multiply where the
+// registers allow), and its multiply runs only the MFMA steps that hold
+// in-range columns.  At the end wave w of
+// every group holds the same outputs in the same lanes and registers; group
+// q owns the q-th of KSPLIT equal slices of those values.  Each group leaves
+// the other groups' slices in LDS, in lane order, and after a barrier adds
+// the others' partial sums for its own slice in group order (a fixed order:
+// the result is deterministic) and stores that slice of C.
 template <class Base, int KSPLIT_>
 struct KsplitCfg {
     static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2 && !Base::PIPE,
@@ -915,15 +934,22 @@ struct KsplitCfg {
     static constexpr int GROUP_THREADS = Base::THREADS, GROUP_WAVES = GROUP_THREADS / kWave;
     static constexpr int THREADS = GROUP_THREADS * KSPLIT;
     static constexpr int STAGES = 2 * KSPLIT;  // stages 2q, 2q+1 belong to group q
-    static constexpr int MIN_WAVES = Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES : THREADS / 256;
+    // Two groups of 256 threads: kept within 128 registers, so that two
+    // workgroups share a CU on grids of more tiles than CUs.
+    static constexpr int MIN_WAVES = THREADS == 512 && KSPLIT == 2 ? 4
+                                     : Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES
+                                                                       : THREADS / 256;
     using TileA = LdsTile<BM, BK, 0, STAGES, Base::TileA::swizzle.unit, Base::TileA::swizzle.shift,
                           Base::TileA::swizzle.mask>;
     using TileB = LdsTile<BK, BN, 0, STAGES, Base::TileB::swizzle.unit, Base::TileB::swizzle.shift,
                           Base::TileB::swizzle.mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
-    // partial sums of groups 1 .. KSPLIT-1, over the stages' LDS
+    // Exchanged partial sums, over the stages' LDS: slice p of group q's
+    // values (q != p) for every wave, KSPLIT x KSPLIT regions in all.
     static constexpr int PARTIAL_VALUES = MI * NI * Op::ACC;  // per lane
-    static_assert((KSPLIT - 1) * GROUP_WAVES * PARTIAL_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
+    static constexpr int SLICE_VALUES = PARTIAL_VALUES / KSPLIT;
+    static_assert(PARTIAL_VALUES % KSPLIT == 0, "the groups' slices are equal");
+    static_assert(KSPLIT * KSPLIT * GROUP_WAVES * SLICE_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
                   "the partial sums fit in the stages");
 };
 
@@ -977,7 +1003,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
     const float* b_tile = B + n0;
     const int64_t T = K > 0 ? (K + BK - 1) / BK : 0;  // K tiles
     const int64_t TF = K / BK;                        // K tiles wholly in range
-    const int64_t ITERS = (T + KS - 1) / KS;          // per group
+    const int64_t ITERS = (TF + KS - 1) / KS;         // per group, over whole tiles
 
     constexpr bool READ_FIRST = Cfg::VEC != Cfg::VEC_B;
     using DA = DirectCopy<TileA, GT, float, 4 * Cfg::VEC, READ_FIRST>;
@@ -992,14 +1018,18 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
         dma_a.issue(a_tile + t * BK, lds_a, stage);
         dma_b.issue(b_tile + t * BK * ldb, lds_b, stage);
     };
-    auto copy_registers = [&](int64_t t, int stage) {
+    auto load_registers = [&](int64_t t) {
         const int64_t k0 = t * BK;
         ldr_a.load(a_tile + k0, lda, M - m0, K - k0, gtid);
         ldr_b.load(b_tile + k0 * ldb, ldb, K - k0, N - n0, gtid);
+    };
+    auto store_registers = [&](int stage) {
         ldr_a.template store<TileA>(lds_a, stage, gtid);
         ldr_b.template store<TileB>(lds_b, stage, gtid);
     };
-    auto multiply = [&](int stage) {
+    // MFMA step j takes k = j + KG g in lane group g, so a tile with only
+    // `steps` columns in range needs steps j < min(steps, KG).
+    auto multiply = [&](int stage, int steps) {
         floatx4 af[MI][KG / 4];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -1009,22 +1039,30 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
                     lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, g * KG + 4 * q));
 #pragma unroll
         for (int j = 0; j < KG; ++j) {
-            float bf[NI];
+            if (j < steps) {  // uniform; constant true for whole tiles
+                float bf[NI];
 #pragma unroll
-            for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, g * KG + j, wn0 + n * Op::NB + r)];
+                for (int n = 0; n < NI; ++n) bf[n] = lds_b[TileB::offset(stage, g * KG + j, wn0 + n * Op::NB + r)];
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[n], acc[i][n]);
+                    for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[n], acc[i][n]);
+            }
         }
     };
+    const int tail_steps = (int)(K - TF * BK) < KG ? (int)(K - TF * BK) : KG;  // the ragged tile's steps
+    // Registers to hold a staged tile across the multiply: 512 threads (a
+    // 256-register budget) and at most 16 values per thread per tile.
+    constexpr bool HOIST = Cfg::THREADS <= 512 && GT >= 256;
 
     const int stage0 = 2 * group;
     if (group < T) {
-        if (interior && group < TF)
+        if (interior && group < TF) {
             copy_direct(group, stage0);
-        else
-            copy_registers(group, stage0);
+        } else {
+            load_registers(group);
+            store_registers(stage0);
+        }
     }
     wait_vector_memory();
     __syncthreads();
@@ -1032,39 +1070,69 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
         const int s = stage0 + (int)(it & 1), ns = stage0 + (int)((it & 1) ^ 1);
         const int64_t t = it * KS + group, tn = t + KS;
         const bool direct = interior && tn < TF;
+        const bool staged = tn < T && !direct;  // tile tn through registers, around the multiply
         if (direct) copy_direct(tn, ns);
-        if (t < T) multiply(s);
-        if (tn < T && !direct) copy_registers(tn, ns);
+        if (HOIST && staged) load_registers(tn);
+        if (t < TF) multiply(s, KG);
+        if (staged) {
+            if (!HOIST) load_registers(tn);
+            store_registers(ns);
+        }
         wait_vector_memory();
         __syncthreads();
     }
+    // The ragged last tile TF belongs to group TF % KS, which stored it into
+    // the stage after its last whole tile's (its first stage if it has none)
+    // and has not written that stage since.
+    if (T > TF) {
+        if (group == (int)(TF % KS)) multiply(stage0 + (int)(((TF - group) / KS) & 1), tail_steps);
+        __syncthreads();
+    }
 
-    // Every LDS read of the loop completed before its last barrier.
-    constexpr int PV = Cfg::PARTIAL_VALUES;
-    if (group > 0) {
-        float* dst = lds + ((group - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
-        int j = 0;
+    // Every LDS read of the loop and of the ragged tile completed before the
+    // last barrier.  Region (p, q): group q's partial sums of group p's
+    // slice, one float per lane per value.  Each group runs its own copy of
+    // the exchange (P = its index), so every register and LDS offset in it
+    // is a constant.
+    constexpr int SV = Cfg::SLICE_VALUES, GW = Cfg::GROUP_WAVES;
+    float* const exch = lds + wave * SV * kWave + lane;
+    auto region = [&](int p, int q) { return exch + (p * KS + q) * GW * SV * kWave; };
+    auto for_each_group = [&](auto&& body) {
+        static_for<KS>([&](auto P_) {
+            if (group == decltype(P_)::value) body(P_);
+        });
+    };
+    for_each_group([&](auto P_) {
+        constexpr int P = decltype(P_)::value;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int n = 0; n < NI; ++n)
 #pragma unroll
-                for (int v = 0; v < Op::ACC; ++v) dst[(j++) * kWave] = acc[i][n][v];
-    }
+                for (int v = 0; v < Op::ACC; ++v) {
+                    const int j = (i * NI + n) * Op::ACC + v;
+                    if (j / SV != P) region(j / SV, P)[(j % SV) * kWave] = acc[i][n][v];
+                }
+    });
     __syncthreads();
-    if (group == 0) {
-        for (int q = 1; q < KS; ++q) {
-            const float* src = lds + ((q - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
-            int j = 0;
+    for_each_group([&](auto P_) {
+        constexpr int P = decltype(P_)::value;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            if (q == P) continue;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int n = 0; n < NI; ++n)
 #pragma unroll
-                    for (int v = 0; v < Op::ACC; ++v) acc[i][n][v] += src[(j++) * kWave];
+                    for (int v = 0; v < Op::ACC; ++v) {
+                        const int j = (i * NI + n) * Op::ACC + v;
+                        if (j / SV == P) acc[i][n][v] += region(P, q)[(j % SV) * kWave];
+                    }
         }
-        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
-    }
+        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc, P * SV,
+                                               P * SV + SV);
+    });
 }
 
 // --------------------------------------------------------------------------

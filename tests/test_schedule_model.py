@@ -6,7 +6,11 @@ Each wavefront runs a list of events on a ring of LDS stages:
 * ("w", s, t): synchronous store of its piece of K tile t into stage s
   (the register path: global load, then LDS store);
 * ("wall", s, t): synchronous store over the whole stage s (every piece:
-  data laid out without regard to the stages' pieces, like partial sums);
+  data laid out without regard to the stages' pieces);
+* ("wx", s, label): synchronous store of this wave's partial sums into its
+  piece of region s, laid out over the stage's bytes without regard to its
+  pieces: the other pieces' tile data is clobbered (other waves' partial
+  sums in the region are kept);
 * ("issue", s, t): an asynchronous direct copy of its piece of tile t into
   stage s; the write lands at any later moment the model chooses;
 * ("wait", t): block until none of this wave's copies of tiles <= t is still
@@ -78,9 +82,12 @@ def check(programs, stages: int):
             kind = ev[0]
             if kind == "b":
                 continue
-            if kind in ("w", "wall"):
+            if kind in ("w", "wall", "wx"):
                 c = [list(row) for row in content]
                 if kind == "w":
+                    c[ev[1]][v] = ev[2]
+                elif kind == "wx":
+                    c[ev[1]] = [x if isinstance(x, str) else "clobbered" for x in c[ev[1]]]
                     c[ev[1]][v] = ev[2]
                 else:
                     c[ev[1]] = [ev[2]] * waves
@@ -174,59 +181,75 @@ def ring(T, S, weak_wait=False):
     return ev
 
 
-def ksplit(T, groups, per_group, wave, drop_final_barrier=False, early_partials=False):
+def ksplit_stages(groups):
+    """Model stages of the K-split kernel: 2 per group, and the exchange
+    regions (p, q) at index p * groups + q, over the working stages where
+    they overlap them in LDS."""
+    return max(2 * groups, groups * groups)
+
+
+def ksplit(TF, tail, groups, per_group, wave, drop_final_barrier=False, early_partials=False):
     """The K-split kernel, as wave `wave` runs it: group q (per_group waves)
-    takes K tiles q, q + groups, ... through its own stages 2q and 2q + 1
-    (two-stage direct copies), every group running ceil(T / groups)
-    iterations and every barrier; then groups 1.. write their partial sums
-    over the LDS (group q's over all of stage q - 1, which another group
-    used), and
-    after a barrier group 0 reads them back (wave w of group 0 reads wave w
-    of each other group)."""
+    takes K tiles q, q + groups, ... through its own stages 2q and 2q + 1;
+    the TF whole tiles by direct copies, a ragged last tile (tail) through
+    registers, stored after the multiply of the group's previous tile.
+    Every group runs ceil(T / groups) iterations and every barrier.  Then
+    each group writes its partial sums of every other group p's slice to
+    region (p, q) (over the stages: index p * groups + q), a barrier, and
+    each group reads the regions of its own slice (wave w reads wave w of
+    each other group)."""
+    T = TF + (1 if tail else 0)
     q, w = divmod(wave, per_group)
     members = [q * per_group + i for i in range(per_group)]
     ev = []
-    if q < T:
+    if q < TF:
         ev.append(("issue", 2 * q, q))
+    elif q < T:
+        ev.append(("w", 2 * q, q))
     ev += [("wait", None), ("b",)]
     iters = (T + groups - 1) // groups
     for it in range(iters):
         s, ns = 2 * q + it % 2, 2 * q + 1 - it % 2
         t, tn = it * groups + q, it * groups + q + groups
-        if tn < T:
+        if tn < TF:
             ev.append(("issue", ns, tn))
         if t < T:
             ev.append(("r", s, t, members))
+        if TF <= tn < T:
+            ev.append(("w", ns, tn))
         ev.append(("wait", None))
         if not (early_partials and it == iters - 1):
             ev.append(("b",))
-    if q > 0:
-        ev.append(("wall", q - 1, f"P{q}"))
+    for p in range(groups):
+        if p != q:
+            ev.append(("wx", p * groups + q, f"P{p}{q}"))
     if early_partials:
         ev.append(("b",))
     if not drop_final_barrier:
         ev.append(("b",))
-    if q == 0:
-        for g in range(1, groups):
-            ev.append(("r", g - 1, f"P{g}", [g * per_group + w]))
+    for g in range(groups):
+        if g != q:
+            ev.append(("r", q * groups + g, f"P{q}{g}", [g * per_group + w]))
     return ev
 
 
-def ksplit_programs(T, groups, per_group, **kw):
-    return [ksplit(T, groups, per_group, v, **kw) for v in range(groups * per_group)]
+def ksplit_programs(TF, tail, groups, per_group, **kw):
+    return [ksplit(TF, tail, groups, per_group, v, **kw) for v in range(groups * per_group)]
 
 
-@pytest.mark.parametrize("T", [1, 3, 4, 5])
+@pytest.mark.parametrize("TF,tail", [(0, True), (1, False), (2, True), (3, False), (3, True), (4, True),
+                                     (5, False)])
 @pytest.mark.parametrize("groups,per_group", [(2, 1), (2, 2), (3, 1)])
-def test_k_split_protocol_is_race_free(T, groups, per_group):
-    assert check(ksplit_programs(T, groups, per_group), 2 * groups) is None
+def test_k_split_protocol_is_race_free(TF, tail, groups, per_group):
+    assert check(ksplit_programs(TF, tail, groups, per_group), ksplit_stages(groups)) is None
 
 
 @pytest.mark.parametrize("mutant", ["drop_final_barrier", "early_partials"])
 def test_k_split_mutant_is_caught(mutant):
-    # T = 5 with 2 groups: group 0's last tile (4) is in its stage 0, the
-    # stage group 1's partial sums overwrite
-    assert check(ksplit_programs(5, 2, 1, **{mutant: True}), 4) is not None
+    # two whole tiles and a tail with 2 groups: group 0 reads the tail from its
+    # stage 1 in the last iteration, where group 1's partial sums of group 0's
+    # slice go
+    assert check(ksplit_programs(2, True, 2, 1, **{mutant: True}), ksplit_stages(2)) is not None
 
 
 CORRECT = [
