@@ -144,14 +144,17 @@ template <int VEC, int VEC_B = VEC>
 using Mfma32x32Direct = MfmaCfg<32, 32, 32, 32, 32, 2, 32, layouts::m32_32x32x32_direct::A,
                                 layouts::m32_32x32x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
                                 VEC_B == VEC ? 0 : VEC_B>;
+// The K-split variants issue the next tile's copies between the first 8 of
+// a tile's 16 MFMA steps (a wave's MFMAs form one dependent chain, which
+// leaves it issue slots while each runs) instead of all before the first.
 template <int VEC, int VEC_B = VEC>
-using Mfma64Ks4 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 4>;
+using Mfma64Ks4 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 4, 8>;
 template <int VEC, int VEC_B = VEC>
-using Mfma32x64Ks4 = KsplitCfg<Mfma32x64Direct<VEC, VEC_B>, 4>;
+using Mfma32x64Ks4 = KsplitCfg<Mfma32x64Direct<VEC, VEC_B>, 4, 8>;
 template <int VEC, int VEC_B = VEC>
-using Mfma32x32Ks8 = KsplitCfg<Mfma32x32Direct<VEC, VEC_B>, 8>;
+using Mfma32x32Ks8 = KsplitCfg<Mfma32x32Direct<VEC, VEC_B>, 8, 8>;
 template <int VEC, int VEC_B>
-using Mfma64Ks2 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 2>;
+using Mfma64Ks2 = KsplitCfg<Mfma64Bk32Direct<VEC, VEC_B>, 2, 8>;
 template <int VEC>
 using Mfma128 = MfmaAt<std::conditional_t<VEC == 4, layouts::m32_128x128x16_v4, layouts::m32_128x128x16_v1>,
                        2, VEC, 128, 128, 16, 32>;
@@ -330,10 +333,10 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         // against 3.7 for the 64x64 kernel.)
         {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 256},
         // Two groups: two waves per SIMD on a one-round 64x64 grid.  Measured
-        // 6 % ahead of the 64x64x32 kernel with neither operand's rows
-        // aligned (1000 x 999 x 513), 3 % behind with both (1024^2 x 512),
-        // 10 % behind on multi-round grids.
-        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {101.0, 94.0, 100.0, 91.0}, false, 16 * 32 * 2, 512},
+        // ahead of the 64x64x32 kernel on one-round grids (1000 x 999 x 513
+        // with neither operand's rows aligned, 1024^2 x 512 with both),
+        // behind it on multi-round grids.
+        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {109.0, 102.0, 108.0, 99.0}, false, 16 * 32 * 2, 512},
     };
     const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;

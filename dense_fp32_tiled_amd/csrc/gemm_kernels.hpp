@@ -489,17 +489,20 @@ struct DirectCopy {
     // Requires fits(ld).
     template <class W>
     __device__ void issue(const T* origin, W* lds, int stage) const {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) issue_one(origin, lds, stage, i);
+    }
+    // Copy i (0 <= i < PER_WAVE, a constant after unrolling) of those.
+    template <class W>
+    __device__ void issue_one(const T* origin, W* lds, int stage, int i) const {
         static_assert(sizeof(W) == 4, "LDS tiles are addressed in 4-byte words");
         typedef __attribute__((address_space(3))) W lds_word;
         const uint32_t base = (uint32_t)(uintptr_t)(lds_word*)lds + lds_piece + stage * (Tile::stage_elems * 4);
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const T* row_base = STRIDED ? origin + i * round_stride : origin;
-            if constexpr (BYTES == 16)
-                copy16_to_lds<READ_FIRST>(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
-            else
-                copy4_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
-        }
+        const T* row_base = STRIDED ? origin + i * round_stride : origin;
+        if constexpr (BYTES == 16)
+            copy16_to_lds<READ_FIRST>(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
+        else
+            copy4_to_lds(row_base, STRIDED ? off[0] : off[i], base + i * (WAVES * PIECE * 4));
     }
 };
 
@@ -920,7 +923,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
 // the other groups' slices in LDS, in lane order, and after a barrier adds
 // the others' partial sums for its own slice in group order (a fixed order:
 // the result is deterministic) and stores that slice of C.
-template <class Base, int KSPLIT_>
+template <class Base, int KSPLIT_, int COPY_STEPS_ = 0>
 struct KsplitCfg {
     static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2 && !Base::PIPE,
                   "groups run Base's two-stage direct-copy loop");
@@ -933,12 +936,9 @@ struct KsplitCfg {
     static constexpr int WAVES_N = Base::WAVES_N, MI = Base::MI, NI = Base::NI, KG = Base::KG;
     static constexpr int GROUP_THREADS = Base::THREADS, GROUP_WAVES = GROUP_THREADS / kWave;
     static constexpr int THREADS = GROUP_THREADS * KSPLIT;
+    static constexpr int COPY_STEPS = COPY_STEPS_;
     static constexpr int STAGES = 2 * KSPLIT;  // stages 2q, 2q+1 belong to group q
-    // Two groups of 256 threads: kept within 128 registers, so that two
-    // workgroups share a CU on grids of more tiles than CUs.
-    static constexpr int MIN_WAVES = THREADS == 512 && KSPLIT == 2 ? 4
-                                     : Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES
-                                                                       : THREADS / 256;
+    static constexpr int MIN_WAVES = Base::MIN_WAVES > THREADS / 256 ? Base::MIN_WAVES : THREADS / 256;
     using TileA = LdsTile<BM, BK, 0, STAGES, Base::TileA::swizzle.unit, Base::TileA::swizzle.shift,
                           Base::TileA::swizzle.mask>;
     using TileB = LdsTile<BK, BN, 0, STAGES, Base::TileB::swizzle.unit, Base::TileB::swizzle.shift,
@@ -1050,6 +1050,49 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
             }
         }
     };
+    // The next tile's direct copies issued between the MFMA steps of the
+    // current one, within the first COPY_STEPS steps (0: all before the
+    // multiply).
+    constexpr int COPY_STEPS = Cfg::COPY_STEPS;
+    constexpr int PC = DA::PER_WAVE + DB::PER_WAVE;
+    auto multiply_copy = [&](int stage, int64_t tn, int nstage, bool copy) {
+        const float* a_src = a_tile + tn * BK;
+        const float* b_src = b_tile + tn * BK * ldb;
+        floatx4 af[MI][KG / 4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int q = 0; q < KG / 4; ++q)
+                af[i][q] = *reinterpret_cast<const floatx4*>(
+                    lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, g * KG + 4 * q));
+        // B of step j + 1 is read before step j's copies (the copies are
+        // ordered with every memory access), so it lands during step j.
+        float bf[2][NI];
+#pragma unroll
+        for (int n = 0; n < NI; ++n) bf[0][n] = lds_b[TileB::offset(stage, g * KG, wn0 + n * Op::NB + r)];
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+            if (j + 1 < KG) {
+#pragma unroll
+                for (int n = 0; n < NI; ++n)
+                    bf[(j + 1) % 2][n] = lds_b[TileB::offset(stage, g * KG + j + 1, wn0 + n * Op::NB + r)];
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int n = 0; n < NI; ++n) acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[j % 2][n], acc[i][n]);
+            if (j < COPY_STEPS && copy) {
+#pragma unroll
+                for (int p = j * PC / (COPY_STEPS > 0 ? COPY_STEPS : 1);
+                     p < (j + 1) * PC / (COPY_STEPS > 0 ? COPY_STEPS : 1); ++p) {
+                    if (p < DA::PER_WAVE)
+                        dma_a.issue_one(a_src, lds_a, nstage, p);
+                    else
+                        dma_b.issue_one(b_src, lds_b, nstage, p - DA::PER_WAVE);
+                }
+            }
+        }
+    };
     const int tail_steps = (int)(K - TF * BK) < KG ? (int)(K - TF * BK) : KG;  // the ragged tile's steps
     // Registers to hold a staged tile across the multiply: 512 threads (a
     // 256-register budget) and at most 16 values per thread per tile.
@@ -1071,9 +1114,14 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_ksplit
         const int64_t t = it * KS + group, tn = t + KS;
         const bool direct = interior && tn < TF;
         const bool staged = tn < T && !direct;  // tile tn through registers, around the multiply
-        if (direct) copy_direct(tn, ns);
-        if (HOIST && staged) load_registers(tn);
-        if (t < TF) multiply(s, KG);
+        if constexpr (COPY_STEPS > 0) {
+            if (HOIST && staged) load_registers(tn);
+            if (t < TF) multiply_copy(s, tn, ns, direct);  // direct implies t < TF
+        } else {
+            if (direct) copy_direct(tn, ns);
+            if (HOIST && staged) load_registers(tn);
+            if (t < TF) multiply(s, KG);
+        }
         if (staged) {
             if (!HOIST) load_registers(tn);
             store_registers(ns);

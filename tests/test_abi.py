@@ -144,7 +144,7 @@ def test_auto_variant_selection(gemm_lib):
     assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 108 (plain 64x64: 112)
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE   # 512 tiles of 64x64: 111 vs 109 plain
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4  # deep K, 128 tiles of 64x64: split K
-    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_KS2  # one round of 64x64 tiles: two groups
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
     assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
     assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 240 tiles of 256x256
@@ -173,9 +173,11 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(256, 256, 65536, 256) == dft.VARIANT_MFMA_32x32_KS8
     # enough tiles, or too short a K: no split
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
-    assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # split 56 against 59
+    # one round of 64x64 tiles from K = 512: two groups (1024^2 x 512: 77 against 75)
+    assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_KS2
+    assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_KS2
+    assert av(1024, 1024, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # too short a K for two groups
     # from K = 1024 when the split's grid has at most one tile per CU
     assert av(512, 512, 1024, 256) == dft.VARIANT_MFMA_32x32_KS8         # 43 against 22
     assert av(1000, 512, 1024, 256) == dft.VARIANT_MFMA_32x64_KS4        # 62 against 42
@@ -185,7 +187,7 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(256, 256, 256, 256) == dft.VARIANT_MFMA_32x32_KS8          # 5.3 against 3.7
     assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
     assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
-    assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # no smaller split in one round
+    assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_KS2
     assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE         # two rounds: split 44 against 51
     assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE
     # a deep K still splits over several rounds of tiles
@@ -212,9 +214,9 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
     assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_PIPE
-    assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 58 against 55
-    assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert ax(1000, 999, 1025, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4      # 73 against 73 (KS2) and 65
+    assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 62 against 53
+    assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_KS2
+    assert ax(1000, 999, 1025, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4      # 71 against 74 (KS2) and 60
     assert ax(2000, 1999, 1025, 256, 0, 0) != dft.VARIANT_MFMA_64_KS2     # multi-round: no two-group split
     assert ax(-1, 4, 4, 256, 1, 1) == dft.GEMM_ERR_INVALID_DIM
 

@@ -188,7 +188,7 @@ def ksplit_stages(groups):
     return max(2 * groups, groups * groups)
 
 
-def ksplit(TF, tail, groups, per_group, wave, drop_final_barrier=False, early_partials=False):
+def ksplit(TF, tail, groups, per_group, wave, drop_final_barrier=False, early_partials=False, copy_late=False):
     """The K-split kernel, as wave `wave` runs it: group q (per_group waves)
     takes K tiles q, q + groups, ... through its own stages 2q and 2q + 1;
     the TF whole tiles by direct copies, a ragged last tile (tail) through
@@ -197,7 +197,9 @@ def ksplit(TF, tail, groups, per_group, wave, drop_final_barrier=False, early_pa
     each group writes its partial sums of every other group p's slice to
     region (p, q) (over the stages: index p * groups + q), a barrier, and
     each group reads the regions of its own slice (wave w reads wave w of
-    each other group)."""
+    each other group).  The next tile's copies are issued between the MFMA
+    steps of the current one: modelled at both ends, before the stage read
+    or (copy_late) after it."""
     T = TF + (1 if tail else 0)
     q, w = divmod(wave, per_group)
     members = [q * per_group + i for i in range(per_group)]
@@ -211,10 +213,12 @@ def ksplit(TF, tail, groups, per_group, wave, drop_final_barrier=False, early_pa
     for it in range(iters):
         s, ns = 2 * q + it % 2, 2 * q + 1 - it % 2
         t, tn = it * groups + q, it * groups + q + groups
-        if tn < TF:
+        if tn < TF and not copy_late:
             ev.append(("issue", ns, tn))
         if t < T:
             ev.append(("r", s, t, members))
+        if tn < TF and copy_late:
+            ev.append(("issue", ns, tn))
         if TF <= tn < T:
             ev.append(("w", ns, tn))
         ev.append(("wait", None))
@@ -240,8 +244,10 @@ def ksplit_programs(TF, tail, groups, per_group, **kw):
 @pytest.mark.parametrize("TF,tail", [(0, True), (1, False), (2, True), (3, False), (3, True), (4, True),
                                      (5, False)])
 @pytest.mark.parametrize("groups,per_group", [(2, 1), (2, 2), (3, 1)])
-def test_k_split_protocol_is_race_free(TF, tail, groups, per_group):
-    assert check(ksplit_programs(TF, tail, groups, per_group), ksplit_stages(groups)) is None
+@pytest.mark.parametrize("copy_late", [False, True])
+def test_k_split_protocol_is_race_free(TF, tail, groups, per_group, copy_late):
+    programs = ksplit_programs(TF, tail, groups, per_group, copy_late=copy_late)
+    assert check(programs, ksplit_stages(groups)) is None
 
 
 @pytest.mark.parametrize("mutant", ["drop_final_barrier", "early_partials"])
