@@ -124,16 +124,20 @@ using Mfma64Direct = MfmaCfg<64, 64, 16, 32, 32, 2, 32, layouts::m32_64x64x16_di
                              layouts::m32_64x64x16_direct::B, VEC, kXcdGroupedOrder, kLoadDirect>;
 // BK = 32 halves the barriers per k of the 64x64 tile (one per 16 MFMAs per
 // wave instead of 8).  Its 4-byte form runs at 2 waves per SIMD (16 staged
-// floats per thread on edge tiles).
+// floats per thread on edge tiles).  The next tile's copies go out between
+// the first 8 of its 16 MFMA steps (a wave's MFMAs form one dependent
+// chain, which leaves it issue slots while each runs).  (The default
+// 256x256 kernel keeps its copies before the first step: spread, they
+// split its straight-line K tile for no measurable gain.)
 template <int VEC, int VEC_B = VEC>
 using Mfma64Bk32Direct = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
                                  layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, false,
-                                 VEC_B == VEC ? 0 : VEC_B>;
+                                 VEC_B == VEC ? 0 : VEC_B, 8>;
 // The 64x64x32 tile with the pipelined multiply.
 template <int VEC, int VEC_B = VEC>
 using Mfma64Bk32Pipe = MfmaCfg<64, 64, 32, 32, 32, 2, 32, layouts::m32_64x64x32_direct::A,
                                layouts::m32_64x64x32_direct::B, VEC, kXcdGroupedOrder, kLoadDirect, true,
-                               VEC_B == VEC ? 0 : VEC_B>;
+                               VEC_B == VEC ? 0 : VEC_B, 8>;
 // Bases of the K-split variants (KsplitCfg): 32x64 and 32x32 tiles of
 // 32x32-wave blocks, BK = 32.
 template <int VEC, int VEC_B = VEC>
@@ -309,17 +313,14 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         int64_t min_k;    // K-split variants: enough K tiles for every group (0: any K)
         int64_t min_k_one_round;  // the same when the grid has at most one tile per CU
     };
-    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     const Candidate candidates[] = {
         {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0, 0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0, 0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
          {144.0, 124.0, 130.0, 118.0}, false, 0, 0},
-        // 64x64x32: the pipelined multiply when the grid has more than one
-        // tile per CU (2-9 % ahead on multi-round grids), else the plain one
-        // (1-3 % ahead in a single round).
-        {t64 > num_cus ? GEMM_VARIANT_MFMA_64_BK32_PIPE : GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1,
-         {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
+        // 64x64x32 with its copies between the MFMA steps: ahead of the
+        // pipelined form on one-round and multi-round grids alike.
+        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
         // K split inside the workgroup: 16 K tiles of 32 per group at
         // least; when the split's grid has at most one tile per CU, from
         // K = 1024 for 64x64 tiles and K = 512 for the smaller ones (whose

@@ -261,8 +261,12 @@ enum LoadPath { kLoadRegisters = 0, kLoadDirect = 1 };
 // multiplies, and the last chunk of tile t multiplies after the barrier,
 // while the first fragments of tile t+1 are read; the matrix pipe then idles
 // only for the barrier itself, not for the LDS latency behind it.
+// COPY_STEPS (direct copies only): the next tile's copies are issued between
+// the first COPY_STEPS MFMA steps of the current one (0: all before the
+// first step).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MB_, class LayA, class LayB, int VEC_,
-          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters, bool PIPE_ = false, int VEC_B_ = 0>
+          int ORDER_ = kRowMajorOrder, int LOAD_ = kLoadRegisters, bool PIPE_ = false, int VEC_B_ = 0,
+          int COPY_STEPS_ = 0>
 struct MfmaCfg {
     using Op = MfmaOp<MB_, 64 / MB_>;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
@@ -271,6 +275,7 @@ struct MfmaCfg {
     static constexpr int STAGES = STAGES_, VEC = VEC_, ORDER = ORDER_, LOAD = LOAD_;
     static constexpr int VEC_B = VEC_B_ ? VEC_B_ : VEC_;
     static constexpr bool PIPE = PIPE_;
+    static constexpr int COPY_STEPS = COPY_STEPS_;
     static constexpr int KSPLIT = 1;  // wave groups splitting K inside the workgroup (KsplitCfg)
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -725,6 +730,52 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
         using DB = DirectCopy<TileB, THREADS, float, 4 * Cfg::VEC_B, READ_FIRST>;
         const DA dma_a(lda, __builtin_amdgcn_readfirstlane(wave), lane);
         const DB dma_b(ldb, __builtin_amdgcn_readfirstlane(wave), lane);
+        // Pieces [CS_lo, CS_hi) of the next tile's copies, issued after MFMA
+        // step kk when COPY_STEPS > 0 (A's copies first, then B's).
+        constexpr int COPY_STEPS = Cfg::COPY_STEPS;
+        constexpr int PC = DA::PER_WAVE + DB::PER_WAVE;
+        auto issue_after_step = [&](int kk, int64_t t_next, int nstage) {
+            if constexpr (COPY_STEPS > 0) {
+                if (kk < COPY_STEPS) {
+#pragma unroll
+                    for (int p = kk * PC / COPY_STEPS; p < (kk + 1) * PC / COPY_STEPS; ++p) {
+                        if (p < DA::PER_WAVE)
+                            dma_a.issue_one(a_tile + t_next * BK, lds_a, nstage, p);
+                        else
+                            dma_b.issue_one(b_tile + t_next * BK * ldb, lds_b, nstage, p - DA::PER_WAVE);
+                    }
+                }
+            }
+        };
+        // The multiply with those copies between its steps; B of step j + 1
+        // is read before step j's copies (the copies are ordered with every
+        // memory access), so it lands during step j.
+        auto multiply_spread = [&](int stage, int64_t t_next, int nstage, bool copy) {
+            floatx4 af[MI][KG / 4];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int q = 0; q < KG / 4; ++q)
+                    af[i][q] = *reinterpret_cast<const floatx4*>(
+                        lds_a + TileA::offset(stage, wm0 + i * Op::MB + r, g * KG + 4 * q));
+            float bf[2][NI];
+#pragma unroll
+            for (int n = 0; n < NI; ++n) bf[0][n] = lds_b[TileB::offset(stage, g * KG, wn0 + n * Op::NB + r)];
+#pragma unroll
+            for (int j = 0; j < KG; ++j) {
+                if (j + 1 < KG) {
+#pragma unroll
+                    for (int n = 0; n < NI; ++n)
+                        bf[(j + 1) % 2][n] = lds_b[TileB::offset(stage, g * KG + j + 1, wn0 + n * Op::NB + r)];
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int n = 0; n < NI; ++n)
+                        acc[i][n] = Op::mma(af[i][j / 4][j % 4], bf[j % 2][n], acc[i][n]);
+                if (copy) issue_after_step(j, t_next, nstage);
+            }
+        };
         // A's tiles are wholly in range when the workgroup's rows are (but for
         // a ragged last K tile), B's when its columns are.
         const bool rows_in = M - m0 >= BM && DA::fits(lda, A);
@@ -804,7 +855,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                 const int s = (int)(t & 1);
                 const bool more = t + 1 < T;
                 const bool direct = t < t_direct;
-                if (direct) {
+                if (direct && COPY_STEPS == 0) {
                     dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
                     dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
                 }
@@ -816,6 +867,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                     __builtin_amdgcn_sched_barrier(0);
                     mma_step(q & 1, j, kk & 1);
                     __builtin_amdgcn_sched_barrier(0);
+                    if (direct) issue_after_step(kk, t + 1, s ^ 1);
                 }
                 if (more && !direct) {
                     // Next tile through registers (zero fill), a few slots at
@@ -852,11 +904,15 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mfma_kernel
                 const int s = (int)(t & 1);
                 const bool more = t + 1 < T;
                 const bool direct = t < t_direct;
-                if (direct) {
-                    dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
-                    dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+                if constexpr (COPY_STEPS > 0) {
+                    multiply_spread(s, t + 1, s ^ 1, direct);
+                } else {
+                    if (direct) {
+                        dma_a.issue(a_tile + (t + 1) * BK, lds_a, s ^ 1);
+                        dma_b.issue(b_tile + (t + 1) * BK * ldb, lds_b, s ^ 1);
+                    }
+                    multiply(s);
                 }
-                multiply(s);
                 if (more && !direct) {
                     load_tile(t + 1);
                     ldr_a.template store<TileA>(lds_a, s ^ 1, tid);

@@ -140,19 +140,19 @@ def test_auto_variant_selection(gemm_lib):
     assert av(4096, 2048, 4096, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 512 tiles of 128x128: two per CU
     assert av(8192, 1024, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 256 tiles of 256x128: one per CU
     assert av(6144, 6144, 2048, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2304 tiles: 9 full rounds
-    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 1024 of 64x64 vs 256 of 128x128: 126 vs 121
-    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 108 (plain 64x64: 112)
-    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE   # 512 tiles of 64x64: 111 vs 109 plain
+    assert av(2048, 2048, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT  # 1024 tiles of 64x64 against 256 of 128x128
+    assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # 512 tiles of 64x64: 131 against 114 pipelined
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4  # deep K, 128 tiles of 64x64: split K
     assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_KS2  # one round of 64x64 tiles: two groups
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
-    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
+    assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 240 tiles of 256x256
     assert av(6000, 6000, 6000, 256) == dft.VARIANT_MFMA_128_BK32_DIRECT  # 2209 tiles in 9 rounds
     assert av(4095, 4095, 4095, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE
-    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_PIPE  # 6400 tiles: 25 full rounds, 135
+    assert av(5120, 5120, 5120, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT  # 6400 tiles: 25 full rounds
     # a dimension below the tile: every workgroup of the big kernels is an edge one
-    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
+    assert av(200, 8192, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(4096, 4096, 2048, 4096) == dft.VARIANT_MFMA_64_KS4  # many more CUs than big tiles
     assert av(-1, 4, 4, 256) == dft.GEMM_ERR_INVALID_DIM
     assert av(4, 4, 4, 0) == dft.GEMM_ERR_INVALID_DIM
@@ -172,7 +172,7 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(512, 512, 16384, 256) == dft.VARIANT_MFMA_32x32_KS8    # 94 against 27
     assert av(256, 256, 65536, 256) == dft.VARIANT_MFMA_32x32_KS8
     # enough tiles, or too short a K: no split
-    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_PIPE
+    assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # one round of 64x64 tiles from K = 512: two groups (1024^2 x 512: 77 against 75)
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_KS2
@@ -188,8 +188,8 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
     assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
     assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_KS2
-    assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE         # two rounds: split 44 against 51
-    assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_PIPE
+    assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT         # two rounds: split 44 against 51
+    assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # a deep K still splits over several rounds of tiles
     assert av(768, 768, 8192, 256) == dft.VARIANT_MFMA_32x32_KS8         # 68 against 57
     # unaligned operands (odd K: A's rows; odd N: B's), measured per alignment class
@@ -213,7 +213,7 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(4095, 4095, 4095, 256, 0, 0) == dft.VARIANT_MFMA_256x256_BK32_PIPE
     assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
-    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_PIPE
+    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 62 against 53
     assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_KS2
     assert ax(1000, 999, 1025, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4      # 71 against 74 (KS2) and 60

@@ -47,7 +47,7 @@ def test_default_mfma_tile_is_straight_line(functions):
     _, funcs = functions
     # 256x256x32, 8 waves of 128x64: 4 x 2 blocks x 16 steps = 128 MFMAs per K tile
     default = [b for n, b in funcs.items()
-               if "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E" in n and "EEELi4ELi1ELi1ELb1ELi0EE" in n]
+               if "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E" in n and "EEELi4ELi1ELi1ELb1ELi0ELi0EE" in n]
     assert len(default) == 1
     assert max_per_block(default[0], r"^\s+v_mfma_f32_32x32x2_f32") >= 128 - 8
 

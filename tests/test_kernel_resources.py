@@ -32,19 +32,19 @@ def test_every_kernel_is_spill_free(report):
 def test_default_kernels_keep_their_occupancy(report):
     # fp32 256x256x32 pipelined kernel (AUTO for large problems): one 8-wave workgroup per CU, 128 KiB of LDS
     fp32_big = {k: v for k, v in kernels(report, "MfmaCfgILi256ELi256ELi32ELi128ELi64ELi2ELi32E").items()
-                if "EEELi4ELi1ELi1ELb1ELi0EE" in k}
+                if "EEELi4ELi1ELi1ELb1ELi0ELi0EE" in k}
     assert len(fp32_big) == 1
     (r,) = fp32_big.values()
     assert r["occupancy"] == 2 and r["lds"] == 128 * 1024
     # its non-pipelined 256x256x16 ablation: same occupancy, 64 KiB of LDS
     fp32_plain = kernels(report, "MfmaCfgILi256ELi256ELi16ELi128ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
-                                 "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0ELi0EE")
+                                 "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0ELi0ELi0EE")
     assert len(fp32_plain) == 1
     (r,) = fp32_plain.values()
     assert r["occupancy"] == 2 and r["lds"] == 64 * 1024
     # fp32 256x128 direct-copy kernel (AUTO when 256x256 tiles round badly): 4 waves per SIMD = two workgroups
     fp32_default = kernels(report, "MfmaCfgILi256ELi128ELi16ELi64ELi64ELi2ELi32ENS_10TileLayoutILi0ELi4ELi2ELi3EEENS2_"
-                                   "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0ELi0EE")
+                                   "ILi0ELi0ELi0ELi0EEELi4ELi1ELi1ELb0ELi0ELi0EE")
     assert len(fp32_default) == 1
     (r,) = fp32_default.values()
     assert r["occupancy"] == 4 and r["lds"] == 48 * 1024
@@ -52,8 +52,8 @@ def test_default_kernels_keep_their_occupancy(report):
     # at least 2 with 4-byte copies; 32 KiB of LDS
     fp32_small = {k: v for k, v in kernels(report, "MfmaCfgILi64ELi64ELi32ELi32ELi32ELi2ELi32E").items()
                   if "16gemm_mfma_kernel" in k}
-    vec4 = [v for k, v in fp32_small.items() if "EEELi4ELi1ELi1ELb0ELi0EE" in k]
-    vec1 = [v for k, v in fp32_small.items() if "EEELi1ELi1ELi1ELb0ELi0EE" in k]
+    vec4 = [v for k, v in fp32_small.items() if "EEELi4ELi1ELi1ELb0ELi0ELi8EE" in k]
+    vec1 = [v for k, v in fp32_small.items() if "EEELi1ELi1ELi1ELb0ELi0ELi8EE" in k]
     assert len(vec4) == 1 and len(vec1) == 1
     assert vec4[0]["occupancy"] >= 4 and vec1[0]["occupancy"] >= 2
     assert vec4[0]["lds"] == vec1[0]["lds"] == 32 * 1024
