@@ -313,14 +313,18 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         int64_t min_k;    // K-split variants: enough K tiles for every group (0: any K)
         int64_t min_k_one_round;  // the same when the grid has at most one tile per CU
     };
+    const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     const Candidate candidates[] = {
         {GEMM_VARIANT_MFMA_256x256_BK32_PIPE, 256, 256, 1, {145.0, 134.0, 133.0, 130.0}, false, 0, 0},
         {GEMM_VARIANT_MFMA_DIRECT, 256, 128, 2, {144.0, 140.0, 130.0, 121.0}, false, 0, 0},
         {K >= 1024 ? GEMM_VARIANT_MFMA_128_BK32_DIRECT : GEMM_VARIANT_MFMA_128_DIRECT, 128, 128, 2,
          {144.0, 124.0, 130.0, 118.0}, false, 0, 0},
         // 64x64x32 with its copies between the MFMA steps: ahead of the
-        // pipelined form on one-round and multi-round grids alike.
-        {GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1, {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
+        // pipelined form on one-round grids and on multi-round grids with an
+        // operand aligned; behind it (2047^3: 4 %) with neither aligned.
+        {cls == 3 && t64 > num_cus ? GEMM_VARIANT_MFMA_64_BK32_PIPE : GEMM_VARIANT_MFMA_64_BK32_DIRECT, 64, 64, 1,
+         {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
         // K split inside the workgroup: 16 K tiles of 32 per group at
         // least; when the split's grid has at most one tile per CU, from
         // K = 1024 for 64x64 tiles and K = 512 for the smaller ones (whose
@@ -334,12 +338,11 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         // against 3.7 for the 64x64 kernel.)
         {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 256},
         // Two groups: two waves per SIMD on a one-round 64x64 grid.  Measured
-        // ahead of the 64x64x32 kernel on one-round grids (1000 x 999 x 513
-        // with neither operand's rows aligned, 1024^2 x 512 with both),
-        // behind it on multi-round grids.
-        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {109.0, 102.0, 108.0, 99.0}, false, 16 * 32 * 2, 512},
+        // ahead of the 64x64x32 kernel with neither operand's rows aligned
+        // (1000 x 999 x 513: 62 against 53), behind it with both (1024^2 x
+        // 512: 78 against 82) and on multi-round grids.
+        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {101.0, 94.0, 100.0, 99.0}, false, 16 * 32 * 2, 512},
     };
-    const int cls = a_aligned ? (b_aligned ? 0 : 1) : (b_aligned ? 2 : 3);
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;
     for (const Candidate& c : candidates) {

@@ -898,9 +898,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 // K split inside the workgroup for 16-bit inputs (the fp32 KsplitCfg's
 // scheme): KSPLIT groups of waves share one output tile, group q taking K
 // tiles q, q + KSPLIT, ... through its own pair of LDS stages with Base's
-// wave tiling, direct copies and step-pipelined multiply; the groups'
-// partial sums are added in LDS in group order.  Copies of 16 bytes
-// (VEC 8) or 4 bytes (VEC 2), as the base's.
+// wave tiling, direct copies and step-pipelined multiply; group p then adds
+// the others' partial sums of its slice of the outputs in LDS, in group
+// order, and stores that slice.  Copies of 16 bytes (VEC 8) or 4 bytes
+// (VEC 2), as the base's.
 template <class Base, int KSPLIT_>
 struct MixedKsplitCfg {
     static_assert(Base::LOAD == kLoadDirect && Base::STAGES == 2, "groups run Base's two-stage direct-copy loop");
@@ -920,8 +921,12 @@ struct MixedKsplitCfg {
     using TileB = LdsTile<BK, BN / 2, 0, STAGES, Base::TileB::swizzle.unit, Base::TileB::swizzle.shift,
                           Base::TileB::swizzle.mask>;
     static constexpr int LDS_BYTES = TileA::bytes + TileB::bytes;
+    // Exchanged partial sums, over the stages' LDS: slice p of group q's
+    // values (q != p) for every wave, KSPLIT x KSPLIT regions in all.
     static constexpr int PARTIAL_VALUES = MI * NI * Op::ACC;  // per lane
-    static_assert((KSPLIT - 1) * GROUP_WAVES * PARTIAL_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
+    static constexpr int SLICE_VALUES = PARTIAL_VALUES / KSPLIT;
+    static_assert(PARTIAL_VALUES % KSPLIT == 0, "the groups' slices are equal");
+    static_assert(KSPLIT * KSPLIT * GROUP_WAVES * SLICE_VALUES * kWave <= TileA::total_elems + TileB::total_elems,
                   "the partial sums fit in the stages");
 };
 
@@ -1055,33 +1060,49 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kspli
         __syncthreads();
     }
 
-    // Every LDS read of the loop completed before its last barrier.
-    constexpr int PV = Cfg::PARTIAL_VALUES;
-    float* const part = reinterpret_cast<float*>(lds);
-    if (group > 0) {
-        float* dst = part + ((group - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
-        int j = 0;
+    // Every LDS read of the loop completed before its last barrier.  Region
+    // (p, q): group q's partial sums of group p's slice, one float per lane
+    // per value.  Each group runs its own copy of the exchange (P = its
+    // index), so every register and LDS offset in it is a constant.
+    constexpr int SV = Cfg::SLICE_VALUES, GW = Cfg::GROUP_WAVES;
+    float* const exch = reinterpret_cast<float*>(lds) + wave * SV * kWave + lane;
+    auto region = [&](int p, int q) { return exch + (p * KS + q) * GW * SV * kWave; };
+    auto for_each_group = [&](auto&& body) {
+        static_for<KS>([&](auto P_) {
+            if (group == decltype(P_)::value) body(P_);
+        });
+    };
+    for_each_group([&](auto P_) {
+        constexpr int P = decltype(P_)::value;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int n = 0; n < NI; ++n)
 #pragma unroll
-                for (int v = 0; v < Op::ACC; ++v) dst[(j++) * kWave] = acc[i][n][v];
-    }
+                for (int v = 0; v < Op::ACC; ++v) {
+                    const int j = (i * NI + n) * Op::ACC + v;
+                    if (j / SV != P) region(j / SV, P)[(j % SV) * kWave] = acc[i][n][v];
+                }
+    });
     __syncthreads();
-    if (group == 0) {
-        for (int q = 1; q < KS; ++q) {
-            const float* src = part + ((q - 1) * Cfg::GROUP_WAVES + wave) * PV * kWave + lane;
-            int j = 0;
+    for_each_group([&](auto P_) {
+        constexpr int P = decltype(P_)::value;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            if (q == P) continue;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int n = 0; n < NI; ++n)
 #pragma unroll
-                    for (int v = 0; v < Op::ACC; ++v) acc[i][n][v] += src[(j++) * kWave];
+                    for (int v = 0; v < Op::ACC; ++v) {
+                        const int j = (i * NI + n) * Op::ACC + v;
+                        if (j / SV == P) acc[i][n][v] += region(P, q)[(j % SV) * kWave];
+                    }
         }
-        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc);
-    }
+        store_accumulators<Op, BM, BN, MI, NI>(C, ldc, M, N, m0, n0, own.m0, own.n0, wm0, wn0, lane, acc, P * SV,
+                                               P * SV + SV);
+    });
 }
 
 }  // namespace dft

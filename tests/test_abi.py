@@ -144,7 +144,7 @@ def test_auto_variant_selection(gemm_lib):
     assert av(3000, 3000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # 512 tiles of 64x64: 131 against 114 pipelined
     assert av(2048, 256, 16384, 256) == dft.VARIANT_MFMA_32x64_KS4  # deep K, 128 tiles of 64x64: split K
-    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_KS2  # one round of 64x64 tiles: two groups
+    assert av(1000, 999, 513, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # ragged grids: edge tiles move back to end at M or N, so only quantisation counts
     assert av(2000, 2000, 1024, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(5000, 3000, 2000, 256) == dft.VARIANT_MFMA_256x256_BK32_PIPE  # 240 tiles of 256x256
@@ -174,10 +174,8 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     # enough tiles, or too short a K: no split
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    # one round of 64x64 tiles from K = 512: two groups (1024^2 x 512: 77 against 75)
-    assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_KS2
-    assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_KS2
-    assert av(1024, 1024, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # too short a K for two groups
+    assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT  # 84 against 81 for two groups
+    assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # from K = 1024 when the split's grid has at most one tile per CU
     assert av(512, 512, 1024, 256) == dft.VARIANT_MFMA_32x32_KS8         # 43 against 22
     assert av(1000, 512, 1024, 256) == dft.VARIANT_MFMA_32x64_KS4        # 62 against 42
@@ -187,7 +185,7 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(256, 256, 256, 256) == dft.VARIANT_MFMA_32x32_KS8          # 5.3 against 3.7
     assert av(768, 512, 768, 256) == dft.VARIANT_MFMA_32x64_KS4          # 41 against 30
     assert av(2048, 256, 512, 256) == dft.VARIANT_MFMA_32x64_KS4         # 46 against 35
-    assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_KS2
+    assert av(1024, 1024, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # 82 against 78 for two groups
     assert ax_(1500, 768, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT         # two rounds: split 44 against 51
     assert ax_(768, 1536, 1025) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # a deep K still splits over several rounds of tiles
@@ -215,7 +213,8 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
     assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 62 against 53
-    assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_KS2
+    assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(2047, 2047, 2047, 256, 0, 0) == dft.VARIANT_MFMA_64_BK32_PIPE  # neither aligned, several rounds
     assert ax(1000, 999, 1025, 256, 0, 0) == dft.VARIANT_MFMA_64_KS4      # 71 against 74 (KS2) and 60
     assert ax(2000, 1999, 1025, 256, 0, 0) != dft.VARIANT_MFMA_64_KS2     # multi-round: no two-group split
     assert ax(-1, 4, 4, 256, 1, 1) == dft.GEMM_ERR_INVALID_DIM
