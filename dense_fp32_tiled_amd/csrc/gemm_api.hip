@@ -332,16 +332,21 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
         // 64x64 KS4 measured 5-7 % under the 64x64 kernel at K = 512 on
         // 1000^2 and 1024^2 grids, and any split up to 22 % under it on
         // grids of two or more rounds at K = 1024-2048.
-        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, 108.0, 110.0, 103.0}, false, 16 * 32 * 4, 1024},
+        {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, K >= 4096 && t64 <= num_cus ? 126.0 : 108.0, 110.0, 103.0},
+         false, 16 * 32 * 4, 1024},
         {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 512},
         // (32x32 KS8 from K = 256 on a one-round grid: at 256^3 5.3 TFLOP/s
         // against 3.7 for the 64x64 kernel.)
         {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 256},
         // Two groups: two waves per SIMD on a one-round 64x64 grid.  Measured
         // ahead of the 64x64x32 kernel with neither operand's rows aligned
-        // (1000 x 999 x 513: 62 against 53), behind it with both (1024^2 x
-        // 512: 78 against 82) and on multi-round grids.
-        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {101.0, 94.0, 100.0, 99.0}, false, 16 * 32 * 2, 512},
+        // (1000 x 999 x 513: 62 against 51) and, with only B's unaligned, on
+        // one-round and multi-round grids alike (3000 x 2999 x 3000: 117
+        // against 107; 2048 x 1023 x 2048: 105 against 92); behind it with
+        // both aligned (1024^2 x 512: 78 against 83).  The four-group split
+        // keeps the one-round grids of deep K (K >= 4096) with only B's
+        // unaligned (1024 x 1023 x 4096: 102 against 101).
+        {GEMM_VARIANT_MFMA_64_KS2, 64, 64, 1, {101.0, 124.0, 100.0, 99.0}, false, 16 * 32 * 2, 512},
     };
     int best = GEMM_VARIANT_MFMA_DIRECT;
     double best_rate = -1.0;

@@ -292,11 +292,13 @@ int gemm_f32_auto_variant(int64_t M, int64_t N, int64_t K, int32_t num_cus);
  * 128x128 and 64x64x32) are, for both aligned, 145, 144, 144, 134; only A
  * aligned 134, 140, 124, 120; only B aligned 133, 130, 130, 128; neither
  * 130, 121, 118, 110; for MFMA_64_KS4, MFMA_32x64_KS4 and MFMA_32x32_KS8
- * (both aligned 117, 101, 96 as above) only A aligned 108, 79, 66; only B
+ * (both aligned 117, 101, 96 as above) only A aligned 108 (126 on a
+ * one-round grid with K >= 4096), 79, 66; only B
  * aligned 110, 95, 81; neither 103, 76, 63; MFMA_64_KS2 (from K >= 1024, or
- * K >= 512 when its grid has at most num_cus tiles) 101, 94, 100, 99: it
- * wins with neither operand aligned, in one round of tiles (1000 x 999 x
- * 513).  With neither aligned and more 64x64 tiles than CUs the 64x64x32
+ * K >= 512 when its grid has at most num_cus tiles) 101, 124, 100, 99: it
+ * wins with neither operand aligned in one round of tiles (1000 x 999 x
+ * 513), and with only A aligned on 64x64 grids of any size (3000 x 2999 x
+ * 3000).  With neither aligned and more 64x64 tiles than CUs the 64x64x32
  * candidate is MFMA_64_BK32_PIPE, else MFMA_64_BK32_DIRECT.
  * GEMM_VARIANT_AUTO in gemm_f32 / gemm_f32_ex applies this with
  * the operands' actual alignment.  gemm_f32_auto_variant is this

@@ -211,7 +211,9 @@ def test_auto_variant_by_operand_alignment(gemm_lib):
     assert ax(4095, 4095, 4095, 256, 0, 0) == dft.VARIANT_MFMA_256x256_BK32_PIPE
     assert ax(6000, 6000, 5999, 256, 0, 1) == dft.VARIANT_MFMA_128_BK32_DIRECT
     assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT
-    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert ax(3000, 2999, 3000, 256, 1, 0) == dft.VARIANT_MFMA_64_KS2   # only B unaligned: 117 against 107
+    assert ax(2048, 1023, 2048, 256, 1, 0) == dft.VARIANT_MFMA_64_KS2   # 105 against 92
+    assert ax(4096, 2047, 4096, 256, 1, 0) == dft.VARIANT_MFMA_DIRECT   # 125 against 124
     assert ax(1000, 999, 513, 256, 0, 0) == dft.VARIANT_MFMA_64_KS2      # 62 against 53
     assert ax(1000, 999, 513, 256, 1, 1) == dft.VARIANT_MFMA_64_BK32_DIRECT
     assert ax(2047, 2047, 2047, 256, 0, 0) == dft.VARIANT_MFMA_64_BK32_PIPE  # neither aligned, several rounds
