@@ -327,14 +327,17 @@ int auto_variant(int64_t M, int64_t N, int64_t K, int num_cus, bool a_aligned = 
          {134.0, 120.0, 128.0, 110.0}, true, 0, 0},
         // K split inside the workgroup: 16 K tiles of 32 per group at
         // least; when the split's grid has at most one tile per CU, from
-        // K = 1024 for 64x64 tiles and K = 512 for the smaller ones (whose
-        // one-round grids leave the 64x64 kernel half the CUs or fewer).
+        // K = 1024 for 64x64 tiles, K = 256 for 32x32 and K = 128 (one K
+        // tile per group) for 32x64, whose one-round grids leave the 64x64
+        // kernel half the CUs or fewer (2176 x 192 x 448: 43 against 33;
+        // with two rounds of 32x64 tiles the 64x64 kernel leads, 1536 x 384
+        // x 320: 40 against 29).
         // 64x64 KS4 measured 5-7 % under the 64x64 kernel at K = 512 on
         // 1000^2 and 1024^2 grids, and any split up to 22 % under it on
         // grids of two or more rounds at K = 1024-2048.
         {GEMM_VARIANT_MFMA_64_KS4, 64, 64, 1, {117.0, K >= 4096 && t64 <= num_cus ? 126.0 : 108.0, 110.0, 103.0},
          false, 16 * 32 * 4, 1024},
-        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 512},
+        {GEMM_VARIANT_MFMA_32x64_KS4, 32, 64, 1, {101.0, 79.0, 95.0, 76.0}, false, 16 * 32 * 4, 128},
         // (32x32 KS8 from K = 256 on a one-round grid: at 256^3 5.3 TFLOP/s
         // against 3.7 for the 64x64 kernel.)
         {GEMM_VARIANT_MFMA_32x32_KS8, 32, 32, 1, {96.0, 66.0, 81.0, 63.0}, false, 16 * 32 * 8, 256},

@@ -265,11 +265,11 @@ const char *gemm_f32_status_string(int status);
  * candidate with the highest rate estimate.  Candidates and full-chip rates:
  * MFMA_256x256_BK32_PIPE 145 TFLOP/s, MFMA_DIRECT (256x128) 144, the 128x128
  * direct variant (BK 32 when K >= 1024, else 16) 144, the 64x64x32 kernel
- * 134 (MFMA_64_BK32_PIPE when its grid has more than num_cus tiles, else
- * MFMA_64_BK32_DIRECT); when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
+ * 134 (MFMA_64_BK32_DIRECT; MFMA_64_BK32_PIPE when neither operand's rows
+ * are aligned and its grid has more than num_cus tiles); when K >= 2048 also MFMA_64_KS4 117 and MFMA_32x64_KS4 101, and when
  * K >= 4096 MFMA_32x32_KS8 96 (K split inside the workgroup; when the
  * split's grid has at most num_cus tiles, already from K >= 1024 for
- * MFMA_64_KS4, K >= 512 for MFMA_32x64_KS4 and K >= 256 for
+ * MFMA_64_KS4, K >= 128 for MFMA_32x64_KS4 and K >= 256 for
  * MFMA_32x32_KS8).  Estimate:
  * the rate times the wave quantisation of the tile grid,
  * tiles / (ceil(tiles / num_cus) * num_cus); times 0.88 for the 256x128 and

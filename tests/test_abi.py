@@ -173,7 +173,10 @@ def test_auto_variant_splits_k_for_few_deep_tiles(gemm_lib):
     assert av(256, 256, 65536, 256) == dft.VARIANT_MFMA_32x32_KS8
     # enough tiles, or too short a K: no split
     assert av(512, 4096, 4096, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
-    assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
+    assert av(2048, 256, 256, 256) == dft.VARIANT_MFMA_32x64_KS4    # one round of 32x64 tiles: 37 against 33
+    assert av(2176, 192, 448, 256) == dft.VARIANT_MFMA_32x64_KS4    # 43 against 33
+    assert av(1536, 384, 320, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT  # two rounds of 32x64 tiles: 40 against 29
+    assert av(2048, 256, 64, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT   # below one K tile per group
     assert av(1000, 1000, 1000, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT  # 84 against 81 for two groups
     assert av(1000, 1000, 512, 256) == dft.VARIANT_MFMA_64_BK32_DIRECT
     # from K = 1024 when the split's grid has at most one tile per CU
