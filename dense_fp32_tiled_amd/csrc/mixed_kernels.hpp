@@ -74,6 +74,21 @@ struct Mfma16Op<TYPE, 16> {
     __host__ __device__ static constexpr int col_base(int) { return 0; }
 };
 
+// Orders the scheduling region that ends here as N pairs of one MFMA then
+// one LDS read, and closes it.  Placed after a step's fragment reads for
+// the next step and its MFMAs, it spreads those reads over the MFMAs, so
+// they issue while the matrix pipe works instead of in one burst ahead of
+// it (groups left without a read stay empty).
+template <int N>
+__device__ __forceinline__ void alternate_mfma_and_lds_reads() {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // A tile of a row-major 16-bit matrix, rows [row0, row0 + ROWS) and columns
 // [col0, col0 + COLS), read under the mask (row < row_bound) & (col <
 // col_bound) with zero fill, through registers; VEC = 8 (16-byte loads, when
@@ -742,9 +757,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
 #pragma unroll
                     for (int st = 0; st + 1 < Cfg::STEPS; ++st) {
                         read_fragments(s, st + 1, af[(st + 1) & 1], bf[(st + 1) & 1]);
-                        __builtin_amdgcn_sched_barrier(0);
                         mma_step(af[st & 1], bf[st & 1]);
-                        __builtin_amdgcn_sched_barrier(0);
+                        alternate_mfma_and_lds_reads<MI * NI>();
                     }
                     if (nt < T && !direct) {
                         // ragged last K tile through registers, a few slots at a time
@@ -760,9 +774,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                         wait_vector_memory();
                     __syncthreads();
                     if (t + 1 < T) read_fragments(ns, 0, af[0], bf[0]);
-                    __builtin_amdgcn_sched_barrier(0);
                     mma_step(af[1], bf[1]);
-                    __builtin_amdgcn_sched_barrier(0);
+                    alternate_mfma_and_lds_reads<MI * NI>();
                     s = ns;
                 }
             } else {
