@@ -150,18 +150,19 @@ def free_cycles(width, store=False):
     return 64 // lanes[(width, store)]
 
 
-# 16x16x4 MFMA blocks: the four passes of an A-fragment read fetch the same 16
-# rows.  The model charges those reads twice the conflict-free cycles with
-# every candidate layout; the probe and the kernel counters time the chosen
-# layout conflict-free (the model is pessimistic there).
-MODEL_DOUBLE_A_READ = {dft.VARIANT_MFMA16, dft.VARIANT_MFMA16_256x256_DIRECT, dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE}
+# The four-wave 16x16x4 kernel's pipelined fragment addressing (a per-lane
+# base plus compile-time offsets) admits no layout whose A-fragment reads are
+# conflict-free: the model charges them twice the conflict-free cycles, and
+# the probe times them so (8 cycles against 4).
+MODEL_DOUBLE_A_READ = {dft.VARIANT_MFMA16_256x256_W4_BK32_PIPE}
 
 
 @pytest.mark.parametrize("variant", MFMA_LAYOUT_VARIANTS)
 def test_mfma_layouts_cost_what_the_model_allows(variant, gemm_lib):
     """Every fragment read and store of the chosen layouts costs the model's
     conflict-free cycles (stores under the measured store geometry), but the
-    A reads of 16x16x4 blocks (exactly twice); the plain layout costs more."""
+    A reads of the four-wave 16x16x4 kernel (exactly twice); the plain layout
+    costs more."""
     c = dft.gemm_f32_tile_config(variant)
     for w, words, store in mfma_accesses(c):
         expect = free_cycles(w, store)

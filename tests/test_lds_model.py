@@ -3,12 +3,10 @@ to what the LDS probe timed on gfx950 and to the kernels' bank-conflict
 counters (profiles/lds_probe_gfx950.txt, profiles/lds_conflicts_square4096.md).
 CPU only: the recorded timings and counters are read from those files.
 
-Known gaps, asserted as such so that a change in either direction shows:
-the 16x16x4 MFMA's A-fragment read with the layout the search picks is timed
-conflict-free but modelled 2-way (no candidate layout is conflict-free under
-the model, and the chosen one happens to be on the hardware), and six
-synthetic patterns that isolate pairs of passes cost one cycle more or less
-than modelled."""
+The lanes that share a pass of a 16-byte read are pinned to the recorded
+timings independently of the library: of the partitions of the 64 lanes into
+four passes of 16 given by two bit-parity functions of the lane index, only
+four reproduce every recorded 16-byte read, and the model's is one of them."""
 
 from __future__ import annotations
 
@@ -22,17 +20,6 @@ from dense_fp32_tiled_amd import lds_probe
 
 PROFILES = Path(__file__).resolve().parent.parent / "profiles"
 
-KNOWN_PATTERN_GAPS = {
-    "mfma16 A read w0 m0 q0",
-    "b128 rows x groups, lanes 16-31 (g = l / 16)",
-    "b128 rows x groups, lanes 0-15,32-47 (g = l / 16)",
-    "b128 rows x groups, lanes 0-7,16-23 (g = l / 16)",
-    "b128 rows x groups, lanes 0-15,48-63 (g = l / 16)",
-    "b128 passes 0 and 2 on the same quads",
-    "b128 passes 0 and 3 on the same quads",
-}
-# kernels whose counters read conflict-free where the model charges the A reads twice
-KNOWN_KERNEL_GAPS = {"mfma16", "mfma16_256x256_direct"}
 
 
 def recorded_patterns():
@@ -65,12 +52,65 @@ def test_model_reproduces_the_recorded_predictions(gemm_lib):
 def test_model_times_the_probe_patterns(gemm_lib):
     gaps = {r["pattern"] for r in recorded_patterns()
             if not close(lds_probe.model_cycles(r["words"], r["mode"]), r["cycles_per_instr"], r["mode"])}
-    assert gaps == KNOWN_PATTERN_GAPS
+    assert gaps == set()
 
 
-def test_model_names_the_mfma16_a_read_gap(gemm_lib):
+def test_model_prices_the_mfma16_a_read_conflict_free(gemm_lib):
+    """Four passes over the same 16 rows at different 16-byte columns: 2-way
+    if a pass were 16 consecutive lanes, conflict-free as timed."""
     r = next(r for r in recorded_patterns() if r["pattern"] == "mfma16 A read w0 m0 q0")
-    assert r["count"] >= 16 and r["model_cycles"] == 8.0 and r["cycles_per_instr"] < 4.5
+    assert r["count"] >= 16 and r["cycles_per_instr"] < 4.5
+    assert lds_probe.model_cycles(r["words"], r["mode"]) == 4.0
+    consecutive = sum(_degree(r["words"], range(16 * p, 16 * p + 16)) for p in range(4))
+    assert consecutive == 8
+
+
+def test_eight_byte_stores_follow_the_model(gemm_lib):
+    rows = [r for r in recorded_patterns() if r["mode"] == 102]
+    assert len(rows) >= 9
+    for r in rows:
+        assert close(lds_probe.model_cycles(r["words"], 102), r["cycles_per_instr"], 102), r["pattern"]
+
+
+def _degree(words, lanes, banks=64):
+    """Worst number of distinct dwords one bank delivers to `lanes` reading 16 bytes each."""
+    per = {}
+    for l in lanes:
+        for e in range(4):
+            per.setdefault((words[l] + e) % banks, set()).add(words[l] + e)
+    return max(len(v) for v in per.values())
+
+
+def test_b128_pass_partition_is_pinned_by_the_recorded_reads():
+    rows = [r for r in recorded_patterns() if r["mode"] == 4]
+    assert len(rows) >= 50
+
+    def parity(x):
+        return bin(x).count("1") & 1
+
+    fits = set()
+    for a in range(1, 64):
+        for b in range(a + 1, 64):
+            passes = [[l for l in range(64) if 2 * parity(l & a) + parity(l & b) == p] for p in range(4)]
+            if any(len(p) != 16 for p in passes):
+                continue
+            if all(close(max(4.0, sum(_degree(r["words"], p) for p in passes)), r["cycles_per_instr"], 4)
+                   for r in rows):
+                fits.add(tuple(sorted({a, b, a ^ b})))
+    # the half-wave bit with the parity of the 4-lane group index, bits 0 and 1 folded in or not
+    assert fits == {(28, 32, 60), (29, 32, 61), (30, 32, 62), (31, 32, 63)}
+    assert (16, 32, 48) not in fits  # a pass = lanes 16p..16p+15
+
+
+def test_library_passes_are_the_half_wave_and_group_parity(gemm_lib):
+    """gemm_lds_access_cycles prices every recorded 16-byte read, and the
+    kernels' reads, as the partition (lane bit 5, parity of lane bits 2-4)."""
+    passes = [[l for l in range(64) if 2 * ((l >> 5) & 1) + (bin(l & 28).count("1") & 1) == p] for p in range(4)]
+    words = [r["words"] for r in recorded_patterns() if r["mode"] == 4]
+    for v in dft.VARIANT_NAMES:
+        words += [w for _, mode, w in lds_probe.kernel_patterns(v) if mode == 4] if dft.gemm_f32_tile_config(v)["mfma_block"] else []
+    for w in words:
+        assert dft.gemm_lds_access_cycles(w, 4) == sum(_degree(w, p) for p in passes)
 
 
 def recorded_kernel_shares():
@@ -102,9 +142,6 @@ def test_model_matches_the_kernel_counters(gemm_lib):
         if dft.gemm_f32_tile_config(v)["mfma_block"] == 0:
             continue  # the vector-ALU kernel's accesses are not replayed
         predicted = model_share(v)
-        if name in KNOWN_KERNEL_GAPS:
-            assert predicted > 10 and share < 1, (name, predicted, share)
-        else:
-            assert abs(predicted - share) <= 5, (name, predicted, share)
+        assert abs(predicted - share) <= 5, (name, predicted, share)
         checked += 1
     assert checked >= 20
