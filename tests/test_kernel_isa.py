@@ -8,7 +8,10 @@ cross-compiled for gfx950 here.
 * The default MFMA kernel's K tile is straight-line code: every MFMA of a
   tile but the last step's (which runs after the barrier) sits in one block.
 * No packed fp32 instruction (v_pk_fma_f32, v_pk_mul_f32, v_pk_add_f32) is
-  emitted anywhere: the build disables them."""
+  emitted anywhere: the build disables them.
+* In the bf16 default kernel's K loop the LDS fragment reads for the next
+  step alternate one for one with the current step's MFMAs instead of
+  issuing in a burst ahead of them."""
 
 from __future__ import annotations
 
@@ -72,3 +75,27 @@ def test_m0_is_used_only_by_the_direct_copies(functions):
         assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", code[i]), code[i]
         assert code[i + 1] == "s_nop 0", code[i + 1]
         assert code[i + 2].startswith(("global_load_lds_dwordx4 ", "global_load_lds_dword ")), code[i + 2]
+
+
+def test_bf16_default_loop_alternates_mfmas_and_lds_reads(functions):
+    _, funcs = functions
+    # 256x256x64 tile, 8 waves of 128x64 (4 x 2 MFMA blocks of 32x32x16), 16-byte copies, 2 stages,
+    # pipelined across K tiles: the loop body holds steps 0..2 of a tile, 8 MFMAs and 8 reads each
+    default = [b for n, b in funcs.items() if "gemm_mixed_kernel" in n and
+               "MixedCfgILi0ELi256ELi256ELi64ELi128ELi64ELi32E" in n and n.endswith("ELi8ELi2ELi2ELi2EEEEEvlllPKtlS7_lPflll")]
+    assert len(default) == 1
+    blocks = re.split(r"^\.LBB\d+_\d+:", default[0], flags=re.M)
+
+    def order(block):
+        kinds = []
+        for line in block.splitlines():
+            op = line.strip()
+            if op.startswith("v_mfma"):
+                kinds.append("M")
+            elif op.startswith("ds_read"):
+                kinds.append("R")
+        return "".join(kinds)
+
+    loop = [o for o in map(order, blocks) if o.count("M") == 24 and "R" in o]
+    assert len(loop) == 1
+    assert loop[0] == "MR" * 24
