@@ -773,7 +773,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_WAVES) void gemm_mixed_kerne
                     else
                         wait_vector_memory();
                     __syncthreads();
-                    if (t + 1 < T) read_fragments(ns, 0, af[0], bf[0]);
+                    // (read on the last tile too, from a stage whose values go
+                    // unused, so that the reads share one block with the MFMAs
+                    // and alternate with them)
+                    read_fragments(ns, 0, af[0], bf[0]);
                     mma_step(af[1], bf[1]);
                     alternate_mfma_and_lds_reads<MI * NI>();
                     s = ns;

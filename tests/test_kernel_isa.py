@@ -80,7 +80,8 @@ def test_m0_is_used_only_by_the_direct_copies(functions):
 def test_bf16_default_loop_alternates_mfmas_and_lds_reads(functions):
     _, funcs = functions
     # 256x256x64 tile, 8 waves of 128x64 (4 x 2 MFMA blocks of 32x32x16), 16-byte copies, 2 stages,
-    # pipelined across K tiles: the loop body holds steps 0..2 of a tile, 8 MFMAs and 8 reads each
+    # pipelined across K tiles: one block holds steps 0..2 of a tile, 8 MFMAs and 8 reads each, and
+    # another the last step, after the barrier
     default = [b for n, b in funcs.items() if "gemm_mixed_kernel" in n and
                "MixedCfgILi0ELi256ELi256ELi64ELi128ELi64ELi32E" in n and n.endswith("ELi8ELi2ELi2ELi2EEEEEvlllPKtlS7_lPflll")]
     assert len(default) == 1
@@ -96,6 +97,9 @@ def test_bf16_default_loop_alternates_mfmas_and_lds_reads(functions):
                 kinds.append("R")
         return "".join(kinds)
 
-    loop = [o for o in map(order, blocks) if o.count("M") == 24 and "R" in o]
+    orders = list(map(order, blocks))
+    loop = [o for o in orders if o.count("M") == 24 and "R" in o]
     assert len(loop) == 1
     assert loop[0] == "MR" * 24
+    # the last step of a tile, after the barrier, with step 0 of the next tile's reads
+    assert "MR" * 8 in orders
